@@ -1,0 +1,240 @@
+"""Seeded synthetic inputs shaped like the source pages' workloads.
+
+This module draws random numbers and lays out batches; it holds none of the
+delta's arithmetic, and both the GPU path's tests/bench and the fp64 oracle
+consume what it returns.  Every generator is a pure function of its seed
+(numpy ``PCG64`` with ``SeedSequence.spawn`` sub-streams), so the oracle and
+the GPU see the same bits.
+
+Value recipe (the pages fix no distributions; these keep every intermediate
+O(1)): x ~ N(0, 1), A ~ N(0, 1/d_in), B ~ N(0, 1/r), y ~ N(0, 1), base
+W ~ N(0, 1/d_in); floats are drawn in fp32 and rounded to bf16 with
+round-to-nearest-even where the workload is bf16.
+
+Batch shapes follow "Multi-LoRA serving: the single translator with a thousand
+glossaries" (blog.lo0.es): ranks 8-64 (section "The bare mechanism"), the
+Llama-3-70B projection shapes (section "The maths that matters", table of
+bytes per matrix), the four-request heterogeneous example (figure in section
+"SGMV: the kernel that holds it all up"); and the skewed-popularity traffic of
+"Multi-LoRA Inference Serving" (clusterbid.com, paragraphs on adapter-aware
+batching and on Punica's 256 concurrent adapters).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+NO_ADAPTER = -1
+
+
+# --------------------------------------------------------------------------- bf16 bits
+def bf16_bits(f: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round-to-nearest-even) and return the 16-bit
+    patterns as uint16.  Inputs here are finite normals; NaN is kept quiet."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Reinterpret bf16 patterns as fp32 (exact)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    f = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        f *= np.float32(std)
+    return bf16_bits(f) if dtype == "bf16" else f
+
+
+# --------------------------------------------------------------------------- problem
+@dataclass
+class LoraProblem:
+    """One adapted projection over one batch.
+
+    ids[t] is the adapter of token t (-1 = none); adapter a has rank ranks[a],
+    A rows a_rows[a] ([r_a, d_in]) and B^T rows bt_rows[a] ([r_a, d_out]).
+    Element arrays are float32 (dtype "f32") or uint16 bf16 patterns ("bf16")."""
+    name: str
+    dtype: str
+    ids: np.ndarray
+    x: np.ndarray
+    y: np.ndarray
+    a_rows: List[np.ndarray]
+    bt_rows: List[np.ndarray]
+    ranks: np.ndarray
+    mode: str = "sgmv"            # "sgmv" (segmented) or "bgmv" (per-token decode)
+    paged: bool = False           # weights live in a shuffled page pool
+    page_rows: int = 16
+    pool_seed: int = 0
+    seg_lengths: Optional[np.ndarray] = None   # request-segment lengths in batch order
+    seg_ids: Optional[np.ndarray] = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.ids.size)
+
+    @property
+    def num_adapters(self) -> int:
+        return int(self.ranks.size)
+
+    @property
+    def d_in(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def d_out(self) -> int:
+        return int(self.y.shape[1])
+
+    @property
+    def r_max(self) -> int:
+        return int(self.ranks.max()) if self.ranks.size else 0
+
+
+def _seeds(seed: int, n: int):
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def zipf_lengths(rng: np.random.Generator, total: int, nseg: int, s: float = 1.1) -> np.ndarray:
+    """Segment lengths summing to ``total``: Multinomial(total, p_k ~ k^-s) over
+    k = 1..nseg; any empty segment takes one token from the current largest;
+    then the order is shuffled."""
+    k = np.arange(1, nseg + 1, dtype=np.float64)
+    p = k ** (-s)
+    p /= p.sum()
+    lengths = rng.multinomial(total, p).astype(np.int64)
+    for i in range(nseg):
+        if lengths[i] == 0:
+            j = int(np.argmax(lengths))
+            lengths[j] -= 1
+            lengths[i] = 1
+    rng.shuffle(lengths)
+    return lengths
+
+
+def _adapters(rng_a, rng_b, ranks, d_in, d_out, dtype):
+    """Per-adapter A [r, d_in] ~ N(0, 1/d_in) and B^T [r, d_out] with B ~ N(0, 1/r).
+    Every resident adapter gets rows, used in the batch or not."""
+    a_rows, bt_rows = [], []
+    for r in ranks:
+        r = int(r)
+        a_rows.append(_normal(rng_a, (r, d_in), 1.0 / np.sqrt(d_in), dtype))
+        bt_rows.append(_normal(rng_b, (r, d_out), 1.0 / np.sqrt(r), dtype))
+    return a_rows, bt_rows
+
+
+def make_problem(name: str, seg_lengths, seg_ids, ranks, d_in: int, d_out: int, dtype: str,
+                 seed: int, mode: str = "sgmv", paged: bool = False, page_rows: int = 16,
+                 ids: Optional[np.ndarray] = None) -> LoraProblem:
+    """Generic builder: requests are contiguous runs of tokens (seg_lengths[i]
+    tokens with adapter seg_ids[i], in batch order), unless ``ids`` is given."""
+    r_ids, r_x, r_y, r_a, r_b = _seeds(seed, 5)
+    ranks = np.asarray(ranks, dtype=np.int32)
+    if ids is None:
+        ids = np.repeat(np.asarray(seg_ids, dtype=np.int32), np.asarray(seg_lengths, dtype=np.int64))
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    t = ids.size
+    x = _normal(r_x, (t, d_in), 1.0, dtype)
+    y = _normal(r_y, (t, d_out), 1.0, dtype)
+    a_rows, bt_rows = _adapters(r_a, r_b, ranks, d_in, d_out, dtype)
+    return LoraProblem(name, dtype, ids, x, y, a_rows, bt_rows, ranks, mode=mode, paged=paged,
+                       page_rows=page_rows, pool_seed=seed,
+                       seg_lengths=None if seg_lengths is None else np.asarray(seg_lengths),
+                       seg_ids=None if seg_ids is None else np.asarray(seg_ids))
+
+
+# --------------------------------------------------------------------------- the five workloads
+def tiny_sgmv(seed: int = 1) -> LoraProblem:
+    """48 tokens as three requests of 16, 1 and 31 tokens on adapters 2, 0, 1;
+    three rank-8 adapters; 512 -> 512; fp32."""
+    return make_problem("tiny_sgmv_48tok_r8_512", [16, 1, 31], [2, 0, 1], [8, 8, 8], 512, 512,
+                        "f32", seed)
+
+
+def bgmv_decode(seed: int = 2, num_tokens: int = 256, num_adapters: int = 128, rank: int = 16,
+                d_in: int = 4096, d_out: int = 4096) -> LoraProblem:
+    """One token per request, adapter uniform over the resident rank-16 adapters;
+    4096 -> 4096; bf16; per-token (decode) mode."""
+    r_ids = _seeds(seed + 1000, 1)[0]
+    ids = r_ids.integers(0, num_adapters, size=num_tokens).astype(np.int32)
+    p = make_problem(f"bgmv_decode_{num_tokens}tok_{num_adapters}ad_r{rank}_{d_in}x{d_out}", None,
+                     None, [rank] * num_adapters, d_in, d_out, "bf16", seed, mode="bgmv", ids=ids)
+    return p
+
+
+def sgmv_prefill(seed: int = 3, shape: str = "q", num_tokens: int = 8192, num_segments: int = 32,
+                 resident: int = 64, rank: int = 16) -> LoraProblem:
+    """Zipf(1.1) request lengths, 32 requests on 32 distinct adapters drawn
+    without replacement from 64 resident rank-16 adapters; q (4096 -> 4096) or
+    MLP up (4096 -> 14336); bf16."""
+    d_in, d_out = {"q": (4096, 4096), "up": (4096, 14336)}[shape]
+    r_len, r_ids = _seeds(seed + 1000, 2)
+    lengths = zipf_lengths(r_len, num_tokens, num_segments)
+    seg_ids = r_ids.choice(resident, size=num_segments, replace=False).astype(np.int32)
+    return make_problem(f"sgmv_prefill_{shape}_{num_tokens}tok_{num_segments}seg_r{rank}",
+                        lengths, seg_ids, [rank] * resident, d_in, d_out, "bf16",
+                        seed + (0 if shape == "q" else 17))
+
+
+def hetero_paged(seed: int = 4, num_tokens: int = 4096, num_segments: int = 64, d: int = 8192,
+                 rank_choices=(8, 16, 32, 64)) -> LoraProblem:
+    """Zipf request lengths, one distinct adapter per request, ranks uniform on
+    {8, 16, 32, 64}; 8192 -> 8192; weights in a shuffled pool of 16-row pages."""
+    r_len, r_rank, r_perm = _seeds(seed + 1000, 3)
+    lengths = zipf_lengths(r_len, num_tokens, num_segments)
+    ranks = r_rank.choice(np.asarray(rank_choices), size=num_segments).astype(np.int32)
+    seg_ids = r_perm.permutation(num_segments).astype(np.int32)
+    return make_problem(f"hetero_paged_{num_tokens}tok_{num_segments}seg_{d}", lengths, seg_ids,
+                        ranks, d, d, "bf16", seed, paged=True, page_rows=16)
+
+
+LAYER_70B = [  # (name, d_in, d_out): Llama-3-70B projections, rank-16 table
+    ("q", 8192, 8192), ("k", 8192, 1024), ("v", 8192, 1024), ("o", 8192, 8192),
+    ("gate", 8192, 28672), ("up", 8192, 28672), ("down", 28672, 8192),
+]
+
+
+def layer_batch_ids(seed: int = 5, decode: int = 256, prefill: int = 1024) -> np.ndarray:
+    """256 decode tokens on a permutation of 256 adapters, then a 1024-token
+    prefill request on adapter 0 (the most popular one)."""
+    r = _seeds(seed + 1000, 1)[0]
+    dec = r.permutation(decode).astype(np.int32)
+    return np.concatenate([dec, np.zeros(prefill, dtype=np.int32)])
+
+
+def layer_projection(name: str, seed: int = 5, num_adapters: int = 256, rank: int = 16,
+                     decode: int = 256, prefill: int = 1024, with_base: bool = True) -> LoraProblem:
+    """One projection of the 70B-shape decoder layer: 1280 tokens, 256 rank-16
+    adapters, base weight W [d_out, d_in] ~ N(0, 1/d_in) in ``extra['w']``."""
+    idx = [n for n, _, _ in LAYER_70B].index(name)
+    _, d_in, d_out = LAYER_70B[idx]
+    ids = layer_batch_ids(seed, decode, prefill)
+    p = make_problem(f"layer70b_{name}_{d_in}x{d_out}", None, None, [rank] * num_adapters, d_in,
+                     d_out, "bf16", seed * 100 + idx, ids=ids)
+    if with_base:
+        rw = _seeds(seed * 100 + idx + 50, 1)[0]
+        p.extra["w"] = _normal(rw, (d_out, d_in), 1.0 / np.sqrt(d_in), "bf16")
+    return p
+
+
+def config(n: int, **kw) -> LoraProblem:
+    """The workload of config n (1..4).  Config 5 is a set of projections: use
+    ``layer_projection``."""
+    if n == 1:
+        return tiny_sgmv(**kw)
+    if n == 2:
+        return bgmv_decode(**kw)
+    if n == 3:
+        return sgmv_prefill(**kw)
+    if n == 4:
+        return hetero_paged(**kw)
+    raise ValueError("config 5 is built per projection by layer_projection()")
