@@ -1,0 +1,271 @@
+/*
+ * lora_sgmv.h -- C ABI of the MI355X (gfx950) multi-LoRA delta path.
+ *
+ * What is computed.  For every token t of a batch whose tokens carry
+ * different LoRA adapters, add the adapter's low-rank correction to the
+ * layer's output:
+ *
+ *     y_t  <-  y_t + B_{a(t)} ( A_{a(t)} x_t )
+ *
+ * with A_a in R^{r_a x d_in}, B_a in R^{d_out x r_a}; the product B A is never
+ * formed.  Sources: "Multi-LoRA serving: the single translator with a thousand
+ * glossaries" (blog.lo0.es), section "The bare mechanism" (y = Wx + B(Ax), the
+ * shapes of A and B) and section "SGMV: the kernel that holds it all up" (the
+ * per-token equation y_t = W x_t + B_{a(t)} A_{a(t)} x_t, its two phases
+ * shrink d_in -> r and expand r -> d_out, grouping tokens by adapter, one
+ * launch for every adapter of the batch, tensor cores for large segments and a
+ * batched gather path for small ones).  y_t enters holding the base term W x_t.
+ *
+ * Storage conventions (shared by every entry point):
+ *   - x [T, d_in] and y [T, d_out] are row-major device arrays indexed by the
+ *     token's ORIGINAL position in the batch; element type = lora_weights.dtype.
+ *   - v [T, r_max] is a row-major fp32 device array (the rank-space
+ *     intermediate A x, never rounded to bf16).  Entries j >= r_{a(t)} and rows
+ *     of tokens without an adapter are not written.
+ *   - A_a is stored as r_a rows of length d_in ("A rows"); B_a as its transpose,
+ *     r_a rows of length d_out ("B^T rows").  Rows live in pages of page_rows
+ *     rows each; a per-adapter page table names the pages (S-LoRA-style unified
+ *     paging: "Multi-LoRA serving ..." TL;DR and section "Operational pitfalls",
+ *     memory fragmentation; and the glossary entry "Multi-LoRA Serving",
+ *     skillsintelligence.tools, intro paragraph).  Dense per-adapter stacks are
+ *     the special case page_rows >= r_max with a NULL page table (page a holds
+ *     adapter a).
+ *   - No alpha/r scale is applied: a caller that wants one pre-scales B.
+ *   - Adapter id LORA_NO_ADAPTER (-1) means the token has no adapter: its y row
+ *     is left bit-unchanged ("Multi-LoRA Inference Serving", clusterbid.com,
+ *     paragraph on vLLM's adapter pool: only a request that names an adapter
+ *     gets one).
+ *   - bf16 arithmetic: products and sums in fp32; y is rounded once, to nearest
+ *     even, when stored.  fp32 workloads compute in fp32 throughout.
+ *
+ * Calls and errors.
+ *   - Every function returns a lora_status; LORA_OK == 0.  On any error nothing
+ *     is launched and no output is touched; lora_last_error() gives a message
+ *     (thread-local, valid until the thread's next call into the library).
+ *   - Host-side functions (segments, plan, pool bookkeeping) are synchronous
+ *     and need no GPU.  Device-side functions enqueue work on `stream` (the
+ *     caller's HIP stream; 0 = default) and return without synchronising.
+ *   - The library allocates no device memory on any call below; every buffer
+ *     is caller-owned.  Pointers to device arrays must be 16-byte aligned, and
+ *     d_in and d_out multiples of 8.
+ *   - Each y element is written by exactly one GPU thread, with no atomics, so
+ *     results are bit-identical from run to run.
+ *   - Device-resident indices (token_perm, plan items, page tables, per-token
+ *     adapter ids) are checked by the kernels: an out-of-range value makes the
+ *     affected token or row contribute nothing instead of reading out of
+ *     bounds.  Outputs for such tokens are then unspecified.
+ */
+#ifndef LORA_SGMV_H
+#define LORA_SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+
+typedef int32_t lora_status;
+#define LORA_OK 0
+#define LORA_EINVAL (-1)        /* null pointer, negative size, misalignment, inconsistent sizes */
+#define LORA_ERANGE (-2)        /* a host-visible adapter id outside {-1} U [0, num_adapters) */
+#define LORA_EUNSUPPORTED (-3)  /* rank outside 1..LORA_MAX_RANK, d not a multiple of 8, unknown dtype */
+#define LORA_ENOMEM (-4)        /* page pool exhausted, or an output array too small */
+#define LORA_EHIP (-5)          /* a HIP runtime error; its text is in lora_last_error() */
+
+#define LORA_F32 0
+#define LORA_BF16 1
+
+#define LORA_NO_ADAPTER (-1)
+#define LORA_MAX_RANK 128
+
+int32_t lora_abi_version(void);
+const char *lora_last_error(void);
+const char *lora_status_name(lora_status status);
+
+/* ------------------------------------------------------------------------ */
+/* Segment build (host).  Groups the batch's tokens by adapter: ascending
+ * adapter id, original token order inside a segment, tokens with id -1
+ * skipped ("SGMV: the kernel that holds it all up": SGMV groups the batch's
+ * tokens by adapter; TL;DR: one pass grouping requests by adapter).  Stable
+ * counting sort, O(T + N).
+ *   token_adapter [num_tokens]     in : adapter per token (-1 = none)
+ *   token_perm    [num_tokens]     out: the T' adapted tokens, segment by segment
+ *   seg_starts    [num_tokens + 1] out: segment s is token_perm[seg_starts[s] ..
+ *                                       seg_starts[s+1]); seg_starts[S] = T'
+ *   seg_adapter   [num_tokens]     out: adapter of segment s (strictly increasing)
+ *   num_segments                   out: S
+ * All arrays are caller-owned host memory with the capacities shown.
+ * Errors: LORA_EINVAL (null pointer with num_tokens > 0, negative sizes),
+ * LORA_ERANGE (an id outside {-1} U [0, num_adapters)); outputs untouched. */
+lora_status lora_segments_build(const int32_t *token_adapter, int32_t num_tokens,
+                                int32_t num_adapters, int32_t *token_perm,
+                                int32_t *seg_starts, int32_t *seg_adapter,
+                                int32_t *num_segments);
+
+/* ------------------------------------------------------------------------ */
+/* Work plan (host).  One launch per phase covers every segment of the batch
+ * ("SGMV ..." section: the correct delta for every token in a single kernel
+ * pass; "Multi-LoRA Inference Serving": blocks from several adapters
+ * dispatched onto different compute units by one launch).  Each segment takes
+ * the MFMA path when it holds at least `mfma_min_tokens` tokens and the
+ * gather/GEMV path otherwise (the page's size-dependent choice: tensor cores
+ * for large segments, batched gather for one-request segments).  The plan is a
+ * flat list of work items, heaviest first, that covers every (token, output)
+ * pair of the batch exactly once; item k is executed by workgroup k.
+ *
+ * Items do not depend on the adapters' ranks.  A shrink plan does not depend
+ * on d_in; an expand plan depends on d_out (its column blocks).  A plan stays
+ * valid for every layer and projection with the same segments (and, for
+ * expand, the same d_out): build once per batch, upload once, launch many.   */
+typedef struct {
+  int32_t perm_begin;  /* first token of the item, as an index into token_perm */
+  int32_t adapter;     /* adapter of the item's segment */
+  int32_t count_path;  /* token count (bits 0..15) | path << 16 */
+  int32_t block;       /* expand: column block index; shrink: 0 */
+} lora_item;
+
+#define LORA_PHASE_SHRINK 0
+#define LORA_PHASE_EXPAND 1
+
+#define LORA_PATH_AUTO 0    /* policy: choose per segment by length */
+#define LORA_PATH_GATHER 1  /* policy: every segment on the gather/GEMV path */
+#define LORA_PATH_MFMA 2    /* policy: every segment on the MFMA path */
+
+#define LORA_DEFAULT_MFMA_MIN_TOKENS 16
+
+/* Tokens per item and columns per expand item, by path.  */
+#define LORA_SHRINK_GATHER_TOKENS 4
+#define LORA_SHRINK_MFMA_TOKENS 16
+#define LORA_EXPAND_GATHER_TOKENS 4
+#define LORA_EXPAND_MFMA_TOKENS 64
+#define LORA_EXPAND_GATHER_COLS 512
+#define LORA_EXPAND_MFMA_COLS 256
+
+/* Builds the plan for `phase` from the host copies of segment_build's output.
+ *   dim            expand: d_out (sets the column blocks); shrink: d_in (unused)
+ *   path_policy    LORA_PATH_AUTO / _GATHER / _MFMA
+ *   mfma_min_tokens  AUTO threshold (<= 0 selects LORA_DEFAULT_MFMA_MIN_TOKENS)
+ *   items, capacity  caller-owned host array; with items == NULL only the item
+ *                    count is returned (in *num_items)
+ * Errors: LORA_EINVAL (bad sizes, non-increasing seg_starts, unknown policy or
+ * phase), LORA_ERANGE (a segment adapter outside [0, num_adapters)),
+ * LORA_ENOMEM (capacity too small; *num_items still holds the needed count). */
+lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
+                           const int32_t *seg_adapter, int32_t num_segments,
+                           int32_t num_adapters, int32_t dim, int32_t path_policy,
+                           int32_t mfma_min_tokens, lora_item *items, int32_t capacity,
+                           int32_t *num_items);
+
+/* ------------------------------------------------------------------------ */
+/* Adapter weights as the kernels read them (the adapter-row gather through the
+ * page table).  Row j of adapter a's A lives at
+ *     a_pages + ((a_page_table[a*max_pages + j/page_rows]) * page_rows
+ *                + j % page_rows) * d_in            (elements)
+ * and row j of its B^T likewise in b_pages with width d_out.  With a NULL
+ * page table the page index is the adapter id (dense stack: page_rows >= r_max,
+ * max_pages ignored).  Rows j >= rank[a] of a page are never read.  */
+typedef struct {
+  int32_t dtype;         /* LORA_F32 or LORA_BF16: element type of x, y, A, B */
+  int32_t d_in, d_out;   /* multiples of 8 */
+  int32_t num_adapters;  /* N: valid adapter ids are 0..N-1 */
+  int32_t r_max;         /* every rank <= r_max <= LORA_MAX_RANK; row stride of v */
+  int32_t page_rows;     /* rows per page (> 0) */
+  int32_t max_pages;     /* page-table row length (pages per adapter) */
+  int32_t num_pages_a;   /* pages in a_pages (bounds for page ids) */
+  int32_t num_pages_b;   /* pages in b_pages */
+  int32_t reserved;      /* must be 0 */
+  const void *a_pages;   /* device [num_pages_a][page_rows][d_in]  */
+  const void *b_pages;   /* device [num_pages_b][page_rows][d_out] (rows of B^T) */
+  const int32_t *rank;   /* device [N]: rank of each adapter (1..r_max) */
+  const int32_t *a_page_table; /* device [N][max_pages] or NULL (dense) */
+  const int32_t *b_page_table; /* device [N][max_pages] or NULL (dense) */
+  const int32_t *host_rank;    /* host [N] copy of rank, or NULL; when given it is
+                                  validated (1..r_max) before launch */
+} lora_weights;
+
+/* ------------------------------------------------------------------------ */
+/* Segmented (SGMV) mode: the batch arrives grouped by lora_segments_build and
+ * planned by lora_sgmv_plan (items uploaded to device memory by the caller).
+ *
+ * Shrink ("SGMV ..." section, phase 1, projection d_in -> r through A_{a(t)}):
+ *     v[t][j] = sum_k A_{a(t)}[j][k] * x[t][k]        for j < r_{a(t)}
+ * Expand (phase 2, projection r -> d_out through B_{a(t)}, added into y):
+ *     y[t][i] = round( y[t][i] + sum_j B_{a(t)}[i][j] * v[t][j] )
+ *   token_perm [num_perm]   device; token indices in [0, num_tokens)
+ *   items      [num_items]  device; a plan of the matching phase
+ * num_items == 0 or num_tokens == 0 is a no-op.  Errors: LORA_EINVAL,
+ * LORA_EUNSUPPORTED, LORA_ERANGE (host_rank out of 1..r_max), LORA_EHIP.   */
+lora_status lora_sgmv_shrink(const lora_weights *w, const int32_t *token_perm, int32_t num_perm,
+                             const lora_item *items, int32_t num_items, int32_t num_tokens,
+                             const void *x, float *v, hipStream_t stream);
+lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, int32_t num_perm,
+                             const lora_item *items, int32_t num_items, int32_t num_tokens,
+                             const float *v, void *y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Per-token (BGMV, decode) mode: adapter ids stay on the device, no host
+ * planning and no host synchronisation; every token takes the gather/GEMV path
+ * (S-LoRA's decode kernel, MBGMV, in the same section: mixed ranks in one
+ * batch).  Same arithmetic as the segmented calls.
+ *   token_adapter [num_tokens]  device; ids outside [0, N) (and -1) are skipped
+ *   order  LORA_BGMV_AUTO, _TOKEN_MAJOR (one workgroup per token) or
+ *          _ADAPTER_MAJOR (one workgroup per adapter and block: each adapter's
+ *          rows are read once however many tokens use it).                  */
+#define LORA_BGMV_AUTO 0
+#define LORA_BGMV_TOKEN_MAJOR 1
+#define LORA_BGMV_ADAPTER_MAJOR 2
+lora_status lora_bgmv_shrink(const lora_weights *w, const int32_t *token_adapter,
+                             int32_t num_tokens, int32_t order, const void *x, float *v,
+                             hipStream_t stream);
+lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *token_adapter,
+                             int32_t num_tokens, int32_t order, const float *v, void *y,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Paged adapter pool (host bookkeeping over caller-owned device storage of
+ * [num_pages][page_rows][row_width] elements).  Pages are handed out from a
+ * free list shuffled by `shuffle_seed` (0 = in order), so an adapter's pages
+ * are scattered through the pool as they are after churn; freed pages return
+ * to the back of the list.  Sources: the unified paging of adapter weights
+ * ("Multi-LoRA serving ..." TL;DR; section "Operational pitfalls", memory
+ * fragmentation) and the fixed-size adapter pool of "Multi-LoRA Inference
+ * Serving" (clusterbid.com).  A lora_pool object is not thread-safe.        */
+typedef struct lora_pool lora_pool;
+lora_status lora_pool_create(int32_t num_pages, int32_t page_rows, int32_t row_width,
+                             int32_t dtype, void *device_storage, uint64_t shuffle_seed,
+                             lora_pool **out);
+/* Takes ceil(rows / page_rows) pages; ids written to page_ids.  LORA_ENOMEM if
+ * too few pages are free (nothing taken). */
+lora_status lora_pool_alloc(lora_pool *pool, int32_t rows, int32_t *page_ids);
+/* Returns pages to the pool.  LORA_EINVAL on an id that is not currently taken
+ * (nothing freed). */
+lora_status lora_pool_free(lora_pool *pool, const int32_t *page_ids, int32_t num_pages);
+lora_status lora_pool_num_free(const lora_pool *pool, int32_t *num_free);
+/* Copies `rows` rows of row_width elements from src (host or device memory)
+ * into the pages, page_rows rows per page, asynchronously on `stream`.  A host
+ * source must stay valid until the stream has passed this point. */
+lora_status lora_pool_write_rows(lora_pool *pool, const int32_t *page_ids, int32_t rows,
+                                 const void *src, hipStream_t stream);
+void lora_pool_destroy(lora_pool *pool);
+
+/* ------------------------------------------------------------------------ */
+/* Base projection y = x W^T computed once for every token of the batch, the
+ * term the adapters' deltas are added to ("Multi-LoRA serving ...", section
+ * "The bare mechanism": Wx is computed only once for all the tokens; W in
+ * R^{d_out x d_in}).  bf16 in, fp32 accumulation (MFMA), bf16 out rounded to
+ * nearest even.
+ *   x [m][k], w [n][k], y [m][n]: row-major device arrays; k, n multiples of 8.
+ * Errors: LORA_EINVAL, LORA_EUNSUPPORTED (dtype other than LORA_BF16), LORA_EHIP. */
+lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *x,
+                           const void *w, void *y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_SGMV_H */

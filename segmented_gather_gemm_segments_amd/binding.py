@@ -1,0 +1,279 @@
+"""Thin ctypes binding over ``liblora_sgmv.so`` -- argument marshalling only.
+
+Functions carry the C names of ``include/lora_sgmv.h``.  Every step of the
+delta path runs in the library's kernels; PyTorch supplies device memory and
+the current HIP stream.  The library must have been built
+(``python -m segmented_gather_gemm_segments_amd.build``); if it is missing this
+module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+LORA_OK, LORA_EINVAL, LORA_ERANGE, LORA_EUNSUPPORTED, LORA_ENOMEM, LORA_EHIP = 0, -1, -2, -3, -4, -5
+LORA_F32, LORA_BF16 = 0, 1
+LORA_NO_ADAPTER = -1
+LORA_MAX_RANK = 128
+LORA_PHASE_SHRINK, LORA_PHASE_EXPAND = 0, 1
+LORA_PATH_AUTO, LORA_PATH_GATHER, LORA_PATH_MFMA = 0, 1, 2
+LORA_BGMV_AUTO, LORA_BGMV_TOKEN_MAJOR, LORA_BGMV_ADAPTER_MAJOR = 0, 1, 2
+LORA_DEFAULT_MFMA_MIN_TOKENS = 16
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+class lora_item(ctypes.Structure):
+    _fields_ = [("perm_begin", ctypes.c_int32), ("adapter", ctypes.c_int32),
+                ("count_path", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+class lora_weights(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("num_adapters", ctypes.c_int32), ("r_max", ctypes.c_int32),
+                ("page_rows", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("num_pages_a", ctypes.c_int32), ("num_pages_b", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("a_pages", ctypes.c_void_p), ("b_pages", ctypes.c_void_p),
+                ("rank", ctypes.c_void_p), ("a_page_table", ctypes.c_void_p),
+                ("b_page_table", ctypes.c_void_p), ("host_rank", ctypes.c_void_p)]
+
+
+_lib = None
+_P, _I32, _U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+
+EXPORTS = {
+    "lora_abi_version": ([], _I32),
+    "lora_last_error": ([], ctypes.c_char_p),
+    "lora_status_name": ([_I32], ctypes.c_char_p),
+    "lora_segments_build": ([_P, _I32, _I32, _P, _P, _P, _P], _I32),
+    "lora_sgmv_plan": ([_I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P], _I32),
+    "lora_sgmv_shrink": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
+    "lora_sgmv_expand": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
+    "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
+    "lora_bgmv_expand": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
+    "lora_pool_create": ([_I32, _I32, _I32, _I32, _P, _U64, _P], _I32),
+    "lora_pool_alloc": ([_P, _I32, _P], _I32),
+    "lora_pool_free": ([_P, _P, _I32], _I32),
+    "lora_pool_num_free": ([_P, _P], _I32),
+    "lora_pool_write_rows": ([_P, _P, _I32, _P, _P], _I32),
+    "lora_pool_destroy": ([_P], None),
+    "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
+}
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(f"{_build.LIB} is missing: build it with "
+                               "`python -m segmented_gather_gemm_segments_amd.build`")
+        h = ctypes.CDLL(_build.LIB)
+        for name, (args, res) in EXPORTS.items():
+            f = getattr(h, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = h
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return lib().lora_status_name(status).decode()
+
+
+def lora_last_error() -> str:
+    return lib().lora_last_error().decode()
+
+
+def _check(status: int):
+    if status != LORA_OK:
+        raise LoraError(status, lora_last_error())
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+# ---------------------------------------------------------------- host calls
+def lora_segments_build(token_adapter, num_adapters: int):
+    """Host segment build.  Returns (token_perm, seg_starts, seg_adapter)."""
+    ids = _i32(token_adapter)
+    t = ids.size
+    perm = np.empty(max(t, 1), np.int32)
+    starts = np.empty(t + 1, np.int32)
+    adapters = np.empty(max(t, 1), np.int32)
+    s = ctypes.c_int32(0)
+    _check(lib().lora_segments_build(_np_ptr(ids), t, num_adapters, _np_ptr(perm), _np_ptr(starts),
+                                     _np_ptr(adapters), ctypes.byref(s)))
+    s = s.value
+    return perm[: starts[s]].copy(), starts[: s + 1].copy(), adapters[:s].copy()
+
+
+def lora_sgmv_plan(phase: int, seg_starts, seg_adapter, num_adapters: int, dim: int,
+                   path_policy: int = LORA_PATH_AUTO,
+                   mfma_min_tokens: int = LORA_DEFAULT_MFMA_MIN_TOKENS) -> np.ndarray:
+    """Work plan as an int32 array [num_items, 4] (perm_begin, adapter, count|path<<16, block)."""
+    starts, adapters = _i32(seg_starts), _i32(seg_adapter)
+    s = adapters.size
+    n = ctypes.c_int32(0)
+    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters, dim,
+                                path_policy, mfma_min_tokens, None, 0, ctypes.byref(n)))
+    items = np.zeros((max(n.value, 1), 4), np.int32)
+    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters, dim,
+                                path_policy, mfma_min_tokens, _np_ptr(items), n.value,
+                                ctypes.byref(n)))
+    return items[: n.value]
+
+
+# ---------------------------------------------------------------- device helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Weights:
+    """Device-resident adapter weights plus the lora_weights descriptor.
+
+    ``a_pages`` [num_pages_a, page_rows, d_in] and ``b_pages`` [num_pages_b,
+    page_rows, d_out] are torch tensors (bf16 or fp32); ``rank`` int32 [N] on
+    device; page tables int32 [N, max_pages] on device or None (dense stack:
+    page a = adapter a)."""
+    dtype: int
+    d_in: int
+    d_out: int
+    r_max: int
+    page_rows: int
+    a_pages: object
+    b_pages: object
+    rank: object
+    host_rank: np.ndarray
+    a_page_table: object = None
+    b_page_table: object = None
+    max_pages: int = 1
+
+    @property
+    def num_adapters(self) -> int:
+        return int(self.host_rank.size)
+
+    def desc(self) -> lora_weights:
+        self._host_rank_c = _i32(self.host_rank)
+        return lora_weights(
+            self.dtype, self.d_in, self.d_out, self.num_adapters, self.r_max, self.page_rows,
+            self.max_pages, int(self.a_pages.shape[0]), int(self.b_pages.shape[0]), 0,
+            _dptr(self.a_pages), _dptr(self.b_pages), _dptr(self.rank), _dptr(self.a_page_table),
+            _dptr(self.b_page_table), self._host_rank_c.ctypes.data)
+
+
+def lora_sgmv_shrink(w: Weights, token_perm, items, x, v, num_tokens: Optional[int] = None,
+                     stream=None):
+    d = w.desc()
+    n_tok = x.shape[0] if num_tokens is None else num_tokens
+    _check(lib().lora_sgmv_shrink(ctypes.byref(d), _dptr(token_perm), int(token_perm.numel()),
+                                  _dptr(items), int(items.shape[0]), n_tok, _dptr(x), _dptr(v),
+                                  _stream(stream)))
+
+
+def lora_sgmv_expand(w: Weights, token_perm, items, v, y, num_tokens: Optional[int] = None,
+                     stream=None):
+    d = w.desc()
+    n_tok = y.shape[0] if num_tokens is None else num_tokens
+    _check(lib().lora_sgmv_expand(ctypes.byref(d), _dptr(token_perm), int(token_perm.numel()),
+                                  _dptr(items), int(items.shape[0]), n_tok, _dptr(v), _dptr(y),
+                                  _stream(stream)))
+
+
+def lora_bgmv_shrink(w: Weights, token_adapter, x, v, order: int = LORA_BGMV_AUTO, stream=None):
+    d = w.desc()
+    _check(lib().lora_bgmv_shrink(ctypes.byref(d), _dptr(token_adapter), int(token_adapter.numel()),
+                                  order, _dptr(x), _dptr(v), _stream(stream)))
+
+
+def lora_bgmv_expand(w: Weights, token_adapter, v, y, order: int = LORA_BGMV_AUTO, stream=None):
+    d = w.desc()
+    _check(lib().lora_bgmv_expand(ctypes.byref(d), _dptr(token_adapter), int(token_adapter.numel()),
+                                  order, _dptr(v), _dptr(y), _stream(stream)))
+
+
+def lora_base_gemm(x, w, y, stream=None):
+    m, k = x.shape
+    n = w.shape[0]
+    _check(lib().lora_base_gemm(LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y), _stream(stream)))
+
+
+class Pool:
+    """lora_pool over caller-owned device storage (a torch tensor
+    [num_pages, page_rows, row_width])."""
+
+    def __init__(self, storage, page_rows: int, shuffle_seed: int = 0):
+        self.storage = storage
+        num_pages, pr, width = storage.shape
+        assert pr == page_rows
+        torch = _torch()
+        dtype = LORA_BF16 if storage.dtype == torch.bfloat16 else LORA_F32
+        self.page_rows = page_rows
+        h = ctypes.c_void_p()
+        _check(lib().lora_pool_create(num_pages, page_rows, width, dtype, _dptr(storage),
+                                      shuffle_seed, ctypes.byref(h)))
+        self._h = h
+
+    def alloc(self, rows: int) -> np.ndarray:
+        ids = np.empty((rows + self.page_rows - 1) // self.page_rows, np.int32)
+        _check(lib().lora_pool_alloc(self._h, rows, _np_ptr(ids)))
+        return ids
+
+    def free(self, page_ids):
+        ids = _i32(page_ids)
+        _check(lib().lora_pool_free(self._h, _np_ptr(ids), ids.size))
+
+    def num_free(self) -> int:
+        n = ctypes.c_int32(0)
+        _check(lib().lora_pool_num_free(self._h, ctypes.byref(n)))
+        return n.value
+
+    def write_rows(self, page_ids, src, stream=None):
+        """src: torch tensor [rows, row_width] on device (or pinned host)."""
+        ids = _i32(page_ids)
+        _check(lib().lora_pool_write_rows(self._h, _np_ptr(ids), int(src.shape[0]), _dptr(src),
+                                          _stream(stream)))
+
+    def close(self):
+        if self._h:
+            lib().lora_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,287 @@
+// Host half of the C ABI: error reporting, the segment build, the one-launch
+// work planner and the paged adapter pool's bookkeeping.  Nothing here touches
+// the GPU except lora_pool_write_rows (async copies on the caller's stream).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lora_internal.h"
+
+namespace lora {
+
+static thread_local std::string g_last_error;
+
+lora_status fail(lora_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+lora_status ok() {
+  g_last_error.clear();
+  return LORA_OK;
+}
+
+lora_status hip_fail(hipError_t e, const char *what) {
+  return fail(LORA_EHIP, "%s: %s (%s)", what, hipGetErrorString(e), hipGetErrorName(e));
+}
+
+}  // namespace lora
+
+using namespace lora;
+
+extern "C" int32_t lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+extern "C" const char *lora_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char *lora_status_name(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_EINVAL: return "LORA_EINVAL";
+    case LORA_ERANGE: return "LORA_ERANGE";
+    case LORA_EUNSUPPORTED: return "LORA_EUNSUPPORTED";
+    case LORA_ENOMEM: return "LORA_ENOMEM";
+    case LORA_EHIP: return "LORA_EHIP";
+    default: return "LORA_UNKNOWN";
+  }
+}
+
+// --------------------------------------------------------------------------
+// Segment build: stable counting sort by adapter id.
+extern "C" lora_status lora_segments_build(const int32_t *token_adapter, int32_t num_tokens,
+                                           int32_t num_adapters, int32_t *token_perm,
+                                           int32_t *seg_starts, int32_t *seg_adapter,
+                                           int32_t *num_segments) {
+  if (num_tokens < 0 || num_adapters < 0) return fail(LORA_EINVAL, "negative size");
+  if (!seg_starts || !num_segments) return fail(LORA_EINVAL, "null seg_starts/num_segments");
+  if (num_tokens > 0 && (!token_adapter || !token_perm || !seg_adapter))
+    return fail(LORA_EINVAL, "null pointer with num_tokens > 0");
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    int32_t a = token_adapter[t];
+    if (a != LORA_NO_ADAPTER && (a < 0 || a >= num_adapters))
+      return fail(LORA_ERANGE, "token %d has adapter id %d outside {-1} U [0, %d)", t, a,
+                  num_adapters);
+  }
+  // count tokens per adapter, then exclusive prefix sum -> first slot per adapter
+  std::vector<int32_t> count((size_t)num_adapters + 1, 0);
+  for (int32_t t = 0; t < num_tokens; ++t)
+    if (token_adapter[t] >= 0) ++count[(size_t)token_adapter[t]];
+  std::vector<int32_t> slot((size_t)num_adapters + 1, 0);
+  int32_t S = 0, run = 0;
+  for (int32_t a = 0; a < num_adapters; ++a) {
+    slot[(size_t)a] = run;
+    if (count[(size_t)a] > 0) {
+      seg_starts[S] = run;
+      seg_adapter[S] = a;
+      ++S;
+    }
+    run += count[(size_t)a];
+  }
+  seg_starts[S] = run;
+  // scatter in original order: tokens of one adapter keep their batch order
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    int32_t a = token_adapter[t];
+    if (a >= 0) token_perm[slot[(size_t)a]++] = t;
+  }
+  *num_segments = S;
+  return ok();
+}
+
+// --------------------------------------------------------------------------
+// Work planner.
+namespace {
+
+struct PlanItem {
+  lora_item item;
+  int64_t weight;  // estimated bytes the item moves, for heaviest-first order
+};
+
+}  // namespace
+
+extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
+                                      const int32_t *seg_adapter, int32_t num_segments,
+                                      int32_t num_adapters, int32_t dim, int32_t path_policy,
+                                      int32_t mfma_min_tokens, lora_item *items, int32_t capacity,
+                                      int32_t *num_items) {
+  if (!num_items) return fail(LORA_EINVAL, "null num_items");
+  if (phase != LORA_PHASE_SHRINK && phase != LORA_PHASE_EXPAND)
+    return fail(LORA_EINVAL, "unknown phase %d", phase);
+  if (path_policy < LORA_PATH_AUTO || path_policy > LORA_PATH_MFMA)
+    return fail(LORA_EINVAL, "unknown path policy %d", path_policy);
+  if (num_segments < 0 || capacity < 0) return fail(LORA_EINVAL, "negative size");
+  if (num_segments > 0 && (!seg_starts || !seg_adapter))
+    return fail(LORA_EINVAL, "null segment arrays");
+  if (phase == LORA_PHASE_EXPAND && (dim <= 0 || dim % 8 != 0))
+    return fail(LORA_EUNSUPPORTED, "expand plan needs d_out > 0 and a multiple of 8 (got %d)",
+                dim);
+  if (mfma_min_tokens <= 0) mfma_min_tokens = LORA_DEFAULT_MFMA_MIN_TOKENS;
+  if (num_segments > 0 && seg_starts[0] < 0) return fail(LORA_EINVAL, "seg_starts[0] < 0");
+  for (int32_t s = 0; s < num_segments; ++s) {
+    if (seg_starts[s + 1] <= seg_starts[s])
+      return fail(LORA_EINVAL, "seg_starts not strictly increasing at %d", s);
+    if (seg_adapter[s] < 0 || seg_adapter[s] >= num_adapters)
+      return fail(LORA_ERANGE, "segment %d has adapter %d outside [0, %d)", s, seg_adapter[s],
+                  num_adapters);
+  }
+  std::vector<PlanItem> plan;
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int32_t begin = seg_starts[s], len = seg_starts[s + 1] - seg_starts[s];
+    const bool mfma = path_policy == LORA_PATH_MFMA ||
+                      (path_policy == LORA_PATH_AUTO && len >= mfma_min_tokens);
+    const int32_t path = mfma ? LORA_PATH_MFMA : LORA_PATH_GATHER;
+    if (phase == LORA_PHASE_SHRINK) {
+      const int32_t step = mfma ? LORA_SHRINK_MFMA_TOKENS : LORA_SHRINK_GATHER_TOKENS;
+      for (int32_t m0 = 0; m0 < len; m0 += step) {
+        int32_t cnt = std::min(step, len - m0);
+        // an MFMA item reads its adapter's rows once per 16 tokens, a gather
+        // item once per <= 4 tokens; both read each token's x row once
+        PlanItem p{{begin + m0, seg_adapter[s], cnt | (path << 16), 0},
+                   (int64_t)cnt * 2 + (mfma ? 16 : 8)};
+        plan.push_back(p);
+      }
+    } else {
+      const int32_t step = mfma ? LORA_EXPAND_MFMA_TOKENS : LORA_EXPAND_GATHER_TOKENS;
+      const int32_t cols = mfma ? LORA_EXPAND_MFMA_COLS : LORA_EXPAND_GATHER_COLS;
+      const int32_t nblk = (dim + cols - 1) / cols;
+      for (int32_t m0 = 0; m0 < len; m0 += step) {
+        int32_t cnt = std::min(step, len - m0);
+        for (int32_t b = 0; b < nblk; ++b) {
+          int32_t c = std::min(cols, dim - b * cols);
+          PlanItem p{{begin + m0, seg_adapter[s], cnt | (path << 16), b},
+                     (int64_t)c * (4 * cnt + 32)};
+          plan.push_back(p);
+        }
+      }
+    }
+  }
+  std::stable_sort(plan.begin(), plan.end(),
+                   [](const PlanItem &a, const PlanItem &b) { return a.weight > b.weight; });
+  if (plan.size() > (size_t)INT32_MAX) return fail(LORA_ENOMEM, "plan too large");
+  *num_items = (int32_t)plan.size();
+  if (!items) return ok();
+  if ((int32_t)plan.size() > capacity)
+    return fail(LORA_ENOMEM, "plan needs %zu items, capacity %d", plan.size(), capacity);
+  for (size_t i = 0; i < plan.size(); ++i) items[i] = plan[i].item;
+  return ok();
+}
+
+// --------------------------------------------------------------------------
+// Paged pool.
+struct lora_pool {
+  int32_t num_pages, page_rows, row_width, dtype;
+  char *storage;
+  std::vector<int32_t> free_list;   // front = next page handed out
+  size_t head = 0;                  // free_list[head..] are free
+  std::vector<uint8_t> taken;
+};
+
+static uint64_t splitmix64(uint64_t &s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+extern "C" lora_status lora_pool_create(int32_t num_pages, int32_t page_rows, int32_t row_width,
+                                        int32_t dtype, void *device_storage,
+                                        uint64_t shuffle_seed, lora_pool **out) {
+  if (!out) return fail(LORA_EINVAL, "null out");
+  if (num_pages <= 0 || page_rows <= 0 || row_width <= 0)
+    return fail(LORA_EINVAL, "pool sizes must be positive");
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "dtype %d", dtype);
+  if (!device_storage) return fail(LORA_EINVAL, "null storage");
+  lora_pool *p = new lora_pool();
+  p->num_pages = num_pages;
+  p->page_rows = page_rows;
+  p->row_width = row_width;
+  p->dtype = dtype;
+  p->storage = (char *)device_storage;
+  p->free_list.resize((size_t)num_pages);
+  for (int32_t i = 0; i < num_pages; ++i) p->free_list[(size_t)i] = i;
+  if (shuffle_seed != 0) {  // Fisher-Yates with a splitmix64 stream
+    uint64_t s = shuffle_seed;
+    for (int32_t i = num_pages - 1; i > 0; --i) {
+      int32_t j = (int32_t)(splitmix64(s) % (uint64_t)(i + 1));
+      std::swap(p->free_list[(size_t)i], p->free_list[(size_t)j]);
+    }
+  }
+  p->taken.assign((size_t)num_pages, 0);
+  *out = p;
+  return ok();
+}
+
+extern "C" lora_status lora_pool_alloc(lora_pool *p, int32_t rows, int32_t *page_ids) {
+  if (!p || !page_ids) return fail(LORA_EINVAL, "null pool or page_ids");
+  if (rows <= 0) return fail(LORA_EINVAL, "rows must be positive");
+  const int32_t need = (rows + p->page_rows - 1) / p->page_rows;
+  if ((int64_t)(p->free_list.size() - p->head) < need)
+    return fail(LORA_ENOMEM, "pool has %zu free pages, %d needed", p->free_list.size() - p->head,
+                need);
+  for (int32_t i = 0; i < need; ++i) {
+    int32_t id = p->free_list[p->head++];
+    p->taken[(size_t)id] = 1;
+    page_ids[i] = id;
+  }
+  // compact the consumed prefix now and then so the list does not grow forever
+  if (p->head > 4096 && p->head * 2 > p->free_list.size()) {
+    p->free_list.erase(p->free_list.begin(), p->free_list.begin() + (ptrdiff_t)p->head);
+    p->head = 0;
+  }
+  return ok();
+}
+
+extern "C" lora_status lora_pool_free(lora_pool *p, const int32_t *page_ids, int32_t n) {
+  if (!p || (n > 0 && !page_ids)) return fail(LORA_EINVAL, "null pool or page_ids");
+  if (n < 0) return fail(LORA_EINVAL, "negative count");
+  std::vector<uint8_t> seen((size_t)p->num_pages, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t id = page_ids[i];
+    if (id < 0 || id >= p->num_pages || !p->taken[(size_t)id] || seen[(size_t)id])
+      return fail(LORA_EINVAL, "page %d is not allocated (or listed twice)", id);
+    seen[(size_t)id] = 1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    p->taken[(size_t)page_ids[i]] = 0;
+    p->free_list.push_back(page_ids[i]);
+  }
+  return ok();
+}
+
+extern "C" lora_status lora_pool_num_free(const lora_pool *p, int32_t *num_free) {
+  if (!p || !num_free) return fail(LORA_EINVAL, "null argument");
+  *num_free = (int32_t)(p->free_list.size() - p->head);
+  return ok();
+}
+
+extern "C" lora_status lora_pool_write_rows(lora_pool *p, const int32_t *page_ids, int32_t rows,
+                                            const void *src, hipStream_t stream) {
+  if (!p || !page_ids || !src) return fail(LORA_EINVAL, "null argument");
+  if (rows <= 0) return fail(LORA_EINVAL, "rows must be positive");
+  const size_t elem = p->dtype == LORA_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)p->row_width * elem;
+  const int32_t npages = (rows + p->page_rows - 1) / p->page_rows;
+  for (int32_t i = 0; i < npages; ++i) {
+    int32_t id = page_ids[i];
+    if (id < 0 || id >= p->num_pages || !p->taken[(size_t)id])
+      return fail(LORA_EINVAL, "page %d is not allocated", id);
+  }
+  for (int32_t i = 0; i < npages; ++i) {
+    const int32_t nr = std::min(p->page_rows, rows - i * p->page_rows);
+    char *dst = p->storage + (size_t)page_ids[i] * p->page_rows * row_bytes;
+    const char *s = (const char *)src + (size_t)i * p->page_rows * row_bytes;
+    hipError_t e = hipMemcpyAsync(dst, s, (size_t)nr * row_bytes, hipMemcpyDefault, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (pool rows)");
+  }
+  return ok();
+}
+
+extern "C" void lora_pool_destroy(lora_pool *p) { delete p; }

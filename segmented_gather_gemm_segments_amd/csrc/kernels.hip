@@ -1,0 +1,842 @@
+// Kernel half of the library: the shrink and expand kernels for gfx950
+// (CDNA4), their launchers, and argument validation.
+//
+// Operation ("Multi-LoRA serving: the single translator with a thousand
+// glossaries", section "SGMV: the kernel that holds it all up"):
+//   shrink   v[t][j] = sum_k A_{a(t)}[j][k] x[t][k]               j < r_{a(t)}
+//   expand   y[t][i] = round(y[t][i] + sum_j B_{a(t)}[i][j] v[t][j])
+// Every adapter of a batch is handled by one launch per phase.  A work item
+// names up to 64 tokens of one adapter; its workgroup takes one of two paths:
+//   * gather/GEMV (short segments, decode): lanes run along the contiguous
+//     dimension of the adapter rows with 16-byte loads; shrink reduces the
+//     lane partials with a cross-lane butterfly and a fixed-order sum over the
+//     four waves;
+//   * MFMA (long segments): the per-adapter product is a dense GEMM and runs on
+//     v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32).
+//     Expand keeps v exact by splitting it into a bf16 pair hi + lo (two MFMA
+//     K-halves), so v never loses precision to bf16.
+// No floating-point atomics: every output element is produced by one thread
+// and summation orders are fixed, so repeated runs are bit-identical.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <utility>
+
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kThreads = 256;  // 4 waves of 64
+
+// ----------------------------------------------------------------- weights
+struct DevW {
+  const char *a_pages;
+  const char *b_pages;
+  const int32_t *rank;
+  const int32_t *a_pt;
+  const int32_t *b_pt;
+  int32_t d_in, d_out, num_adapters, r_max, page_rows, max_pages, num_pages_a, num_pages_b;
+};
+
+// Row j of adapter a through the page table; nullptr when the page id is out
+// of range (the row then contributes nothing).
+template <typename T>
+__device__ __forceinline__ const T *page_row(const char *base, const int32_t *pt, int32_t num_pages,
+                                             const DevW &w, int a, int j, int width) {
+  int page, r_in;
+  if (pt) {
+    const int pi = j / w.page_rows;
+    if (pi >= w.max_pages) return nullptr;
+    page = pt[(int64_t)a * w.max_pages + pi];
+    r_in = j - pi * w.page_rows;
+  } else {
+    page = a;
+    r_in = j;
+  }
+  if ((unsigned)page >= (unsigned)num_pages) return nullptr;
+  return reinterpret_cast<const T *>(base) + ((int64_t)page * w.page_rows + r_in) * width;
+}
+
+template <typename T>
+__device__ __forceinline__ const T *a_row(const DevW &w, int a, int j) {
+  return page_row<T>(w.a_pages, w.a_pt, w.num_pages_a, w, a, j, w.d_in);
+}
+template <typename T>
+__device__ __forceinline__ const T *b_row(const DevW &w, int a, int j) {
+  return page_row<T>(w.b_pages, w.b_pt, w.num_pages_b, w, a, j, w.d_out);
+}
+
+__device__ __forceinline__ int adapter_rank(const DevW &w, int a) {
+  int r = w.rank[a];
+  return r < 0 ? 0 : (r > w.r_max ? w.r_max : r);
+}
+
+// ----------------------------------------------------------------- elements
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// 8 consecutive elements -> fp32 (16 B for bf16, 32 B for fp32).
+__device__ __forceinline__ void load8(const uint16_t *p, float (&o)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+  o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
+}
+__device__ __forceinline__ void load8(const float *p, float (&o)[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t *p, const float (&o)[8]) {
+  uint4 u;
+  u.x = bf16_rne(o[0]) | (bf16_rne(o[1]) << 16);
+  u.y = bf16_rne(o[2]) | (bf16_rne(o[3]) << 16);
+  u.z = bf16_rne(o[4]) | (bf16_rne(o[5]) << 16);
+  u.w = bf16_rne(o[6]) | (bf16_rne(o[7]) << 16);
+  *reinterpret_cast<uint4 *>(p) = u;
+}
+__device__ __forceinline__ void store8(float *p, const float (&o)[8]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<float4 *>(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+// MFMA operand fragments: 8 consecutive elements of one row per lane.
+template <typename T> struct Frag;
+template <> struct Frag<uint16_t> { uint4 u; };
+template <> struct Frag<float> { float4 a, b; };
+
+__device__ __forceinline__ void frag_load(Frag<uint16_t> &f, const uint16_t *p) {
+  f.u = *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void frag_load(Frag<float> &f, const float *p) {
+  f.a = *reinterpret_cast<const float4 *>(p);
+  f.b = *reinterpret_cast<const float4 *>(p + 4);
+}
+__device__ __forceinline__ void frag_zero(Frag<uint16_t> &f) { f.u = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void frag_zero(Frag<float> &f) {
+  f.a = make_float4(0, 0, 0, 0);
+  f.b = f.a;
+}
+
+// D += A·B over the 8 k-elements held per lane.  For both types the k index
+// contracted is (lane group, element), identical for A and B, so the product
+// is a plain dot product over the 32 k of the step whatever order the unit
+// uses internally.
+__device__ __forceinline__ f32x4_t frag_mfma(const Frag<uint16_t> &a, const Frag<uint16_t> &b,
+                                             f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.u),
+                                                 __builtin_bit_cast(bf16x8_t, b.u), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t frag_mfma(const Frag<float> &a, const Frag<float> &b,
+                                             f32x4_t c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, b.a.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, b.a.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.z, b.a.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.w, b.a.w, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.x, b.b.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.y, b.b.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, b.b.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ----------------------------------------------------------------- reductions
+// Reduce-scatter of 64 values over the 64 lanes of a wave: on return lane l
+// holds the wave-wide sum of vals[l].  Six halving butterfly steps (masks 32
+// .. 1); every index is summed over the same lane tree, so the result for a
+// value does not depend on which slot it occupies.
+__device__ __forceinline__ float wave_reduce_scatter64(float (&vals)[64]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int step = 0; step < 6; ++step) {
+    const int n = 64 >> step;
+    const int m = 32 >> step;
+    // bitwise select (v_bfi_b32): a value select here would be folded into
+    // an address select and push the array out of registers
+    const uint32_t up = (lane & m) ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const uint32_t lo = __float_as_uint(vals[i]), hi = __float_as_uint(vals[i + n / 2]);
+      const float keep = __uint_as_float((up & hi) | (~up & lo));
+      const float send = __uint_as_float((up & lo) | (~up & hi));
+      vals[i] = keep + __shfl_xor(send, m, 64);
+    }
+  }
+  return vals[0];
+}
+
+// ----------------------------------------------------------------- shrink cores
+// Token list of the current item in LDS: toks[0..cnt).  Tokens outside
+// [0, num_tokens) are skipped.
+constexpr int kMaxItemTokens = 256;
+
+struct ShrinkSmem {
+  int toks[kMaxItemTokens];
+  union {
+    float red_gemv[4 * 64];           // one value per (wave, lane)
+    float red_mfma[4 * 4 * 4 * 64];   // [wave][row tile][element][lane]
+  };
+};
+
+// One 8-element step of the GEMV shrink for row JJ of the current 16-row
+// pass: acc[t*16 + JJ] += A[JJ][k..k+7] . x_t[k..k+7].  Expanded per row at
+// compile time so the 64 accumulators stay in registers.
+template <int JJ, typename T>
+__device__ __forceinline__ void gemv_row(const T *const (&ar)[16], int k, const float (&xv)[4][8],
+                                         int ntok, float (&acc)[64]) {
+  if (ar[JJ]) {
+    float av[8];
+    load8(ar[JJ] + k, av);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < ntok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t * 16 + JJ] = fmaf(av[e], xv[t][e], acc[t * 16 + JJ]);
+      }
+    }
+  }
+}
+template <typename T, int... JJ>
+__device__ __forceinline__ void gemv_rows(const T *const (&ar)[16], int k, const float (&xv)[4][8],
+                                          int ntok, float (&acc)[64],
+                                          std::integer_sequence<int, JJ...>) {
+  (gemv_row<JJ>(ar, k, xv, ntok, acc), ...);
+}
+
+// Gather/GEMV shrink for tokens toks[0..cnt) of adapter a, rows [j_lo, j_hi).
+// The 256 threads run along d_in, 8 elements (16 B of bf16) each per step;
+// each step loads the x chunk of up to 4 tokens once and reuses it across 16
+// A rows.  Lane partials (4 tokens x 16 rows = 64 values) are reduce-scattered
+// across the wave and the four wave results are summed in wave order.
+template <typename T>
+__device__ void shrink_gemv(const DevW &w, int a, int j_lo, int j_hi, const int *toks, int cnt,
+                            int num_tokens, const T *__restrict__ x, float *__restrict__ v,
+                            ShrinkSmem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int g0 = 0; g0 < cnt; g0 += 4) {
+    const int ntok = min(4, cnt - g0);
+    const T *xr[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
+      xr[t] = (tok >= 0 && tok < num_tokens) ? x + (int64_t)tok * w.d_in : nullptr;
+    }
+    for (int j0 = j_lo; j0 < j_hi; j0 += 16) {
+      const int nr = min(16, j_hi - j0);
+      const T *ar[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) ar[jj] = jj < nr ? a_row<T>(w, a, j0 + jj) : nullptr;
+      float acc[64];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+      for (int k = tid * 8; k < w.d_in; k += kThreads * 8) {
+        float xv[4][8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (xr[t]) {
+            load8(xr[t] + k, xv[t]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[t][e] = 0.f;
+          }
+        }
+        gemv_rows(ar, k, xv, ntok, acc, std::make_integer_sequence<int, 16>{});
+      }
+      const float part = wave_reduce_scatter64(acc);   // lane l: value (t = l/16, jj = l%16)
+      sm.red_gemv[wave * 64 + lane] = part;
+      __syncthreads();
+      if (tid < 64) {
+        const float s = ((sm.red_gemv[tid] + sm.red_gemv[64 + tid]) + sm.red_gemv[128 + tid]) +
+                        sm.red_gemv[192 + tid];
+        const int t = tid >> 4, jj = tid & 15;
+        if (t < ntok && jj < nr) {
+          const int tok = toks[g0 + t];
+          if (tok >= 0 && tok < num_tokens) v[(int64_t)tok * w.r_max + j0 + jj] = s;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// MFMA shrink for tokens toks[0..cnt) of adapter a (all rows < r).  One
+// 16-token tile at a time: the four waves split d_in (32-element steps
+// interleaved), each wave accumulates D[j][token] = A_rows · x^T for up to 4
+// row tiles of 16, and the four partial tiles are summed in wave order.
+template <typename T>
+__device__ void shrink_mfma(const DevW &w, int a, int r, const int *toks, int cnt, int num_tokens,
+                            const T *__restrict__ x, float *__restrict__ v, ShrinkSmem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  for (int m0 = 0; m0 < cnt; m0 += 16) {
+    int tok = m0 + m < cnt ? toks[m0 + m] : -1;
+    if (tok >= num_tokens) tok = -1;
+    const T *xr = tok >= 0 ? x + (int64_t)tok * w.d_in : nullptr;
+    for (int j0 = 0; j0 < r; j0 += 64) {
+      const int nrt = min(4, (r - j0 + 15) >> 4);
+      const T *ar[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int row = j0 + rt * 16 + m;
+        ar[rt] = (rt < nrt && row < r) ? a_row<T>(w, a, row) : nullptr;
+      }
+      f32x4_t acc[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s = wave; s * 32 < w.d_in; s += 4) {
+        const int k = s * 32 + g * 8;
+        const bool kin = k < w.d_in;
+        Frag<T> xf;
+        if (xr && kin) frag_load(xf, xr + k); else frag_zero(xf);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          if (rt < nrt) {
+            Frag<T> af;
+            if (ar[rt] && kin) frag_load(af, ar[rt] + k); else frag_zero(af);
+            acc[rt] = frag_mfma(af, xf, acc[rt]);
+          }
+        }
+      }
+      // lane (g, m) of row tile rt holds D[4g + e][m] = v[tok(m)][j0 + 16 rt + 4g + e]
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        if (rt < nrt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.red_mfma[((wave * 4 + rt) * 4 + e) * 64 + lane] = acc[rt][e];
+      __syncthreads();
+      if (wave < nrt) {
+        const int rt = wave;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float s = ((sm.red_mfma[((0 * 4 + rt) * 4 + e) * 64 + lane] +
+                            sm.red_mfma[((1 * 4 + rt) * 4 + e) * 64 + lane]) +
+                           sm.red_mfma[((2 * 4 + rt) * 4 + e) * 64 + lane]) +
+                          sm.red_mfma[((3 * 4 + rt) * 4 + e) * 64 + lane];
+          const int j = j0 + rt * 16 + 4 * g + e;
+          if (tok >= 0 && j < r) v[(int64_t)tok * w.r_max + j] = s;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ----------------------------------------------------------------- expand cores
+template <typename T> struct ExpandCfg;
+template <> struct ExpandCfg<uint16_t> { static constexpr int kRowStride = 72; };  // 64 j + pad
+template <> struct ExpandCfg<float> { static constexpr int kRowStride = 68; };
+
+template <typename T>
+struct ExpandSmem {
+  int toks[kMaxItemTokens];
+  union {
+    float red_gemv[4 * 4 * 8 * 64];                          // [wave][token][elem][lane]
+    T bt[4 * 64 * ExpandCfg<T>::kRowStride];                 // per wave: [64 cols][j]
+  };
+};
+
+// Gather/GEMV expand for tokens toks[0..cnt) of adapter a over the 512
+// columns of block `blk`: lane l owns 8 consecutive columns; wave w
+// accumulates rank indices j = w, w+4, ...; the four wave partials are summed
+// in wave order and added to y once.
+template <typename T>
+__device__ void expand_gemv(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
+                            int num_tokens, const float *__restrict__ v, T *__restrict__ y,
+                            ExpandSmem<T> &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = blk * LORA_EXPAND_GATHER_COLS + lane * 8;
+  const bool cin = col < w.d_out;
+  for (int g0 = 0; g0 < cnt; g0 += 4) {
+    const int ntok = min(4, cnt - g0);
+    int tk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
+      tk[t] = (tok >= 0 && tok < num_tokens) ? tok : -1;
+    }
+    float acc[4][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+    for (int j = wave; j < r; j += 4) {
+      const T *br = b_row<T>(w, a, j);
+      float bv[8];
+      if (br && cin) {
+        load8(br + col, bv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (tk[t] >= 0) {
+          const float vj = v[(int64_t)tk[t] * w.r_max + j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vj, bv[e], acc[t][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t < ntok)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.red_gemv[((wave * 4 + t) * 8 + e) * 64 + lane] = acc[t][e];
+    __syncthreads();
+    if (wave < ntok) {
+      const int t = wave;
+      const int tok = toks[g0 + t];
+      if (tok >= 0 && tok < num_tokens && cin) {
+        T *yp = y + (int64_t)tok * w.d_out + col;
+        float yv[8];
+        load8(yp, yv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float s = ((sm.red_gemv[((0 * 4 + t) * 8 + e) * 64 + lane] +
+                            sm.red_gemv[((1 * 4 + t) * 8 + e) * 64 + lane]) +
+                           sm.red_gemv[((2 * 4 + t) * 8 + e) * 64 + lane]) +
+                          sm.red_gemv[((3 * 4 + t) * 8 + e) * 64 + lane];
+          yv[e] += s;
+        }
+        store8(yp, yv);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Column of the wave's 64-column slab that MFMA row `rho` of sub-tile `t`
+// stands for.  Chosen so that after the MFMA, lane (g, m) holds 8 consecutive
+// columns 32q + 8g .. +7 of token m in sub-tiles 2q and 2q+1: one 16-byte y
+// access per lane instead of four 4-byte ones.
+__device__ __forceinline__ int slab_col(int t, int rho) {
+  return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3);
+}
+
+// MFMA expand for tokens toks[0..cnt) of adapter a over the 256 columns of
+// block `blk` (wave w: 64 columns).  D[col][token] = B^T-slab^T · v^T with the
+// B^T slab staged transposed in LDS.  bf16: v is split into hi + lo bf16 so
+// each K=32 MFMA covers 16 rank indices exactly; fp32: 16x16x4 steps.
+template <typename T>
+__device__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
+                            int num_tokens, const float *__restrict__ v, T *__restrict__ y,
+                            ExpandSmem<T> &sm) {
+  constexpr int RS = ExpandCfg<T>::kRowStride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int c0 = blk * LORA_EXPAND_MFMA_COLS + wave * 64;
+  T *bt = sm.bt + wave * 64 * RS;
+  for (int m0 = 0; m0 < cnt; m0 += 64) {
+    const int ntt = min(4, (cnt - m0 + 15) >> 4);
+    int tok[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int i = m0 + tt * 16 + m;
+      int t = (tt < ntt && i < cnt) ? toks[i] : -1;
+      tok[tt] = (t >= 0 && t < num_tokens) ? t : -1;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int jc = 0; jc < r; jc += 64) {
+      const int nj = min(64, r - jc);
+      const int nj16 = (nj + 15) & ~15;
+      __syncthreads();  // previous users of the slab are done
+      // stage B^T rows jc .. jc+nj16 of this wave's 64 columns, transposed
+      for (int jr = lane >> 3; jr < nj16; jr += 8) {
+        const int cc = (lane & 7) * 8;
+        float bv[8];
+        const T *br = (jr < nj && c0 + cc < w.d_out) ? b_row<T>(w, a, jc + jr) : nullptr;
+        if (br) {
+          load8(br + c0 + cc, bv);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (sizeof(T) == 2)
+            bt[(cc + e) * RS + jr] = (T)(__float_as_uint(bv[e]) >> 16);  // exact: bv is bf16
+          else
+            bt[(cc + e) * RS + jr] = bv[e];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (tt < ntt) {
+          const float *vr = tok[tt] >= 0 ? v + (int64_t)tok[tt] * w.r_max + jc : nullptr;
+          for (int kb = 0; kb * 16 < nj; ++kb) {
+            if constexpr (sizeof(T) == 2) {
+              // B operand: lane (g, m) -> rank indices kb*16 + (g&1)*8 + e, hi (g<2) or lo
+              const int jb = kb * 16 + (g & 1) * 8;
+              uint32_t h[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float f = (vr && jb + e < nj) ? vr[jb + e] : 0.f;
+                uint32_t hb = bf16_rne(f);
+                if (g >= 2) hb = bf16_rne(f - __uint_as_float(hb << 16));
+                h[e] = hb;
+              }
+              const uint4 bu = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                          h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+              const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bu);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const uint4 au =
+                    *reinterpret_cast<const uint4 *>(bt + slab_col(t, m) * RS + jb);
+                acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, au), bop, acc[tt][t], 0, 0, 0);
+              }
+            } else {
+              // four K=4 steps: lane group g takes rank index kb*16 + 4q + g
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int j = kb * 16 + 4 * q + g;
+                const float bop = (vr && j < nj) ? vr[j] : 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  const float aop = bt[slab_col(t, m) * RS + j];
+                  acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop, acc[tt][t], 0, 0, 0);
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    // y update: lane (g, m) holds columns c0 + 32q + 8g .. +7 of token tok[tt]
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (tt < ntt && tok[tt] >= 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int col = c0 + 32 * q + 8 * g;
+          if (col < w.d_out) {
+            T *yp = y + (int64_t)tok[tt] * w.d_out + col;
+            float yv[8];
+            load8(yp, yv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              yv[e] += acc[tt][2 * q][e];
+              yv[4 + e] += acc[tt][2 * q + 1][e];
+            }
+            store8(yp, yv);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- kernels
+__device__ __forceinline__ bool decode_item(const lora_item &it, const DevW &w, int num_perm,
+                                            int &pb, int &a, int &cnt, int &path, int &blk) {
+  pb = it.perm_begin;
+  a = it.adapter;
+  cnt = it.count_path & 0xffff;
+  path = it.count_path >> 16;
+  blk = it.block;
+  if (a < 0 || a >= w.num_adapters || pb < 0 || cnt <= 0 || cnt > kMaxItemTokens ||
+      pb + cnt > num_perm || blk < 0)
+    return false;
+  return true;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sgmv_shrink_kernel(DevW w, const int32_t *__restrict__ perm,
+                                                               int32_t num_perm,
+                                                               const lora_item *__restrict__ items,
+                                                               int32_t num_tokens,
+                                                               const T *__restrict__ x,
+                                                               float *__restrict__ v) {
+  __shared__ ShrinkSmem sm;
+  const lora_item it = items[blockIdx.x];
+  int pb, a, cnt, path, blk;
+  if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
+  for (int i = threadIdx.x; i < cnt; i += kThreads) sm.toks[i] = perm[pb + i];
+  __syncthreads();
+  const int r = adapter_rank(w, a);
+  if (path == LORA_PATH_MFMA)
+    shrink_mfma<T>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
+  else
+    shrink_gemv<T>(w, a, 0, r, sm.toks, cnt, num_tokens, x, v, sm);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
+                                                               int32_t num_perm,
+                                                               const lora_item *__restrict__ items,
+                                                               int32_t num_tokens,
+                                                               const float *__restrict__ v,
+                                                               T *__restrict__ y) {
+  __shared__ ExpandSmem<T> sm;
+  const lora_item it = items[blockIdx.x];
+  int pb, a, cnt, path, blk;
+  if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
+  for (int i = threadIdx.x; i < cnt; i += kThreads) sm.toks[i] = perm[pb + i];
+  __syncthreads();
+  const int r = adapter_rank(w, a);
+  if (path == LORA_PATH_MFMA)
+    expand_mfma<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+  else
+    expand_gemv<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+}
+
+// Collects, in token order, the tokens of ids[c0 .. c0+256) whose adapter is
+// `a` into toks[]; returns their count.  All threads must call it.
+__device__ int gather_adapter_tokens(const int32_t *__restrict__ ids, int num_tokens, int c0, int a,
+                                     int *toks, int *wave_cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = c0 + tid;
+  const bool hit = t < num_tokens && ids[t] == a;
+  const unsigned long long mask = __ballot(hit);
+  if (lane == 0) wave_cnt[wave] = __popcll(mask);
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wave; ++i) base += wave_cnt[i];
+  const int total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+  if (hit) toks[base + __popcll(mask & ((1ull << lane) - 1ull))] = t;
+  __syncthreads();
+  return total;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int32_t *__restrict__ ids,
+                                                               int32_t num_tokens, int32_t adapter_major,
+                                                               const T *__restrict__ x,
+                                                               float *__restrict__ v) {
+  __shared__ ShrinkSmem sm;
+  __shared__ int wave_cnt[4];
+  const int rb_lo = blockIdx.y * 16;
+  if (!adapter_major) {
+    const int t = blockIdx.x;
+    const int a = ids[t];
+    if (a < 0 || a >= w.num_adapters) return;
+    const int r = adapter_rank(w, a);
+    if (rb_lo >= r) return;
+    if (threadIdx.x == 0) sm.toks[0] = t;
+    __syncthreads();
+    shrink_gemv<T>(w, a, rb_lo, min(r, rb_lo + 16), sm.toks, 1, num_tokens, x, v, sm);
+  } else {
+    const int a = blockIdx.x;
+    const int r = adapter_rank(w, a);
+    if (rb_lo >= r) return;
+    for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
+      const int n = gather_adapter_tokens(ids, num_tokens, c0, a, sm.toks, wave_cnt);
+      if (n > 0) shrink_gemv<T>(w, a, rb_lo, min(r, rb_lo + 16), sm.toks, n, num_tokens, x, v, sm);
+      __syncthreads();
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(DevW w, const int32_t *__restrict__ ids,
+                                                               int32_t num_tokens, int32_t adapter_major,
+                                                               const float *__restrict__ v,
+                                                               T *__restrict__ y) {
+  __shared__ ExpandSmem<T> sm;
+  __shared__ int wave_cnt[4];
+  const int blk = blockIdx.y;
+  if (!adapter_major) {
+    const int t = blockIdx.x;
+    const int a = ids[t];
+    if (a < 0 || a >= w.num_adapters) return;
+    if (threadIdx.x == 0) sm.toks[0] = t;
+    __syncthreads();
+    expand_gemv<T>(w, a, adapter_rank(w, a), blk, sm.toks, 1, num_tokens, v, y, sm);
+  } else {
+    const int a = blockIdx.x;
+    const int r = adapter_rank(w, a);
+    for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
+      const int n = gather_adapter_tokens(ids, num_tokens, c0, a, sm.toks, wave_cnt);
+      if (n > 0) expand_gemv<T>(w, a, r, blk, sm.toks, n, num_tokens, v, y, sm);
+      __syncthreads();
+    }
+  }
+}
+
+// ----------------------------------------------------------------- validation
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+lora_status to_dev(const lora_weights *w, DevW *d) {
+  if (!w) return fail(LORA_EINVAL, "null weights");
+  if (w->dtype != LORA_F32 && w->dtype != LORA_BF16)
+    return fail(LORA_EUNSUPPORTED, "unknown dtype %d", w->dtype);
+  if (w->d_in <= 0 || w->d_out <= 0 || w->d_in % 8 || w->d_out % 8)
+    return fail(LORA_EUNSUPPORTED, "d_in (%d) and d_out (%d) must be positive multiples of 8",
+                w->d_in, w->d_out);
+  if (w->r_max < 1 || w->r_max > LORA_MAX_RANK)
+    return fail(LORA_EUNSUPPORTED, "r_max %d outside 1..%d", w->r_max, LORA_MAX_RANK);
+  if (w->num_adapters < 0) return fail(LORA_EINVAL, "negative num_adapters");
+  if (w->page_rows <= 0) return fail(LORA_EINVAL, "page_rows must be positive");
+  if (w->num_pages_a <= 0 || w->num_pages_b <= 0) return fail(LORA_EINVAL, "empty page pool");
+  if (w->reserved != 0) return fail(LORA_EINVAL, "reserved field must be 0");
+  if (!w->a_pages || !w->b_pages || !w->rank) return fail(LORA_EINVAL, "null weight pointer");
+  if (!aligned16(w->a_pages) || !aligned16(w->b_pages))
+    return fail(LORA_EINVAL, "page storage must be 16-byte aligned");
+  if ((w->a_page_table == nullptr) != (w->b_page_table == nullptr))
+    return fail(LORA_EINVAL, "give both page tables or neither");
+  if (w->a_page_table) {
+    if (w->max_pages < (w->r_max + w->page_rows - 1) / w->page_rows)
+      return fail(LORA_EINVAL, "max_pages %d too small for r_max %d with %d-row pages",
+                  w->max_pages, w->r_max, w->page_rows);
+  } else {
+    if (w->page_rows < w->r_max)
+      return fail(LORA_EINVAL, "dense stacks need page_rows (%d) >= r_max (%d)", w->page_rows,
+                  w->r_max);
+    if (w->num_pages_a < w->num_adapters || w->num_pages_b < w->num_adapters)
+      return fail(LORA_EINVAL, "dense stacks need one page per adapter");
+  }
+  if (w->host_rank)
+    for (int32_t a = 0; a < w->num_adapters; ++a)
+      if (w->host_rank[a] < 1 || w->host_rank[a] > w->r_max)
+        return fail(LORA_ERANGE, "adapter %d has rank %d outside 1..r_max (%d)", a,
+                    w->host_rank[a], w->r_max);
+  d->a_pages = (const char *)w->a_pages;
+  d->b_pages = (const char *)w->b_pages;
+  d->rank = w->rank;
+  d->a_pt = w->a_page_table;
+  d->b_pt = w->b_page_table;
+  d->d_in = w->d_in;
+  d->d_out = w->d_out;
+  d->num_adapters = w->num_adapters;
+  d->r_max = w->r_max;
+  d->page_rows = w->page_rows;
+  d->max_pages = w->a_page_table ? w->max_pages : 1;
+  d->num_pages_a = w->num_pages_a;
+  d->num_pages_b = w->num_pages_b;
+  return LORA_OK;
+}
+
+lora_status check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  return ok();
+}
+
+lora_status check_sgmv_args(const int32_t *perm, int32_t num_perm, const lora_item *items,
+                            int32_t num_items, int32_t num_tokens, const void *in, const void *out) {
+  if (num_perm < 0 || num_items < 0 || num_tokens < 0) return fail(LORA_EINVAL, "negative size");
+  if (num_items > 0 && num_tokens > 0) {
+    if (!perm || !items || !in || !out) return fail(LORA_EINVAL, "null pointer");
+    if (!aligned16(in) || !aligned16(out) || !aligned16(items))
+      return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
+  }
+  return LORA_OK;
+}
+
+int bgmv_order(int order, int num_tokens, int num_adapters) {
+  if (order == LORA_BGMV_TOKEN_MAJOR || order == LORA_BGMV_ADAPTER_MAJOR) return order;
+  return num_adapters <= num_tokens ? LORA_BGMV_ADAPTER_MAJOR : LORA_BGMV_TOKEN_MAJOR;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- C ABI
+extern "C" lora_status lora_sgmv_shrink(const lora_weights *w, const int32_t *token_perm,
+                                        int32_t num_perm, const lora_item *items,
+                                        int32_t num_items, int32_t num_tokens, const void *x,
+                                        float *v, hipStream_t stream) {
+  DevW d;
+  lora_status st = to_dev(w, &d);
+  if (st != LORA_OK) return st;
+  if ((st = check_sgmv_args(token_perm, num_perm, items, num_items, num_tokens, x, v)) != LORA_OK)
+    return st;
+  if (num_items == 0 || num_tokens == 0) return ok();
+  if (w->dtype == LORA_BF16)
+    hipLaunchKernelGGL(sgmv_shrink_kernel<uint16_t>, dim3(num_items), dim3(kThreads), 0, stream, d,
+                       token_perm, num_perm, items, num_tokens, (const uint16_t *)x, v);
+  else
+    hipLaunchKernelGGL(sgmv_shrink_kernel<float>, dim3(num_items), dim3(kThreads), 0, stream, d,
+                       token_perm, num_perm, items, num_tokens, (const float *)x, v);
+  return check_launch("sgmv shrink launch");
+}
+
+extern "C" lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm,
+                                        int32_t num_perm, const lora_item *items,
+                                        int32_t num_items, int32_t num_tokens, const float *v,
+                                        void *y, hipStream_t stream) {
+  DevW d;
+  lora_status st = to_dev(w, &d);
+  if (st != LORA_OK) return st;
+  if ((st = check_sgmv_args(token_perm, num_perm, items, num_items, num_tokens, v, y)) != LORA_OK)
+    return st;
+  if (num_items == 0 || num_tokens == 0) return ok();
+  if (w->dtype == LORA_BF16)
+    hipLaunchKernelGGL(sgmv_expand_kernel<uint16_t>, dim3(num_items), dim3(kThreads), 0, stream, d,
+                       token_perm, num_perm, items, num_tokens, v, (uint16_t *)y);
+  else
+    hipLaunchKernelGGL(sgmv_expand_kernel<float>, dim3(num_items), dim3(kThreads), 0, stream, d,
+                       token_perm, num_perm, items, num_tokens, v, (float *)y);
+  return check_launch("sgmv expand launch");
+}
+
+extern "C" lora_status lora_bgmv_shrink(const lora_weights *w, const int32_t *token_adapter,
+                                        int32_t num_tokens, int32_t order, const void *x, float *v,
+                                        hipStream_t stream) {
+  DevW d;
+  lora_status st = to_dev(w, &d);
+  if (st != LORA_OK) return st;
+  if (num_tokens < 0) return fail(LORA_EINVAL, "negative num_tokens");
+  if (order < LORA_BGMV_AUTO || order > LORA_BGMV_ADAPTER_MAJOR)
+    return fail(LORA_EINVAL, "unknown order %d", order);
+  if (num_tokens == 0 || w->num_adapters == 0) return ok();
+  if (!token_adapter || !x || !v) return fail(LORA_EINVAL, "null pointer");
+  if (!aligned16(x) || !aligned16(v)) return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
+  const int am = bgmv_order(order, num_tokens, w->num_adapters) == LORA_BGMV_ADAPTER_MAJOR;
+  const dim3 grid(am ? w->num_adapters : num_tokens, (w->r_max + 15) / 16);
+  if (w->dtype == LORA_BF16)
+    hipLaunchKernelGGL(bgmv_shrink_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, d,
+                       token_adapter, num_tokens, am, (const uint16_t *)x, v);
+  else
+    hipLaunchKernelGGL(bgmv_shrink_kernel<float>, grid, dim3(kThreads), 0, stream, d,
+                       token_adapter, num_tokens, am, (const float *)x, v);
+  return check_launch("bgmv shrink launch");
+}
+
+extern "C" lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *token_adapter,
+                                        int32_t num_tokens, int32_t order, const float *v, void *y,
+                                        hipStream_t stream) {
+  DevW d;
+  lora_status st = to_dev(w, &d);
+  if (st != LORA_OK) return st;
+  if (num_tokens < 0) return fail(LORA_EINVAL, "negative num_tokens");
+  if (order < LORA_BGMV_AUTO || order > LORA_BGMV_ADAPTER_MAJOR)
+    return fail(LORA_EINVAL, "unknown order %d", order);
+  if (num_tokens == 0 || w->num_adapters == 0) return ok();
+  if (!token_adapter || !v || !y) return fail(LORA_EINVAL, "null pointer");
+  if (!aligned16(v) || !aligned16(y)) return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
+  const int am = bgmv_order(order, num_tokens, w->num_adapters) == LORA_BGMV_ADAPTER_MAJOR;
+  const dim3 grid(am ? w->num_adapters : num_tokens,
+                  (w->d_out + LORA_EXPAND_GATHER_COLS - 1) / LORA_EXPAND_GATHER_COLS);
+  if (w->dtype == LORA_BF16)
+    hipLaunchKernelGGL(bgmv_expand_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, d,
+                       token_adapter, num_tokens, am, v, (uint16_t *)y);
+  else
+    hipLaunchKernelGGL(bgmv_expand_kernel<float>, grid, dim3(kThreads), 0, stream, d,
+                       token_adapter, num_tokens, am, v, (float *)y);
+  return check_launch("bgmv expand launch");
+}
+
+extern "C" lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k,
+                                      const void *x, const void *w, void *y, hipStream_t stream) {
+  (void)m; (void)n; (void)k; (void)x; (void)w; (void)y; (void)stream;
+  if (dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "base gemm supports bf16 only");
+  return fail(LORA_EUNSUPPORTED, "base gemm not built yet");
+}

@@ -1,0 +1,165 @@
+"""Puts a generated batch on the GPU and drives the C ABI over it.
+
+Data movement and bookkeeping only: tensors for x, y, v and the adapter
+weights (as a dense stack or in a shuffled page pool), the host segment build,
+plans, and uploads.  All arithmetic of the delta runs in the library's kernels.
+Used by the GPU tests, the benchmark and the smoke check.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import binding as B
+from .workloads import LoraProblem
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(arr: np.ndarray, dtype: str, device):
+    """numpy (float32, or uint16 bf16 patterns) -> torch tensor on `device`."""
+    torch = _torch()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def to_host(t, dtype: str) -> np.ndarray:
+    """torch tensor -> numpy (float32, or uint16 bf16 patterns)."""
+    torch = _torch()
+    if dtype == "bf16":
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy().astype(np.float32, copy=False)
+
+
+class DeviceProblem:
+    """A LoraProblem resident on one GPU.
+
+    layout: "dense" -- [N, r_max, d] stacks, rows r_a..r_max-1 filled with NaN;
+            "paged" -- a lora_pool of 16-row pages, shuffled, unused page rows
+                       NaN, A and B^T rows sharing one pool when d_in == d_out.
+    """
+
+    def __init__(self, p: LoraProblem, device="cuda", layout: Optional[str] = None,
+                 page_rows: int = 16, pool_slack: float = 2.0, pool_seed: Optional[int] = None):
+        torch = _torch()
+        self.p = p
+        self.device = torch.device(device)
+        self.layout = layout or ("paged" if p.paged else "dense")
+        self.tdtype = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+        self.cdtype = B.LORA_BF16 if p.dtype == "bf16" else B.LORA_F32
+        self.x = to_device(p.x, p.dtype, self.device)
+        self.y0 = to_device(p.y, p.dtype, self.device)
+        self.ids = torch.from_numpy(p.ids).to(self.device)
+        self.rank = torch.from_numpy(p.ranks.astype(np.int32)).to(self.device)
+        self.r_max = p.r_max
+        self._pools = []
+        if self.layout == "dense":
+            self._dense()
+        else:
+            self._paged(page_rows, pool_slack, p.pool_seed if pool_seed is None else pool_seed)
+        self._seg = None
+
+    # ------------------------------------------------------------- weights
+    def _stack(self, rows, width):
+        torch = self._torch = _torch()
+        n = len(rows)
+        st = torch.full((n, self.r_max, width), float("nan"), dtype=self.tdtype, device=self.device)
+        for a, r in enumerate(rows):
+            st[a, : r.shape[0]] = to_device(r, self.p.dtype, self.device)
+        return st
+
+    def _dense(self):
+        p = self.p
+        self.a_pages = self._stack(p.a_rows, p.d_in)
+        self.b_pages = self._stack(p.bt_rows, p.d_out)
+        self.weights = B.Weights(self.cdtype, p.d_in, p.d_out, self.r_max, self.r_max,
+                                 self.a_pages, self.b_pages, self.rank, p.ranks.astype(np.int32))
+
+    def _paged(self, page_rows, slack, seed):
+        torch = _torch()
+        p = self.p
+        pages_a = sum((int(r) + page_rows - 1) // page_rows for r in p.ranks)
+        shared = p.d_in == p.d_out
+        max_pages = (self.r_max + page_rows - 1) // page_rows
+
+        def make_pool(n_pages, width, s):
+            storage = torch.full((n_pages, page_rows, width), float("nan"), dtype=self.tdtype,
+                                 device=self.device)
+            pool = B.Pool(storage, page_rows, shuffle_seed=s)
+            self._pools.append(pool)
+            return pool
+
+        if shared:
+            cap = int(np.ceil(2 * pages_a * slack))
+            pool_a = pool_b = make_pool(cap, p.d_in, seed * 7919 + 1)
+        else:
+            cap = int(np.ceil(pages_a * slack))
+            pool_a = make_pool(cap, p.d_in, seed * 7919 + 1)
+            pool_b = make_pool(cap, p.d_out, seed * 7919 + 2)
+        a_pt = np.full((p.num_adapters, max_pages), -1, np.int32)
+        b_pt = np.full((p.num_adapters, max_pages), -1, np.int32)
+        for a in range(p.num_adapters):
+            r = int(p.ranks[a])
+            ia = pool_a.alloc(r)
+            pool_a.write_rows(ia, to_device(p.a_rows[a], p.dtype, self.device))
+            ib = pool_b.alloc(r)
+            pool_b.write_rows(ib, to_device(p.bt_rows[a], p.dtype, self.device))
+            a_pt[a, : ia.size] = ia
+            b_pt[a, : ib.size] = ib
+        torch.cuda.synchronize(self.device)
+        self.host_a_pt, self.host_b_pt = a_pt, b_pt
+        self.a_pages, self.b_pages = pool_a.storage, pool_b.storage
+        self.weights = B.Weights(self.cdtype, p.d_in, p.d_out, self.r_max, page_rows,
+                                 self.a_pages, self.b_pages, self.rank, p.ranks.astype(np.int32),
+                                 torch.from_numpy(a_pt).to(self.device),
+                                 torch.from_numpy(b_pt).to(self.device), max_pages)
+
+    # ------------------------------------------------------------- segments, plans
+    def segments(self):
+        if self._seg is None:
+            torch = _torch()
+            perm, starts, adapters = B.lora_segments_build(self.p.ids, self.p.num_adapters)
+            self._seg = (perm, starts, adapters,
+                         torch.from_numpy(np.ascontiguousarray(perm)).to(self.device))
+        return self._seg
+
+    def plan(self, phase: int, policy: int = B.LORA_PATH_AUTO,
+             mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS):
+        torch = _torch()
+        _, starts, adapters, _ = self.segments()
+        dim = self.p.d_in if phase == B.LORA_PHASE_SHRINK else self.p.d_out
+        items = B.lora_sgmv_plan(phase, starts, adapters, self.p.num_adapters, dim, policy,
+                                 mfma_min_tokens)
+        return torch.from_numpy(np.ascontiguousarray(items)).to(self.device)
+
+    # ------------------------------------------------------------- runs
+    def new_v(self):
+        torch = _torch()
+        return torch.zeros((self.p.num_tokens, max(self.r_max, 1)), dtype=torch.float32,
+                           device=self.device)
+
+    def run_sgmv(self, policy: int = B.LORA_PATH_AUTO,
+                 mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS, y=None, v=None):
+        """shrink then expand over the segmented batch; returns (y, v)."""
+        _, _, _, perm_d = self.segments()
+        sp = self.plan(B.LORA_PHASE_SHRINK, policy, mfma_min_tokens)
+        ep = self.plan(B.LORA_PHASE_EXPAND, policy, mfma_min_tokens)
+        y = self.y0.clone() if y is None else y
+        v = self.new_v() if v is None else v
+        B.lora_sgmv_shrink(self.weights, perm_d, sp, self.x, v)
+        B.lora_sgmv_expand(self.weights, perm_d, ep, v, y)
+        return y, v
+
+    def run_bgmv(self, order: int = B.LORA_BGMV_AUTO, y=None, v=None):
+        y = self.y0.clone() if y is None else y
+        v = self.new_v() if v is None else v
+        B.lora_bgmv_shrink(self.weights, self.ids, self.x, v, order)
+        B.lora_bgmv_expand(self.weights, self.ids, v, y, order)
+        return y, v

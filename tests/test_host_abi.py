@@ -1,0 +1,255 @@
+"""Host half of the C ABI, exercised without a GPU: symbol exports, the segment
+build (bit-exact against the oracle's different algorithm), the planner's
+coverage, the page pool's bookkeeping and the error conventions."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import ROOT, read_golden_examples
+from segmented_gather_gemm_segments_amd import binding as B
+from segmented_gather_gemm_segments_amd import build as lbuild
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_lib():
+    if not lbuild.up_to_date():
+        lbuild.build()
+    return B.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "lora_sgmv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 15
+    h = ctypes.CDLL(B.lib_path())
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) == set(B.EXPORTS), "binding and header disagree"
+    assert B.lib().lora_abi_version() == 1
+
+
+# ------------------------------------------------------------------ segments
+@pytest.mark.parametrize("ex", read_golden_examples("segments_worked_examples.txt"),
+                         ids=lambda e: e["name"])
+def test_segments_worked_examples(ex):
+    ids = np.array(ex["ids"].split(), np.int32)
+    perm, starts, adapters = B.lora_segments_build(ids, int(ex["num_adapters"]))
+    assert perm.tolist() == [int(v) for v in ex["token_perm"].split()]
+    assert starts.tolist() == [int(v) for v in ex["seg_starts"].split()]
+    assert adapters.tolist() == [int(v) for v in ex["seg_adapter"].split()]
+
+
+def test_segments_bit_exact_vs_oracle_random():
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        n = int(rng.integers(1, 300))
+        t = int(rng.integers(0, 2000))
+        p_none = rng.random() * 0.3
+        ids = rng.integers(0, n, size=t).astype(np.int32)
+        ids[rng.random(t) < p_none] = -1
+        got = B.lora_segments_build(ids, n)
+        want = oracle.segments(ids, n)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w)
+
+
+def test_segments_full_size_workloads():
+    from segmented_gather_gemm_segments_amd import workloads as wl
+    for ids, n in [(wl.sgmv_prefill().ids, 64), (wl.layer_batch_ids(), 256),
+                   (wl.hetero_paged().ids, 64)]:
+        got = B.lora_segments_build(ids, n)
+        want = oracle.segments(ids, n)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w)
+
+
+def test_segments_edge_cases():
+    perm, starts, adapters = B.lora_segments_build(np.zeros(0, np.int32), 5)
+    assert perm.size == 0 and starts.tolist() == [0] and adapters.size == 0
+    perm, starts, adapters = B.lora_segments_build(np.full(7, -1, np.int32), 5)
+    assert perm.size == 0 and starts.tolist() == [0]
+    perm, starts, adapters = B.lora_segments_build(np.full(9, 3, np.int32), 5)
+    assert perm.tolist() == list(range(9)) and starts.tolist() == [0, 9] and adapters.tolist() == [3]
+    with pytest.raises(B.LoraError) as e:
+        B.lora_segments_build(np.array([0, 5], np.int32), 5)
+    assert e.value.status == B.LORA_ERANGE
+    with pytest.raises(B.LoraError) as e:
+        B.lora_segments_build(np.array([-2], np.int32), 5)
+    assert e.value.status == B.LORA_ERANGE
+
+
+# ------------------------------------------------------------------ planner
+def _coverage(items, starts, dim, phase):
+    """Count, per (perm position, output column block unit), how often it is covered."""
+    n_tok = int(starts[-1])
+    if phase == B.LORA_PHASE_SHRINK:
+        cov = np.zeros(n_tok, np.int32)
+    else:
+        cov = np.zeros((n_tok, dim // 8), np.int32)
+    seg_of = np.repeat(np.arange(starts.size - 1), np.diff(starts))
+    for pb, a, cp, blk in items:
+        cnt, path = cp & 0xFFFF, cp >> 16
+        assert 1 <= cnt and path in (B.LORA_PATH_GATHER, B.LORA_PATH_MFMA)
+        assert len(set(seg_of[pb:pb + cnt])) == 1        # one segment per item
+        if phase == B.LORA_PHASE_SHRINK:
+            cov[pb:pb + cnt] += 1
+        else:
+            cols = 256 if path == B.LORA_PATH_MFMA else 512
+            c0, c1 = blk * cols, min(dim, (blk + 1) * cols)
+            assert c0 < dim
+            cov[pb:pb + cnt, c0 // 8:c1 // 8] += 1
+    return cov
+
+
+@pytest.mark.parametrize("policy", [B.LORA_PATH_AUTO, B.LORA_PATH_GATHER, B.LORA_PATH_MFMA])
+def test_plan_covers_every_output_once(policy):
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        n = int(rng.integers(1, 40))
+        t = int(rng.integers(1, 600))
+        ids = rng.integers(-1, n, size=t).astype(np.int32)
+        perm, starts, adapters = B.lora_segments_build(ids, n)
+        if adapters.size == 0:
+            continue
+        dim = int(rng.integers(1, 200)) * 8
+        for phase in (B.LORA_PHASE_SHRINK, B.LORA_PHASE_EXPAND):
+            items = B.lora_sgmv_plan(phase, starts, adapters, n, dim, policy)
+            cov = _coverage(items, starts, dim, phase)
+            assert np.all(cov == 1)
+            # adapter of each item is its segment's adapter
+            seg_of = np.repeat(np.arange(adapters.size), np.diff(starts))
+            assert np.all(adapters[seg_of[items[:, 0]]] == items[:, 1])
+
+
+def test_plan_path_choice_and_order():
+    starts = np.array([0, 1, 16, 116], np.int32)     # lengths 1, 15, 100
+    adapters = np.array([0, 1, 2], np.int32)
+    items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 64)
+    paths = {int(a): int(cp >> 16) for _, a, cp, _ in items}
+    assert paths == {0: B.LORA_PATH_GATHER, 1: B.LORA_PATH_GATHER, 2: B.LORA_PATH_MFMA}
+    items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 64, mfma_min_tokens=1)
+    assert all((cp >> 16) == B.LORA_PATH_MFMA for _, _, cp, _ in items)
+    # heaviest first: MFMA expand items (64 tokens) lead
+    items = B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, starts, adapters, 3, 4096)
+    assert (items[0, 2] >> 16) == B.LORA_PATH_MFMA and (items[0, 2] & 0xFFFF) == 64
+
+
+def test_plan_errors():
+    with pytest.raises(B.LoraError) as e:
+        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2], np.int32), np.array([7], np.int32), 3, 64)
+    assert e.value.status == B.LORA_ERANGE
+    with pytest.raises(B.LoraError) as e:
+        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2, 2], np.int32), np.array([0, 1], np.int32), 3, 64)
+    assert e.value.status == B.LORA_EINVAL
+    with pytest.raises(B.LoraError) as e:
+        B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, np.array([0, 2], np.int32), np.array([0], np.int32), 3, 12)
+    assert e.value.status == B.LORA_EUNSUPPORTED
+    with pytest.raises(B.LoraError):
+        B.lora_sgmv_plan(7, np.array([0, 2], np.int32), np.array([0], np.int32), 3, 64)
+    # capacity too small -> ENOMEM, count still reported
+    lib = B.lib()
+    st = np.array([0, 40], np.int32)
+    ad = np.array([0], np.int32)
+    n = ctypes.c_int32(0)
+    items = np.zeros((1, 4), np.int32)
+    rc = lib.lora_sgmv_plan(0, st.ctypes.data, ad.ctypes.data, 1, 1, 64, 0, 16, items.ctypes.data, 1,
+                            ctypes.byref(n))
+    assert rc == B.LORA_ENOMEM and n.value == 3
+    # an empty batch plans to nothing
+    assert B.lora_sgmv_plan(0, np.array([0], np.int32), np.zeros(0, np.int32), 3, 64).shape == (0, 4)
+
+
+# ------------------------------------------------------------------ pool
+class _FakeStorage:
+    """Host-only stand-in for a device tensor: the pool's bookkeeping never
+    dereferences storage except in write_rows (GPU-tier)."""
+
+    def __init__(self, n, pr, w):
+        self.shape = (n, pr, w)
+        self.buf = np.zeros(1, np.uint8)
+        import torch
+        self.dtype = torch.bfloat16
+
+    def data_ptr(self):
+        return self.buf.ctypes.data
+
+
+def test_pool_alloc_free_and_shuffle():
+    s = _FakeStorage(64, 16, 128)
+    p = B.Pool(s, 16, shuffle_seed=1234)
+    assert p.num_free() == 64
+    got = [p.alloc(r) for r in (8, 16, 17, 64, 1)]
+    assert [g.size for g in got] == [1, 1, 2, 4, 1]
+    flat = np.concatenate(got)
+    assert len(set(flat.tolist())) == flat.size and flat.min() >= 0 and flat.max() < 64
+    assert p.num_free() == 64 - 9
+    assert flat.tolist() != sorted(flat.tolist())            # shuffled order
+    q = B.Pool(_FakeStorage(64, 16, 128), 16, shuffle_seed=1234)
+    assert np.array_equal(np.concatenate([q.alloc(r) for r in (8, 16, 17, 64, 1)]), flat)
+    z = B.Pool(_FakeStorage(8, 16, 128), 16, shuffle_seed=0)
+    assert z.alloc(48).tolist() == [0, 1, 2]                  # seed 0: in order
+    p.free(got[2])
+    assert p.num_free() == 64 - 7
+    with pytest.raises(B.LoraError) as e:
+        p.free(got[2])                                       # double free
+    assert e.value.status == B.LORA_EINVAL
+    with pytest.raises(B.LoraError) as e:
+        p.alloc(16 * 100)
+    assert e.value.status == B.LORA_ENOMEM
+    assert p.num_free() == 64 - 7                             # nothing taken on failure
+    rest = p.alloc(16 * p.num_free())
+    assert p.num_free() == 0 and rest.size == 57
+
+
+# ------------------------------------------------------------------ ABI errors
+def _desc(**kw):
+    base = dict(dtype=1, d_in=64, d_out=64, num_adapters=2, r_max=16, page_rows=16, max_pages=1,
+                num_pages_a=2, num_pages_b=2, reserved=0, a_pages=16, b_pages=16, rank=16,
+                a_page_table=None, b_page_table=None, host_rank=None)
+    base.update(kw)
+    return B.lora_weights(*[base[f] for f, _ in B.lora_weights._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), B.LORA_EUNSUPPORTED),
+    (dict(d_in=60), B.LORA_EUNSUPPORTED),
+    (dict(d_out=0), B.LORA_EUNSUPPORTED),
+    (dict(r_max=200), B.LORA_EUNSUPPORTED),
+    (dict(r_max=0), B.LORA_EUNSUPPORTED),
+    (dict(a_pages=None), B.LORA_EINVAL),
+    (dict(a_pages=18), B.LORA_EINVAL),            # misaligned
+    (dict(page_rows=8), B.LORA_EINVAL),           # dense stack needs page_rows >= r_max
+    (dict(reserved=1), B.LORA_EINVAL),
+    (dict(a_page_table=64), B.LORA_EINVAL),       # one table without the other
+])
+def test_weight_validation_errors(kw, status):
+    d = _desc(**kw)
+    rc = B.lib().lora_sgmv_shrink(ctypes.byref(d), 16, 1, 16, 1, 1, 16, 16, None)
+    assert rc == status, B.lora_last_error()
+    assert B.lora_last_error()
+
+
+def test_host_rank_validation():
+    hr = np.array([16, 17], np.int32)
+    d = _desc(host_rank=hr.ctypes.data)
+    rc = B.lib().lora_bgmv_expand(ctypes.byref(d), 16, 1, 0, 16, 16, None)
+    assert rc == B.LORA_ERANGE
+
+
+def test_empty_batches_are_noops():
+    d = _desc()
+    lib = B.lib()
+    assert lib.lora_sgmv_shrink(ctypes.byref(d), None, 0, None, 0, 0, None, None, None) == B.LORA_OK
+    assert lib.lora_sgmv_expand(ctypes.byref(d), 16, 4, 16, 0, 8, 16, 16, None) == B.LORA_OK
+    assert lib.lora_bgmv_shrink(ctypes.byref(d), None, 0, 0, None, None, None) == B.LORA_OK
+    assert lib.lora_bgmv_expand(ctypes.byref(d), 16, 1, 9, 16, 16, None) == B.LORA_EINVAL  # bad order
+    assert lib.lora_sgmv_shrink(ctypes.byref(d), None, 4, 16, 2, 8, 16, 16, None) == B.LORA_EINVAL
