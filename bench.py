@@ -1,0 +1,228 @@
+"""Benchmark of the multi-LoRA delta hot path on one MI355X.
+
+A step is one pass of the delta path over one batch already resident in HBM:
+shrink then expand.  The default workload is the decode batch (256 tokens, one
+token per request, adapters drawn uniformly from 128 resident rank-16
+adapters, 4096 -> 4096, bf16, per-token mode).  Steps rotate over replicas of
+the inputs and weights whose total exceeds twice the 256 MB last-level
+(Infinity) cache, so every step reads its bytes from HBM.
+
+Metric: delta tokens/s (whole job) plus achieved HBM GB/s of the dominant
+kernel against the 8 TB/s peak.  Per-kernel durations come from HIP events
+recorded on the launch stream around every launch inside the timed region.
+The fp64 CPU oracle is timed beside it on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+LLC_BYTES = 256 * 2**20        # Infinity Cache
+KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemm_segments_amd", "csrc", f)
+                  for f in ("kernels.hip", "host.cpp", "lora_internal.h")] + \
+                 [os.path.join(ROOT, "include", "lora_sgmv.h")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="1..4 (2 = decode, the default)")
+    ap.add_argument("--shape", default="q", help="config 3 shape: q or up")
+    ap.add_argument("--order", type=int, default=0, help="BGMV order (0 auto, 1 token, 2 adapter)")
+    ap.add_argument("--policy", type=int, default=0, help="SGMV path policy (0 auto, 1 gather, 2 mfma)")
+    ap.add_argument("--graph", action="store_true", help="replay the timed steps as one HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bound on the oracle's CPU time (0 disables the CPU baseline)")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the LLC")
+    return ap.parse_args()
+
+
+def workload(cfg: int, shape: str):
+    from segmented_gather_gemm_segments_amd import workloads as wl
+    if cfg == 1:
+        return wl.tiny_sgmv()
+    if cfg == 2:
+        return wl.bgmv_decode()
+    if cfg == 3:
+        return wl.sgmv_prefill(shape=shape)
+    if cfg == 4:
+        return wl.hetero_paged()
+    raise SystemExit("bench.py times configs 1-4; the 70B layer is timed by --config 5 (not yet)")
+
+
+def read_traffic(kernel: str, workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, budget_s: float):
+    """The oracle as it stands (single-threaded C, fp64) on the same batch:
+    whole batches repeated until the time budget is used (at least one)."""
+    import oracle
+    ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
+    ids = p.ids
+    # bounded sample: a prefix of the batch sized to the budget
+    t0 = time.perf_counter()
+    oracle.apply(p.x[:8], p.y[:8], ids[:8], ad)
+    per_tok = max((time.perf_counter() - t0) / 8, 1e-7)
+    n_tok = int(min(p.num_tokens, max(8, budget_s / per_tok)))
+    reps, elapsed = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        oracle.apply(p.x[:n_tok], p.y[:n_tok], ids[:n_tok], ad)
+        reps += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s or n_tok < p.num_tokens or reps >= 1000:
+            break
+    sample = (f"{n_tok} of {p.num_tokens} tokens" if n_tok < p.num_tokens
+              else f"the full {p.num_tokens}-token batch") + f" x {reps} pass(es), {elapsed:.1f} s"
+    return {"value": n_tok * reps / elapsed, "unit": "delta tokens/s", "cores": 1,
+            "kind": "oracle", "sample": sample}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a built path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from segmented_gather_gemm_segments_amd import accounting as acc
+    from segmented_gather_gemm_segments_amd import binding as B
+    from segmented_gather_gemm_segments_amd import runner as R
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B.lib()
+    p = workload(args.config, args.shape)
+    elem = 2 if p.dtype == "bf16" else 4
+    mode = "bgmv" if p.mode == "bgmv" else "sgmv"
+
+    # ---- replicas (each its own x, y, v, weights): defeat the last-level cache
+    one = R.DeviceProblem(p)
+    per_rep = sum(t.numel() * t.element_size() for t in (one.x, one.y0, one.a_pages, one.b_pages))
+    n_rep = args.replicas or max(2, int(np.ceil(2 * LLC_BYTES / per_rep)))
+    n_rep = min(n_rep, 64)
+    reps = [one] + [R.DeviceProblem(p) for _ in range(n_rep - 1)]
+    calls = []
+    for dp in reps:
+        y, v = dp.y0.clone(), dp.new_v()
+        if mode == "bgmv":
+            calls.append(B.prepare_bgmv(dp.weights, dp.ids, dp.x, v, y, args.order))
+        else:
+            _, _, _, perm_d = dp.segments()
+            sp = dp.plan(B.LORA_PHASE_SHRINK, args.policy)
+            ep = dp.plan(B.LORA_PHASE_EXPAND, args.policy)
+            dp._plans = (sp, ep)
+            calls.append(B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y))
+    torch.cuda.synchronize()
+
+    # ---- warmup
+    for i in range(args.warmup):
+        s, e = calls[i % n_rep]
+        s()
+        e()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events around every launch
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        s, e = calls[i % n_rep]
+        ev[i][0].record()
+        s()
+        ev[i][1].record()
+        e()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_shrink = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]) * 1e-3
+    t_expand = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]) * 1e-3
+    gpu_span = ev[0][0].elapsed_time(ev[K - 1][2]) * 1e-3
+
+    # ---- accounting
+    sb = acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem)
+    eb = acc.expand_bytes(p.ids, p.ranks, p.d_out, elem)
+    tokens = int(np.sum(p.ids >= 0))
+    ms_per_step = wall / K * 1e3
+    kern = {
+        "shrink": {"avg_us": float(t_shrink.mean() * 1e6), "p10_us": float(np.percentile(t_shrink, 10) * 1e6),
+                   "p90_us": float(np.percentile(t_shrink, 90) * 1e6), "bytes": sb,
+                   "gbs": sb / t_shrink.mean() / 1e9},
+        "expand": {"avg_us": float(t_expand.mean() * 1e6), "p10_us": float(np.percentile(t_expand, 10) * 1e6),
+                   "p90_us": float(np.percentile(t_expand, 90) * 1e6), "bytes": eb,
+                   "gbs": eb / t_expand.mean() / 1e9},
+    }
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    kname = {"bgmv": {"shrink": "bgmv_shrink", "expand": "bgmv_expand"},
+             "sgmv": {"shrink": "sgmv_shrink", "expand": "sgmv_expand"}}[mode][dom]
+    traffic = read_traffic(kname, p.name)
+    achieved = kern[dom]["gbs"]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": kname, "algorithmic_bytes_per_launch": kern[dom]["bytes"],
+                "avg_launch_us": round(kern[dom]["avg_us"], 3)}
+    out = {
+        "metric": "LoRA delta tokens/sec per layer + achieved HBM GB/s (% of MI355X peak)",
+        "value": round(tokens * K / wall, 1),
+        "unit": "delta tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": p.dtype, "data": "synthetic (seeded; random-init adapters)",
+        "config": {"workload": p.name, "tokens": p.num_tokens, "adapters": p.num_adapters,
+                   "ranks": sorted(set(int(r) for r in p.ranks)), "d_in": p.d_in, "d_out": p.d_out,
+                   "mode": mode, "replicas": n_rep, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in d.items()}
+                    for k, d in kern.items()},
+        "gpu_tokens_per_s_kernel_time": round(tokens / (t_shrink.mean() + t_expand.mean()), 1),
+        "gpu_span_ms_per_step": round(gpu_span / K * 1e3, 5),
+        "kernel_sources_sha256_16": kernel_hash(),
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

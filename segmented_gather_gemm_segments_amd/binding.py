@@ -277,3 +277,46 @@ class Pool:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------- prepared launches
+class Prepared:
+    """A device call with its ctypes arguments marshalled once; calling it only
+    enqueues the launch (for launch-bound loops and graph capture).  Keeps the
+    descriptor and every tensor it points to alive."""
+
+    def __init__(self, fn_name: str, args: tuple, keep: tuple):
+        self._fn = getattr(lib(), fn_name)
+        self._args = args
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def prepare_bgmv(w: Weights, token_adapter, x, v, y, order: int = LORA_BGMV_AUTO, stream=None):
+    """(shrink, expand) prepared BGMV launches on `stream` (default: current)."""
+    d = w.desc()
+    s = _stream(stream)
+    n = int(token_adapter.numel())
+    keep = (d, w, token_adapter, x, v, y)
+    shrink = Prepared("lora_bgmv_shrink", (ctypes.byref(d), _dptr(token_adapter), n, order, _dptr(x),
+                                           _dptr(v), s), keep)
+    expand = Prepared("lora_bgmv_expand", (ctypes.byref(d), _dptr(token_adapter), n, order, _dptr(v),
+                                           _dptr(y), s), keep)
+    return shrink, expand
+
+
+def prepare_sgmv(w: Weights, token_perm, shrink_items, expand_items, x, v, y, stream=None):
+    """(shrink, expand) prepared SGMV launches on `stream` (default: current)."""
+    d = w.desc()
+    s = _stream(stream)
+    keep = (d, w, token_perm, shrink_items, expand_items, x, v, y)
+    npm = int(token_perm.numel())
+    shrink = Prepared("lora_sgmv_shrink", (ctypes.byref(d), _dptr(token_perm), npm, _dptr(shrink_items),
+                                           int(shrink_items.shape[0]), int(x.shape[0]), _dptr(x),
+                                           _dptr(v), s), keep)
+    expand = Prepared("lora_sgmv_expand", (ctypes.byref(d), _dptr(token_perm), npm, _dptr(expand_items),
+                                           int(expand_items.shape[0]), int(y.shape[0]), _dptr(v),
+                                           _dptr(y), s), keep)
+    return shrink, expand
