@@ -154,15 +154,22 @@ __device__ __forceinline__ f32x4_t frag_mfma(const Frag<float> &a, const Frag<fl
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ----------------------------------------------------------------- reductions
-// Reduce-scatter of 64 values over the 64 lanes of a wave: on return lane l
-// holds the wave-wide sum of vals[l].  Six halving butterfly steps (masks 32
-// .. 1); every index is summed over the same lane tree, so the result for a
-// value does not depend on which slot it occupies.
-__device__ __forceinline__ float wave_reduce_scatter64(float (&vals)[64]) {
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+// Reduce-scatter of NV values (a power of two <= 64) over the 64 lanes of a
+// wave: on return lane l holds the wave-wide sum of vals[l >> (6 - log2 NV)].
+// Halving butterfly steps with masks 32, 16, ... while values remain, then
+// plain butterflies for the rest.  The masks are always applied in the order
+// 32 .. 1, so every value is summed over the same lane tree whatever NV is: a
+// token's result does not depend on how many values were reduced beside it.
+template <int NV>
+__device__ __forceinline__ float wave_reduce_scatter(float (&vals)[NV]) {
+  static_assert(NV >= 1 && NV <= 64 && (NV & (NV - 1)) == 0, "NV must be a power of two <= 64");
+  constexpr int LOG = ilog2(NV);
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int step = 0; step < 6; ++step) {
-    const int n = 64 >> step;
+  for (int step = 0; step < LOG; ++step) {
+    const int n = NV >> step;
     const int m = 32 >> step;
     // bitwise select (v_bfi_b32): a value select here would be folded into
     // an address select and push the array out of registers
@@ -175,7 +182,31 @@ __device__ __forceinline__ float wave_reduce_scatter64(float (&vals)[64]) {
       vals[i] = keep + __shfl_xor(send, m, 64);
     }
   }
-  return vals[0];
+  float s = vals[0];
+#pragma unroll
+  for (int m = 32 >> LOG; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  return s;
+}
+
+// Raw 8-element chunks (16 B of bf16 or 32 B of fp32): loads are issued as a
+// batch first and converted afterwards, so a thread keeps many in flight.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> { uint4 u; };
+template <> struct Raw8<float> { float4 a, b; };
+__device__ __forceinline__ void raw_load(Raw8<uint16_t> &r, const uint16_t *p) {
+  r.u = *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void raw_load(Raw8<float> &r, const float *p) {
+  r.a = *reinterpret_cast<const float4 *>(p);
+  r.b = *reinterpret_cast<const float4 *>(p + 4);
+}
+__device__ __forceinline__ void raw_cvt(const Raw8<uint16_t> &r, float (&o)[8]) {
+  o[0] = bf16_lo(r.u.x); o[1] = bf16_hi(r.u.x); o[2] = bf16_lo(r.u.y); o[3] = bf16_hi(r.u.y);
+  o[4] = bf16_lo(r.u.z); o[5] = bf16_hi(r.u.z); o[6] = bf16_lo(r.u.w); o[7] = bf16_hi(r.u.w);
+}
+__device__ __forceinline__ void raw_cvt(const Raw8<float> &r, float (&o)[8]) {
+  o[0] = r.a.x; o[1] = r.a.y; o[2] = r.a.z; o[3] = r.a.w;
+  o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
 }
 
 // ----------------------------------------------------------------- shrink cores
@@ -186,150 +217,191 @@ constexpr int kMaxItemTokens = 256;
 struct ShrinkSmem {
   int toks[kMaxItemTokens];
   union {
-    float red_gemv[4 * 64];           // one value per (wave, lane)
+    float red_gemv[4 * 64];           // one value per (wave, value index)
     float red_mfma[4 * 4 * 4 * 64];   // [wave][row tile][element][lane]
   };
 };
 
-// One 8-element step of the GEMV shrink for row JJ of the current 16-row
-// pass: acc[t*16 + JJ] += A[JJ][k..k+7] . x_t[k..k+7].  Expanded per row at
-// compile time so the 64 accumulators stay in registers.
-template <int JJ, typename T>
-__device__ __forceinline__ void gemv_row(const T *const (&ar)[16], int k, const float (&xv)[4][8],
-                                         int ntok, float (&acc)[64]) {
-  if (ar[JJ]) {
-    float av[8];
-    load8(ar[JJ] + k, av);
+// One GEMV shrink tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) against rows
+// [j0, j0+nr) (nr <= RB) of adapter a.  The 256 threads run along d_in, 8
+// elements each per step; every step issues the TG x loads and RB A-row loads
+// together, then accumulates acc[t*RB + jj].  Rows and tokens beyond the tile
+// read a safe in-bounds address (row 0 of x) and their sums are dropped.  The
+// lane partials are reduce-scattered over the wave and the four wave results
+// summed in wave order.
+template <typename T, int TG, int RB>
+__device__ void shrink_gemv_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
+                                 int ntok, int num_tokens, const T *__restrict__ x,
+                                 float *__restrict__ v, ShrinkSmem &sm) {
+  constexpr int NV = TG * RB;
+  constexpr int SH = 6 - ilog2(NV);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const T *safe = x;
+  const T *xr[TG];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < ntok) {
+  for (int t = 0; t < TG; ++t) {
+    const int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
+    xr[t] = (tok >= 0 && tok < num_tokens) ? x + (int64_t)tok * w.d_in : safe;
+  }
+  const T *ar[RB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[t * 16 + JJ] = fmaf(av[e], xv[t][e], acc[t * 16 + JJ]);
-      }
+  for (int jj = 0; jj < RB; ++jj) {
+    const T *p = jj < nr ? a_row<T>(w, a, j0 + jj) : nullptr;
+    ar[jj] = p ? p : safe;
+  }
+  float acc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+  for (int k = tid * 8; k < w.d_in; k += kThreads * 8) {
+    Raw8<T> xraw[TG], araw[RB];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) raw_load(xraw[t], xr[t] + k);
+#pragma unroll
+    for (int jj = 0; jj < RB; ++jj) raw_load(araw[jj], ar[jj] + k);
+    float xv[TG][8];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) raw_cvt(xraw[t], xv[t]);
+#pragma unroll
+    for (int jj = 0; jj < RB; ++jj) {
+      float av[8];
+      raw_cvt(araw[jj], av);
+#pragma unroll
+      for (int t = 0; t < TG; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t * RB + jj] = fmaf(av[e], xv[t][e], acc[t * RB + jj]);
     }
   }
-}
-template <typename T, int... JJ>
-__device__ __forceinline__ void gemv_rows(const T *const (&ar)[16], int k, const float (&xv)[4][8],
-                                          int ntok, float (&acc)[64],
-                                          std::integer_sequence<int, JJ...>) {
-  (gemv_row<JJ>(ar, k, xv, ntok, acc), ...);
+  const float part = wave_reduce_scatter<NV>(acc);
+  if ((lane & ((1 << SH) - 1)) == 0) sm.red_gemv[wave * 64 + (lane >> SH)] = part;
+  __syncthreads();
+  if (tid < NV) {
+    const float s = ((sm.red_gemv[tid] + sm.red_gemv[64 + tid]) + sm.red_gemv[128 + tid]) +
+                    sm.red_gemv[192 + tid];
+    const int t = tid / RB, jj = tid % RB;
+    if (t < ntok && jj < nr) {
+      const int tok = toks[g0 + t];
+      if (tok >= 0 && tok < num_tokens) v[(int64_t)tok * w.r_max + j0 + jj] = s;
+    }
+  }
+  __syncthreads();
 }
 
-// Gather/GEMV shrink for tokens toks[0..cnt) of adapter a, rows [j_lo, j_hi).
-// The 256 threads run along d_in, 8 elements (16 B of bf16) each per step;
-// each step loads the x chunk of up to 4 tokens once and reuses it across 16
-// A rows.  Lane partials (4 tokens x 16 rows = 64 values) are reduce-scattered
-// across the wave and the four wave results are summed in wave order.
+// Gather/GEMV shrink for tokens toks[0..cnt) of adapter a, rows [j_lo, j_hi):
+// one token at a time in passes of 8 or 16 rows, or groups of up to 4 tokens
+// in passes of 8 rows.
 template <typename T>
 __device__ void shrink_gemv(const DevW &w, int a, int j_lo, int j_hi, const int *toks, int cnt,
                             int num_tokens, const T *__restrict__ x, float *__restrict__ v,
                             ShrinkSmem &sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = (j_hi - j_lo) <= 8 ? 8 : 16;
   for (int g0 = 0; g0 < cnt; g0 += 4) {
     const int ntok = min(4, cnt - g0);
-    const T *xr[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
-      xr[t] = (tok >= 0 && tok < num_tokens) ? x + (int64_t)tok * w.d_in : nullptr;
-    }
-    for (int j0 = j_lo; j0 < j_hi; j0 += 16) {
-      const int nr = min(16, j_hi - j0);
-      const T *ar[16];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) ar[jj] = jj < nr ? a_row<T>(w, a, j0 + jj) : nullptr;
-      float acc[64];
-#pragma unroll
-      for (int i = 0; i < 64; ++i) acc[i] = 0.f;
-      for (int k = tid * 8; k < w.d_in; k += kThreads * 8) {
-        float xv[4][8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (xr[t]) {
-            load8(xr[t] + k, xv[t]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xv[t][e] = 0.f;
-          }
-        }
-        gemv_rows(ar, k, xv, ntok, acc, std::make_integer_sequence<int, 16>{});
+    for (int j0 = j_lo; j0 < j_hi; j0 += rb) {
+      const int nr = min(rb, j_hi - j0);
+      if (ntok == 1) {
+        if (rb == 8) shrink_gemv_tile<T, 1, 8>(w, a, j0, nr, toks, g0, ntok, num_tokens, x, v, sm);
+        else shrink_gemv_tile<T, 1, 16>(w, a, j0, nr, toks, g0, ntok, num_tokens, x, v, sm);
+      } else {
+        // several tokens: 8-row passes keep the 4 x 8 accumulators and the
+        // batch of loads within the register budget
+        for (int j8 = j0; j8 < j0 + nr; j8 += 8)
+          shrink_gemv_tile<T, 4, 8>(w, a, j8, min(8, j0 + nr - j8), toks, g0, ntok, num_tokens, x,
+                                    v, sm);
       }
-      const float part = wave_reduce_scatter64(acc);   // lane l: value (t = l/16, jj = l%16)
-      sm.red_gemv[wave * 64 + lane] = part;
-      __syncthreads();
-      if (tid < 64) {
-        const float s = ((sm.red_gemv[tid] + sm.red_gemv[64 + tid]) + sm.red_gemv[128 + tid]) +
-                        sm.red_gemv[192 + tid];
-        const int t = tid >> 4, jj = tid & 15;
-        if (t < ntok && jj < nr) {
-          const int tok = toks[g0 + t];
-          if (tok >= 0 && tok < num_tokens) v[(int64_t)tok * w.r_max + j0 + jj] = s;
-        }
-      }
-      __syncthreads();
     }
   }
 }
 
-// MFMA shrink for tokens toks[0..cnt) of adapter a (all rows < r).  One
-// 16-token tile at a time: the four waves split d_in (32-element steps
-// interleaved), each wave accumulates D[j][token] = A_rows · x^T for up to 4
-// row tiles of 16, and the four partial tiles are summed in wave order.
+// One MFMA shrink tile: 16 tokens (this lane's token row xp, or a safe row)
+// against RT row tiles of 16 starting at j0.  The four waves take interleaved
+// 32-element k-steps; each batch issues the loads of U steps before its
+// MFMAs.  Lanes beyond the rank or the tile read safe rows whose outputs are
+// dropped; the last, partial k-step zeroes both operands past d_in.
+template <typename T, int RT>
+__device__ void shrink_mfma_tile(const DevW &w, int a, int r, int j0, const T *xp, int tok,
+                                 const T *__restrict__ x, float *__restrict__ v, ShrinkSmem &sm) {
+  constexpr int U = RT == 1 ? 8 : 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const T *safe = x;
+  const T *ap[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = j0 + rt * 16 + m;
+    const T *p = row < r ? a_row<T>(w, a, row) : nullptr;
+    ap[rt] = p ? p : safe;
+  }
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int full = w.d_in >> 5;             // k-steps entirely inside d_in
+  const int nsteps = (w.d_in + 31) >> 5;
+  int s = wave;
+  for (; s + 4 * (U - 1) < full; s += 4 * U) {
+    Frag<T> xf[U], af[U][RT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s + 4 * u) * 32 + g * 8;
+      frag_load(xf[u], xp + k);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) frag_load(af[u][rt], ap[rt] + k);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = frag_mfma(af[u][rt], xf[u], acc[rt]);
+  }
+  for (; s < nsteps; s += 4) {
+    const int k = s * 32 + g * 8;
+    const bool kin = k < w.d_in;
+    Frag<T> xf, af[RT];
+    if (kin) frag_load(xf, xp + k); else frag_zero(xf);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (kin) frag_load(af[rt], ap[rt] + k); else frag_zero(af[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = frag_mfma(af[rt], xf, acc[rt]);
+  }
+  // lane (g, m) of row tile rt holds D[4g + e][m] = v[tok(m)][j0 + 16 rt + 4g + e]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.red_mfma[((wave * 4 + rt) * 4 + e) * 64 + lane] = acc[rt][e];
+  __syncthreads();
+  if (wave < RT) {
+    const int rt = wave;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float s4 = ((sm.red_mfma[((0 * 4 + rt) * 4 + e) * 64 + lane] +
+                         sm.red_mfma[((1 * 4 + rt) * 4 + e) * 64 + lane]) +
+                        sm.red_mfma[((2 * 4 + rt) * 4 + e) * 64 + lane]) +
+                       sm.red_mfma[((3 * 4 + rt) * 4 + e) * 64 + lane];
+      const int j = j0 + rt * 16 + 4 * g + e;
+      if (tok >= 0 && j < r) v[(int64_t)tok * w.r_max + j] = s4;
+    }
+  }
+  __syncthreads();
+}
+
+// MFMA shrink for tokens toks[0..cnt) of adapter a: 16-token tiles, passes of
+// up to 64 rows.
 template <typename T>
 __device__ void shrink_mfma(const DevW &w, int a, int r, const int *toks, int cnt, int num_tokens,
                             const T *__restrict__ x, float *__restrict__ v, ShrinkSmem &sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 15, g = lane >> 4;
+  const int m = threadIdx.x & 15;
   for (int m0 = 0; m0 < cnt; m0 += 16) {
     int tok = m0 + m < cnt ? toks[m0 + m] : -1;
     if (tok >= num_tokens) tok = -1;
-    const T *xr = tok >= 0 ? x + (int64_t)tok * w.d_in : nullptr;
+    const T *xp = tok >= 0 ? x + (int64_t)tok * w.d_in : x;
     for (int j0 = 0; j0 < r; j0 += 64) {
       const int nrt = min(4, (r - j0 + 15) >> 4);
-      const T *ar[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int row = j0 + rt * 16 + m;
-        ar[rt] = (rt < nrt && row < r) ? a_row<T>(w, a, row) : nullptr;
+      switch (nrt) {
+        case 1: shrink_mfma_tile<T, 1>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 2: shrink_mfma_tile<T, 2>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 3: shrink_mfma_tile<T, 3>(w, a, r, j0, xp, tok, x, v, sm); break;
+        default: shrink_mfma_tile<T, 4>(w, a, r, j0, xp, tok, x, v, sm); break;
       }
-      f32x4_t acc[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int s = wave; s * 32 < w.d_in; s += 4) {
-        const int k = s * 32 + g * 8;
-        const bool kin = k < w.d_in;
-        Frag<T> xf;
-        if (xr && kin) frag_load(xf, xr + k); else frag_zero(xf);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          if (rt < nrt) {
-            Frag<T> af;
-            if (ar[rt] && kin) frag_load(af, ar[rt] + k); else frag_zero(af);
-            acc[rt] = frag_mfma(af, xf, acc[rt]);
-          }
-        }
-      }
-      // lane (g, m) of row tile rt holds D[4g + e][m] = v[tok(m)][j0 + 16 rt + 4g + e]
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        if (rt < nrt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.red_mfma[((wave * 4 + rt) * 4 + e) * 64 + lane] = acc[rt][e];
-      __syncthreads();
-      if (wave < nrt) {
-        const int rt = wave;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float s = ((sm.red_mfma[((0 * 4 + rt) * 4 + e) * 64 + lane] +
-                            sm.red_mfma[((1 * 4 + rt) * 4 + e) * 64 + lane]) +
-                           sm.red_mfma[((2 * 4 + rt) * 4 + e) * 64 + lane]) +
-                          sm.red_mfma[((3 * 4 + rt) * 4 + e) * 64 + lane];
-          const int j = j0 + rt * 16 + 4 * g + e;
-          if (tok >= 0 && j < r) v[(int64_t)tok * w.r_max + j] = s;
-        }
-      }
-      __syncthreads();
     }
   }
 }
@@ -348,73 +420,100 @@ struct ExpandSmem {
   };
 };
 
-// Gather/GEMV expand for tokens toks[0..cnt) of adapter a over the 512
-// columns of block `blk`: lane l owns 8 consecutive columns; wave w
-// accumulates rank indices j = w, w+4, ...; the four wave partials are summed
-// in wave order and added to y once.
+// One GEMV expand tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) over the 512
+// columns of block `blk`.  Lane l owns 8 consecutive columns; wave w
+// accumulates rank indices j = w, w+4, ..., loading the B^T chunks of JW such
+// indices at a time; the four wave partials are summed in wave order and
+// added to y once (wave t finalises token t, its y chunk prefetched at the
+// start).
+template <typename T, int TG>
+__device__ void expand_gemv_tile(const DevW &w, int a, int r, int blk, const int *toks, int g0,
+                                 int ntok, int num_tokens, const float *__restrict__ v,
+                                 T *__restrict__ y, ExpandSmem<T> &sm) {
+  constexpr int JW = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = blk * LORA_EXPAND_GATHER_COLS + lane * 8;
+  const bool cin = col < w.d_out;
+  const int colc = cin ? col : 0;
+  int tk[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
+    tk[t] = (tok >= 0 && tok < num_tokens) ? tok : -1;
+  }
+  // prefetch the y chunk this wave finalises
+  const int my_tok = wave < ntok ? toks[g0 + wave] : -1;
+  const bool my_ok = my_tok >= 0 && my_tok < num_tokens && cin;
+  T *yp = my_ok ? y + (int64_t)my_tok * w.d_out + col : nullptr;
+  Raw8<T> yraw;
+  if (my_ok) raw_load(yraw, yp);
+  const T *safe = reinterpret_cast<const T *>(w.b_pages);
+  float acc[TG][8];
+#pragma unroll
+  for (int t = 0; t < TG; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+  for (int jb = wave; jb < r; jb += 4 * JW) {
+    Raw8<T> braw[JW];
+#pragma unroll
+    for (int i = 0; i < JW; ++i) {
+      const int j = jb + 4 * i;
+      const T *p = j < r ? b_row<T>(w, a, j) : nullptr;
+      raw_load(braw[i], p ? p + colc : safe);
+    }
+    float vj[TG][JW];
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int i = 0; i < JW; ++i) {
+        const int j = jb + 4 * i;
+        vj[t][i] = (tk[t] >= 0 && j < r) ? v[(int64_t)tk[t] * w.r_max + j] : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < JW; ++i) {
+      if (jb + 4 * i < r) {
+        float bv[8];
+        raw_cvt(braw[i], bv);
+#pragma unroll
+        for (int t = 0; t < TG; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vj[t][i], bv[e], acc[t][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TG; ++t)
+    if (t < ntok)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.red_gemv[((wave * 4 + t) * 8 + e) * 64 + lane] = acc[t][e];
+  __syncthreads();
+  if (my_ok) {
+    const int t = wave;
+    float yv[8];
+    raw_cvt(yraw, yv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = ((sm.red_gemv[((0 * 4 + t) * 8 + e) * 64 + lane] +
+                        sm.red_gemv[((1 * 4 + t) * 8 + e) * 64 + lane]) +
+                       sm.red_gemv[((2 * 4 + t) * 8 + e) * 64 + lane]) +
+                      sm.red_gemv[((3 * 4 + t) * 8 + e) * 64 + lane];
+      yv[e] += s;
+    }
+    store8(yp, yv);
+  }
+  __syncthreads();
+}
+
 template <typename T>
 __device__ void expand_gemv(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y,
                             ExpandSmem<T> &sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = blk * LORA_EXPAND_GATHER_COLS + lane * 8;
-  const bool cin = col < w.d_out;
   for (int g0 = 0; g0 < cnt; g0 += 4) {
     const int ntok = min(4, cnt - g0);
-    int tk[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
-      tk[t] = (tok >= 0 && tok < num_tokens) ? tok : -1;
-    }
-    float acc[4][8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
-    for (int j = wave; j < r; j += 4) {
-      const T *br = b_row<T>(w, a, j);
-      float bv[8];
-      if (br && cin) {
-        load8(br + col, bv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (tk[t] >= 0) {
-          const float vj = v[(int64_t)tk[t] * w.r_max + j];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vj, bv[e], acc[t][e]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (t < ntok)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.red_gemv[((wave * 4 + t) * 8 + e) * 64 + lane] = acc[t][e];
-    __syncthreads();
-    if (wave < ntok) {
-      const int t = wave;
-      const int tok = toks[g0 + t];
-      if (tok >= 0 && tok < num_tokens && cin) {
-        T *yp = y + (int64_t)tok * w.d_out + col;
-        float yv[8];
-        load8(yp, yv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float s = ((sm.red_gemv[((0 * 4 + t) * 8 + e) * 64 + lane] +
-                            sm.red_gemv[((1 * 4 + t) * 8 + e) * 64 + lane]) +
-                           sm.red_gemv[((2 * 4 + t) * 8 + e) * 64 + lane]) +
-                          sm.red_gemv[((3 * 4 + t) * 8 + e) * 64 + lane];
-          yv[e] += s;
-        }
-        store8(yp, yv);
-      }
-    }
-    __syncthreads();
+    if (ntok == 1)
+      expand_gemv_tile<T, 1>(w, a, r, blk, toks, g0, ntok, num_tokens, v, y, sm);
+    else
+      expand_gemv_tile<T, 4>(w, a, r, blk, toks, g0, ntok, num_tokens, v, y, sm);
   }
 }
 
@@ -426,10 +525,25 @@ __device__ __forceinline__ int slab_col(int t, int rho) {
   return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3);
 }
 
+// v[tok][jb .. jb+7] as 8 floats (zero past nj or for no token).
+__device__ __forceinline__ void load_v8(const float *vr, int jb, int nj, bool vec, float (&o)[8]) {
+  if (vr && vec && jb + 8 <= nj) {
+    const float4 p = *reinterpret_cast<const float4 *>(vr + jb);
+    const float4 q = *reinterpret_cast<const float4 *>(vr + jb + 4);
+    o[0] = p.x; o[1] = p.y; o[2] = p.z; o[3] = p.w; o[4] = q.x; o[5] = q.y; o[6] = q.z; o[7] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (vr && jb + e < nj) ? vr[jb + e] : 0.f;
+  }
+}
+
 // MFMA expand for tokens toks[0..cnt) of adapter a over the 256 columns of
-// block `blk` (wave w: 64 columns).  D[col][token] = B^T-slab^T · v^T with the
-// B^T slab staged transposed in LDS.  bf16: v is split into hi + lo bf16 so
-// each K=32 MFMA covers 16 rank indices exactly; fp32: 16x16x4 steps.
+// block `blk` (wave w: 64 columns), 64 tokens (four 16-token tiles) at a time.
+// D[col][token] = B^T-slab^T · v^T with the B^T slab staged transposed in LDS;
+// the slab fragments of a 16-index K block are read once and used by all four
+// token tiles.  bf16: v is split into hi + lo bf16 so each K=32 MFMA covers 16
+// rank indices exactly; fp32: 16x16x4 steps.  The y chunks of the 64 tokens
+// are prefetched before the slab is staged.
 template <typename T>
 __device__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y,
@@ -438,6 +552,7 @@ __device__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *tok
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int c0 = blk * LORA_EXPAND_MFMA_COLS + wave * 64;
+  const bool vec_v = (w.r_max & 3) == 0;
   T *bt = sm.bt + wave * 64 * RS;
   for (int m0 = 0; m0 < cnt; m0 += 64) {
     const int ntt = min(4, (cnt - m0 + 15) >> 4);
@@ -445,9 +560,19 @@ __device__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *tok
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const int i = m0 + tt * 16 + m;
-      int t = (tt < ntt && i < cnt) ? toks[i] : -1;
+      const int t = (tt < ntt && i < cnt) ? toks[i] : -1;
       tok[tt] = (t >= 0 && t < num_tokens) ? t : -1;
     }
+    // prefetch y: lane (g, m) of tile tt touches columns c0 + 32q + 8g .. +7
+    Raw8<T> yraw[4][2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int col = c0 + 32 * q + 8 * g;
+        if (tt < ntt && tok[tt] >= 0 && col < w.d_out)
+          raw_load(yraw[tt][q], y + (int64_t)tok[tt] * w.d_out + col);
+      }
     f32x4_t acc[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -477,43 +602,54 @@ __device__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *tok
         }
       }
       __syncthreads();
+      const float *vr[4];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (tt < ntt) {
-          const float *vr = tok[tt] >= 0 ? v + (int64_t)tok[tt] * w.r_max + jc : nullptr;
-          for (int kb = 0; kb * 16 < nj; ++kb) {
-            if constexpr (sizeof(T) == 2) {
-              // B operand: lane (g, m) -> rank indices kb*16 + (g&1)*8 + e, hi (g<2) or lo
-              const int jb = kb * 16 + (g & 1) * 8;
+      for (int tt = 0; tt < 4; ++tt) vr[tt] = tok[tt] >= 0 ? v + (int64_t)tok[tt] * w.r_max + jc : nullptr;
+      for (int kb = 0; kb * 16 < nj; ++kb) {
+        if constexpr (sizeof(T) == 2) {
+          // A operand (B^T slab, transposed): sub-tile t, row rho = m -> column slab_col(t, m),
+          // rank indices kb*16 + (g&1)*8 .. +7 for both the hi (g < 2) and lo (g >= 2) halves
+          const int jb = kb * 16 + (g & 1) * 8;
+          bf16x8_t aop[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            aop[t] = __builtin_bit_cast(bf16x8_t,
+                                        *reinterpret_cast<const uint4 *>(bt + slab_col(t, m) * RS + jb));
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            if (tt < ntt) {
+              float f[8];
+              load_v8(vr[tt], jb, nj, vec_v, f);
               uint32_t h[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
-                const float f = (vr && jb + e < nj) ? vr[jb + e] : 0.f;
-                uint32_t hb = bf16_rne(f);
-                if (g >= 2) hb = bf16_rne(f - __uint_as_float(hb << 16));
+                uint32_t hb = bf16_rne(f[e]);
+                if (g >= 2) hb = bf16_rne(f[e] - __uint_as_float(hb << 16));
                 h[e] = hb;
               }
-              const uint4 bu = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                          h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-              const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bu);
+              const bf16x8_t bop = __builtin_bit_cast(
+                  bf16x8_t, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                       h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
 #pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const uint4 au =
-                    *reinterpret_cast<const uint4 *>(bt + slab_col(t, m) * RS + jb);
-                acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, au), bop, acc[tt][t], 0, 0, 0);
-              }
-            } else {
-              // four K=4 steps: lane group g takes rank index kb*16 + 4q + g
+              for (int t = 0; t < 4; ++t)
+                acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop, acc[tt][t], 0, 0, 0);
+            }
+          }
+        } else {
+          // four K=4 steps: lane group g takes rank index kb*16 + 4q + g
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int j = kb * 16 + 4 * q + g;
-                const float bop = (vr && j < nj) ? vr[j] : 0.f;
+          for (int q = 0; q < 4; ++q) {
+            const int j = kb * 16 + 4 * q + g;
+            float aop[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  const float aop = bt[slab_col(t, m) * RS + j];
-                  acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop, acc[tt][t], 0, 0, 0);
-                }
+            for (int t = 0; t < 4; ++t) aop[t] = bt[slab_col(t, m) * RS + j];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              if (tt < ntt) {
+                const float bop = (vr[tt] && j < nj) ? vr[tt][j] : 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[t], bop, acc[tt][t], 0, 0, 0);
               }
             }
           }
@@ -523,21 +659,18 @@ __device__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *tok
     // y update: lane (g, m) holds columns c0 + 32q + 8g .. +7 of token tok[tt]
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      if (tt < ntt && tok[tt] >= 0) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int col = c0 + 32 * q + 8 * g;
-          if (col < w.d_out) {
-            T *yp = y + (int64_t)tok[tt] * w.d_out + col;
-            float yv[8];
-            load8(yp, yv);
+      for (int q = 0; q < 2; ++q) {
+        const int col = c0 + 32 * q + 8 * g;
+        if (tt < ntt && tok[tt] >= 0 && col < w.d_out) {
+          float yv[8];
+          raw_cvt(yraw[tt][q], yv);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              yv[e] += acc[tt][2 * q][e];
-              yv[4 + e] += acc[tt][2 * q + 1][e];
-            }
-            store8(yp, yv);
+          for (int e = 0; e < 4; ++e) {
+            yv[e] += acc[tt][2 * q][e];
+            yv[4 + e] += acc[tt][2 * q + 1][e];
           }
+          store8(y + (int64_t)tok[tt] * w.d_out + col, yv);
         }
       }
     }
