@@ -118,15 +118,25 @@ lora_status lora_segments_build(const int32_t *token_adapter, int32_t num_tokens
  * flat list of work items, heaviest first, that covers every (token, output)
  * pair of the batch exactly once; item k is executed by workgroup k.
  *
- * Items do not depend on the adapters' ranks.  A shrink plan does not depend
- * on d_in; an expand plan depends on d_out (its column blocks).  A plan stays
- * valid for every layer and projection with the same segments (and, for
- * expand, the same d_out): build once per batch, upload once, launch many.   */
+ * Items:
+ *   shrink, gather path: up to LORA_SHRINK_GATHER_TOKENS tokens x one group of
+ *     LORA_SHRINK_GATHER_ROWS rows of A (block = row group); one item per row
+ *     group the adapter's rank needs;
+ *   shrink, MFMA path: up to LORA_SHRINK_MFMA_TOKENS tokens x every row (block 0);
+ *   expand, gather path: up to LORA_EXPAND_GATHER_TOKENS tokens x one block of
+ *     LORA_EXPAND_GATHER_COLS columns of y;
+ *   expand, MFMA path: up to LORA_EXPAND_MFMA_TOKENS tokens x one block of
+ *     LORA_EXPAND_MFMA_COLS columns.
+ * A shrink plan depends on the adapters' ranks (host_rank, or r_max for every
+ * adapter when host_rank is NULL) but not on d_in; an expand plan depends on
+ * d_out but not on the ranks.  A plan stays valid for every projection with
+ * the same segments, ranks (shrink) and d_out (expand): build once per batch,
+ * upload once, launch many.                                                  */
 typedef struct {
   int32_t perm_begin;  /* first token of the item, as an index into token_perm */
   int32_t adapter;     /* adapter of the item's segment */
   int32_t count_path;  /* token count (bits 0..15) | path << 16 */
-  int32_t block;       /* expand: column block index; shrink: 0 */
+  int32_t block;       /* shrink: row group (gather) or 0 (MFMA); expand: column block */
 } lora_item;
 
 #define LORA_PHASE_SHRINK 0
@@ -138,28 +148,33 @@ typedef struct {
 
 #define LORA_DEFAULT_MFMA_MIN_TOKENS 16
 
-/* Tokens per item and columns per expand item, by path.  */
+/* Tokens, rows and columns per item, by path.  */
 #define LORA_SHRINK_GATHER_TOKENS 4
+#define LORA_SHRINK_GATHER_ROWS 4
 #define LORA_SHRINK_MFMA_TOKENS 16
 #define LORA_EXPAND_GATHER_TOKENS 4
 #define LORA_EXPAND_MFMA_TOKENS 64
-#define LORA_EXPAND_GATHER_COLS 512
+#define LORA_EXPAND_GATHER_COLS 2048
 #define LORA_EXPAND_MFMA_COLS 256
 
 /* Builds the plan for `phase` from the host copies of segment_build's output.
- *   dim            expand: d_out (sets the column blocks); shrink: d_in (unused)
+ *   host_rank      shrink: host [num_adapters] ranks (1..r_max), or NULL (every
+ *                  adapter planned at r_max); expand: ignored
+ *   dim            shrink: r_max (1..LORA_MAX_RANK); expand: d_out (> 0, a
+ *                  multiple of 8)
  *   path_policy    LORA_PATH_AUTO / _GATHER / _MFMA
  *   mfma_min_tokens  AUTO threshold (<= 0 selects LORA_DEFAULT_MFMA_MIN_TOKENS)
  *   items, capacity  caller-owned host array; with items == NULL only the item
  *                    count is returned (in *num_items)
  * Errors: LORA_EINVAL (bad sizes, non-increasing seg_starts, unknown policy or
- * phase), LORA_ERANGE (a segment adapter outside [0, num_adapters)),
- * LORA_ENOMEM (capacity too small; *num_items still holds the needed count). */
+ * phase), LORA_ERANGE (a segment adapter outside [0, num_adapters), a rank
+ * outside 1..r_max), LORA_EUNSUPPORTED (dim out of range), LORA_ENOMEM
+ * (capacity too small; *num_items still holds the needed count).            */
 lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
                            const int32_t *seg_adapter, int32_t num_segments,
-                           int32_t num_adapters, int32_t dim, int32_t path_policy,
-                           int32_t mfma_min_tokens, lora_item *items, int32_t capacity,
-                           int32_t *num_items);
+                           int32_t num_adapters, const int32_t *host_rank, int32_t dim,
+                           int32_t path_policy, int32_t mfma_min_tokens, lora_item *items,
+                           int32_t capacity, int32_t *num_items);
 
 /* ------------------------------------------------------------------------ */
 /* Adapter weights as the kernels read them (the adapter-row gather through the
@@ -213,9 +228,15 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
  * (S-LoRA's decode kernel, MBGMV, in the same section: mixed ranks in one
  * batch).  Same arithmetic as the segmented calls.
  *   token_adapter [num_tokens]  device; ids outside [0, N) (and -1) are skipped
- *   order  LORA_BGMV_AUTO, _TOKEN_MAJOR (one workgroup per token) or
- *          _ADAPTER_MAJOR (one workgroup per adapter and block: each adapter's
- *          rows are read once however many tokens use it).                  */
+ *   order  LORA_BGMV_TOKEN_MAJOR: workgroups per token (shrink: one per
+ *          group of LORA_SHRINK_GATHER_ROWS rows; expand: one per block of
+ *          LORA_EXPAND_GATHER_COLS columns);
+ *          LORA_BGMV_ADAPTER_MAJOR: the same split per adapter, each workgroup
+ *          scanning token_adapter for its adapter's tokens, so each adapter's
+ *          rows are read once however many tokens use it;
+ *          LORA_BGMV_AUTO: shrink adapter-major when num_adapters <= num_tokens,
+ *          expand adapter-major when num_tokens >= 16 num_adapters, otherwise
+ *          token-major.  Every order gives bit-identical results.           */
 #define LORA_BGMV_AUTO 0
 #define LORA_BGMV_TOKEN_MAJOR 1
 #define LORA_BGMV_ADAPTER_MAJOR 2

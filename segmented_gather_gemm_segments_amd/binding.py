@@ -25,6 +25,9 @@ LORA_PHASE_SHRINK, LORA_PHASE_EXPAND = 0, 1
 LORA_PATH_AUTO, LORA_PATH_GATHER, LORA_PATH_MFMA = 0, 1, 2
 LORA_BGMV_AUTO, LORA_BGMV_TOKEN_MAJOR, LORA_BGMV_ADAPTER_MAJOR = 0, 1, 2
 LORA_DEFAULT_MFMA_MIN_TOKENS = 16
+LORA_SHRINK_GATHER_TOKENS, LORA_SHRINK_GATHER_ROWS, LORA_SHRINK_MFMA_TOKENS = 4, 4, 16
+LORA_EXPAND_GATHER_TOKENS, LORA_EXPAND_MFMA_TOKENS = 4, 64
+LORA_EXPAND_GATHER_COLS, LORA_EXPAND_MFMA_COLS = 2048, 256
 
 
 class LoraError(RuntimeError):
@@ -57,7 +60,7 @@ EXPORTS = {
     "lora_last_error": ([], ctypes.c_char_p),
     "lora_status_name": ([_I32], ctypes.c_char_p),
     "lora_segments_build": ([_P, _I32, _I32, _P, _P, _P, _P], _I32),
-    "lora_sgmv_plan": ([_I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P], _I32),
+    "lora_sgmv_plan": ([_I32, _P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, _P], _I32),
     "lora_sgmv_shrink": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_sgmv_expand": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
@@ -130,17 +133,21 @@ def lora_segments_build(token_adapter, num_adapters: int):
 
 def lora_sgmv_plan(phase: int, seg_starts, seg_adapter, num_adapters: int, dim: int,
                    path_policy: int = LORA_PATH_AUTO,
-                   mfma_min_tokens: int = LORA_DEFAULT_MFMA_MIN_TOKENS) -> np.ndarray:
-    """Work plan as an int32 array [num_items, 4] (perm_begin, adapter, count|path<<16, block)."""
+                   mfma_min_tokens: int = LORA_DEFAULT_MFMA_MIN_TOKENS,
+                   host_rank=None) -> np.ndarray:
+    """Work plan as an int32 array [num_items, 4] (perm_begin, adapter, count|path<<16, block).
+    dim: r_max for a shrink plan, d_out for an expand plan."""
     starts, adapters = _i32(seg_starts), _i32(seg_adapter)
+    ranks = None if host_rank is None else _i32(host_rank)
     s = adapters.size
     n = ctypes.c_int32(0)
-    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters, dim,
-                                path_policy, mfma_min_tokens, None, 0, ctypes.byref(n)))
-    items = np.zeros((max(n.value, 1), 4), np.int32)
-    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters, dim,
-                                path_policy, mfma_min_tokens, _np_ptr(items), n.value,
+    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters,
+                                _np_ptr(ranks), dim, path_policy, mfma_min_tokens, None, 0,
                                 ctypes.byref(n)))
+    items = np.zeros((max(n.value, 1), 4), np.int32)
+    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters,
+                                _np_ptr(ranks), dim, path_policy, mfma_min_tokens, _np_ptr(items),
+                                n.value, ctypes.byref(n)))
     return items[: n.value]
 
 

@@ -109,20 +109,22 @@ struct PlanItem {
 
 extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
                                       const int32_t *seg_adapter, int32_t num_segments,
-                                      int32_t num_adapters, int32_t dim, int32_t path_policy,
-                                      int32_t mfma_min_tokens, lora_item *items, int32_t capacity,
-                                      int32_t *num_items) {
+                                      int32_t num_adapters, const int32_t *host_rank, int32_t dim,
+                                      int32_t path_policy, int32_t mfma_min_tokens,
+                                      lora_item *items, int32_t capacity, int32_t *num_items) {
   if (!num_items) return fail(LORA_EINVAL, "null num_items");
   if (phase != LORA_PHASE_SHRINK && phase != LORA_PHASE_EXPAND)
     return fail(LORA_EINVAL, "unknown phase %d", phase);
   if (path_policy < LORA_PATH_AUTO || path_policy > LORA_PATH_MFMA)
     return fail(LORA_EINVAL, "unknown path policy %d", path_policy);
-  if (num_segments < 0 || capacity < 0) return fail(LORA_EINVAL, "negative size");
+  if (num_segments < 0 || capacity < 0 || num_adapters < 0) return fail(LORA_EINVAL, "negative size");
   if (num_segments > 0 && (!seg_starts || !seg_adapter))
     return fail(LORA_EINVAL, "null segment arrays");
   if (phase == LORA_PHASE_EXPAND && (dim <= 0 || dim % 8 != 0))
     return fail(LORA_EUNSUPPORTED, "expand plan needs d_out > 0 and a multiple of 8 (got %d)",
                 dim);
+  if (phase == LORA_PHASE_SHRINK && (dim < 1 || dim > LORA_MAX_RANK))
+    return fail(LORA_EUNSUPPORTED, "shrink plan needs r_max in 1..%d (got %d)", LORA_MAX_RANK, dim);
   if (mfma_min_tokens <= 0) mfma_min_tokens = LORA_DEFAULT_MFMA_MIN_TOKENS;
   if (num_segments > 0 && seg_starts[0] < 0) return fail(LORA_EINVAL, "seg_starts[0] < 0");
   for (int32_t s = 0; s < num_segments; ++s) {
@@ -131,40 +133,51 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
     if (seg_adapter[s] < 0 || seg_adapter[s] >= num_adapters)
       return fail(LORA_ERANGE, "segment %d has adapter %d outside [0, %d)", s, seg_adapter[s],
                   num_adapters);
+    if (phase == LORA_PHASE_SHRINK && host_rank) {
+      const int32_t r = host_rank[seg_adapter[s]];
+      if (r < 1 || r > dim)
+        return fail(LORA_ERANGE, "adapter %d has rank %d outside 1..r_max (%d)", seg_adapter[s], r,
+                    dim);
+    }
   }
   std::vector<PlanItem> plan;
   for (int32_t s = 0; s < num_segments; ++s) {
     const int32_t begin = seg_starts[s], len = seg_starts[s + 1] - seg_starts[s];
+    const int32_t a = seg_adapter[s];
     const bool mfma = path_policy == LORA_PATH_MFMA ||
                       (path_policy == LORA_PATH_AUTO && len >= mfma_min_tokens);
     const int32_t path = mfma ? LORA_PATH_MFMA : LORA_PATH_GATHER;
     if (phase == LORA_PHASE_SHRINK) {
+      const int32_t r = host_rank ? host_rank[a] : dim;
       const int32_t step = mfma ? LORA_SHRINK_MFMA_TOKENS : LORA_SHRINK_GATHER_TOKENS;
+      const int32_t groups = mfma ? 1 : (r + LORA_SHRINK_GATHER_ROWS - 1) / LORA_SHRINK_GATHER_ROWS;
       for (int32_t m0 = 0; m0 < len; m0 += step) {
-        int32_t cnt = std::min(step, len - m0);
-        // an MFMA item reads its adapter's rows once per 16 tokens, a gather
-        // item once per <= 4 tokens; both read each token's x row once
-        PlanItem p{{begin + m0, seg_adapter[s], cnt | (path << 16), 0},
-                   (int64_t)cnt * 2 + (mfma ? 16 : 8)};
-        plan.push_back(p);
+        const int32_t cnt = std::min(step, len - m0);
+        for (int32_t g = 0; g < groups; ++g) {
+          // bytes moved, in units of one d_in row: the item's x rows plus the
+          // adapter rows it reads
+          const int32_t rows = mfma ? r : std::min(LORA_SHRINK_GATHER_ROWS, r - g * LORA_SHRINK_GATHER_ROWS);
+          PlanItem p{{begin + m0, a, cnt | (path << 16), g}, (int64_t)cnt + rows};
+          plan.push_back(p);
+        }
       }
     } else {
       const int32_t step = mfma ? LORA_EXPAND_MFMA_TOKENS : LORA_EXPAND_GATHER_TOKENS;
       const int32_t cols = mfma ? LORA_EXPAND_MFMA_COLS : LORA_EXPAND_GATHER_COLS;
       const int32_t nblk = (dim + cols - 1) / cols;
       for (int32_t m0 = 0; m0 < len; m0 += step) {
-        int32_t cnt = std::min(step, len - m0);
+        const int32_t cnt = std::min(step, len - m0);
         for (int32_t b = 0; b < nblk; ++b) {
-          int32_t c = std::min(cols, dim - b * cols);
-          PlanItem p{{begin + m0, seg_adapter[s], cnt | (path << 16), b},
-                     (int64_t)c * (4 * cnt + 32)};
+          const int32_t c = std::min(cols, dim - b * cols);
+          // y read and written per token (2 x 2 bytes per column) plus B^T rows (assumed 16)
+          PlanItem p{{begin + m0, a, cnt | (path << 16), b}, (int64_t)c * (4 * cnt + 32)};
           plan.push_back(p);
         }
       }
     }
   }
   std::stable_sort(plan.begin(), plan.end(),
-                   [](const PlanItem &a, const PlanItem &b) { return a.weight > b.weight; });
+                   [](const PlanItem &x, const PlanItem &y) { return x.weight > y.weight; });
   if (plan.size() > (size_t)INT32_MAX) return fail(LORA_ENOMEM, "plan too large");
   *num_items = (int32_t)plan.size();
   if (!items) return ok();

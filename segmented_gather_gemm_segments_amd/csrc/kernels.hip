@@ -213,6 +213,10 @@ __device__ __forceinline__ void raw_cvt(const Raw8<float> &r, float (&o)[8]) {
 // Token list of the current item in LDS: toks[0..cnt).  Tokens outside
 // [0, num_tokens) are skipped.
 constexpr int kMaxItemTokens = 256;
+constexpr int kRowGroup = LORA_SHRINK_GATHER_ROWS;    // rows of A per gather workgroup
+constexpr int kGatherCols = LORA_EXPAND_GATHER_COLS;  // columns of y per gather workgroup
+constexpr int kStep = kThreads * 8;                   // d elements covered by one pass of 256 threads
+static_assert(kGatherCols == kThreads * 8, "one 8-column chunk per thread");
 
 struct ShrinkSmem {
   int toks[kMaxItemTokens];
@@ -222,17 +226,20 @@ struct ShrinkSmem {
   };
 };
 
-// One GEMV shrink tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) against rows
-// [j0, j0+nr) (nr <= RB) of adapter a.  The 256 threads run along d_in, 8
-// elements each per step; every step issues the TG x loads and RB A-row loads
-// together, then accumulates acc[t*RB + jj].  Rows and tokens beyond the tile
-// read a safe in-bounds address (row 0 of x) and their sums are dropped.  The
-// lane partials are reduce-scattered over the wave and the four wave results
-// summed in wave order.
-template <typename T, int TG, int RB>
-__device__ void shrink_gemv_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
+// One gather/GEMV shrink tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) against
+// the rows [j0, j0+nr) (nr <= 4) of adapter a.  The 256 threads split d_in into
+// 8-element chunks (thread tid: k = 8 tid + 2048 s); each pass issues the loads
+// of two such steps (TG x chunks and 4 A chunks each) before the first FMA, and
+// the x chunks of a token are reused across the 4 rows in registers.  Rows and
+// tokens beyond the tile read a safe in-bounds address (row 0 of x) and their
+// sums are dropped.  The TG x 4 lane partials are reduce-scattered over the
+// wave and the four wave results summed in wave order, so a token's result
+// does not depend on TG or on which other tokens share the tile.
+template <typename T, int TG>
+__device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
                                  int ntok, int num_tokens, const T *__restrict__ x,
                                  float *__restrict__ v, ShrinkSmem &sm) {
+  constexpr int RB = kRowGroup;
   constexpr int NV = TG * RB;
   constexpr int SH = 6 - ilog2(NV);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -252,23 +259,43 @@ __device__ void shrink_gemv_tile(const DevW &w, int a, int j0, int nr, const int
   float acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-  for (int k = tid * 8; k < w.d_in; k += kThreads * 8) {
-    Raw8<T> xraw[TG], araw[RB];
+  for (int k = tid * 8; k < w.d_in; k += 2 * kStep) {
+    const bool two = k + kStep < w.d_in;
+    Raw8<T> xa[TG], aa[RB], xb[TG], ab[RB];
 #pragma unroll
-    for (int t = 0; t < TG; ++t) raw_load(xraw[t], xr[t] + k);
+    for (int t = 0; t < TG; ++t) raw_load(xa[t], xr[t] + k);
 #pragma unroll
-    for (int jj = 0; jj < RB; ++jj) raw_load(araw[jj], ar[jj] + k);
+    for (int jj = 0; jj < RB; ++jj) raw_load(aa[jj], ar[jj] + k);
+    if (two) {
+#pragma unroll
+      for (int t = 0; t < TG; ++t) raw_load(xb[t], xr[t] + k + kStep);
+#pragma unroll
+      for (int jj = 0; jj < RB; ++jj) raw_load(ab[jj], ar[jj] + k + kStep);
+    }
     float xv[TG][8];
 #pragma unroll
-    for (int t = 0; t < TG; ++t) raw_cvt(xraw[t], xv[t]);
+    for (int t = 0; t < TG; ++t) raw_cvt(xa[t], xv[t]);
 #pragma unroll
     for (int jj = 0; jj < RB; ++jj) {
       float av[8];
-      raw_cvt(araw[jj], av);
+      raw_cvt(aa[jj], av);
 #pragma unroll
       for (int t = 0; t < TG; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[t * RB + jj] = fmaf(av[e], xv[t][e], acc[t * RB + jj]);
+    }
+    if (two) {
+#pragma unroll
+      for (int t = 0; t < TG; ++t) raw_cvt(xb[t], xv[t]);
+#pragma unroll
+      for (int jj = 0; jj < RB; ++jj) {
+        float av[8];
+        raw_cvt(ab[jj], av);
+#pragma unroll
+        for (int t = 0; t < TG; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[t * RB + jj] = fmaf(av[e], xv[t][e], acc[t * RB + jj]);
+      }
     }
   }
   const float part = wave_reduce_scatter<NV>(acc);
@@ -286,30 +313,19 @@ __device__ void shrink_gemv_tile(const DevW &w, int a, int j0, int nr, const int
   __syncthreads();
 }
 
-// Gather/GEMV shrink for tokens toks[0..cnt) of adapter a, rows [j_lo, j_hi):
-// one token at a time in passes of 8 or 16 rows, or groups of up to 4 tokens
-// in passes of 8 rows.
+// Gather/GEMV shrink of tokens toks[0..cnt) of adapter a over its row group
+// [j0, j0 + nr): groups of up to 4 tokens, one group of 1 to 3 at the end.
 template <typename T>
-__device__ void shrink_gemv(const DevW &w, int a, int j_lo, int j_hi, const int *toks, int cnt,
+__device__ __forceinline__ void shrink_gemv(const DevW &w, int a, int j0, int nr, const int *toks, int cnt,
                             int num_tokens, const T *__restrict__ x, float *__restrict__ v,
                             ShrinkSmem &sm) {
-  const int rb = (j_hi - j_lo) <= 8 ? 8 : 16;
-  for (int g0 = 0; g0 < cnt; g0 += 4) {
-    const int ntok = min(4, cnt - g0);
-    for (int j0 = j_lo; j0 < j_hi; j0 += rb) {
-      const int nr = min(rb, j_hi - j0);
-      if (ntok == 1) {
-        if (rb == 8) shrink_gemv_tile<T, 1, 8>(w, a, j0, nr, toks, g0, ntok, num_tokens, x, v, sm);
-        else shrink_gemv_tile<T, 1, 16>(w, a, j0, nr, toks, g0, ntok, num_tokens, x, v, sm);
-      } else {
-        // several tokens: 8-row passes keep the 4 x 8 accumulators and the
-        // batch of loads within the register budget
-        for (int j8 = j0; j8 < j0 + nr; j8 += 8)
-          shrink_gemv_tile<T, 4, 8>(w, a, j8, min(8, j0 + nr - j8), toks, g0, ntok, num_tokens, x,
-                                    v, sm);
-      }
-    }
-  }
+  int g0 = 0;
+  for (; g0 + 4 <= cnt; g0 += 4)
+    shrink_rows_tile<T, 4>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
+  const int rest = cnt - g0;
+  if (rest == 1) shrink_rows_tile<T, 1>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
+  else if (rest == 2) shrink_rows_tile<T, 2>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
+  else if (rest == 3) shrink_rows_tile<T, 4>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
 }
 
 // One MFMA shrink tile: 16 tokens (this lane's token row xp, or a safe row)
@@ -318,7 +334,7 @@ __device__ void shrink_gemv(const DevW &w, int a, int j_lo, int j_hi, const int 
 // MFMAs.  Lanes beyond the rank or the tile read safe rows whose outputs are
 // dropped; the last, partial k-step zeroes both operands past d_in.
 template <typename T, int RT>
-__device__ void shrink_mfma_tile(const DevW &w, int a, int r, int j0, const T *xp, int tok,
+__device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, int j0, const T *xp, int tok,
                                  const T *__restrict__ x, float *__restrict__ v, ShrinkSmem &sm) {
   constexpr int U = RT == 1 ? 8 : 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -387,7 +403,7 @@ __device__ void shrink_mfma_tile(const DevW &w, int a, int r, int j0, const T *x
 // MFMA shrink for tokens toks[0..cnt) of adapter a: 16-token tiles, passes of
 // up to 64 rows.
 template <typename T>
-__device__ void shrink_mfma(const DevW &w, int a, int r, const int *toks, int cnt, int num_tokens,
+__device__ __forceinline__ void shrink_mfma(const DevW &w, int a, int r, const int *toks, int cnt, int num_tokens,
                             const T *__restrict__ x, float *__restrict__ v, ShrinkSmem &sm) {
   const int m = threadIdx.x & 15;
   for (int m0 = 0; m0 < cnt; m0 += 16) {
@@ -414,64 +430,68 @@ template <> struct ExpandCfg<float> { static constexpr int kRowStride = 68; };
 template <typename T>
 struct ExpandSmem {
   int toks[kMaxItemTokens];
-  union {
-    float red_gemv[4 * 4 * 8 * 64];                          // [wave][token][elem][lane]
-    T bt[4 * 64 * ExpandCfg<T>::kRowStride];                 // per wave: [64 cols][j]
-  };
+  T bt[4 * 64 * ExpandCfg<T>::kRowStride];  // MFMA path, per wave: [64 cols][j]
 };
 
-// One GEMV expand tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) over the 512
-// columns of block `blk`.  Lane l owns 8 consecutive columns; wave w
-// accumulates rank indices j = w, w+4, ..., loading the B^T chunks of JW such
-// indices at a time; the four wave partials are summed in wave order and
-// added to y once (wave t finalises token t, its y chunk prefetched at the
-// start).
+// One gather/GEMV expand tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) over
+// the 2048 columns of block cb.  Thread tid owns the 8 consecutive columns
+// 2048 cb + 8 tid and runs the whole rank sum for them itself -- no cross-lane
+// or cross-wave reduction, no barrier.  B^T rows are loaded 16 at a time
+// (16-byte loads, all issued before the first FMA); the y chunks of the tile's
+// tokens are fetched at the start; v is read as uniform values.  Every output
+// is y + sum_j v_j b_j summed in ascending j, independent of TG.
 template <typename T, int TG>
-__device__ void expand_gemv_tile(const DevW &w, int a, int r, int blk, const int *toks, int g0,
+__device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, int cb, const int *toks, int g0,
                                  int ntok, int num_tokens, const float *__restrict__ v,
-                                 T *__restrict__ y, ExpandSmem<T> &sm) {
-  constexpr int JW = 4;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = blk * LORA_EXPAND_GATHER_COLS + lane * 8;
-  const bool cin = col < w.d_out;
-  const int colc = cin ? col : 0;
+                                 T *__restrict__ y) {
+  const int col = cb * kGatherCols + (int)threadIdx.x * 8;
+  if (col >= w.d_out) return;
   int tk[TG];
 #pragma unroll
   for (int t = 0; t < TG; ++t) {
     const int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
     tk[t] = (tok >= 0 && tok < num_tokens) ? tok : -1;
   }
-  // prefetch the y chunk this wave finalises
-  const int my_tok = wave < ntok ? toks[g0 + wave] : -1;
-  const bool my_ok = my_tok >= 0 && my_tok < num_tokens && cin;
-  T *yp = my_ok ? y + (int64_t)my_tok * w.d_out + col : nullptr;
-  Raw8<T> yraw;
-  if (my_ok) raw_load(yraw, yp);
+  Raw8<T> yraw[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t)
+    if (tk[t] >= 0) raw_load(yraw[t], y + (int64_t)tk[t] * w.d_out + col);
   const T *safe = reinterpret_cast<const T *>(w.b_pages);
+  const bool vec_v = (w.r_max & 3) == 0;
   float acc[TG][8];
 #pragma unroll
   for (int t = 0; t < TG; ++t)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
-  for (int jb = wave; jb < r; jb += 4 * JW) {
-    Raw8<T> braw[JW];
+  for (int j0 = 0; j0 < r; j0 += 16) {
+    Raw8<T> braw[16];
 #pragma unroll
-    for (int i = 0; i < JW; ++i) {
-      const int j = jb + 4 * i;
-      const T *p = j < r ? b_row<T>(w, a, j) : nullptr;
-      raw_load(braw[i], p ? p + colc : safe);
+    for (int i = 0; i < 16; ++i) {
+      const T *p = j0 + i < r ? b_row<T>(w, a, j0 + i) : nullptr;
+      raw_load(braw[i], p ? p + col : safe);
     }
-    float vj[TG][JW];
+    // v[tok][j0 .. j0+16): the same address in every lane, read with 16-byte
+    // vector loads (one request per wave) where r_max keeps them aligned
+    float vj[TG][16];
 #pragma unroll
-    for (int t = 0; t < TG; ++t)
+    for (int t = 0; t < TG; ++t) {
+      const float *vr = v + (int64_t)(tk[t] >= 0 ? tk[t] : 0) * w.r_max + j0;
 #pragma unroll
-      for (int i = 0; i < JW; ++i) {
-        const int j = jb + 4 * i;
-        vj[t][i] = (tk[t] >= 0 && j < r) ? v[(int64_t)tk[t] * w.r_max + j] : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const int jq = j0 + 4 * q;
+        if (tk[t] >= 0 && vec_v && jq + 4 <= r) {
+          const float4 f = *reinterpret_cast<const float4 *>(vr + 4 * q);
+          vj[t][4 * q] = f.x; vj[t][4 * q + 1] = f.y; vj[t][4 * q + 2] = f.z; vj[t][4 * q + 3] = f.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vj[t][4 * q + e] = (tk[t] >= 0 && jq + e < r) ? vr[4 * q + e] : 0.f;
+        }
       }
+    }
 #pragma unroll
-    for (int i = 0; i < JW; ++i) {
-      if (jb + 4 * i < r) {
+    for (int i = 0; i < 16; ++i) {
+      if (j0 + i < r) {
         float bv[8];
         raw_cvt(braw[i], bv);
 #pragma unroll
@@ -482,39 +502,26 @@ __device__ void expand_gemv_tile(const DevW &w, int a, int r, int blk, const int
     }
   }
 #pragma unroll
-  for (int t = 0; t < TG; ++t)
-    if (t < ntok)
+  for (int t = 0; t < TG; ++t) {
+    if (tk[t] >= 0) {
+      float yv[8];
+      raw_cvt(yraw[t], yv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.red_gemv[((wave * 4 + t) * 8 + e) * 64 + lane] = acc[t][e];
-  __syncthreads();
-  if (my_ok) {
-    const int t = wave;
-    float yv[8];
-    raw_cvt(yraw, yv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float s = ((sm.red_gemv[((0 * 4 + t) * 8 + e) * 64 + lane] +
-                        sm.red_gemv[((1 * 4 + t) * 8 + e) * 64 + lane]) +
-                       sm.red_gemv[((2 * 4 + t) * 8 + e) * 64 + lane]) +
-                      sm.red_gemv[((3 * 4 + t) * 8 + e) * 64 + lane];
-      yv[e] += s;
+      for (int e = 0; e < 8; ++e) yv[e] += acc[t][e];
+      store8(y + (int64_t)tk[t] * w.d_out + col, yv);
     }
-    store8(yp, yv);
   }
-  __syncthreads();
 }
 
 template <typename T>
-__device__ void expand_gemv(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
-                            int num_tokens, const float *__restrict__ v, T *__restrict__ y,
-                            ExpandSmem<T> &sm) {
-  for (int g0 = 0; g0 < cnt; g0 += 4) {
-    const int ntok = min(4, cnt - g0);
-    if (ntok == 1)
-      expand_gemv_tile<T, 1>(w, a, r, blk, toks, g0, ntok, num_tokens, v, y, sm);
-    else
-      expand_gemv_tile<T, 4>(w, a, r, blk, toks, g0, ntok, num_tokens, v, y, sm);
-  }
+__device__ __forceinline__ void expand_gemv(const DevW &w, int a, int r, int cb, const int *toks, int cnt,
+                            int num_tokens, const float *__restrict__ v, T *__restrict__ y) {
+  int g0 = 0;
+  for (; g0 + 4 <= cnt; g0 += 4) expand_cols_tile<T, 4>(w, a, r, cb, toks, g0, 4, num_tokens, v, y);
+  const int rest = cnt - g0;
+  if (rest == 1) expand_cols_tile<T, 1>(w, a, r, cb, toks, g0, 1, num_tokens, v, y);
+  else if (rest == 2) expand_cols_tile<T, 2>(w, a, r, cb, toks, g0, 2, num_tokens, v, y);
+  else if (rest == 3) expand_cols_tile<T, 4>(w, a, r, cb, toks, g0, 3, num_tokens, v, y);
 }
 
 // Column of the wave's 64-column slab that MFMA row `rho` of sub-tile `t`
@@ -545,7 +552,7 @@ __device__ __forceinline__ void load_v8(const float *vr, int jb, int nj, bool ve
 // rank indices exactly; fp32: 16x16x4 steps.  The y chunks of the 64 tokens
 // are prefetched before the slab is staged.
 template <typename T>
-__device__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
+__device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y,
                             ExpandSmem<T> &sm) {
   constexpr int RS = ExpandCfg<T>::kRowStride;
@@ -702,13 +709,15 @@ __global__ __launch_bounds__(kThreads) void sgmv_shrink_kernel(DevW w, const int
   const lora_item it = items[blockIdx.x];
   int pb, a, cnt, path, blk;
   if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
+  const int r = adapter_rank(w, a);
+  if (path != LORA_PATH_MFMA && blk >= (r + kRowGroup - 1) / kRowGroup) return;
+  const int j0 = path == LORA_PATH_MFMA ? 0 : blk * kRowGroup;
   for (int i = threadIdx.x; i < cnt; i += kThreads) sm.toks[i] = perm[pb + i];
   __syncthreads();
-  const int r = adapter_rank(w, a);
   if (path == LORA_PATH_MFMA)
     shrink_mfma<T>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
   else
-    shrink_gemv<T>(w, a, 0, r, sm.toks, cnt, num_tokens, x, v, sm);
+    shrink_gemv<T>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
 }
 
 template <typename T>
@@ -722,18 +731,29 @@ __global__ __launch_bounds__(kThreads) void sgmv_expand_kernel(DevW w, const int
   const lora_item it = items[blockIdx.x];
   int pb, a, cnt, path, blk;
   if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
+  const int cols = path == LORA_PATH_MFMA ? LORA_EXPAND_MFMA_COLS : kGatherCols;
+  if ((int64_t)blk * cols >= w.d_out) return;
   for (int i = threadIdx.x; i < cnt; i += kThreads) sm.toks[i] = perm[pb + i];
   __syncthreads();
   const int r = adapter_rank(w, a);
   if (path == LORA_PATH_MFMA)
     expand_mfma<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
   else
-    expand_gemv<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+    expand_gemv<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
 }
+
+// Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups to
+// the eight XCDs in turn).  With the grid padded to a multiple of 8, logical
+// index (b % 8) * (grid / 8) + b / 8 hands each XCD a contiguous run of logical
+// indices, so neighbouring work units -- the row groups of one adapter, which
+// read the same x rows -- share that XCD's L2.
+__device__ __forceinline__ int xcd_logical(int b, int grid) { return (b & 7) * (grid >> 3) + (b >> 3); }
+
+inline int pad8(int n) { return (n + 7) & ~7; }
 
 // Collects, in token order, the tokens of ids[c0 .. c0+256) whose adapter is
 // `a` into toks[]; returns their count.  All threads must call it.
-__device__ int gather_adapter_tokens(const int32_t *__restrict__ ids, int num_tokens, int c0, int a,
+__device__ __forceinline__ int gather_adapter_tokens(const int32_t *__restrict__ ids, int num_tokens, int c0, int a,
                                      int *toks, int *wave_cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = c0 + tid;
@@ -749,56 +769,65 @@ __device__ int gather_adapter_tokens(const int32_t *__restrict__ ids, int num_to
   return total;
 }
 
+// Per-token (BGMV) shrink.  Work unit u is a token (token-major) or an adapter
+// (adapter-major); each unit is split into row groups of 4, one per workgroup.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int32_t *__restrict__ ids,
                                                                int32_t num_tokens, int32_t adapter_major,
+                                                               int32_t units, int32_t groups,
                                                                const T *__restrict__ x,
                                                                float *__restrict__ v) {
   __shared__ ShrinkSmem sm;
   __shared__ int wave_cnt[4];
-  const int rb_lo = blockIdx.y * 16;
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  if (L >= units * groups) return;
+  const int u = L / groups, j0 = (L - u * groups) * kRowGroup;
   if (!adapter_major) {
-    const int t = blockIdx.x;
+    const int t = u;
     const int a = ids[t];
     if (a < 0 || a >= w.num_adapters) return;
     const int r = adapter_rank(w, a);
-    if (rb_lo >= r) return;
+    if (j0 >= r) return;
     if (threadIdx.x == 0) sm.toks[0] = t;
     __syncthreads();
-    shrink_gemv<T>(w, a, rb_lo, min(r, rb_lo + 16), sm.toks, 1, num_tokens, x, v, sm);
+    shrink_gemv<T>(w, a, j0, min(kRowGroup, r - j0), sm.toks, 1, num_tokens, x, v, sm);
   } else {
-    const int a = blockIdx.x;
+    const int a = u;
     const int r = adapter_rank(w, a);
-    if (rb_lo >= r) return;
+    if (j0 >= r) return;
     for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
       const int n = gather_adapter_tokens(ids, num_tokens, c0, a, sm.toks, wave_cnt);
-      if (n > 0) shrink_gemv<T>(w, a, rb_lo, min(r, rb_lo + 16), sm.toks, n, num_tokens, x, v, sm);
+      if (n > 0) shrink_gemv<T>(w, a, j0, min(kRowGroup, r - j0), sm.toks, n, num_tokens, x, v, sm);
       __syncthreads();
     }
   }
 }
 
+// Per-token (BGMV) expand.  Work unit u as above, split into column blocks of
+// 2048, one per workgroup.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(DevW w, const int32_t *__restrict__ ids,
                                                                int32_t num_tokens, int32_t adapter_major,
+                                                               int32_t units, int32_t groups,
                                                                const float *__restrict__ v,
                                                                T *__restrict__ y) {
-  __shared__ ExpandSmem<T> sm;
+  __shared__ int toks[kMaxItemTokens];
   __shared__ int wave_cnt[4];
-  const int blk = blockIdx.y;
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  if (L >= units * groups) return;
+  const int u = L / groups, cb = L - u * groups;
   if (!adapter_major) {
-    const int t = blockIdx.x;
+    const int t = u;
     const int a = ids[t];
     if (a < 0 || a >= w.num_adapters) return;
-    if (threadIdx.x == 0) sm.toks[0] = t;
-    __syncthreads();
-    expand_gemv<T>(w, a, adapter_rank(w, a), blk, sm.toks, 1, num_tokens, v, y, sm);
+    const int tok1[1] = {t};
+    expand_cols_tile<T, 1>(w, a, adapter_rank(w, a), cb, tok1, 0, 1, num_tokens, v, y);
   } else {
-    const int a = blockIdx.x;
+    const int a = u;
     const int r = adapter_rank(w, a);
     for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
-      const int n = gather_adapter_tokens(ids, num_tokens, c0, a, sm.toks, wave_cnt);
-      if (n > 0) expand_gemv<T>(w, a, r, blk, sm.toks, n, num_tokens, v, y, sm);
+      const int n = gather_adapter_tokens(ids, num_tokens, c0, a, toks, wave_cnt);
+      if (n > 0) expand_gemv<T>(w, a, r, cb, toks, n, num_tokens, v, y);
       __syncthreads();
     }
   }
@@ -874,9 +903,16 @@ lora_status check_sgmv_args(const int32_t *perm, int32_t num_perm, const lora_it
   return LORA_OK;
 }
 
-int bgmv_order(int order, int num_tokens, int num_adapters) {
+// Automatic order.  Shrink: adapter-major once adapters are no more numerous
+// than tokens (each adapter's A rows are then read by one group of workgroups
+// instead of once per token).  Expand: token-major unless an adapter carries
+// many tokens on average -- a token-major workgroup needs no scan of the ids
+// and its B^T rows, shared with the adapter's other tokens, come from cache.
+int bgmv_order(int phase, int order, int num_tokens, int num_adapters) {
   if (order == LORA_BGMV_TOKEN_MAJOR || order == LORA_BGMV_ADAPTER_MAJOR) return order;
-  return num_adapters <= num_tokens ? LORA_BGMV_ADAPTER_MAJOR : LORA_BGMV_TOKEN_MAJOR;
+  if (phase == LORA_PHASE_SHRINK)
+    return num_adapters <= num_tokens ? LORA_BGMV_ADAPTER_MAJOR : LORA_BGMV_TOKEN_MAJOR;
+  return num_tokens >= 16 * num_adapters ? LORA_BGMV_ADAPTER_MAJOR : LORA_BGMV_TOKEN_MAJOR;
 }
 
 }  // namespace
@@ -932,14 +968,18 @@ extern "C" lora_status lora_bgmv_shrink(const lora_weights *w, const int32_t *to
   if (num_tokens == 0 || w->num_adapters == 0) return ok();
   if (!token_adapter || !x || !v) return fail(LORA_EINVAL, "null pointer");
   if (!aligned16(x) || !aligned16(v)) return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
-  const int am = bgmv_order(order, num_tokens, w->num_adapters) == LORA_BGMV_ADAPTER_MAJOR;
-  const dim3 grid(am ? w->num_adapters : num_tokens, (w->r_max + 15) / 16);
+  const int am = bgmv_order(LORA_PHASE_SHRINK, order, num_tokens, w->num_adapters) ==
+                 LORA_BGMV_ADAPTER_MAJOR;
+  const int units = am ? w->num_adapters : num_tokens;
+  const int groups = (w->r_max + kRowGroup - 1) / kRowGroup;
+  if ((int64_t)units * groups > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
+  const dim3 grid(pad8(units * groups));
   if (w->dtype == LORA_BF16)
     hipLaunchKernelGGL(bgmv_shrink_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, (const uint16_t *)x, v);
+                       token_adapter, num_tokens, am, units, groups, (const uint16_t *)x, v);
   else
     hipLaunchKernelGGL(bgmv_shrink_kernel<float>, grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, (const float *)x, v);
+                       token_adapter, num_tokens, am, units, groups, (const float *)x, v);
   return check_launch("bgmv shrink launch");
 }
 
@@ -955,15 +995,18 @@ extern "C" lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *to
   if (num_tokens == 0 || w->num_adapters == 0) return ok();
   if (!token_adapter || !v || !y) return fail(LORA_EINVAL, "null pointer");
   if (!aligned16(v) || !aligned16(y)) return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
-  const int am = bgmv_order(order, num_tokens, w->num_adapters) == LORA_BGMV_ADAPTER_MAJOR;
-  const dim3 grid(am ? w->num_adapters : num_tokens,
-                  (w->d_out + LORA_EXPAND_GATHER_COLS - 1) / LORA_EXPAND_GATHER_COLS);
+  const int am = bgmv_order(LORA_PHASE_EXPAND, order, num_tokens, w->num_adapters) ==
+                 LORA_BGMV_ADAPTER_MAJOR;
+  const int units = am ? w->num_adapters : num_tokens;
+  const int groups = (w->d_out + kGatherCols - 1) / kGatherCols;
+  if ((int64_t)units * groups > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
+  const dim3 grid(pad8(units * groups));
   if (w->dtype == LORA_BF16)
     hipLaunchKernelGGL(bgmv_expand_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, v, (uint16_t *)y);
+                       token_adapter, num_tokens, am, units, groups, v, (uint16_t *)y);
   else
     hipLaunchKernelGGL(bgmv_expand_kernel<float>, grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, v, (float *)y);
+                       token_adapter, num_tokens, am, units, groups, v, (float *)y);
   return check_launch("bgmv expand launch");
 }
 

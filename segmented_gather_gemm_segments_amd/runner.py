@@ -134,9 +134,9 @@ class DeviceProblem:
              mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS):
         torch = _torch()
         _, starts, adapters, _ = self.segments()
-        dim = self.p.d_in if phase == B.LORA_PHASE_SHRINK else self.p.d_out
+        dim = self.r_max if phase == B.LORA_PHASE_SHRINK else self.p.d_out
         items = B.lora_sgmv_plan(phase, starts, adapters, self.p.num_adapters, dim, policy,
-                                 mfma_min_tokens)
+                                 mfma_min_tokens, host_rank=self.p.ranks.astype(np.int32))
         return torch.from_numpy(np.ascontiguousarray(items)).to(self.device)
 
     # ------------------------------------------------------------- runs

@@ -88,22 +88,30 @@ def test_segments_edge_cases():
 
 
 # ------------------------------------------------------------------ planner
-def _coverage(items, starts, dim, phase):
-    """Count, per (perm position, output column block unit), how often it is covered."""
+def _coverage(items, starts, adapters, ranks, dim, phase):
+    """Count how often each (perm position, output unit) is covered: rows of v
+    for a shrink plan, 8-column chunks of y for an expand plan."""
     n_tok = int(starts[-1])
-    if phase == B.LORA_PHASE_SHRINK:
-        cov = np.zeros(n_tok, np.int32)
-    else:
-        cov = np.zeros((n_tok, dim // 8), np.int32)
+    width = dim if phase == B.LORA_PHASE_SHRINK else dim // 8
+    cov = np.zeros((n_tok, width), np.int32)
     seg_of = np.repeat(np.arange(starts.size - 1), np.diff(starts))
     for pb, a, cp, blk in items:
         cnt, path = cp & 0xFFFF, cp >> 16
         assert 1 <= cnt and path in (B.LORA_PATH_GATHER, B.LORA_PATH_MFMA)
         assert len(set(seg_of[pb:pb + cnt])) == 1        # one segment per item
         if phase == B.LORA_PHASE_SHRINK:
-            cov[pb:pb + cnt] += 1
+            r = int(ranks[a])
+            if path == B.LORA_PATH_MFMA:
+                assert cnt <= B.LORA_SHRINK_MFMA_TOKENS and blk == 0
+                j0, j1 = 0, r
+            else:
+                assert cnt <= B.LORA_SHRINK_GATHER_TOKENS
+                j0 = blk * B.LORA_SHRINK_GATHER_ROWS
+                j1 = min(r, j0 + B.LORA_SHRINK_GATHER_ROWS)
+                assert j0 < r                                # no empty row group is planned
+            cov[pb:pb + cnt, j0:j1] += 1
         else:
-            cols = 256 if path == B.LORA_PATH_MFMA else 512
+            cols = B.LORA_EXPAND_MFMA_COLS if path == B.LORA_PATH_MFMA else B.LORA_EXPAND_GATHER_COLS
             c0, c1 = blk * cols, min(dim, (blk + 1) * cols)
             assert c0 < dim
             cov[pb:pb + cnt, c0 // 8:c1 // 8] += 1
@@ -120,35 +128,54 @@ def test_plan_covers_every_output_once(policy):
         perm, starts, adapters = B.lora_segments_build(ids, n)
         if adapters.size == 0:
             continue
-        dim = int(rng.integers(1, 200)) * 8
-        for phase in (B.LORA_PHASE_SHRINK, B.LORA_PHASE_EXPAND):
-            items = B.lora_sgmv_plan(phase, starts, adapters, n, dim, policy)
-            cov = _coverage(items, starts, dim, phase)
-            assert np.all(cov == 1)
-            # adapter of each item is its segment's adapter
+        ranks = rng.integers(1, 65, size=n).astype(np.int32)
+        r_max = int(ranks.max())
+        d_out = int(rng.integers(1, 600)) * 8
+        for phase, dim in ((B.LORA_PHASE_SHRINK, r_max), (B.LORA_PHASE_EXPAND, d_out)):
+            items = B.lora_sgmv_plan(phase, starts, adapters, n, dim, policy, host_rank=ranks)
+            cov = _coverage(items, starts, adapters, ranks, dim, phase)
             seg_of = np.repeat(np.arange(adapters.size), np.diff(starts))
+            if phase == B.LORA_PHASE_SHRINK:
+                want = (np.arange(r_max)[None, :] < ranks[adapters[seg_of]][:, None]).astype(np.int32)
+                assert np.array_equal(cov, want)
+            else:
+                assert np.all(cov == 1)
+            # adapter of each item is its segment's adapter
             assert np.all(adapters[seg_of[items[:, 0]]] == items[:, 1])
+        # without host ranks every adapter is planned at r_max
+        items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, n, r_max, policy)
+        cov = _coverage(items, starts, adapters, np.full(n, r_max, np.int32), r_max,
+                        B.LORA_PHASE_SHRINK)
+        assert np.all(cov == 1)
 
 
 def test_plan_path_choice_and_order():
     starts = np.array([0, 1, 16, 116], np.int32)     # lengths 1, 15, 100
     adapters = np.array([0, 1, 2], np.int32)
-    items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 64)
+    items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 16)
     paths = {int(a): int(cp >> 16) for _, a, cp, _ in items}
     assert paths == {0: B.LORA_PATH_GATHER, 1: B.LORA_PATH_GATHER, 2: B.LORA_PATH_MFMA}
-    items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 64, mfma_min_tokens=1)
+    items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 16, mfma_min_tokens=1)
     assert all((cp >> 16) == B.LORA_PATH_MFMA for _, _, cp, _ in items)
-    # heaviest first: MFMA expand items (64 tokens) lead
+    # heaviest first: expand items ordered by the bytes they move (y read and
+    # written per token, plus 16 B^T rows over the item's columns)
     items = B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, starts, adapters, 3, 4096)
-    assert (items[0, 2] >> 16) == B.LORA_PATH_MFMA and (items[0, 2] & 0xFFFF) == 64
+    cols = np.where((items[:, 2] >> 16) == B.LORA_PATH_MFMA, B.LORA_EXPAND_MFMA_COLS,
+                    B.LORA_EXPAND_GATHER_COLS)
+    weight = cols * (4 * (items[:, 2] & 0xFFFF) + 32)
+    assert np.all(np.diff(weight) <= 0)
+    # a rank-8 adapter on the gather path needs two row groups, a rank-16 one four
+    items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 16, B.LORA_PATH_GATHER,
+                             host_rank=np.array([8, 16, 16], np.int32))
+    assert sorted(int(b) for _, a, _, b in items if a == 0) == [0, 1]
 
 
 def test_plan_errors():
     with pytest.raises(B.LoraError) as e:
-        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2], np.int32), np.array([7], np.int32), 3, 64)
+        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2], np.int32), np.array([7], np.int32), 3, 16)
     assert e.value.status == B.LORA_ERANGE
     with pytest.raises(B.LoraError) as e:
-        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2, 2], np.int32), np.array([0, 1], np.int32), 3, 64)
+        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2, 2], np.int32), np.array([0, 1], np.int32), 3, 16)
     assert e.value.status == B.LORA_EINVAL
     with pytest.raises(B.LoraError) as e:
         B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, np.array([0, 2], np.int32), np.array([0], np.int32), 3, 12)
@@ -161,11 +188,19 @@ def test_plan_errors():
     ad = np.array([0], np.int32)
     n = ctypes.c_int32(0)
     items = np.zeros((1, 4), np.int32)
-    rc = lib.lora_sgmv_plan(0, st.ctypes.data, ad.ctypes.data, 1, 1, 64, 0, 16, items.ctypes.data, 1,
-                            ctypes.byref(n))
+    rc = lib.lora_sgmv_plan(0, st.ctypes.data, ad.ctypes.data, 1, 1, None, 16, 0, 16,
+                            items.ctypes.data, 1, ctypes.byref(n))
     assert rc == B.LORA_ENOMEM and n.value == 3
     # an empty batch plans to nothing
-    assert B.lora_sgmv_plan(0, np.array([0], np.int32), np.zeros(0, np.int32), 3, 64).shape == (0, 4)
+    assert B.lora_sgmv_plan(0, np.array([0], np.int32), np.zeros(0, np.int32), 3, 16).shape == (0, 4)
+    # r_max out of range for a shrink plan; a rank above r_max
+    with pytest.raises(B.LoraError) as e:
+        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2], np.int32), np.array([0], np.int32), 3, 129)
+    assert e.value.status == B.LORA_EUNSUPPORTED
+    with pytest.raises(B.LoraError) as e:
+        B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2], np.int32), np.array([0], np.int32), 3, 16,
+                         host_rank=np.array([32, 8, 8], np.int32))
+    assert e.value.status == B.LORA_ERANGE
 
 
 # ------------------------------------------------------------------ pool
