@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU time (0 disables the CPU baseline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the LLC")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run torch device copies of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -128,6 +130,18 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.calibrate_copy > 0:
+        # a plain copy of known size: FETCH_SIZE and WRITE_SIZE of these
+        # dispatches should each read MIB MiB
+        n = args.calibrate_copy * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_mib": args.calibrate_copy, "dispatches": 5}), flush=True)
+        return
+
     from segmented_gather_gemm_segments_amd import accounting as acc
     from segmented_gather_gemm_segments_amd import binding as B
     from segmented_gather_gemm_segments_amd import runner as R
@@ -177,13 +191,15 @@ def main():
             s()
             e()
     torch.cuda.synchronize()
-    graph.replay()                       # untimed replay: first-touch of the graph
+    with torch.cuda.stream(stream):
+        graph.replay()                   # untimed replay: first-touch of the graph
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps, bracketed by synchronisation
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    graph.replay()
+    with torch.cuda.stream(stream):
+        graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -195,12 +211,14 @@ def main():
         with torch.cuda.graph(g, stream=stream):
             for i in range(K):
                 calls[i % n_rep][which]()
-        g.replay()
+        with torch.cuda.stream(stream):
+            g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
+        with torch.cuda.stream(stream):       # replay() launches on the current stream
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / K
 

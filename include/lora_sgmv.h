@@ -229,8 +229,7 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
  * batch).  Same arithmetic as the segmented calls.
  *   token_adapter [num_tokens]  device; ids outside [0, N) (and -1) are skipped
  *   order  LORA_BGMV_TOKEN_MAJOR: workgroups per token (shrink: one per
- *          group of LORA_SHRINK_GATHER_ROWS rows; expand: one per block of
- *          LORA_EXPAND_GATHER_COLS columns);
+ *          group of 2 rows of A; expand: one per block of 1024 columns);
  *          LORA_BGMV_ADAPTER_MAJOR: the same split per adapter, each workgroup
  *          scanning token_adapter for its adapter's tokens, so each adapter's
  *          rows are read once however many tokens use it;

@@ -213,10 +213,23 @@ __device__ __forceinline__ void raw_cvt(const Raw8<float> &r, float (&o)[8]) {
 // Token list of the current item in LDS: toks[0..cnt).  Tokens outside
 // [0, num_tokens) are skipped.
 constexpr int kMaxItemTokens = 256;
-constexpr int kRowGroup = LORA_SHRINK_GATHER_ROWS;    // rows of A per gather workgroup
-constexpr int kGatherCols = LORA_EXPAND_GATHER_COLS;  // columns of y per gather workgroup
+constexpr int kRowGroup = LORA_SHRINK_GATHER_ROWS;    // rows of A per segmented gather item
+constexpr int kGatherCols = LORA_EXPAND_GATHER_COLS;  // columns of y per segmented gather item
 constexpr int kStep = kThreads * 8;                   // d elements covered by one pass of 256 threads
 static_assert(kGatherCols == kThreads * 8, "one 8-column chunk per thread");
+
+// Per-token (BGMV) work split: rows of A per shrink workgroup, and threads per
+// expand workgroup (8 columns of y per thread).
+#ifndef LORA_BGMV_SHRINK_ROWS
+#define LORA_BGMV_SHRINK_ROWS 2
+#endif
+#ifndef LORA_BGMV_EXPAND_THREADS
+#define LORA_BGMV_EXPAND_THREADS 128
+#endif
+constexpr int kBgmvRows = LORA_BGMV_SHRINK_ROWS;
+constexpr int kBgmvExpandThreads = LORA_BGMV_EXPAND_THREADS;
+static_assert(kBgmvRows == 1 || kBgmvRows == 2 || kBgmvRows == 4, "BGMV shrink rows: 1, 2 or 4");
+static_assert(kBgmvExpandThreads % 64 == 0 && kBgmvExpandThreads <= kThreads, "whole waves");
 
 struct ShrinkSmem {
   int toks[kMaxItemTokens];
@@ -235,11 +248,10 @@ struct ShrinkSmem {
 // sums are dropped.  The TG x 4 lane partials are reduce-scattered over the
 // wave and the four wave results summed in wave order, so a token's result
 // does not depend on TG or on which other tokens share the tile.
-template <typename T, int TG>
+template <typename T, int TG, int RB>
 __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
                                  int ntok, int num_tokens, const T *__restrict__ x,
                                  float *__restrict__ v, ShrinkSmem &sm) {
-  constexpr int RB = kRowGroup;
   constexpr int NV = TG * RB;
   constexpr int SH = 6 - ilog2(NV);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -314,18 +326,18 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
 }
 
 // Gather/GEMV shrink of tokens toks[0..cnt) of adapter a over its row group
-// [j0, j0 + nr): groups of up to 4 tokens, one group of 1 to 3 at the end.
-template <typename T>
+// [j0, j0 + nr), nr <= RB: groups of up to 4 tokens, one group of 1 to 3 at the end.
+template <typename T, int RB>
 __device__ __forceinline__ void shrink_gemv(const DevW &w, int a, int j0, int nr, const int *toks, int cnt,
                             int num_tokens, const T *__restrict__ x, float *__restrict__ v,
                             ShrinkSmem &sm) {
   int g0 = 0;
   for (; g0 + 4 <= cnt; g0 += 4)
-    shrink_rows_tile<T, 4>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
+    shrink_rows_tile<T, 4, RB>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
   const int rest = cnt - g0;
-  if (rest == 1) shrink_rows_tile<T, 1>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
-  else if (rest == 2) shrink_rows_tile<T, 2>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
-  else if (rest == 3) shrink_rows_tile<T, 4>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
+  if (rest == 1) shrink_rows_tile<T, 1, RB>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
+  else if (rest == 2) shrink_rows_tile<T, 2, RB>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
+  else if (rest == 3) shrink_rows_tile<T, 4, RB>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
 }
 
 // One MFMA shrink tile: 16 tokens (this lane's token row xp, or a safe row)
@@ -434,17 +446,17 @@ struct ExpandSmem {
 };
 
 // One gather/GEMV expand tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) over
-// the 2048 columns of block cb.  Thread tid owns the 8 consecutive columns
-// 2048 cb + 8 tid and runs the whole rank sum for them itself -- no cross-lane
-// or cross-wave reduction, no barrier.  B^T rows are loaded 16 at a time
+// the 8 NT columns of block cb (NT = threads of the workgroup).  Thread tid
+// owns the 8 consecutive columns 8 (NT cb + tid) and runs the whole rank sum
+// for them itself -- no cross-lane or cross-wave reduction, no barrier.  B^T rows are loaded 16 at a time
 // (16-byte loads, all issued before the first FMA); the y chunks of the tile's
 // tokens are fetched at the start; v is read as uniform values.  Every output
 // is y + sum_j v_j b_j summed in ascending j, independent of TG.
-template <typename T, int TG>
+template <typename T, int TG, int NT>
 __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, int cb, const int *toks, int g0,
                                  int ntok, int num_tokens, const float *__restrict__ v,
                                  T *__restrict__ y) {
-  const int col = cb * kGatherCols + (int)threadIdx.x * 8;
+  const int col = (cb * NT + (int)threadIdx.x) * 8;
   if (col >= w.d_out) return;
   int tk[TG];
 #pragma unroll
@@ -513,15 +525,15 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
   }
 }
 
-template <typename T>
+template <typename T, int NT>
 __device__ __forceinline__ void expand_gemv(const DevW &w, int a, int r, int cb, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y) {
   int g0 = 0;
-  for (; g0 + 4 <= cnt; g0 += 4) expand_cols_tile<T, 4>(w, a, r, cb, toks, g0, 4, num_tokens, v, y);
+  for (; g0 + 4 <= cnt; g0 += 4) expand_cols_tile<T, 4, NT>(w, a, r, cb, toks, g0, 4, num_tokens, v, y);
   const int rest = cnt - g0;
-  if (rest == 1) expand_cols_tile<T, 1>(w, a, r, cb, toks, g0, 1, num_tokens, v, y);
-  else if (rest == 2) expand_cols_tile<T, 2>(w, a, r, cb, toks, g0, 2, num_tokens, v, y);
-  else if (rest == 3) expand_cols_tile<T, 4>(w, a, r, cb, toks, g0, 3, num_tokens, v, y);
+  if (rest == 1) expand_cols_tile<T, 1, NT>(w, a, r, cb, toks, g0, 1, num_tokens, v, y);
+  else if (rest == 2) expand_cols_tile<T, 2, NT>(w, a, r, cb, toks, g0, 2, num_tokens, v, y);
+  else if (rest == 3) expand_cols_tile<T, 4, NT>(w, a, r, cb, toks, g0, 3, num_tokens, v, y);
 }
 
 // Column of the wave's 64-column slab that MFMA row `rho` of sub-tile `t`
@@ -717,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_shrink_kernel(DevW w, const int
   if (path == LORA_PATH_MFMA)
     shrink_mfma<T>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
   else
-    shrink_gemv<T>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
+    shrink_gemv<T, kRowGroup>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
 }
 
 template <typename T>
@@ -739,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_expand_kernel(DevW w, const int
   if (path == LORA_PATH_MFMA)
     expand_mfma<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
   else
-    expand_gemv<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
+    expand_gemv<T, kThreads>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
 }
 
 // Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups to
@@ -751,27 +763,32 @@ __device__ __forceinline__ int xcd_logical(int b, int grid) { return (b & 7) * (
 
 inline int pad8(int n) { return (n + 7) & ~7; }
 
-// Collects, in token order, the tokens of ids[c0 .. c0+256) whose adapter is
-// `a` into toks[]; returns their count.  All threads must call it.
+// Collects, in token order, the tokens of ids[c0 .. c0+NT) whose adapter is
+// `a` into toks[]; returns their count.  All NT threads must call it.
+template <int NT>
 __device__ __forceinline__ int gather_adapter_tokens(const int32_t *__restrict__ ids, int num_tokens, int c0, int a,
                                      int *toks, int *wave_cnt) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = c0 + tid;
   const bool hit = t < num_tokens && ids[t] == a;
   const unsigned long long mask = __ballot(hit);
   if (lane == 0) wave_cnt[wave] = __popcll(mask);
   __syncthreads();
-  int base = 0;
-  for (int i = 0; i < wave; ++i) base += wave_cnt[i];
-  const int total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+  int base = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    base += i < wave ? wave_cnt[i] : 0;
+    total += wave_cnt[i];
+  }
   if (hit) toks[base + __popcll(mask & ((1ull << lane) - 1ull))] = t;
   __syncthreads();
   return total;
 }
 
 // Per-token (BGMV) shrink.  Work unit u is a token (token-major) or an adapter
-// (adapter-major); each unit is split into row groups of 4, one per workgroup.
-template <typename T>
+// (adapter-major); each unit is split into groups of RB rows, one per workgroup.
+template <typename T, int RB>
 __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int32_t *__restrict__ ids,
                                                                int32_t num_tokens, int32_t adapter_major,
                                                                int32_t units, int32_t groups,
@@ -781,7 +798,7 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
   __shared__ int wave_cnt[4];
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   if (L >= units * groups) return;
-  const int u = L / groups, j0 = (L - u * groups) * kRowGroup;
+  const int u = L / groups, j0 = (L - u * groups) * RB;
   if (!adapter_major) {
     const int t = u;
     const int a = ids[t];
@@ -790,29 +807,29 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
     if (j0 >= r) return;
     if (threadIdx.x == 0) sm.toks[0] = t;
     __syncthreads();
-    shrink_gemv<T>(w, a, j0, min(kRowGroup, r - j0), sm.toks, 1, num_tokens, x, v, sm);
+    shrink_gemv<T, RB>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
     if (j0 >= r) return;
     for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
-      const int n = gather_adapter_tokens(ids, num_tokens, c0, a, sm.toks, wave_cnt);
-      if (n > 0) shrink_gemv<T>(w, a, j0, min(kRowGroup, r - j0), sm.toks, n, num_tokens, x, v, sm);
+      const int n = gather_adapter_tokens<kThreads>(ids, num_tokens, c0, a, sm.toks, wave_cnt);
+      if (n > 0) shrink_gemv<T, RB>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
       __syncthreads();
     }
   }
 }
 
 // Per-token (BGMV) expand.  Work unit u as above, split into column blocks of
-// 2048, one per workgroup.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(DevW w, const int32_t *__restrict__ ids,
-                                                               int32_t num_tokens, int32_t adapter_major,
-                                                               int32_t units, int32_t groups,
-                                                               const float *__restrict__ v,
-                                                               T *__restrict__ y) {
-  __shared__ int toks[kMaxItemTokens];
-  __shared__ int wave_cnt[4];
+// 8 NT columns, one per workgroup of NT threads.
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void bgmv_expand_kernel(DevW w, const int32_t *__restrict__ ids,
+                                                         int32_t num_tokens, int32_t adapter_major,
+                                                         int32_t units, int32_t groups,
+                                                         const float *__restrict__ v,
+                                                         T *__restrict__ y) {
+  __shared__ int toks[NT];
+  __shared__ int wave_cnt[NT / 64];
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   if (L >= units * groups) return;
   const int u = L / groups, cb = L - u * groups;
@@ -821,13 +838,13 @@ __global__ __launch_bounds__(kThreads) void bgmv_expand_kernel(DevW w, const int
     const int a = ids[t];
     if (a < 0 || a >= w.num_adapters) return;
     const int tok1[1] = {t};
-    expand_cols_tile<T, 1>(w, a, adapter_rank(w, a), cb, tok1, 0, 1, num_tokens, v, y);
+    expand_cols_tile<T, 1, NT>(w, a, adapter_rank(w, a), cb, tok1, 0, 1, num_tokens, v, y);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
-    for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
-      const int n = gather_adapter_tokens(ids, num_tokens, c0, a, toks, wave_cnt);
-      if (n > 0) expand_gemv<T>(w, a, r, cb, toks, n, num_tokens, v, y);
+    for (int c0 = 0; c0 < num_tokens; c0 += NT) {
+      const int n = gather_adapter_tokens<NT>(ids, num_tokens, c0, a, toks, wave_cnt);
+      if (n > 0) expand_gemv<T, NT>(w, a, r, cb, toks, n, num_tokens, v, y);
       __syncthreads();
     }
   }
@@ -971,14 +988,14 @@ extern "C" lora_status lora_bgmv_shrink(const lora_weights *w, const int32_t *to
   const int am = bgmv_order(LORA_PHASE_SHRINK, order, num_tokens, w->num_adapters) ==
                  LORA_BGMV_ADAPTER_MAJOR;
   const int units = am ? w->num_adapters : num_tokens;
-  const int groups = (w->r_max + kRowGroup - 1) / kRowGroup;
+  const int groups = (w->r_max + kBgmvRows - 1) / kBgmvRows;
   if ((int64_t)units * groups > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
   const dim3 grid(pad8(units * groups));
   if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL(bgmv_shrink_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, d,
+    hipLaunchKernelGGL((bgmv_shrink_kernel<uint16_t, kBgmvRows>), grid, dim3(kThreads), 0, stream, d,
                        token_adapter, num_tokens, am, units, groups, (const uint16_t *)x, v);
   else
-    hipLaunchKernelGGL(bgmv_shrink_kernel<float>, grid, dim3(kThreads), 0, stream, d,
+    hipLaunchKernelGGL((bgmv_shrink_kernel<float, kBgmvRows>), grid, dim3(kThreads), 0, stream, d,
                        token_adapter, num_tokens, am, units, groups, (const float *)x, v);
   return check_launch("bgmv shrink launch");
 }
@@ -998,15 +1015,18 @@ extern "C" lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *to
   const int am = bgmv_order(LORA_PHASE_EXPAND, order, num_tokens, w->num_adapters) ==
                  LORA_BGMV_ADAPTER_MAJOR;
   const int units = am ? w->num_adapters : num_tokens;
-  const int groups = (w->d_out + kGatherCols - 1) / kGatherCols;
+  constexpr int cols = kBgmvExpandThreads * 8;
+  const int groups = (w->d_out + cols - 1) / cols;
   if ((int64_t)units * groups > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
   const dim3 grid(pad8(units * groups));
   if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL(bgmv_expand_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, units, groups, v, (uint16_t *)y);
+    hipLaunchKernelGGL((bgmv_expand_kernel<uint16_t, kBgmvExpandThreads>), grid,
+                       dim3(kBgmvExpandThreads), 0, stream, d, token_adapter, num_tokens, am, units,
+                       groups, v, (uint16_t *)y);
   else
-    hipLaunchKernelGGL(bgmv_expand_kernel<float>, grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, units, groups, v, (float *)y);
+    hipLaunchKernelGGL((bgmv_expand_kernel<float, kBgmvExpandThreads>), grid,
+                       dim3(kBgmvExpandThreads), 0, stream, d, token_adapter, num_tokens, am, units,
+                       groups, v, (float *)y);
   return check_launch("bgmv expand launch");
 }
 
