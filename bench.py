@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 LLC_BYTES = 256 * 2**20        # Infinity Cache
 KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemm_segments_amd", "csrc", f)
-                  for f in ("kernels.hip", "host.cpp", "lora_internal.h")] + \
+                  for f in ("kernels.hip", "base_gemm.hip", "host.cpp", "lora_internal.h")] + \
                  [os.path.join(ROOT, "include", "lora_sgmv.h")]
 
 
@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="1..4 (2 = decode, the default)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="1..5 (2 = decode, the default; 5 = the 70B-shape layer)")
     ap.add_argument("--shape", default="q", help="config 3 shape: q or up")
     ap.add_argument("--order", type=int, default=0, help="BGMV order (0 auto, 1 token, 2 adapter)")
     ap.add_argument("--policy", type=int, default=0, help="SGMV path policy (0 auto, 1 gather, 2 mfma)")
@@ -75,7 +76,7 @@ def workload(cfg: int, shape: str):
         return wl.sgmv_prefill(shape=shape)
     if cfg == 4:
         return wl.hetero_paged()
-    raise SystemExit("bench.py times configs 1-4; the 70B layer is timed by --config 5 (not yet)")
+    raise SystemExit("unknown config")
 
 
 def read_traffic(kernel: str, workload_name: str):
@@ -122,6 +123,137 @@ def cpu_baseline(p, budget_s: float):
             "kind": "oracle", "sample": sample}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+
+def graph_span(torch, stream, fns, reps: int = 3) -> float:
+    """Seconds per launch: HIP events on `stream` around a graph of the
+    launches `fns` (one each, back to back), best of `reps` replays."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fns:
+            f()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / len(fns)
+        best = t if best is None else min(best, t)
+    return best
+
+
+def bench_layer(args, torch):
+    """The 70B-shape decoder layer: seven projections, each the base GEMM
+    y = x W^T followed by the SGMV delta (segmented mode, automatic paths)."""
+    from segmented_gather_gemm_segments_amd import accounting as acc
+    from segmented_gather_gemm_segments_amd import binding as B
+    from segmented_gather_gemm_segments_amd import runner as R
+    from segmented_gather_gemm_segments_amd import workloads as wl
+
+    stream = torch.cuda.Stream()
+    projs = []
+    for name, _, _ in wl.LAYER_70B:
+        p = wl.layer_projection(name)
+        dp = R.DeviceProblem(p)
+        y = torch.empty((p.num_tokens, p.d_out), dtype=torch.bfloat16, device="cuda")
+        v = dp.new_v()
+        _, _, _, perm_d = dp.segments()
+        sp = dp.plan(B.LORA_PHASE_SHRINK)
+        ep = dp.plan(B.LORA_PHASE_EXPAND)
+        dp._plans = (sp, ep)
+        shrink, expand = B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream)
+        base = B.prepare_base_gemm(dp.x, dp.w, y, stream=stream)
+        projs.append({"name": name, "p": p, "dp": dp, "base": base, "shrink": shrink,
+                      "expand": expand, "y": y})
+    torch.cuda.synchronize()
+    K = args.steps
+    for _ in range(args.warmup):
+        for q in projs:
+            q["base"](); q["shrink"](); q["expand"]()
+    torch.cuda.synchronize()
+    # timed region: K layer-deltas (all seven projections' shrink + expand) as one graph
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(K):
+            for q in projs:
+                q["shrink"](); q["expand"]()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    reps = max(4, min(K, 20))
+    per = {}
+    tot = {"base": 0.0, "shrink": 0.0, "expand": 0.0}
+    for q in projs:
+        p = q["p"]
+        d = {k: graph_span(torch, stream, [q[k]] * reps) for k in ("base", "shrink", "expand")}
+        sb = acc.shrink_bytes(p.ids, p.ranks, p.d_in, 2)
+        eb = acc.expand_bytes(p.ids, p.ranks, p.d_out, 2)
+        bf = acc.base_gemm_flops(p.num_tokens, p.d_out, p.d_in)
+        per[q["name"]] = {"d_in": p.d_in, "d_out": p.d_out,
+                          "base_us": round(d["base"] * 1e6, 2),
+                          "base_tflops": round(bf / d["base"] / 1e12, 1),
+                          "shrink_us": round(d["shrink"] * 1e6, 2),
+                          "shrink_gbs": round(sb / d["shrink"] / 1e9, 1),
+                          "expand_us": round(d["expand"] * 1e6, 2),
+                          "expand_gbs": round(eb / d["expand"] / 1e9, 1),
+                          "_sb": sb, "_eb": eb, "_bf": bf, "_t": d}
+        for k in tot:
+            tot[k] += d[k]
+    tokens = projs[0]["p"].num_tokens
+    delta = tot["shrink"] + tot["expand"]
+    # dominant delta kernel (HBM-bound) and the base GEMM (MFMA-bound)
+    dom = max(((n, k) for n in per for k in ("shrink", "expand")), key=lambda nk: per[nk[0]]["_t"][nk[1]])
+    dn, dk = dom
+    dbytes = per[dn]["_sb" if dk == "shrink" else "_eb"]
+    dt = per[dn]["_t"][dk]
+    base_flops = sum(per[n]["_bf"] for n in per)
+    for n in per:
+        for k in ("_sb", "_eb", "_bf", "_t"):
+            per[n].pop(k)
+    out = {
+        "metric": "LoRA delta tokens/sec per layer + achieved HBM GB/s (% of MI355X peak)",
+        "value": round(tokens * K / wall, 1),
+        "unit": "delta tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; random-init adapters and base weights)",
+        "config": {"workload": "layer70b_1280tok_256ad_r16", "tokens": tokens, "adapters": 256,
+                   "ranks": [16], "projections": [q["name"] for q in projs], "mode": "sgmv",
+                   "timed": "HIP graph replay of K layer deltas (7 projections x shrink + expand)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(dbytes / dt / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(f"sgmv_{dk}", f"layer70b_{dn}"),
+                     "kernel": f"sgmv_{dk} ({dn})", "algorithmic_bytes_per_launch": dbytes,
+                     "avg_launch_us": round(dt * 1e6, 3)},
+        "base_roofline": {"bound": "mfma", "achieved": round(base_flops / tot["base"] / 1e12, 1),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(base_flops / tot["base"] / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "layer": {"base_us": round(tot["base"] * 1e6, 2), "delta_us": round(delta * 1e6, 2),
+                  "lora_overhead_fraction": round(delta / tot["base"], 4),
+                  "delta_tokens_per_s_kernel_time": round(tokens / delta, 1),
+                  "projections": per},
+        "kernel_sources_sha256_16": kernel_hash(),
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(projs[0]["p"], args.cpu_seconds)
+        out["cpu_baseline"]["sample"] += " (q projection only)"
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -149,6 +281,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     B.lib()
+    if args.config == 5:
+        return bench_layer(args, torch)
     p = workload(args.config, args.shape)
     elem = 2 if p.dtype == "bf16" else 4
     mode = "bgmv" if p.mode == "bgmv" else "sgmv"
@@ -206,24 +340,10 @@ def main():
     # ---- per-launch durations: HIP events on the launch stream around a graph
     # of K back-to-back launches of one kernel (the same launches as in the
     # timed steps); duration per launch = event span / K
-    def per_launch(which: int) -> float:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(K):
-                calls[i % n_rep][which]()
-        with torch.cuda.stream(stream):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):       # replay() launches on the current stream
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / K
-
-    t_shrink = np.array([per_launch(0) for _ in range(3)])
-    t_expand = np.array([per_launch(1) for _ in range(3)])
+    t_shrink = np.array([graph_span(torch, stream, [calls[i % n_rep][0] for i in range(K)], 1)
+                         for _ in range(3)])
+    t_expand = np.array([graph_span(torch, stream, [calls[i % n_rep][1] for i in range(K)], 1)
+                         for _ in range(3)])
 
     # ---- accounting
     sb = acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem)

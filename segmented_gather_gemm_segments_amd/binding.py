@@ -327,3 +327,11 @@ def prepare_sgmv(w: Weights, token_perm, shrink_items, expand_items, x, v, y, st
                                            int(expand_items.shape[0]), int(y.shape[0]), _dptr(v),
                                            _dptr(y), s), keep)
     return shrink, expand
+
+
+def prepare_base_gemm(x, w, y, stream=None):
+    """Prepared lora_base_gemm launch y = x w^T on `stream` (default: current)."""
+    m, k = x.shape
+    n = w.shape[0]
+    return Prepared("lora_base_gemm", (LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y),
+                                       _stream(stream)), (x, w, y))

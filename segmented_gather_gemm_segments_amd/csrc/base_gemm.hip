@@ -1,0 +1,171 @@
+// Base projection y = x W^T for the layer the adapters modify: bf16 operands,
+// fp32 accumulation on the matrix cores, bf16 output rounded to nearest even.
+// It is computed once for every token of the batch, whatever the tokens'
+// adapters ("Multi-LoRA serving: the single translator with a thousand
+// glossaries", section "The bare mechanism"); the SGMV delta is then added to
+// it.  Both operands are contiguous along k (x [m][k], W [n][k]), the layout in
+// which every MFMA operand fragment is a run of 8 consecutive k.
+//
+// Tiling for gfx950: a workgroup of four waves computes a 128 x 128 tile of y
+// over k in steps of 64; each wave owns a 64 x 64 sub-tile as 4 x 4 blocks of
+// v_mfma_f32_16x16x32_bf16 with W rows as the A operand and x rows as the B
+// operand, so D[n][m] leaves each lane holding 4 consecutive output columns of
+// one token (one 8-byte store).  The k-tiles of both operands are staged in LDS
+// with padded rows (72 elements) and double-buffered through registers: the
+// global loads of tile t+1 are in flight while tile t is multiplied, and one
+// barrier separates the steps.  Tiles are ordered so that the m-tiles sharing
+// one W tile run on the same XCD (workgroup b runs on XCD b % 8) and share its
+// L2.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kBM = 128;       // tokens per tile
+constexpr int kBN = 128;       // output columns per tile
+constexpr int kBK = 64;        // k per step
+constexpr int kLd = kBK + 8;   // LDS row stride in elements (16-byte pad)
+constexpr int kGemmThreads = 256;
+constexpr int kChunks = kBM * kBK / 8 / kGemmThreads;  // 16-byte chunks per thread per operand
+static_assert(kBM == kBN, "one chunk map serves both operands");
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Loads this thread's chunks of one k-tile of rows [row0, row0 + 128) of a
+// [rows][k] operand: chunk c = tid + 256 i is row c / 8, elements 8 (c % 8) ..
+// +7 of the tile.  Rows past `rows` and k past `k` read as zero.
+__device__ __forceinline__ void load_tile(const uint16_t *__restrict__ src, int rows, int k, int row0,
+                                          int k0, uint4 (&r)[kChunks]) {
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = (int)threadIdx.x + kGemmThreads * i;
+    const int row = row0 + (c >> 3), kk = k0 + (c & 7) * 8;
+    if (row < rows && kk < k)
+      r[i] = *reinterpret_cast<const uint4 *>(src + (int64_t)row * k + kk);
+    else
+      r[i] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_tile(uint16_t *lds, const uint4 (&r)[kChunks]) {
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = (int)threadIdx.x + kGemmThreads * i;
+    *reinterpret_cast<uint4 *>(lds + (c >> 3) * kLd + (c & 7) * 8) = r[i];
+  }
+}
+
+__global__ __launch_bounds__(kGemmThreads) void base_gemm_kernel(int m, int n, int k, int tiles_m,
+                                                                 int tiles,
+                                                                 const uint16_t *__restrict__ x,
+                                                                 const uint16_t *__restrict__ w,
+                                                                 uint16_t *__restrict__ y) {
+  __shared__ uint16_t sw[2][kBN * kLd];
+  __shared__ uint16_t sx[2][kBM * kLd];
+  // XCD-aware order: the grid is a multiple of 8; logical tile L = (b % 8) *
+  // (grid / 8) + b / 8 gives each XCD a contiguous run, m fastest.
+  const int b = blockIdx.x, g8 = gridDim.x >> 3;
+  const int L = (b & 7) * g8 + (b >> 3);
+  if (L >= tiles) return;
+  const int tm = L % tiles_m, tn = L / tiles_m;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave & 1, wm = wave >> 1;     // 2 x 2 waves, 64 x 64 each
+  const int fr = lane & 15, fg = lane >> 4;    // fragment row, k group
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (k + kBK - 1) / kBK;
+  uint4 rw[kChunks], rx[kChunks];
+  load_tile(w, n, k, n0, 0, rw);
+  load_tile(x, m, k, m0, 0, rx);
+  store_tile(sw[0], rw);
+  store_tile(sx[0], rx);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      load_tile(w, n, k, n0, (kt + 1) * kBK, rw);
+      load_tile(x, m, k, m0, (kt + 1) * kBK, rx);
+    }
+    const uint16_t *tw = sw[buf] + (wn * 64 + fr) * kLd + fg * 8;
+    const uint16_t *tx = sx[buf] + (wm * 64 + fr) * kLd + fg * 8;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      bf16x8_t fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(tw + i * 16 * kLd + ks * 32));
+        fb[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(tx + i * 16 * kLd + ks * 32));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      store_tile(sw[buf ^ 1], rw);
+      store_tile(sx[buf ^ 1], rx);
+    }
+    __syncthreads();
+  }
+  // D[n][m] of block (i, j): lane (fg, fr) holds columns n0 + 64 wn + 16 i + 4 fg
+  // .. +3 of token m0 + 64 wm + 16 j + fr
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int col = n0 + wn * 64 + i * 16 + fg * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = m0 + wm * 64 + j * 16 + fr;
+      if (row < m && col < n) {
+        uint2 o;
+        o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2 *>(y + (int64_t)row * n + col) = o;
+      }
+    }
+  }
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k,
+                                      const void *x, const void *w, void *y, hipStream_t stream) {
+  if (dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "base gemm supports bf16 only");
+  if (m < 0 || n <= 0 || k <= 0) return fail(LORA_EINVAL, "base gemm sizes m=%d n=%d k=%d", m, n, k);
+  if (n % 8 || k % 8) return fail(LORA_EUNSUPPORTED, "base gemm needs n and k multiples of 8");
+  if (m == 0) return ok();
+  if (!x || !w || !y) return fail(LORA_EINVAL, "null pointer");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+    return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
+  const int64_t tiles_m = (m + kBM - 1) / kBM, tiles_n = (n + kBN - 1) / kBN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles > INT32_MAX - 8) return fail(LORA_EINVAL, "base gemm too large");
+  const int grid = (int)((tiles + 7) & ~int64_t(7));
+  hipLaunchKernelGGL(base_gemm_kernel, dim3(grid), dim3(kGemmThreads), 0, stream, m, n, k,
+                     (int)tiles_m, (int)tiles, (const uint16_t *)x, (const uint16_t *)w,
+                     (uint16_t *)y);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "base gemm launch");
+  return ok();
+}

@@ -1029,10 +1029,3 @@ extern "C" lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *to
                        groups, v, (float *)y);
   return check_launch("bgmv expand launch");
 }
-
-extern "C" lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k,
-                                      const void *x, const void *w, void *y, hipStream_t stream) {
-  (void)m; (void)n; (void)k; (void)x; (void)w; (void)y; (void)stream;
-  if (dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "base gemm supports bf16 only");
-  return fail(LORA_EUNSUPPORTED, "base gemm not built yet");
-}

@@ -60,6 +60,7 @@ class DeviceProblem:
         self.rank = torch.from_numpy(p.ranks.astype(np.int32)).to(self.device)
         self.r_max = p.r_max
         self._pools = []
+        self.w = to_device(p.extra["w"], p.dtype, self.device) if "w" in p.extra else None
         if self.layout == "dense":
             self._dense()
         else:
@@ -163,3 +164,12 @@ class DeviceProblem:
         B.lora_bgmv_shrink(self.weights, self.ids, self.x, v, order)
         B.lora_bgmv_expand(self.weights, self.ids, v, y, order)
         return y, v
+
+    def run_base(self, y=None):
+        """Base projection y = x W^T (bf16, through lora_base_gemm); returns y."""
+        torch = _torch()
+        assert self.w is not None, "problem has no base weight"
+        if y is None:
+            y = torch.empty((self.p.num_tokens, self.p.d_out), dtype=self.tdtype, device=self.device)
+        B.lora_base_gemm(self.x, self.w, y)
+        return y

@@ -1,0 +1,129 @@
+"""GPU parity of the base projection (lora_base_gemm) and of the 70B-shape
+decoder-layer projections (base y = x W^T, then the SGMV delta added to it),
+through the C ABI, against the fp64 oracle.  Normwise tolerance 2e-2 (bf16
+I/O, fp32 accumulation); each sampled element also within one bf16 rounding
+of the exact value plus 1e-3 of its row's scale."""
+import numpy as np
+import pytest
+
+import oracle
+from segmented_gather_gemm_segments_amd import binding as B
+from segmented_gather_gemm_segments_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    return True
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def runner():
+    from segmented_gather_gemm_segments_amd import runner as R
+    return R
+
+
+def bf16_host(t):
+    return wl.bf16_to_f32(t.detach().view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+def check_sampled(got, want, row_scale, label):
+    """got/want: values at sampled pairs; row_scale: max |row| of the exact output."""
+    err = float(np.max(np.abs(got - want) / row_scale))
+    say(f"{label}: sampled normwise error {err:.3e}")
+    assert err <= 2e-2, label
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0**-8 + 1e-3 * row_scale), label
+
+
+def rand_bf16(rng, shape, std):
+    return wl.bf16_bits((rng.standard_normal(shape, dtype=np.float32) * np.float32(std)))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 8, 8), (77, 264, 520), (200, 136, 1032), (129, 128, 64),
+                                   (256, 1024, 768)])
+def test_base_gemm_small_full(m, n, k):
+    """Every output of ragged shapes (partial tiles in m, n and k)."""
+    rng = np.random.default_rng(m * 7 + n + k)
+    x = rand_bf16(rng, (m, k), 1.0)
+    w = rand_bf16(rng, (n, k), 1.0 / np.sqrt(k))
+    say(f"base gemm full m={m} n={n} k={k}")
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    yd = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    B.lora_base_gemm(xd, wd, yd)
+    torch.cuda.synchronize()
+    got = bf16_host(yd)
+    tok, col = np.meshgrid(np.arange(m, dtype=np.int32), np.arange(n, dtype=np.int32), indexing="ij")
+    want = oracle.base_sampled(x, w, tok.ravel(), col.ravel()).reshape(m, n)
+    scale = np.maximum(np.max(np.abs(want), axis=1, keepdims=True), 1e-30)
+    check_sampled(got, want, np.broadcast_to(scale, want.shape), f"gemm {m}x{n}x{k}")
+
+
+def test_base_gemm_errors():
+    lib = B.lib()
+    assert lib.lora_base_gemm(B.LORA_F32, 8, 8, 8, 16, 16, 16, None) == B.LORA_EUNSUPPORTED
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 12, 8, 16, 16, 16, None) == B.LORA_EUNSUPPORTED
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, None, 16, 16, None) == B.LORA_EINVAL
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, 18, 16, 16, None) == B.LORA_EINVAL
+    assert lib.lora_base_gemm(B.LORA_BF16, 0, 8, 8, None, None, None, None) == B.LORA_OK
+
+
+# tokens whose full output rows are checked: decode tokens (one-token
+# segments), the decode token sharing adapter 0 with the prefill request, and
+# prefill tokens at the segment's start, middle and end
+def _check_rows(p):
+    rows = [0, 1, 77, 200, 255, 256, 257, 700, 1100, 1279]
+    rows.append(int(np.flatnonzero(p.ids[:256] == 0)[0]))
+    return np.array(sorted(set(rows)), dtype=np.int32)
+
+
+def _rows_close(got, want, label, elementwise=True):
+    scale = np.max(np.abs(want), axis=1, keepdims=True)
+    err = float(np.max(np.max(np.abs(got - want), axis=1, keepdims=True) / scale))
+    say(f"{label}: normwise error {err:.3e} over {want.shape[0]} full rows")
+    assert err <= 2e-2, label
+    if elementwise:
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0**-8 + 1e-3 * scale), label
+
+
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
+def test_layer70b_projection(name):
+    """One projection of the 70B-shape layer at full size (1280 tokens: 256
+    decode tokens on 256 rank-16 adapters plus a 1024-token prefill request on
+    adapter 0): the base GEMM, then the SGMV delta (segmented mode, automatic
+    path: one 1025-token MFMA segment, 255 gather segments) added to the GPU's
+    base output, both checked on full rows; and the per-token (BGMV) delta
+    equals the segmented gather delta bit for bit."""
+    R = runner()
+    p = wl.layer_projection(name)
+    say(f"layer70b {name}: {p.d_in} -> {p.d_out}")
+    dp = R.DeviceProblem(p)
+    y_base = dp.run_base()
+    torch.cuda.synchronize()
+    rows = _check_rows(p)
+    yb = bf16_host(y_base)
+    tok = np.repeat(rows, p.d_out).astype(np.int32)
+    col = np.tile(np.arange(p.d_out, dtype=np.int32), rows.size)
+    want_b = oracle.base_sampled(p.x, p.extra["w"], tok, col).reshape(rows.size, p.d_out)
+    _rows_close(yb[rows], want_b, f"{name} base")
+    # delta on top of the GPU's base output (the oracle takes the same y_in)
+    y, _ = dp.run_sgmv(B.LORA_PATH_AUTO, y=y_base.clone())
+    torch.cuda.synchronize()
+    got = bf16_host(y)
+    ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
+    want = oracle.apply(p.x[rows], yb[rows], p.ids[rows], ad)
+    _rows_close(got[rows], want, f"{name} base+delta")
+    # per-token mode on the same batch gives the gather path's bits
+    y2, _ = dp.run_bgmv(B.LORA_BGMV_AUTO, y=y_base.clone())
+    y3, _ = dp.run_sgmv(B.LORA_PATH_GATHER, y=y_base.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
