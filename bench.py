@@ -57,6 +57,8 @@ def parse():
                     help="1..5 (2 = decode, the default; 5 = the 70B-shape layer)")
     ap.add_argument("--shape", default="q", help="config 3 shape: q or up")
     ap.add_argument("--order", type=int, default=0, help="BGMV order (0 auto, 1 token, 2 adapter)")
+    ap.add_argument("--path", choices=("fused", "two"), default="fused",
+                    help="per-token (decode) step: one fused launch, or shrink + expand launches")
     ap.add_argument("--policy", type=int, default=0, help="SGMV path policy (0 auto, 1 gather, 2 mfma)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU time (0 disables the CPU baseline)")
@@ -298,7 +300,9 @@ def main():
     for dp in reps:
         y, v = dp.y0.clone(), dp.new_v()
         if mode == "bgmv":
-            calls.append(B.prepare_bgmv(dp.weights, dp.ids, dp.x, v, y, args.order, stream=stream))
+            sh, ex = B.prepare_bgmv(dp.weights, dp.ids, dp.x, v, y, args.order, stream=stream)
+            fu = B.prepare_bgmv_fused(dp.weights, dp.ids, dp.x, y, None, args.order, stream=stream)
+            calls.append((sh, ex, fu))
         else:
             _, _, _, perm_d = dp.segments()
             sp = dp.plan(B.LORA_PHASE_SHRINK, args.policy)
@@ -306,13 +310,20 @@ def main():
             dp._plans = (sp, ep)
             calls.append(B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream))
     torch.cuda.synchronize()
+    fused = mode == "bgmv" and args.path == "fused"
+
+    def step(i):
+        c = calls[i % n_rep]
+        if fused:
+            c[2]()
+        else:
+            c[0]()
+            c[1]()
 
     # ---- warmup (eager), also measures the host's cost of one step
     t0 = time.perf_counter()
     for i in range(args.warmup):
-        s, e = calls[i % n_rep]
-        s()
-        e()
+        step(i)
     host_step_s = (time.perf_counter() - t0) / max(args.warmup, 1)
     torch.cuda.synchronize()
 
@@ -321,9 +332,7 @@ def main():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for i in range(K):
-            s, e = calls[i % n_rep]
-            s()
-            e()
+            step(i)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         graph.replay()                   # untimed replay: first-touch of the graph
@@ -340,24 +349,25 @@ def main():
     # ---- per-launch durations: HIP events on the launch stream around a graph
     # of K back-to-back launches of one kernel (the same launches as in the
     # timed steps); duration per launch = event span / K
-    t_shrink = np.array([graph_span(torch, stream, [calls[i % n_rep][0] for i in range(K)], 1)
-                         for _ in range(3)])
-    t_expand = np.array([graph_span(torch, stream, [calls[i % n_rep][1] for i in range(K)], 1)
+    def span(which):
+        return np.array([graph_span(torch, stream, [calls[i % n_rep][which] for i in range(K)], 1)
                          for _ in range(3)])
 
     # ---- accounting
-    sb = acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem)
-    eb = acc.expand_bytes(p.ids, p.ranks, p.d_out, elem)
+    timed = {"shrink": (span(0), acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem)),
+             "expand": (span(1), acc.expand_bytes(p.ids, p.ranks, p.d_out, elem))}
+    if mode == "bgmv":
+        timed["fused"] = (span(2), acc.fused_bytes(p.ids, p.ranks, p.d_in, p.d_out, elem))
     tokens = int(np.sum(p.ids >= 0))
     ms_per_step = wall / K * 1e3
     kern = {}
-    for name, t, nbytes in (("shrink", t_shrink, sb), ("expand", t_expand, eb)):
+    for name, (t, nbytes) in timed.items():
         kern[name] = {"avg_us": float(t.mean() * 1e6), "min_us": float(t.min() * 1e6),
                       "max_us": float(t.max() * 1e6), "bytes": nbytes,
                       "gbs": nbytes / t.mean() / 1e9}
-    dom = max(kern, key=lambda k: kern[k]["avg_us"])
-    kname = {"bgmv": {"shrink": "bgmv_shrink", "expand": "bgmv_expand"},
-             "sgmv": {"shrink": "sgmv_shrink", "expand": "sgmv_expand"}}[mode][dom]
+    t_shrink, t_expand = timed["shrink"][0], timed["expand"][0]
+    dom = "fused" if fused else max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
+    kname = f"{mode}_{dom}"
     traffic = read_traffic(kname, p.name)
     achieved = kern[dom]["gbs"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -374,12 +384,14 @@ def main():
         "dtype": p.dtype, "data": "synthetic (seeded; random-init adapters)",
         "config": {"workload": p.name, "tokens": p.num_tokens, "adapters": p.num_adapters,
                    "ranks": sorted(set(int(r) for r in p.ranks)), "d_in": p.d_in, "d_out": p.d_out,
-                   "mode": mode, "replicas": n_rep, "timed": "HIP graph replay of the K steps",
+                   "mode": mode, "path": ("fused" if fused else "shrink+expand"),
+                   "replicas": n_rep, "timed": "HIP graph replay of the K steps",
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for k, d in kern.items()},
-        "gpu_tokens_per_s_kernel_time": round(tokens / (t_shrink.mean() + t_expand.mean()), 1),
+        "gpu_tokens_per_s_kernel_time": round(
+            tokens / (kern["fused"]["avg_us"] * 1e-6 if fused else t_shrink.mean() + t_expand.mean()), 1),
         "host_ms_per_step_eager": round(host_step_s * 1e3, 5),
         "kernel_sources_sha256_16": kernel_hash(),
     }

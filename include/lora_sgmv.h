@@ -233,9 +233,9 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
  *          LORA_BGMV_ADAPTER_MAJOR: the same split per adapter, each workgroup
  *          scanning token_adapter for its adapter's tokens, so each adapter's
  *          rows are read once however many tokens use it;
- *          LORA_BGMV_AUTO: shrink adapter-major when num_adapters <= num_tokens,
- *          expand adapter-major when num_tokens >= 16 num_adapters, otherwise
- *          token-major.  Every order gives bit-identical results.           */
+ *          LORA_BGMV_AUTO: shrink adapter-major when num_adapters <= num_tokens
+ *          <= 4 num_adapters, otherwise token-major; expand token-major.
+ *          Every order gives bit-identical results.                        */
 #define LORA_BGMV_AUTO 0
 #define LORA_BGMV_TOKEN_MAJOR 1
 #define LORA_BGMV_ADAPTER_MAJOR 2
@@ -245,6 +245,26 @@ lora_status lora_bgmv_shrink(const lora_weights *w, const int32_t *token_adapter
 lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *token_adapter,
                              int32_t num_tokens, int32_t order, const float *v, void *y,
                              hipStream_t stream);
+
+/* Per-token (BGMV) delta in ONE launch: shrink and expand of each token fused
+ * in one workgroup (S-LoRA's decode kernel MBGMV in "Multi-LoRA serving ...",
+ * section "SGMV: the kernel that holds it all up"; the launch and gather
+ * overhead per adapted layer that the glossary entry "Multi-LoRA Serving",
+ * section "Limits and open questions", attributes to unmerged adapters).
+ * Computes y[t] += B_{a(t)} (A_{a(t)} x[t]) for every token with the same
+ * arithmetic as lora_bgmv_shrink + lora_bgmv_expand (fp32 v, one rounding of
+ * y); v [num_tokens, r_max] receives the rank-space values when non-NULL.
+ * The fused and two-launch paths sum in different orders, so their results
+ * agree to rounding, not bit for bit; the fused path's two orders give
+ * identical bits.  token_adapter, x, y as for lora_bgmv_shrink/expand.
+ *   order  LORA_BGMV_TOKEN_MAJOR (and LORA_BGMV_AUTO): one workgroup per
+ *          token and column block;
+ *          LORA_BGMV_ADAPTER_MAJOR: one workgroup per adapter and column block,
+ *          finding its tokens by scanning token_adapter and processing them
+ *          four at a time (for few tokens per adapter).                     */
+lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
+                            int32_t num_tokens, int32_t order, const void *x, float *v,
+                            void *y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Paged adapter pool (host bookkeeping over caller-owned device storage of

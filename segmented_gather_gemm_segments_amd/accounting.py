@@ -9,6 +9,7 @@ matters", bytes-per-matrix equation and the Llama-3-70B rank-16 table).
 Per launch:
   shrink bytes = T_a*d_in*s + sum_{a used} r_a*d_in*s + sum_t r_{a(t)}*4
   expand bytes = sum_t r_{a(t)}*4 + sum_{a used} r_a*d_out*s + 2*T_a*d_out*s
+  fused bytes  = T_a*d_in*s + sum_{a used} r_a*(d_in + d_out)*s + 2*T_a*d_out*s
   shrink flops = 2*d_in*sum_t r_{a(t)};  expand flops = 2*d_out*sum_t r_{a(t)}
 where T_a counts tokens that carry an adapter, s is the activation/weight
 element size and v is fp32.  Token ids, segments, plans and page tables are
@@ -48,6 +49,14 @@ def shrink_bytes(ids, ranks, d_in: int, elem_bytes: int) -> int:
 def expand_bytes(ids, ranks, d_out: int, elem_bytes: int) -> int:
     t_a, sum_r_tok, sum_r_distinct = _usage(ids, ranks)
     return sum_r_tok * 4 + sum_r_distinct * d_out * elem_bytes + 2 * t_a * d_out * elem_bytes
+
+
+def fused_bytes(ids, ranks, d_in: int, d_out: int, elem_bytes: int) -> int:
+    """One-launch delta (shrink and expand fused, v kept on chip): x, each used
+    adapter's A and B rows, y read and written."""
+    t_a, _, sum_r_distinct = _usage(ids, ranks)
+    return (t_a * d_in * elem_bytes + sum_r_distinct * (d_in + d_out) * elem_bytes
+            + 2 * t_a * d_out * elem_bytes)
 
 
 def shrink_flops(ids, ranks, d_in: int) -> int:

@@ -65,6 +65,7 @@ EXPORTS = {
     "lora_sgmv_expand": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_expand": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
+    "lora_bgmv_fused": ([_P, _P, _I32, _I32, _P, _P, _P, _P], _I32),
     "lora_pool_create": ([_I32, _I32, _I32, _I32, _P, _U64, _P], _I32),
     "lora_pool_alloc": ([_P, _I32, _P], _I32),
     "lora_pool_free": ([_P, _P, _I32], _I32),
@@ -232,6 +233,13 @@ def lora_bgmv_expand(w: Weights, token_adapter, v, y, order: int = LORA_BGMV_AUT
                                   order, _dptr(v), _dptr(y), _stream(stream)))
 
 
+def lora_bgmv_fused(w: Weights, token_adapter, x, y, v=None, order: int = LORA_BGMV_AUTO,
+                    stream=None):
+    d = w.desc()
+    _check(lib().lora_bgmv_fused(ctypes.byref(d), _dptr(token_adapter), int(token_adapter.numel()),
+                                 order, _dptr(x), _dptr(v), _dptr(y), _stream(stream)))
+
+
 def lora_base_gemm(x, w, y, stream=None):
     m, k = x.shape
     n = w.shape[0]
@@ -335,3 +343,13 @@ def prepare_base_gemm(x, w, y, stream=None):
     n = w.shape[0]
     return Prepared("lora_base_gemm", (LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y),
                                        _stream(stream)), (x, w, y))
+
+
+def prepare_bgmv_fused(w: Weights, token_adapter, x, y, v=None, order: int = LORA_BGMV_AUTO,
+                       stream=None):
+    """Prepared fused BGMV launch (shrink + expand in one kernel) on `stream`."""
+    d = w.desc()
+    keep = (d, w, token_adapter, x, v, y)
+    return Prepared("lora_bgmv_fused", (ctypes.byref(d), _dptr(token_adapter),
+                                        int(token_adapter.numel()), order, _dptr(x), _dptr(v),
+                                        _dptr(y), _stream(stream)), keep)

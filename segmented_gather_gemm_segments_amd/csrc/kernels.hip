@@ -51,8 +51,10 @@ __device__ __forceinline__ const T *page_row(const char *base, const int32_t *pt
   int page, r_in;
   if (pt) {
     const int pi = j / w.page_rows;
-    if (pi >= w.max_pages) return nullptr;
-    page = pt[(int64_t)a * w.max_pages + pi];
+    // the page-id load is unconditional (clamped index) so that several rows'
+    // lookups can be in flight together
+    page = pt[(int64_t)a * w.max_pages + (pi < w.max_pages ? pi : w.max_pages - 1)];
+    if (pi >= w.max_pages) page = -1;
     r_in = j - pi * w.page_rows;
   } else {
     page = a;
@@ -69,6 +71,40 @@ __device__ __forceinline__ const T *a_row(const DevW &w, int a, int j) {
 template <typename T>
 __device__ __forceinline__ const T *b_row(const DevW &w, int a, int j) {
   return page_row<T>(w.b_pages, w.b_pt, w.num_pages_b, w, a, j, w.d_out);
+}
+
+// Addresses of rows j0 .. j0+15 of adapter a's B^T, offset by `col` (rows at
+// or past the rank, or on an out-of-range page, get `safe`).  When the 16 rows
+// lie in one page (the usual case: 16-row pages, j0 a multiple of 16) a single
+// page lookup serves them all; a dense stack needs none.
+template <typename T>
+__device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, int col, const T *safe,
+                                         const T *(&rp)[16]) {
+  const T *base = reinterpret_cast<const T *>(w.b_pages);
+  const int pr = w.page_rows;
+  if (!w.b_pt || (pr >= 16 && j0 % pr + 16 <= pr)) {
+    int page, r0;
+    if (w.b_pt) {
+      const int pi = j0 / pr;
+      page = w.b_pt[(int64_t)a * w.max_pages + (pi < w.max_pages ? pi : w.max_pages - 1)];
+      if (pi >= w.max_pages) page = -1;
+      r0 = j0 - pi * pr;
+    } else {
+      page = a;
+      r0 = j0;
+    }
+    const bool ok = (unsigned)page < (unsigned)w.num_pages_b;
+    const T *p0 = base + ((int64_t)(ok ? page : 0) * pr + r0) * w.d_out + col;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rp[i] = (ok && j0 + i < r) ? p0 + (int64_t)i * w.d_out : safe;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const T *p = j0 + i < r ? page_row<T>(w.b_pages, w.b_pt, w.num_pages_b, w, a, j0 + i, w.d_out)
+                              : nullptr;
+      rp[i] = p ? p + col : safe;
+    }
+  }
 }
 
 __device__ __forceinline__ int adapter_rank(const DevW &w, int a) {
@@ -208,6 +244,21 @@ __device__ __forceinline__ void raw_cvt(const Raw8<float> &r, float (&o)[8]) {
   o[0] = r.a.x; o[1] = r.a.y; o[2] = r.a.z; o[3] = r.a.w;
   o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
 }
+__device__ __forceinline__ void raw_zero(Raw8<uint16_t> &r) { r.u = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void raw_zero(Raw8<float> &r) {
+  r.a = make_float4(0.f, 0.f, 0.f, 0.f);
+  r.b = r.a;
+}
+// Element e (0..7, a compile-time index after unrolling) of a raw chunk, as stored.
+__device__ __forceinline__ uint16_t raw_elem(const Raw8<uint16_t> &r, int e) {
+  const uint32_t wd = e < 2 ? r.u.x : e < 4 ? r.u.y : e < 6 ? r.u.z : r.u.w;
+  return (uint16_t)(e & 1 ? wd >> 16 : wd & 0xffffu);
+}
+__device__ __forceinline__ float raw_elem(const Raw8<float> &r, int e) {
+  const float4 q = e < 4 ? r.a : r.b;
+  const int i = e & 3;
+  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+}
 
 // ----------------------------------------------------------------- shrink cores
 // Token list of the current item in LDS: toks[0..cnt).  Tokens outside
@@ -215,8 +266,12 @@ __device__ __forceinline__ void raw_cvt(const Raw8<float> &r, float (&o)[8]) {
 constexpr int kMaxItemTokens = 256;
 constexpr int kRowGroup = LORA_SHRINK_GATHER_ROWS;    // rows of A per segmented gather item
 constexpr int kGatherCols = LORA_EXPAND_GATHER_COLS;  // columns of y per segmented gather item
-constexpr int kStep = kThreads * 8;                   // d elements covered by one pass of 256 threads
 static_assert(kGatherCols == kThreads * 8, "one 8-column chunk per thread");
+#ifndef LORA_SGMV_SHRINK_THREADS
+#define LORA_SGMV_SHRINK_THREADS 256
+#endif
+constexpr int kSgmvShrinkThreads = LORA_SGMV_SHRINK_THREADS;  // threads of a segmented shrink workgroup
+static_assert(kSgmvShrinkThreads % 64 == 0 && kSgmvShrinkThreads <= 1024, "whole waves, <= 1024");
 
 // Per-token (BGMV) work split: rows of A per shrink workgroup, and threads per
 // expand workgroup (8 columns of y per thread).
@@ -231,27 +286,31 @@ constexpr int kBgmvExpandThreads = LORA_BGMV_EXPAND_THREADS;
 static_assert(kBgmvRows == 1 || kBgmvRows == 2 || kBgmvRows == 4, "BGMV shrink rows: 1, 2 or 4");
 static_assert(kBgmvExpandThreads % 64 == 0 && kBgmvExpandThreads <= kThreads, "whole waves");
 
-struct ShrinkSmem {
+// LDS of a shrink workgroup of NW waves.
+template <int NW>
+struct alignas(16) ShrinkSmem {
   int toks[kMaxItemTokens];
   union {
-    float red_gemv[4 * 64];           // one value per (wave, value index)
-    float red_mfma[4 * 4 * 4 * 64];   // [wave][row tile][element][lane]
+    float red_gemv[NW * 64];           // one value per (wave, value index)
+    float red_mfma[NW * 4 * 4 * 64];   // [wave][row tile][element][lane]
   };
 };
 
 // One gather/GEMV shrink tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) against
-// the rows [j0, j0+nr) (nr <= 4) of adapter a.  The 256 threads split d_in into
-// 8-element chunks (thread tid: k = 8 tid + 2048 s); each pass issues the loads
-// of two such steps (TG x chunks and 4 A chunks each) before the first FMA, and
-// the x chunks of a token are reused across the 4 rows in registers.  Rows and
-// tokens beyond the tile read a safe in-bounds address (row 0 of x) and their
-// sums are dropped.  The TG x 4 lane partials are reduce-scattered over the
-// wave and the four wave results summed in wave order, so a token's result
-// does not depend on TG or on which other tokens share the tile.
-template <typename T, int TG, int RB>
+// the rows [j0, j0+nr) (nr <= RB) of adapter a.  The 64 NW threads split d_in
+// into 8-element chunks (thread tid: k = 8 tid + 512 NW s); each pass issues
+// the loads of two such steps (TG x chunks and RB A chunks each) before the
+// first FMA, and the x chunks of a token are reused across the rows in
+// registers.  Rows and tokens beyond the tile read a safe in-bounds address
+// (row 0 of x) and their sums are dropped.  The TG x RB lane partials are
+// reduce-scattered over the wave and the NW wave results summed in wave order,
+// so a token's result does not depend on TG or on which other tokens share the
+// tile (for a given NW).
+template <typename T, int TG, int RB, int NW>
 __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
                                  int ntok, int num_tokens, const T *__restrict__ x,
-                                 float *__restrict__ v, ShrinkSmem &sm) {
+                                 float *__restrict__ v, ShrinkSmem<NW> &sm) {
+  constexpr int kStep = NW * 64 * 8;
   constexpr int NV = TG * RB;
   constexpr int SH = 6 - ilog2(NV);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -271,30 +330,35 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
   float acc[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-  for (int k = tid * 8; k < w.d_in; k += 2 * kStep) {
-    const bool two = k + kStep < w.d_in;
+  // uniform trip count; every load is issued unconditionally (a step past
+  // d_in reads chunk 0 and is not accumulated) so a pass keeps all its loads
+  // in flight together
+  for (int base = 0; base < w.d_in; base += 2 * kStep) {
+    const int k0 = base + tid * 8, k1 = k0 + kStep;
+    const bool one = k0 < w.d_in, two = k1 < w.d_in;
+    const int c0 = one ? k0 : 0, c1 = two ? k1 : 0;
     Raw8<T> xa[TG], aa[RB], xb[TG], ab[RB];
 #pragma unroll
-    for (int t = 0; t < TG; ++t) raw_load(xa[t], xr[t] + k);
+    for (int t = 0; t < TG; ++t) raw_load(xa[t], xr[t] + c0);
 #pragma unroll
-    for (int jj = 0; jj < RB; ++jj) raw_load(aa[jj], ar[jj] + k);
-    if (two) {
+    for (int jj = 0; jj < RB; ++jj) raw_load(aa[jj], ar[jj] + c0);
 #pragma unroll
-      for (int t = 0; t < TG; ++t) raw_load(xb[t], xr[t] + k + kStep);
+    for (int t = 0; t < TG; ++t) raw_load(xb[t], xr[t] + c1);
 #pragma unroll
-      for (int jj = 0; jj < RB; ++jj) raw_load(ab[jj], ar[jj] + k + kStep);
-    }
+    for (int jj = 0; jj < RB; ++jj) raw_load(ab[jj], ar[jj] + c1);
     float xv[TG][8];
+    if (one) {
 #pragma unroll
-    for (int t = 0; t < TG; ++t) raw_cvt(xa[t], xv[t]);
+      for (int t = 0; t < TG; ++t) raw_cvt(xa[t], xv[t]);
 #pragma unroll
-    for (int jj = 0; jj < RB; ++jj) {
-      float av[8];
-      raw_cvt(aa[jj], av);
+      for (int jj = 0; jj < RB; ++jj) {
+        float av[8];
+        raw_cvt(aa[jj], av);
 #pragma unroll
-      for (int t = 0; t < TG; ++t)
+        for (int t = 0; t < TG; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[t * RB + jj] = fmaf(av[e], xv[t][e], acc[t * RB + jj]);
+          for (int e = 0; e < 8; ++e) acc[t * RB + jj] = fmaf(av[e], xv[t][e], acc[t * RB + jj]);
+      }
     }
     if (two) {
 #pragma unroll
@@ -314,8 +378,9 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
   if ((lane & ((1 << SH) - 1)) == 0) sm.red_gemv[wave * 64 + (lane >> SH)] = part;
   __syncthreads();
   if (tid < NV) {
-    const float s = ((sm.red_gemv[tid] + sm.red_gemv[64 + tid]) + sm.red_gemv[128 + tid]) +
-                    sm.red_gemv[192 + tid];
+    float s = sm.red_gemv[tid];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) s += sm.red_gemv[wv * 64 + tid];
     const int t = tid / RB, jj = tid % RB;
     if (t < ntok && jj < nr) {
       const int tok = toks[g0 + t];
@@ -327,27 +392,28 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
 
 // Gather/GEMV shrink of tokens toks[0..cnt) of adapter a over its row group
 // [j0, j0 + nr), nr <= RB: groups of up to 4 tokens, one group of 1 to 3 at the end.
-template <typename T, int RB>
+template <typename T, int RB, int NW>
 __device__ __forceinline__ void shrink_gemv(const DevW &w, int a, int j0, int nr, const int *toks, int cnt,
                             int num_tokens, const T *__restrict__ x, float *__restrict__ v,
-                            ShrinkSmem &sm) {
+                            ShrinkSmem<NW> &sm) {
   int g0 = 0;
   for (; g0 + 4 <= cnt; g0 += 4)
-    shrink_rows_tile<T, 4, RB>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
+    shrink_rows_tile<T, 4, RB, NW>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
   const int rest = cnt - g0;
-  if (rest == 1) shrink_rows_tile<T, 1, RB>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
-  else if (rest == 2) shrink_rows_tile<T, 2, RB>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
-  else if (rest == 3) shrink_rows_tile<T, 4, RB>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
+  if (rest == 1) shrink_rows_tile<T, 1, RB, NW>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
+  else if (rest == 2) shrink_rows_tile<T, 2, RB, NW>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
+  else if (rest == 3) shrink_rows_tile<T, 4, RB, NW>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
 }
 
 // One MFMA shrink tile: 16 tokens (this lane's token row xp, or a safe row)
-// against RT row tiles of 16 starting at j0.  The four waves take interleaved
+// against RT row tiles of 16 starting at j0.  The NW waves take interleaved
 // 32-element k-steps; each batch issues the loads of U steps before its
 // MFMAs.  Lanes beyond the rank or the tile read safe rows whose outputs are
-// dropped; the last, partial k-step zeroes both operands past d_in.
-template <typename T, int RT>
+// dropped; the last, partial k-step zeroes both operands past d_in.  The wave
+// results are summed in wave order.
+template <typename T, int RT, int NW>
 __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, int j0, const T *xp, int tok,
-                                 const T *__restrict__ x, float *__restrict__ v, ShrinkSmem &sm) {
+                                 const T *__restrict__ x, float *__restrict__ v, ShrinkSmem<NW> &sm) {
   constexpr int U = RT == 1 ? 8 : 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
@@ -365,11 +431,11 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
   const int full = w.d_in >> 5;             // k-steps entirely inside d_in
   const int nsteps = (w.d_in + 31) >> 5;
   int s = wave;
-  for (; s + 4 * (U - 1) < full; s += 4 * U) {
+  for (; s + NW * (U - 1) < full; s += NW * U) {
     Frag<T> xf[U], af[U][RT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (s + 4 * u) * 32 + g * 8;
+      const int k = (s + NW * u) * 32 + g * 8;
       frag_load(xf[u], xp + k);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) frag_load(af[u][rt], ap[rt] + k);
@@ -379,14 +445,17 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt] = frag_mfma(af[u][rt], xf[u], acc[rt]);
   }
-  for (; s < nsteps; s += 4) {
+  for (; s < nsteps; s += NW) {
     const int k = s * 32 + g * 8;
     const bool kin = k < w.d_in;
+    const int kc = kin ? k : 0;       // loads stay unconditional; past d_in they are zeroed
     Frag<T> xf, af[RT];
-    if (kin) frag_load(xf, xp + k); else frag_zero(xf);
+    frag_load(xf, xp + kc);
+    if (!kin) frag_zero(xf);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      if (kin) frag_load(af[rt], ap[rt] + k); else frag_zero(af[rt]);
+      frag_load(af[rt], ap[rt] + kc);
+      if (!kin) frag_zero(af[rt]);
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = frag_mfma(af[rt], xf, acc[rt]);
@@ -401,10 +470,9 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
     const int rt = wave;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float s4 = ((sm.red_mfma[((0 * 4 + rt) * 4 + e) * 64 + lane] +
-                         sm.red_mfma[((1 * 4 + rt) * 4 + e) * 64 + lane]) +
-                        sm.red_mfma[((2 * 4 + rt) * 4 + e) * 64 + lane]) +
-                       sm.red_mfma[((3 * 4 + rt) * 4 + e) * 64 + lane];
+      float s4 = sm.red_mfma[(rt * 4 + e) * 64 + lane];
+#pragma unroll
+      for (int wv = 1; wv < NW; ++wv) s4 += sm.red_mfma[((wv * 4 + rt) * 4 + e) * 64 + lane];
       const int j = j0 + rt * 16 + 4 * g + e;
       if (tok >= 0 && j < r) v[(int64_t)tok * w.r_max + j] = s4;
     }
@@ -414,9 +482,9 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
 
 // MFMA shrink for tokens toks[0..cnt) of adapter a: 16-token tiles, passes of
 // up to 64 rows.
-template <typename T>
+template <typename T, int NW>
 __device__ __forceinline__ void shrink_mfma(const DevW &w, int a, int r, const int *toks, int cnt, int num_tokens,
-                            const T *__restrict__ x, float *__restrict__ v, ShrinkSmem &sm) {
+                            const T *__restrict__ x, float *__restrict__ v, ShrinkSmem<NW> &sm) {
   const int m = threadIdx.x & 15;
   for (int m0 = 0; m0 < cnt; m0 += 16) {
     int tok = m0 + m < cnt ? toks[m0 + m] : -1;
@@ -425,10 +493,10 @@ __device__ __forceinline__ void shrink_mfma(const DevW &w, int a, int r, const i
     for (int j0 = 0; j0 < r; j0 += 64) {
       const int nrt = min(4, (r - j0 + 15) >> 4);
       switch (nrt) {
-        case 1: shrink_mfma_tile<T, 1>(w, a, r, j0, xp, tok, x, v, sm); break;
-        case 2: shrink_mfma_tile<T, 2>(w, a, r, j0, xp, tok, x, v, sm); break;
-        case 3: shrink_mfma_tile<T, 3>(w, a, r, j0, xp, tok, x, v, sm); break;
-        default: shrink_mfma_tile<T, 4>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 1: shrink_mfma_tile<T, 1, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 2: shrink_mfma_tile<T, 2, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 3: shrink_mfma_tile<T, 3, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
+        default: shrink_mfma_tile<T, 4, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
       }
     }
   }
@@ -439,10 +507,13 @@ template <typename T> struct ExpandCfg;
 template <> struct ExpandCfg<uint16_t> { static constexpr int kRowStride = 72; };  // 64 j + pad
 template <> struct ExpandCfg<float> { static constexpr int kRowStride = 68; };
 
+constexpr int kVStride = 68;  // LDS row stride (floats) of the staged v rows: 64 j + pad
+
 template <typename T>
-struct ExpandSmem {
+struct alignas(16) ExpandSmem {
   int toks[kMaxItemTokens];
   T bt[4 * 64 * ExpandCfg<T>::kRowStride];  // MFMA path, per wave: [64 cols][j]
+  float vs[64 * kVStride];                   // MFMA path: [token][j] of the 64 tokens
 };
 
 // One gather/GEMV expand tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) over
@@ -464,10 +535,11 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
     const int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
     tk[t] = (tok >= 0 && tok < num_tokens) ? tok : -1;
   }
+  // every load is issued unconditionally (token row 0 stands in for an absent
+  // token; its values are not used) so the tile's loads are in flight together
   Raw8<T> yraw[TG];
 #pragma unroll
-  for (int t = 0; t < TG; ++t)
-    if (tk[t] >= 0) raw_load(yraw[t], y + (int64_t)tk[t] * w.d_out + col);
+  for (int t = 0; t < TG; ++t) raw_load(yraw[t], y + (int64_t)(tk[t] >= 0 ? tk[t] : 0) * w.d_out + col);
   const T *safe = reinterpret_cast<const T *>(w.b_pages);
   const bool vec_v = (w.r_max & 3) == 0;
   float acc[TG][8];
@@ -476,31 +548,38 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
   for (int j0 = 0; j0 < r; j0 += 16) {
+    // all 16 row addresses first (their page lookups in flight together), then
+    // all 16 row loads
+    const T *rp[16];
+    b_rows16<T>(w, a, j0, r, col, safe, rp);
     Raw8<T> braw[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const T *p = j0 + i < r ? b_row<T>(w, a, j0 + i) : nullptr;
-      raw_load(braw[i], p ? p + col : safe);
-    }
+    for (int i = 0; i < 16; ++i) raw_load(braw[i], rp[i]);
     // v[tok][j0 .. j0+16): the same address in every lane, read with 16-byte
     // vector loads (one request per wave) where r_max keeps them aligned
     float vj[TG][16];
+    if (vec_v && j0 + 16 <= w.r_max) {
 #pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      const float *vr = v + (int64_t)(tk[t] >= 0 ? tk[t] : 0) * w.r_max + j0;
+      for (int t = 0; t < TG; ++t) {
+        const float *vr = v + (int64_t)(tk[t] >= 0 ? tk[t] : 0) * w.r_max + j0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int jq = j0 + 4 * q;
-        if (tk[t] >= 0 && vec_v && jq + 4 <= r) {
+        for (int q = 0; q < 4; ++q) {
           const float4 f = *reinterpret_cast<const float4 *>(vr + 4 * q);
           vj[t][4 * q] = f.x; vj[t][4 * q + 1] = f.y; vj[t][4 * q + 2] = f.z; vj[t][4 * q + 3] = f.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            vj[t][4 * q + e] = (tk[t] >= 0 && jq + e < r) ? vr[4 * q + e] : 0.f;
         }
       }
+    } else {
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        const float *vr = v + (int64_t)(tk[t] >= 0 ? tk[t] : 0) * w.r_max;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vj[t][i] = vr[min(j0 + i, w.r_max - 1)];
+      }
     }
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vj[t][i] = (tk[t] >= 0 && j0 + i < r) ? vj[t][i] : 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (j0 + i < r) {
@@ -556,13 +635,46 @@ __device__ __forceinline__ void load_v8(const float *vr, int jb, int nj, bool ve
   }
 }
 
+// Stages rows jc .. jc + 8 NR of this wave's 64-column B^T slab into LDS,
+// transposed ([column][j]); lane l takes row (l >> 3) + 8 i and columns
+// 8 (l & 7) .. +7.  Rows past nj (the rank) and columns past d_out are zero.
+// The NR loads are issued unconditionally (safe address, zero-selected) before
+// the first store.
+template <typename T, int NR>
+__device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj, int c0, T *bt, int lane) {
+  constexpr int RS = ExpandCfg<T>::kRowStride;
+  const T *safe = reinterpret_cast<const T *>(w.b_pages);
+  const int cc = (lane & 7) * 8;
+  const T *rp[NR];
+  bool ok[NR];
+#pragma unroll
+  for (int it = 0; it < NR; ++it) {
+    const int jr = (lane >> 3) + 8 * it;
+    const T *br = (jr < nj && c0 + cc < w.d_out) ? b_row<T>(w, a, jc + jr) : nullptr;
+    ok[it] = br != nullptr;
+    rp[it] = br ? br + c0 + cc : safe;
+  }
+  Raw8<T> braw[NR];
+#pragma unroll
+  for (int it = 0; it < NR; ++it) raw_load(braw[it], rp[it]);
+#pragma unroll
+  for (int it = 0; it < NR; ++it) {
+    const int jr = (lane >> 3) + 8 * it;
+    if (!ok[it]) raw_zero(braw[it]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bt[(cc + e) * RS + jr] = raw_elem(braw[it], e);
+  }
+}
+
 // MFMA expand for tokens toks[0..cnt) of adapter a over the 256 columns of
 // block `blk` (wave w: 64 columns), 64 tokens (four 16-token tiles) at a time.
-// D[col][token] = B^T-slab^T · v^T with the B^T slab staged transposed in LDS;
-// the slab fragments of a 16-index K block are read once and used by all four
-// token tiles.  bf16: v is split into hi + lo bf16 so each K=32 MFMA covers 16
-// rank indices exactly; fp32: 16x16x4 steps.  The y chunks of the 64 tokens
-// are prefetched before the slab is staged.
+// D[col][token] = B^T-slab^T · v^T.  The y chunks of the 64 tokens are fetched
+// first; then, in one round trip, each wave loads its B^T slab (64 columns x
+// up to 64 rank indices, stored transposed in LDS) and the workgroup loads the
+// 64 tokens' v rows (stored in LDS); after one barrier the slab fragments of a
+// 16-index K block are read once and used by all four token tiles.  bf16: v is
+// split into hi + lo bf16 so each K=32 MFMA covers 16 rank indices exactly;
+// fp32: 16x16x4 steps.
 template <typename T>
 __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y,
@@ -582,15 +694,17 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
       const int t = (tt < ntt && i < cnt) ? toks[i] : -1;
       tok[tt] = (t >= 0 && t < num_tokens) ? t : -1;
     }
-    // prefetch y: lane (g, m) of tile tt touches columns c0 + 32q + 8g .. +7
+    // prefetch y: lane (g, m) of tile tt touches columns c0 + 32q + 8g .. +7;
+    // issued unconditionally (row 0 / column 0 stand in where there is no
+    // token or column; those values are never stored)
     Raw8<T> yraw[4][2];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int col = c0 + 32 * q + 8 * g;
-        if (tt < ntt && tok[tt] >= 0 && col < w.d_out)
-          raw_load(yraw[tt][q], y + (int64_t)tok[tt] * w.d_out + col);
+        const int64_t row = tok[tt] >= 0 ? tok[tt] : 0;
+        raw_load(yraw[tt][q], y + row * w.d_out + (col < w.d_out ? col : 0));
       }
     f32x4_t acc[4][4];
 #pragma unroll
@@ -600,30 +714,47 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
     for (int jc = 0; jc < r; jc += 64) {
       const int nj = min(64, r - jc);
       const int nj16 = (nj + 15) & ~15;
-      __syncthreads();  // previous users of the slab are done
-      // stage B^T rows jc .. jc+nj16 of this wave's 64 columns, transposed
-      for (int jr = lane >> 3; jr < nj16; jr += 8) {
-        const int cc = (lane & 7) * 8;
-        float bv[8];
-        const T *br = (jr < nj && c0 + cc < w.d_out) ? b_row<T>(w, a, jc + jr) : nullptr;
-        if (br) {
-          load8(br + c0 + cc, bv);
+      const int nq = nj16 >> 2;  // float4 groups per staged v row
+      __syncthreads();  // previous users of the slab and of the v rows are done
+      // v rows of the 64 tokens (issued first), then this wave's B^T rows
+      // jc .. jc+nj16; all loads unconditional (safe addresses, zero-selected),
+      // so they are in flight together before the first LDS store
+      float4 vq[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int idx = tid + kThreads * it;     // (token, float4 group) pairs
+        const int ti = idx / nq, q = idx - ti * nq;
+        const int i = m0 + ti;
+        const int t = (ti < 64 && i < cnt) ? toks[i] : -1;
+        const bool ok = t >= 0 && t < num_tokens;
+        const int j = jc + 4 * q;
+        const float *vr = v + (int64_t)(ok ? t : 0) * w.r_max;
+        if (vec_v && j + 4 <= w.r_max) {
+          vq[it] = *reinterpret_cast<const float4 *>(vr + j);
         } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+          vq[it].x = vr[min(j, w.r_max - 1)];
+          vq[it].y = vr[min(j + 1, w.r_max - 1)];
+          vq[it].z = vr[min(j + 2, w.r_max - 1)];
+          vq[it].w = vr[min(j + 3, w.r_max - 1)];
         }
+        vq[it].x = ok && j < r ? vq[it].x : 0.f;
+        vq[it].y = ok && j + 1 < r ? vq[it].y : 0.f;
+        vq[it].z = ok && j + 2 < r ? vq[it].z : 0.f;
+        vq[it].w = ok && j + 3 < r ? vq[it].w : 0.f;
+      }
+      switch (nj16 >> 3) {
+        case 2: stage_slab<T, 2>(w, a, jc, nj, c0, bt, lane); break;
+        case 4: stage_slab<T, 4>(w, a, jc, nj, c0, bt, lane); break;
+        case 6: stage_slab<T, 6>(w, a, jc, nj, c0, bt, lane); break;
+        default: stage_slab<T, 8>(w, a, jc, nj, c0, bt, lane); break;
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if constexpr (sizeof(T) == 2)
-            bt[(cc + e) * RS + jr] = (T)(__float_as_uint(bv[e]) >> 16);  // exact: bv is bf16
-          else
-            bt[(cc + e) * RS + jr] = bv[e];
-        }
+      for (int it = 0; it < 4; ++it) {
+        const int idx = tid + kThreads * it;
+        const int ti = idx / nq, q = idx - ti * nq;
+        if (ti < 64) *reinterpret_cast<float4 *>(&sm.vs[ti * kVStride + 4 * q]) = vq[it];
       }
       __syncthreads();
-      const float *vr[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) vr[tt] = tok[tt] >= 0 ? v + (int64_t)tok[tt] * w.r_max + jc : nullptr;
       for (int kb = 0; kb * 16 < nj; ++kb) {
         if constexpr (sizeof(T) == 2) {
           // A operand (B^T slab, transposed): sub-tile t, row rho = m -> column slab_col(t, m),
@@ -637,8 +768,10 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             if (tt < ntt) {
-              float f[8];
-              load_v8(vr[tt], jb, nj, vec_v, f);
+              const float *vl = &sm.vs[(tt * 16 + m) * kVStride + jb];
+              const float4 p0 = *reinterpret_cast<const float4 *>(vl);
+              const float4 p1 = *reinterpret_cast<const float4 *>(vl + 4);
+              const float f[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
               uint32_t h[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
@@ -665,7 +798,7 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
               if (tt < ntt) {
-                const float bop = (vr[tt] && j < nj) ? vr[tt][j] : 0.f;
+                const float bop = sm.vs[(tt * 16 + m) * kVStride + j];
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                   acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[t], bop, acc[tt][t], 0, 0, 0);
@@ -710,26 +843,27 @@ __device__ __forceinline__ bool decode_item(const lora_item &it, const DevW &w, 
   return true;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void sgmv_shrink_kernel(DevW w, const int32_t *__restrict__ perm,
-                                                               int32_t num_perm,
-                                                               const lora_item *__restrict__ items,
-                                                               int32_t num_tokens,
-                                                               const T *__restrict__ x,
-                                                               float *__restrict__ v) {
-  __shared__ ShrinkSmem sm;
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *__restrict__ perm,
+                                                         int32_t num_perm,
+                                                         const lora_item *__restrict__ items,
+                                                         int32_t num_tokens,
+                                                         const T *__restrict__ x,
+                                                         float *__restrict__ v) {
+  constexpr int NW = NT / 64;
+  __shared__ ShrinkSmem<NW> sm;
   const lora_item it = items[blockIdx.x];
   int pb, a, cnt, path, blk;
   if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
   const int r = adapter_rank(w, a);
   if (path != LORA_PATH_MFMA && blk >= (r + kRowGroup - 1) / kRowGroup) return;
   const int j0 = path == LORA_PATH_MFMA ? 0 : blk * kRowGroup;
-  for (int i = threadIdx.x; i < cnt; i += kThreads) sm.toks[i] = perm[pb + i];
+  for (int i = threadIdx.x; i < cnt; i += NT) sm.toks[i] = perm[pb + i];
   __syncthreads();
   if (path == LORA_PATH_MFMA)
-    shrink_mfma<T>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
+    shrink_mfma<T, NW>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
   else
-    shrink_gemv<T, kRowGroup>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
+    shrink_gemv<T, kRowGroup, NW>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
 }
 
 template <typename T>
@@ -771,7 +905,8 @@ __device__ __forceinline__ int gather_adapter_tokens(const int32_t *__restrict__
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = c0 + tid;
-  const bool hit = t < num_tokens && ids[t] == a;
+  const int id = ids[t < num_tokens ? t : num_tokens - 1];  // unconditional load
+  const bool hit = t < num_tokens && id == a;
   const unsigned long long mask = __ballot(hit);
   if (lane == 0) wave_cnt[wave] = __popcll(mask);
   __syncthreads();
@@ -794,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
                                                                int32_t units, int32_t groups,
                                                                const T *__restrict__ x,
                                                                float *__restrict__ v) {
-  __shared__ ShrinkSmem sm;
+  __shared__ ShrinkSmem<4> sm;
   __shared__ int wave_cnt[4];
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   if (L >= units * groups) return;
@@ -807,14 +942,14 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
     if (j0 >= r) return;
     if (threadIdx.x == 0) sm.toks[0] = t;
     __syncthreads();
-    shrink_gemv<T, RB>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
+    shrink_gemv<T, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
     if (j0 >= r) return;
     for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
       const int n = gather_adapter_tokens<kThreads>(ids, num_tokens, c0, a, sm.toks, wave_cnt);
-      if (n > 0) shrink_gemv<T, RB>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
+      if (n > 0) shrink_gemv<T, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
       __syncthreads();
     }
   }
@@ -847,6 +982,314 @@ __global__ __launch_bounds__(NT) void bgmv_expand_kernel(DevW w, const int32_t *
       if (n > 0) expand_gemv<T, NT>(w, a, r, cb, toks, n, num_tokens, v, y);
       __syncthreads();
     }
+  }
+}
+
+// Fused per-token (BGMV) delta: shrink and expand of one token in one
+// workgroup of NT = 512 threads, for decode batches where both phases are
+// small and each separate launch would pay its own start-up and round trips.
+// Work unit (token t, column block cb).  The loads of the first shrink pass
+// (x chunk, 16 A rows) and of the first expand pass (y chunk, 16 B^T rows) are
+// all issued before any arithmetic, so the common case (r <= 16, d_in and the
+// column block <= 4096) costs one round trip after the adapter id: v[t] is
+// reduced over the workgroup into LDS, then each thread owns 8 columns and
+// runs the whole rank sum for them.  Every thread's k chunks and the wave and
+// workgroup reduction orders are fixed, so results are run-to-run identical.
+constexpr int kFusedThreads = 512;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kFusedPass = kFusedThreads * 8;  // d elements per pass of the workgroup
+
+struct alignas(16) FusedSmem {
+  float red[kFusedWaves * 16];
+  float vs[LORA_MAX_RANK];
+};
+
+// Addresses of rows j0 .. j0+15 of adapter a's A (offset k), `safe` past the
+// rank or on an out-of-range page.
+template <typename T>
+__device__ __forceinline__ void a_rows16(const DevW &w, int a, int j0, int r, int k, const T *safe,
+                                         const T *(&rp)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const T *p = j0 + i < r ? a_row<T>(w, a, j0 + i) : nullptr;
+    rp[i] = p ? p + k : safe;
+  }
+}
+
+// One token t (adapter a) of the fused kernel over columns [c_begin, c_end).
+template <typename T>
+__device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb, int c_begin,
+                                           int c_end, const T *__restrict__ x,
+                                           float *__restrict__ v, T *__restrict__ y,
+                                           FusedSmem &sm) {
+  const int r = adapter_rank(w, a);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const T *xr = x + (int64_t)t * w.d_in;
+  T *yr = y + (int64_t)t * w.d_out;
+  const T *safe_a = x, *safe_b = reinterpret_cast<const T *>(w.b_pages);
+
+  // ---- first expand pass: y chunk and B^T rows 0..15, issued up front
+  const int col0 = c_begin + tid * 8;
+  const bool cin0 = col0 < c_end;
+  const int colc0 = cin0 ? col0 : c_begin;
+  Raw8<T> y0;
+  raw_load(y0, yr + colc0);
+  const T *bp0[16];
+  b_rows16<T>(w, a, 0, r, colc0, safe_b, bp0);
+  Raw8<T> b0[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) raw_load(b0[i], bp0[i]);
+
+  // ---- shrink: v[j] = sum_k A[j][k] x[k], 16 rows at a time
+  for (int jc = 0; jc < r; jc += 16) {
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < w.d_in; k0 += kFusedPass) {
+      const int k = k0 + tid * 8;
+      const bool kin = k < w.d_in;
+      const int kc = kin ? k : 0;
+      const T *ap[16];
+      a_rows16<T>(w, a, jc, r, kc, safe_a, ap);
+      Raw8<T> xraw, araw[16];
+      raw_load(xraw, xr + kc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) raw_load(araw[i], ap[i]);
+      if (kin) {
+        float xv[8];
+        raw_cvt(xraw, xv);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float av[8];
+          raw_cvt(araw[i], av);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[i] = fmaf(av[e], xv[e], acc[i]);
+        }
+      }
+    }
+    // reduce the 16 row sums over the workgroup: reduce-scatter in each wave,
+    // then the waves in order
+    const float part = wave_reduce_scatter<16>(acc);
+    if ((lane & 3) == 0) sm.red[wave * 16 + (lane >> 2)] = part;
+    __syncthreads();
+    if (tid < 16) {
+      float sum = sm.red[tid];
+#pragma unroll
+      for (int wv = 1; wv < kFusedWaves; ++wv) sum += sm.red[wv * 16 + tid];
+      sm.vs[jc + tid] = sum;
+      if (v && cb == 0 && jc + tid < r) v[(int64_t)t * w.r_max + jc + tid] = sum;
+    }
+    __syncthreads();
+  }
+
+  // ---- expand: y[col] += sum_j B^T[j][col] v[j], 8 columns per thread
+  for (int c0 = c_begin; c0 < c_end; c0 += kFusedPass) {
+    const int col = c0 + tid * 8;
+    const bool cin = col < c_end;
+    const int colc = cin ? col : c_begin;
+    Raw8<T> yraw;
+    if (c0 == c_begin) yraw = y0;
+    else raw_load(yraw, yr + colc);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      Raw8<T> braw[16];
+      if (c0 == c_begin && j0 == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) braw[i] = b0[i];
+      } else {
+        const T *bp[16];
+        b_rows16<T>(w, a, j0, r, colc, safe_b, bp);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) raw_load(braw[i], bp[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (j0 + i < r) {
+          const float vj = sm.vs[j0 + i];
+          float bv[8];
+          raw_cvt(braw[i], bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(vj, bv[e], acc[e]);
+        }
+      }
+    }
+    if (cin) {
+      float yv[8];
+      raw_cvt(yraw, yv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] += acc[e];
+      store8(yr + col, yv);
+    }
+  }
+}
+
+// Work unit u = (token u / nblk, column block u % nblk).
+template <typename T>
+__global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const int32_t *__restrict__ ids,
+                                                                   int32_t num_tokens, int32_t nblk,
+                                                                   int32_t block_cols,
+                                                                   const T *__restrict__ x,
+                                                                   float *__restrict__ v,
+                                                                   T *__restrict__ y) {
+  __shared__ FusedSmem sm;
+  const int u = blockIdx.x;
+  const int t = u / nblk, cb = u - t * nblk;
+  if (t >= num_tokens) return;
+  const int a = ids[t];
+  if (a < 0 || a >= w.num_adapters) return;
+  const int c_begin = cb * block_cols, c_end = min(w.d_out, c_begin + block_cols);
+  fused_token<T>(w, t, a, cb, c_begin, c_end, x, v, y, sm);
+}
+
+// Fused per-token delta, adapter-major: work unit (adapter a, column block
+// cb); the workgroup finds a's tokens by scanning the device ids, computes
+// their v (up to 4 tokens at a time) with the adapter's A rows held in
+// registers across the tokens, reduces v into LDS, and expands its columns
+// with the B^T rows likewise shared by the tokens.  Units of one adapter share
+// an XCD (and so its L2), so each adapter's rows cross the fabric once however
+// many tokens use them.  Each token's arithmetic (per-thread k chunks, wave
+// and workgroup reduction orders, per-column rank sums) is the same as in the
+// token-major fused kernel, so the two orders give identical results.
+struct alignas(16) FusedAmSmem {
+  int toks[kFusedThreads];
+  int wave_cnt[kFusedWaves];
+  float red[kFusedWaves * 64];
+  float vs[4][LORA_MAX_RANK];
+};
+
+template <typename T, int TG>
+__device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int c_begin, int c_end,
+                                               const int *toks, int g0, int ntok,
+                                               const T *__restrict__ x, float *__restrict__ v,
+                                               T *__restrict__ y, bool write_v, FusedAmSmem &sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tk[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) tk[t] = t < ntok ? uniform(toks[g0 + t]) : toks[g0];
+  const T *safe_a = x, *safe_b = reinterpret_cast<const T *>(w.b_pages);
+  // shrink: acc[t][i] = sum over this thread's k chunks of A[jc+i][k] x_t[k]
+  for (int jc = 0; jc < r; jc += 16) {
+    float acc[TG * 16];
+#pragma unroll
+    for (int i = 0; i < TG * 16; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < w.d_in; k0 += kFusedPass) {
+      const int k = k0 + tid * 8;
+      const bool kin = k < w.d_in;
+      const int kc = kin ? k : 0;
+      const T *ap[16];
+      a_rows16<T>(w, a, jc, r, kc, safe_a, ap);
+      Raw8<T> xraw[TG], araw[16];
+#pragma unroll
+      for (int t = 0; t < TG; ++t) raw_load(xraw[t], x + (int64_t)tk[t] * w.d_in + kc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) raw_load(araw[i], ap[i]);
+      if (kin) {
+        float xv[TG][8];
+#pragma unroll
+        for (int t = 0; t < TG; ++t) raw_cvt(xraw[t], xv[t]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float av[8];
+          raw_cvt(araw[i], av);
+#pragma unroll
+          for (int t = 0; t < TG; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[t * 16 + i] = fmaf(av[e], xv[t][e], acc[t * 16 + i]);
+        }
+      }
+    }
+    constexpr int NV = TG * 16, SH = 6 - ilog2(NV);
+    const float part = wave_reduce_scatter<NV>(acc);
+    if ((lane & ((1 << SH) - 1)) == 0) sm.red[wave * 64 + (lane >> SH)] = part;
+    __syncthreads();
+    if (tid < NV) {
+      float sum = sm.red[tid];
+#pragma unroll
+      for (int wv = 1; wv < kFusedWaves; ++wv) sum += sm.red[wv * 64 + tid];
+      const int t = tid >> 4, i = tid & 15;
+      sm.vs[t][jc + i] = sum;
+      if (write_v && t < ntok && jc + i < r) v[(int64_t)tk[t] * w.r_max + jc + i] = sum;
+    }
+    __syncthreads();
+  }
+  // expand: thread owns 8 columns per pass; the B^T rows are loaded once per
+  // pass and shared by the group's tokens
+  for (int c0 = c_begin; c0 < c_end; c0 += kFusedPass) {
+    const int col = c0 + tid * 8;
+    const bool cin = col < c_end;
+    const int colc = cin ? col : c_begin;
+    Raw8<T> yraw[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) raw_load(yraw[t], y + (int64_t)tk[t] * w.d_out + colc);
+    float acc[TG][8];
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      const T *bp[16];
+      b_rows16<T>(w, a, j0, r, colc, safe_b, bp);
+      Raw8<T> braw[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) raw_load(braw[i], bp[i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (j0 + i < r) {
+          float bv[8];
+          raw_cvt(braw[i], bv);
+#pragma unroll
+          for (int t = 0; t < TG; ++t) {
+            const float vj = sm.vs[t][j0 + i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vj, bv[e], acc[t][e]);
+          }
+        }
+      }
+    }
+    if (cin) {
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        if (t < ntok) {
+          float yv[8];
+          raw_cvt(yraw[t], yv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) yv[e] += acc[t][e];
+          store8(y + (int64_t)tk[t] * w.d_out + col, yv);
+        }
+      }
+    }
+  }
+  __syncthreads();  // vs is rewritten by the next group
+}
+
+template <typename T>
+__global__ __launch_bounds__(kFusedThreads) void bgmv_fused_am_kernel(DevW w, const int32_t *__restrict__ ids,
+                                                                      int32_t num_tokens, int32_t nblk,
+                                                                      int32_t block_cols,
+                                                                      const T *__restrict__ x,
+                                                                      float *__restrict__ v,
+                                                                      T *__restrict__ y) {
+  __shared__ FusedAmSmem sm;
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  if (L >= w.num_adapters * nblk) return;
+  const int a = L / nblk, cb = L - a * nblk;
+  const int r = adapter_rank(w, a);
+  const int c_begin = cb * block_cols, c_end = min(w.d_out, c_begin + block_cols);
+  for (int c0 = 0; c0 < num_tokens; c0 += kFusedThreads) {
+    const int n = gather_adapter_tokens<kFusedThreads>(ids, num_tokens, c0, a, sm.toks, sm.wave_cnt);
+    int g0 = 0;
+    for (; g0 + 4 <= n; g0 += 4)
+      fused_am_group<T, 4>(w, a, r, c_begin, c_end, sm.toks, g0, 4, x, v, y, v && cb == 0, sm);
+    const int rest = n - g0;
+    if (rest == 1)
+      fused_am_group<T, 1>(w, a, r, c_begin, c_end, sm.toks, g0, 1, x, v, y, v && cb == 0, sm);
+    else if (rest == 2)
+      fused_am_group<T, 2>(w, a, r, c_begin, c_end, sm.toks, g0, 2, x, v, y, v && cb == 0, sm);
+    else if (rest == 3)
+      fused_am_group<T, 4>(w, a, r, c_begin, c_end, sm.toks, g0, 3, x, v, y, v && cb == 0, sm);
+    __syncthreads();
   }
 }
 
@@ -920,16 +1363,17 @@ lora_status check_sgmv_args(const int32_t *perm, int32_t num_perm, const lora_it
   return LORA_OK;
 }
 
-// Automatic order.  Shrink: adapter-major once adapters are no more numerous
-// than tokens (each adapter's A rows are then read by one group of workgroups
-// instead of once per token).  Expand: token-major unless an adapter carries
-// many tokens on average -- a token-major workgroup needs no scan of the ids
-// and its B^T rows, shared with the adapter's other tokens, come from cache.
+// Automatic order.  Shrink: adapter-major when adapters carry one to four
+// tokens on average (each adapter's A rows are then read by one group of
+// workgroups instead of once per token, and no workgroup serialises many
+// tokens).  Expand: token-major (no scan of the ids; an adapter's B^T rows,
+// shared by its tokens, come from cache).
 int bgmv_order(int phase, int order, int num_tokens, int num_adapters) {
   if (order == LORA_BGMV_TOKEN_MAJOR || order == LORA_BGMV_ADAPTER_MAJOR) return order;
   if (phase == LORA_PHASE_SHRINK)
-    return num_adapters <= num_tokens ? LORA_BGMV_ADAPTER_MAJOR : LORA_BGMV_TOKEN_MAJOR;
-  return num_tokens >= 16 * num_adapters ? LORA_BGMV_ADAPTER_MAJOR : LORA_BGMV_TOKEN_MAJOR;
+    return (num_adapters <= num_tokens && num_tokens <= 4 * num_adapters) ? LORA_BGMV_ADAPTER_MAJOR
+                                                                          : LORA_BGMV_TOKEN_MAJOR;
+  return LORA_BGMV_TOKEN_MAJOR;
 }
 
 }  // namespace
@@ -946,10 +1390,12 @@ extern "C" lora_status lora_sgmv_shrink(const lora_weights *w, const int32_t *to
     return st;
   if (num_items == 0 || num_tokens == 0) return ok();
   if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL(sgmv_shrink_kernel<uint16_t>, dim3(num_items), dim3(kThreads), 0, stream, d,
+    hipLaunchKernelGGL((sgmv_shrink_kernel<uint16_t, kSgmvShrinkThreads>), dim3(num_items),
+                       dim3(kSgmvShrinkThreads), 0, stream, d,
                        token_perm, num_perm, items, num_tokens, (const uint16_t *)x, v);
   else
-    hipLaunchKernelGGL(sgmv_shrink_kernel<float>, dim3(num_items), dim3(kThreads), 0, stream, d,
+    hipLaunchKernelGGL((sgmv_shrink_kernel<float, kSgmvShrinkThreads>), dim3(num_items),
+                       dim3(kSgmvShrinkThreads), 0, stream, d,
                        token_perm, num_perm, items, num_tokens, (const float *)x, v);
   return check_launch("sgmv shrink launch");
 }
@@ -1028,4 +1474,55 @@ extern "C" lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *to
                        dim3(kBgmvExpandThreads), 0, stream, d, token_adapter, num_tokens, am, units,
                        groups, v, (float *)y);
   return check_launch("bgmv expand launch");
+}
+
+extern "C" lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
+                                       int32_t num_tokens, int32_t order, const void *x, float *v,
+                                       void *y, hipStream_t stream) {
+  DevW d;
+  lora_status st = to_dev(w, &d);
+  if (st != LORA_OK) return st;
+  if (num_tokens < 0) return fail(LORA_EINVAL, "negative num_tokens");
+  if (num_tokens == 0 || w->num_adapters == 0) return ok();
+  if (!token_adapter || !x || !y) return fail(LORA_EINVAL, "null pointer");
+  if (!aligned16(x) || !aligned16(y) || (v && !aligned16(v)))
+    return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
+  if (order < LORA_BGMV_AUTO || order > LORA_BGMV_ADAPTER_MAJOR)
+    return fail(LORA_EINVAL, "unknown order %d", order);
+  // automatic order: token-major (with the sorted placement above it shares
+  // an adapter's rows through L2 without serialising its tokens)
+  const bool am = order == LORA_BGMV_ADAPTER_MAJOR;
+  const int units = am ? w->num_adapters : num_tokens;
+  // enough column blocks that the launch has at least ~256 workgroups, one
+  // per compute unit: token-major blocks are whole 4096-column passes of the
+  // 512 threads; adapter-major blocks are 2048 columns (an adapter-major unit
+  // already repeats its shrink per block, so finer blocks add parallelism)
+  const int pass = am ? kFusedPass / 2 : kFusedPass;
+  const int passes = (w->d_out + pass - 1) / pass;
+  int nblk = (256 + units - 1) / units;
+  nblk = nblk < 1 ? 1 : (nblk > passes ? passes : nblk);
+  const int block_cols = ((passes + nblk - 1) / nblk) * pass;
+  nblk = (w->d_out + block_cols - 1) / block_cols;
+  if ((int64_t)units * nblk > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
+  if (am) {
+    const dim3 grid(pad8(units * nblk));
+    if (w->dtype == LORA_BF16)
+      hipLaunchKernelGGL(bgmv_fused_am_kernel<uint16_t>, grid, dim3(kFusedThreads), 0, stream, d,
+                         token_adapter, num_tokens, nblk, block_cols, (const uint16_t *)x, v,
+                         (uint16_t *)y);
+    else
+      hipLaunchKernelGGL(bgmv_fused_am_kernel<float>, grid, dim3(kFusedThreads), 0, stream, d,
+                         token_adapter, num_tokens, nblk, block_cols, (const float *)x, v,
+                         (float *)y);
+    return check_launch("bgmv fused launch");
+  }
+  const dim3 grid(num_tokens * nblk);
+  if (w->dtype == LORA_BF16)
+    hipLaunchKernelGGL(bgmv_fused_kernel<uint16_t>, grid, dim3(kFusedThreads), 0, stream, d,
+                       token_adapter, num_tokens, nblk, block_cols, (const uint16_t *)x, v,
+                       (uint16_t *)y);
+  else
+    hipLaunchKernelGGL(bgmv_fused_kernel<float>, grid, dim3(kFusedThreads), 0, stream, d,
+                       token_adapter, num_tokens, nblk, block_cols, (const float *)x, v, (float *)y);
+  return check_launch("bgmv fused launch");
 }

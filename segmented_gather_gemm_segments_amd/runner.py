@@ -165,6 +165,13 @@ class DeviceProblem:
         B.lora_bgmv_expand(self.weights, self.ids, v, y, order)
         return y, v
 
+    def run_bgmv_fused(self, order: int = B.LORA_BGMV_AUTO, y=None, v=None):
+        """Fused per-token delta (one launch); returns (y, v)."""
+        y = self.y0.clone() if y is None else y
+        v = self.new_v() if v is None else v
+        B.lora_bgmv_fused(self.weights, self.ids, self.x, y, v, order)
+        return y, v
+
     def run_base(self, y=None):
         """Base projection y = x W^T (bf16, through lora_base_gemm); returns y."""
         torch = _torch()

@@ -121,6 +121,26 @@ def test_bgmv_decode_full_size(order):
     check_y(dp, y, oracle_y(p), f"bgmv/{order}")
 
 
+def test_bgmv_fused_decode_full_size():
+    """The one-launch per-token delta on the decode batch, and its agreement
+    with the two-launch path (different summation orders: within rounding)."""
+    R = runner()
+    p = wl.bgmv_decode()
+    say("bgmv fused decode full size")
+    dp = R.DeviceProblem(p)
+    y, v = dp.run_bgmv_fused(B.LORA_BGMV_ADAPTER_MAJOR)
+    y2, v2 = dp.run_bgmv()
+    y3, _ = dp.run_bgmv_fused(B.LORA_BGMV_ADAPTER_MAJOR)
+    y4, v4 = dp.run_bgmv_fused(B.LORA_BGMV_TOKEN_MAJOR)
+    torch.cuda.synchronize()
+    check_v(dp, v, "fused")
+    check_y(dp, y, oracle_y(p), "fused")
+    assert torch.equal(y.view(torch.int16), y3.view(torch.int16))      # run-to-run identical
+    assert torch.equal(y.view(torch.int16), y4.view(torch.int16))      # both orders, same bits
+    assert torch.equal(v, v4)
+    assert normwise(host_y(dp, y), host_y(dp, y2)) <= 2e-2
+
+
 def test_bgmv_orders_and_sgmv_gather_bit_identical():
     """Per-token results do not depend on grouping: token-major, adapter-major
     and the segmented gather path give the same bits."""
@@ -210,6 +230,9 @@ def test_zero_adapter_leaves_y_bit_unchanged():
         assert torch.equal(y.view(torch.int16), dp.y0.view(torch.int16))
     y, _ = dp.run_bgmv()
     assert torch.equal(y.view(torch.int16), dp.y0.view(torch.int16))
+    y, _ = dp.run_bgmv_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), dp.y0.view(torch.int16))
 
 
 def test_token_permutation_invariance():
@@ -238,9 +261,11 @@ def test_repeat_runs_bit_identical():
     dp = R.DeviceProblem(p)
     outs = [dp.run_sgmv()[0].view(torch.int16).clone() for _ in range(3)]
     outs += [dp.run_bgmv()[0].view(torch.int16).clone() for _ in range(2)]
+    outs += [dp.run_bgmv_fused()[0].view(torch.int16).clone() for _ in range(2)]
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
     assert torch.equal(outs[3], outs[4])
+    assert torch.equal(outs[5], outs[6])
 
 
 @pytest.mark.parametrize("case", ["one_token", "all_single", "one_segment", "ragged_d", "none_ids",
@@ -278,6 +303,11 @@ def test_edge_cases(case):
             y, v = dp.run_bgmv(order)
             torch.cuda.synchronize()
             check_y(dp, y, want, f"{case}/{layout}/bgmv{order}")
+        for order in (B.LORA_BGMV_TOKEN_MAJOR, B.LORA_BGMV_ADAPTER_MAJOR):
+            y, v = dp.run_bgmv_fused(order)
+            torch.cuda.synchronize()
+            check_v(dp, v, f"{case}/{layout}/fused{order}")
+            check_y(dp, y, want, f"{case}/{layout}/fused{order}")
 
 
 def test_empty_batch_noop():
@@ -287,6 +317,8 @@ def test_empty_batch_noop():
     dp = R.DeviceProblem(p)
     y, _ = dp.run_sgmv()
     y2, _ = dp.run_bgmv()
+    y3, _ = dp.run_bgmv_fused()
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), dp.y0.view(torch.int16))
     assert torch.equal(y2.view(torch.int16), dp.y0.view(torch.int16))
+    assert torch.equal(y3.view(torch.int16), dp.y0.view(torch.int16))
