@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU time (0 disables the CPU baseline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the LLC")
+    ap.add_argument("--serial", action="store_true",
+                    help="also time the adapter-serial comparator (one shrink + expand launch "
+                         "per adapter sub-batch, same kernels)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch device copies of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -149,6 +152,30 @@ def graph_span(torch, stream, fns, reps: int = 3) -> float:
         t = e0.elapsed_time(e1) * 1e-3 / len(fns)
         best = t if best is None else min(best, t)
     return best
+
+
+def serial_comparator(torch, stream, steps_calls, tokens: int, one_launch_s: float, K: int):
+    """Times the adapter-serial comparator: steps_calls[i] is the list of
+    launches of step i (replayed as one graph of K steps, like the main path).
+    Returns its record, with the one-launch path's speed-up over it."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(K):
+            for f in steps_calls[i % len(steps_calls)]:
+                f()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launches = len(steps_calls[0])
+    return {"kind": "adapter-serial (one shrink + expand launch per adapter sub-batch)",
+            "launches_per_step": launches, "ms_per_step": round(wall / K * 1e3, 5),
+            "value": round(tokens * K / wall, 1), "unit": "delta tokens/s",
+            "one_launch_speedup": round((wall / K) / one_launch_s, 3), "steps": K}
 
 
 def bench_layer(args, torch):
@@ -250,6 +277,12 @@ def bench_layer(args, torch):
                   "projections": per},
         "kernel_sources_sha256_16": kernel_hash(),
     }
+    if args.serial:
+        Ks = min(K, 5)
+        calls = []
+        for q in projs:
+            calls += [f for pair in q["dp"].serial_calls(q["y"], q["dp"].new_v(), stream) for f in pair]
+        out["comparator"] = serial_comparator(torch, stream, [calls], tokens, wall / K, Ks)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(projs[0]["p"], args.cpu_seconds)
         out["cpu_baseline"]["sample"] += " (q projection only)"
@@ -395,6 +428,13 @@ def main():
         "host_ms_per_step_eager": round(host_step_s * 1e3, 5),
         "kernel_sources_sha256_16": kernel_hash(),
     }
+    if args.serial:
+        Ks = min(K, 50)
+        steps_calls = []
+        for dp in reps[: min(n_rep, Ks)]:
+            y, v = dp.y0.clone(), dp.new_v()
+            steps_calls.append([f for pair in dp.serial_calls(y, v, stream) for f in pair])
+        out["comparator"] = serial_comparator(torch, stream, steps_calls, tokens, wall / K, Ks)
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -180,3 +180,26 @@ class DeviceProblem:
             y = torch.empty((self.p.num_tokens, self.p.d_out), dtype=self.tdtype, device=self.device)
         B.lora_base_gemm(self.x, self.w, y)
         return y
+
+    def serial_calls(self, y, v, stream=None, policy: int = B.LORA_PATH_AUTO):
+        """Adapter-serial comparator: one (shrink, expand) pair of prepared
+        launches per segment -- each adapter's tokens as a separate sub-batch,
+        through the same kernels -- instead of one launch per phase for all of
+        them.  Returns the list of pairs (plans kept alive on the object)."""
+        torch = _torch()
+        perm, starts, adapters, perm_d = self.segments()
+        ranks = self.p.ranks.astype(np.int32)
+        pairs, keep = [], []
+        for sgi in range(adapters.size):
+            st = starts[sgi:sgi + 2]
+            ad = adapters[sgi:sgi + 1]
+            sp = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, st, ad, self.p.num_adapters, self.r_max,
+                                  policy, host_rank=ranks)
+            ep = B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, st, ad, self.p.num_adapters, self.p.d_out,
+                                  policy)
+            spd = torch.from_numpy(np.ascontiguousarray(sp)).to(self.device)
+            epd = torch.from_numpy(np.ascontiguousarray(ep)).to(self.device)
+            keep += [spd, epd]
+            pairs.append(B.prepare_sgmv(self.weights, perm_d, spd, epd, self.x, v, y, stream=stream))
+        self._serial_keep = keep
+        return pairs

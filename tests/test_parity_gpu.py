@@ -322,3 +322,21 @@ def test_empty_batch_noop():
     assert torch.equal(y.view(torch.int16), dp.y0.view(torch.int16))
     assert torch.equal(y2.view(torch.int16), dp.y0.view(torch.int16))
     assert torch.equal(y3.view(torch.int16), dp.y0.view(torch.int16))
+
+
+def test_adapter_serial_comparator_matches_one_launch():
+    """The adapter-serial comparator (one shrink + expand launch per adapter
+    sub-batch) runs the same work items as the one-launch plan, so it gives
+    the same bits."""
+    R = runner()
+    p = wl.hetero_paged(num_tokens=500, num_segments=12, d=768, seed=21)
+    say("adapter-serial comparator")
+    dp = R.DeviceProblem(p)
+    y1, v1 = dp.run_sgmv()
+    y2, v2 = dp.y0.clone(), dp.new_v()
+    for shrink, expand in dp.serial_calls(y2, v2):
+        shrink()
+        expand()
+    torch.cuda.synchronize()
+    assert torch.equal(v1, v2)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
