@@ -18,12 +18,14 @@ source pages it follows, is stated beside the C function:
 * ``apply_segmented``   -- the same, walked segment by segment.
 * ``apply_sampled``     -- ``apply`` restricted to sampled (token, column) pairs.
 * ``base_sampled``      -- W x at sampled (token, column) pairs.
+* ``dequant_rows``      -- code * per-row scale for FP8 E4M3 / INT4 adapter rows.
 
 Pins (tests/test_oracle_pins.py): the merge identity Wx + B(Ax) = (W + BA)x
 with BA materialised by numpy, zero adapters leave y bit-unchanged, token-order
 invariance, the single-adapter batch against a numpy matmul, rank-1 unit
 adapters, rank splitting (linearity), exact bf16 widening of fixed bit
-patterns, and the worked segment examples.
+patterns, exact FP8 E4M3 and INT4 decoding of fixed patterns, and the worked
+segment examples.
 """
 from __future__ import annotations
 
@@ -38,7 +40,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sgmv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libsgmv_oracle.so")
 
-F32, BF16, F64 = 0, 1, 2
+F32, BF16, F64, FP8_E4M3, INT4 = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -63,6 +65,7 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I32, I64, I = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
     lib.oracle_widen.argtypes = [P, I, I64, P]
+    lib.oracle_dequant_rows.argtypes = [P, I, P, I64, I64, P]
     lib.oracle_segments.argtypes = [P, I32, I32, P, P, P, P]
     lib.oracle_segments.restype = I
     lib.oracle_shrink.argtypes = [I32, I32, I32, P, P, P, P, I, P, I, P]
@@ -72,7 +75,7 @@ def _load():
                                            I, P]
     lib.oracle_base_sampled.argtypes = [I32, P, I, P, I, I32, P, P, P]
     lib.oracle_apply_sampled.argtypes = [I32, I32, P, P, P, P, I, P, P, I, I32, P, P, P, P]
-    for f in ("oracle_widen", "oracle_shrink", "oracle_expand", "oracle_apply",
+    for f in ("oracle_widen", "oracle_dequant_rows", "oracle_shrink", "oracle_expand", "oracle_apply",
               "oracle_apply_segmented", "oracle_base_sampled", "oracle_apply_sampled"):
         getattr(lib, f).restype = None
     _lib = lib
@@ -118,11 +121,43 @@ class Adapters:
         return Adapters(rank, off, _c(np.concatenate(a_list, 0)), _c(np.concatenate(bt_list, 0)))
 
     @staticmethod
+    def from_quantized(kind: str, a_codes, a_scales, bt_codes, bt_scales) -> "Adapters":
+        """Per-adapter quantised rows (codes + per-row scales), dequantised
+        exactly into fp64 rows."""
+        a = [dequant_rows(c, kind, s) for c, s in zip(a_codes, a_scales)]
+        bt = [dequant_rows(c, kind, s) for c, s in zip(bt_codes, bt_scales)]
+        return Adapters.from_stacks(a, bt)
+
+    @staticmethod
     def uniform(a: np.ndarray, bt: np.ndarray) -> "Adapters":
         """From dense stacks a [N, r, d_in], bt [N, r, d_out]."""
         n, r = a.shape[0], a.shape[1]
         return Adapters(np.full(n, r, dtype=np.int32), np.arange(n, dtype=np.int64) * r,
                         _c(a.reshape(n * r, a.shape[2])), _c(bt.reshape(n * r, bt.shape[2])))
+
+
+def dequant_rows(codes: np.ndarray, kind: str, scales: np.ndarray) -> np.ndarray:
+    """Dequantised adapter rows [rows, width] in fp64: code * per-row scale.
+    kind "fp8" (OCP E4M3 bytes, [rows, width] uint8) or "int4" (packed nibbles,
+    [rows, width // 2] uint8, even element in the low nibble)."""
+    codes = _c(np.asarray(codes, dtype=np.uint8))
+    scales = _c(np.asarray(scales, dtype=np.float32))
+    rows = codes.shape[0]
+    width = codes.shape[1] * (2 if kind == "int4" else 1)
+    assert scales.shape == (rows,)
+    out = np.empty((rows, width), dtype=np.float64)
+    _load().oracle_dequant_rows(_p(codes), FP8_E4M3 if kind == "fp8" else INT4, _p(scales), rows,
+                                width, _p(out))
+    return out
+
+
+def widen_codes(codes: np.ndarray, kind: str) -> np.ndarray:
+    """The values of FP8 E4M3 bytes or packed INT4 nibbles, as fp64 (flat)."""
+    codes = _c(np.asarray(codes, dtype=np.uint8))
+    n = codes.size * (2 if kind == "int4" else 1)
+    out = np.empty(n, dtype=np.float64)
+    _load().oracle_widen(_p(codes), FP8_E4M3 if kind == "fp8" else INT4, n, _p(out))
+    return out
 
 
 def widen(a: np.ndarray) -> np.ndarray:

@@ -27,7 +27,8 @@
  *   - Every bf16 or fp32 value is widened exactly to double before use and
  *     every sum runs in double, in plain sequential index order.
  *
- * Element types: 0 = fp32, 1 = bf16 (raw 16-bit patterns), 2 = fp64.
+ * Element types: 0 = fp32, 1 = bf16 (raw 16-bit patterns), 2 = fp64,
+ * 3 = FP8 E4M3 (raw bytes), 4 = INT4 (packed nibbles).
  * Build: gcc -O2 -std=c11 -shared -fPIC (no -ffast-math, no BLAS, no SIMD
  * intrinsics).
  */
@@ -38,6 +39,8 @@
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
 #define ORACLE_F64 2
+#define ORACLE_FP8_E4M3 3
+#define ORACLE_INT4 4
 
 /* bf16 is the upper half of an IEEE binary32: put the 16 bits on top of 16
  * zero bits and reinterpret.  Exact for every pattern, NaN and Inf included. */
@@ -48,13 +51,50 @@ static double widen_bf16(uint16_t bits) {
   return (double)f;
 }
 
+/* FP8 E4M3 in the OCP 8-bit floating-point format: 1 sign bit, 4 exponent bits
+ * (bias 7), 3 fraction bits; exponent field 0 encodes subnormals f/8 * 2^-6;
+ * no infinities, and S.1111.111 is NaN (largest finite magnitude 448).  Used
+ * for low-precision adapter rows ("Multi-LoRA Inference Serving",
+ * clusterbid.com, paragraph on the GPU memory budget: FP8 adapter storage
+ * halves the memory). */
+static double widen_fp8_e4m3(uint8_t b) {
+  const int e = (b >> 3) & 15, f = b & 7;
+  const double sign = (b & 0x80) ? -1.0 : 1.0;
+  if (e == 15 && f == 7) return 0.0 / 0.0;
+  if (e == 0) return sign * ((double)f / 8.0) * (1.0 / 64.0);
+  double p = 1.0;
+  for (int i = 0; i < e - 7; ++i) p *= 2.0;
+  for (int i = 0; i < 7 - e; ++i) p /= 2.0;
+  return sign * (1.0 + (double)f / 8.0) * p;
+}
+
+/* INT4: two's-complement 4-bit integers -8..7, two per byte, element 2i in the
+ * low nibble of byte i ("Multi-LoRA Inference Serving", paragraph on adapter
+ * weight quantization: INT4 adapters dequantised in the layer). */
+static double widen_int4(const uint8_t *base, int64_t i) {
+  const int nib = (base[i >> 1] >> ((i & 1) * 4)) & 15;
+  return (double)(nib >= 8 ? nib - 16 : nib);
+}
+
 /* Element i of an array of the given element type, widened to double. */
 static double elem(const void *base, int dtype, int64_t i) {
   switch (dtype) {
     case ORACLE_F32: return (double)((const float *)base)[i];
     case ORACLE_BF16: return widen_bf16(((const uint16_t *)base)[i]);
+    case ORACLE_FP8_E4M3: return widen_fp8_e4m3(((const uint8_t *)base)[i]);
+    case ORACLE_INT4: return widen_int4((const uint8_t *)base, i);
     default: return ((const double *)base)[i];
   }
+}
+
+/* Dequantised rows: out[r][c] = code[r][c] * scale[r], exactly in double (a
+ * code has at most 4 significant bits and a scale 24, so the product is
+ * exact).  rows x width codes of type q_dtype (FP8_E4M3 or INT4). */
+void oracle_dequant_rows(const void *q, int q_dtype, const float *scale, int64_t rows,
+                         int64_t width, double *out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < width; ++c)
+      out[r * width + c] = elem(q, q_dtype, r * width + c) * (double)scale[r];
 }
 
 /* Exact widening of n elements into dst (exposed so tests can pin it). */

@@ -48,6 +48,40 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+# --------------------------------------------------------------------------- low-precision rows
+def _fp8_e4m3_magnitudes() -> np.ndarray:
+    """Magnitudes of the OCP FP8 E4M3 codes 0x00..0x7E, ascending (code = index):
+    exponent field e (bias 7), fraction f; e = 0 is subnormal f/8 * 2^-6."""
+    codes = np.arange(127)
+    e, f = codes >> 3, codes & 7
+    return np.where(e == 0, f / 8.0 * 2.0**-6, (1.0 + f / 8.0) * 2.0**(e - 7.0))
+
+
+def quantize_rows(rows: np.ndarray, kind: str):
+    """Symmetric per-row quantization of fp32 rows [r, d]: scale = max|row| /
+    qmax (448 for FP8 E4M3, 7 for INT4; 1 for an all-zero row), codes =
+    round-to-nearest-even(row / scale).  Returns (codes uint8, scales float32):
+    FP8 -> [r, d] bytes; INT4 -> [r, d/2] bytes, element 2i in the low nibble."""
+    rows = np.asarray(rows, dtype=np.float32)
+    qmax = 448.0 if kind == "fp8" else 7.0
+    amax = np.max(np.abs(rows), axis=1)
+    scales = np.where(amax > 0, amax / np.float32(qmax), 1.0).astype(np.float32)
+    q = rows.astype(np.float64) / scales.astype(np.float64)[:, None]
+    if kind == "fp8":
+        mags = _fp8_e4m3_magnitudes()
+        m = np.minimum(np.abs(q), 448.0)
+        hi = np.clip(np.searchsorted(mags, m), 1, 126)
+        lo = hi - 1
+        dl, dh = m - mags[lo], mags[hi] - m
+        pick = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+        pick = np.where(m >= mags[126], 126, pick)
+        codes = (pick | np.where(q < 0, 0x80, 0)).astype(np.uint8)
+        return codes, scales
+    qi = np.clip(np.rint(q), -8, 7).astype(np.int64) & 15
+    packed = (qi[:, 0::2] | (qi[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales
+
+
 def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
     f = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
@@ -78,6 +112,9 @@ class LoraProblem:
     seg_lengths: Optional[np.ndarray] = None   # request-segment lengths in batch order
     seg_ids: Optional[np.ndarray] = None
     extra: dict = field(default_factory=dict)
+    wq: str = ""                  # "" (rows in `dtype`), "fp8" (E4M3 bytes) or "int4" (packed)
+    a_scales: Optional[List[np.ndarray]] = None   # per-row fp32 scales of quantized rows
+    bt_scales: Optional[List[np.ndarray]] = None
 
     @property
     def num_tokens(self) -> int:
@@ -121,20 +158,26 @@ def zipf_lengths(rng: np.random.Generator, total: int, nseg: int, s: float = 1.1
     return lengths
 
 
-def _adapters(rng_a, rng_b, ranks, d_in, d_out, dtype):
+def _adapters(rng_a, rng_b, ranks, d_in, d_out, dtype, wq: str = ""):
     """Per-adapter A [r, d_in] ~ N(0, 1/d_in) and B^T [r, d_out] with B ~ N(0, 1/r).
-    Every resident adapter gets rows, used in the batch or not."""
-    a_rows, bt_rows = [], []
+    Every resident adapter gets rows, used in the batch or not.  With wq set,
+    the fp32 draws are quantized per row instead (codes, scales)."""
+    a_rows, bt_rows, a_sc, bt_sc = [], [], [], []
     for r in ranks:
         r = int(r)
-        a_rows.append(_normal(rng_a, (r, d_in), 1.0 / np.sqrt(d_in), dtype))
-        bt_rows.append(_normal(rng_b, (r, d_out), 1.0 / np.sqrt(r), dtype))
-    return a_rows, bt_rows
+        if wq:
+            ca, sa = quantize_rows(_normal(rng_a, (r, d_in), 1.0 / np.sqrt(d_in), "f32"), wq)
+            cb, sb = quantize_rows(_normal(rng_b, (r, d_out), 1.0 / np.sqrt(r), "f32"), wq)
+            a_rows.append(ca); bt_rows.append(cb); a_sc.append(sa); bt_sc.append(sb)
+        else:
+            a_rows.append(_normal(rng_a, (r, d_in), 1.0 / np.sqrt(d_in), dtype))
+            bt_rows.append(_normal(rng_b, (r, d_out), 1.0 / np.sqrt(r), dtype))
+    return a_rows, bt_rows, a_sc, bt_sc
 
 
 def make_problem(name: str, seg_lengths, seg_ids, ranks, d_in: int, d_out: int, dtype: str,
                  seed: int, mode: str = "sgmv", paged: bool = False, page_rows: int = 16,
-                 ids: Optional[np.ndarray] = None) -> LoraProblem:
+                 ids: Optional[np.ndarray] = None, wq: str = "") -> LoraProblem:
     """Generic builder: requests are contiguous runs of tokens (seg_lengths[i]
     tokens with adapter seg_ids[i], in batch order), unless ``ids`` is given."""
     r_ids, r_x, r_y, r_a, r_b = _seeds(seed, 5)
@@ -145,11 +188,12 @@ def make_problem(name: str, seg_lengths, seg_ids, ranks, d_in: int, d_out: int, 
     t = ids.size
     x = _normal(r_x, (t, d_in), 1.0, dtype)
     y = _normal(r_y, (t, d_out), 1.0, dtype)
-    a_rows, bt_rows = _adapters(r_a, r_b, ranks, d_in, d_out, dtype)
+    a_rows, bt_rows, a_sc, bt_sc = _adapters(r_a, r_b, ranks, d_in, d_out, dtype, wq)
     return LoraProblem(name, dtype, ids, x, y, a_rows, bt_rows, ranks, mode=mode, paged=paged,
                        page_rows=page_rows, pool_seed=seed,
                        seg_lengths=None if seg_lengths is None else np.asarray(seg_lengths),
-                       seg_ids=None if seg_ids is None else np.asarray(seg_ids))
+                       seg_ids=None if seg_ids is None else np.asarray(seg_ids), wq=wq,
+                       a_scales=a_sc or None, bt_scales=bt_sc or None)
 
 
 # --------------------------------------------------------------------------- the five workloads
@@ -161,13 +205,16 @@ def tiny_sgmv(seed: int = 1) -> LoraProblem:
 
 
 def bgmv_decode(seed: int = 2, num_tokens: int = 256, num_adapters: int = 128, rank: int = 16,
-                d_in: int = 4096, d_out: int = 4096) -> LoraProblem:
+                d_in: int = 4096, d_out: int = 4096, wq: str = "") -> LoraProblem:
     """One token per request, adapter uniform over the resident rank-16 adapters;
-    4096 -> 4096; bf16; per-token (decode) mode."""
+    4096 -> 4096; bf16 activations; adapter rows bf16, or FP8 E4M3 / INT4 with
+    per-row scales (wq); per-token (decode) mode."""
     r_ids = _seeds(seed + 1000, 1)[0]
     ids = r_ids.integers(0, num_adapters, size=num_tokens).astype(np.int32)
-    p = make_problem(f"bgmv_decode_{num_tokens}tok_{num_adapters}ad_r{rank}_{d_in}x{d_out}", None,
-                     None, [rank] * num_adapters, d_in, d_out, "bf16", seed, mode="bgmv", ids=ids)
+    suffix = f"_{wq}" if wq else ""
+    p = make_problem(f"bgmv_decode_{num_tokens}tok_{num_adapters}ad_r{rank}_{d_in}x{d_out}{suffix}",
+                     None, None, [rank] * num_adapters, d_in, d_out, "bf16", seed, mode="bgmv",
+                     ids=ids, wq=wq)
     return p
 
 
@@ -186,15 +233,16 @@ def sgmv_prefill(seed: int = 3, shape: str = "q", num_tokens: int = 8192, num_se
 
 
 def hetero_paged(seed: int = 4, num_tokens: int = 4096, num_segments: int = 64, d: int = 8192,
-                 rank_choices=(8, 16, 32, 64)) -> LoraProblem:
+                 rank_choices=(8, 16, 32, 64), wq: str = "") -> LoraProblem:
     """Zipf request lengths, one distinct adapter per request, ranks uniform on
     {8, 16, 32, 64}; 8192 -> 8192; weights in a shuffled pool of 16-row pages."""
     r_len, r_rank, r_perm = _seeds(seed + 1000, 3)
     lengths = zipf_lengths(r_len, num_tokens, num_segments)
     ranks = r_rank.choice(np.asarray(rank_choices), size=num_segments).astype(np.int32)
     seg_ids = r_perm.permutation(num_segments).astype(np.int32)
-    return make_problem(f"hetero_paged_{num_tokens}tok_{num_segments}seg_{d}", lengths, seg_ids,
-                        ranks, d, d, "bf16", seed, paged=True, page_rows=16)
+    suffix = f"_{wq}" if wq else ""
+    return make_problem(f"hetero_paged_{num_tokens}tok_{num_segments}seg_{d}{suffix}", lengths,
+                        seg_ids, ranks, d, d, "bf16", seed, paged=True, page_rows=16, wq=wq)
 
 
 LAYER_70B = [  # (name, d_in, d_out): Llama-3-70B projections, rank-16 table

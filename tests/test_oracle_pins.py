@@ -282,6 +282,11 @@ MUTATIONS = {
     # B read untransposed (index of j and i swapped within the row block)
     "transposed_b": ("s += elem(bt_rows, w_dtype, (row_off[a] + j) * (int64_t)d_out + i) * v[j];",
                      "s += elem(bt_rows, w_dtype, (row_off[a] + (i % (r > 0 ? r : 1))) * (int64_t)d_out + j) * v[j];"),
+    # FP8 exponent bias off by one
+    "fp8_bias": ("for (int i = 0; i < e - 7; ++i) p *= 2.0;\n  for (int i = 0; i < 7 - e; ++i) p /= 2.0;",
+                 "for (int i = 0; i < e - 8; ++i) p *= 2.0;\n  for (int i = 0; i < 8 - e; ++i) p /= 2.0;"),
+    # INT4 nibbles in the wrong order
+    "int4_nibbles": ("(base[i >> 1] >> ((i & 1) * 4)) & 15", "(base[i >> 1] >> (((i + 1) & 1) * 4)) & 15"),
     # wrong adapter row offset (adapter a reads adapter 0's rows)
     "wrong_adapter": ("int64_t arow = (row_off[a] + j) * (int64_t)d_in;\n      for (int32_t k = 0; k < d_in; ++k)\n        s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);\n      v[j] = s;",
                       "int64_t arow = (row_off[0] + j) * (int64_t)d_in;\n      for (int32_t k = 0; k < d_in; ++k)\n        s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);\n      v[j] = s;"),
@@ -295,6 +300,8 @@ def _pin_suite_passes():
         test_mixed_ranks_against_numpy_per_token()
         test_rank1_unit_adapter_is_exact_copy()
         test_zero_adapter_leaves_y_bit_unchanged("B")
+        test_fp8_e4m3_decoding_matches_format_definition()
+        test_int4_decoding_matches_twos_complement()
     except AssertionError:
         return False
     return True
@@ -321,3 +328,85 @@ def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
     oracle._load()
     assert not _pin_suite_passes(), f"planted mistake {name} went unnoticed"
     monkeypatch.setattr(oracle, "_lib", real)
+
+
+# ------------------------------------------------------------------ low-precision adapter rows
+def test_fp8_e4m3_decoding_matches_format_definition():
+    """Bytes from tests/golden/fp8_e4m3_patterns.txt decode to the printed values
+    (OCP E4M3), sign of zero included; NaN patterns decode to NaN."""
+    for line in open(golden_path("fp8_e4m3_patterns.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        h, v = line.split()
+        got = oracle.widen_codes(np.array([int(h, 16)], np.uint8), "fp8")[0]
+        want = float(v)
+        if math.isnan(want):
+            assert math.isnan(got), h
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), h
+
+
+def test_int4_decoding_matches_twos_complement():
+    for line in open(golden_path("int4_patterns.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        h, e0, e1 = line.split()
+        got = oracle.widen_codes(np.array([int(h, 16)], np.uint8), "int4")
+        assert got.tolist() == [float(e0), float(e1)], h
+
+
+def test_fp8_codes_ordered_and_rne_quantizer():
+    """Non-negative FP8 codes 0x00..0x7E are strictly increasing in value (the
+    quantizer relies on it); the generator's round-to-nearest-even lands on a
+    neighbouring code of every input, with ties to the even code."""
+    vals = oracle.widen_codes(np.arange(127, dtype=np.uint8), "fp8")
+    assert np.all(np.diff(vals) > 0)
+    rng = np.random.default_rng(3)
+    rows = rng.standard_normal((6, 64)).astype(np.float32)
+    codes, scales = wl.quantize_rows(rows, "fp8")
+    deq = oracle.dequant_rows(codes, "fp8", scales)
+    q = rows.astype(np.float64) / scales.astype(np.float64)[:, None]
+    mags = np.minimum(np.abs(q), 448.0)   # the quantizer clamps to the largest finite code
+    for r in range(rows.shape[0]):
+        assert np.max(np.abs(deq[r])) == pytest.approx(np.max(np.abs(rows[r])), rel=1e-6)
+        for c in range(rows.shape[1]):
+            got = abs(deq[r, c]) / scales[r]
+            lo = vals[vals <= mags[r, c]].max()
+            hi = vals[vals >= mags[r, c]].min()
+            assert got in (lo, hi)
+            if abs(mags[r, c] - lo) != abs(hi - mags[r, c]):
+                assert got == (lo if abs(mags[r, c] - lo) < abs(hi - mags[r, c]) else hi)
+    # an exact tie: halfway between 1.0 (0x38, even) and 1.125 (0x39) rounds to 1.0
+    c, s = wl.quantize_rows(np.array([[448.0, 1.0625]], np.float32), "fp8")
+    assert s[0] == 1.0 and c[0, 1] == 0x38
+
+
+def test_quantized_rank1_adapter_is_exact():
+    """FP8 and INT4 rank-1 adapters with unit codes and power-of-two scales move
+    x[t, k] * s_A * s_B exactly into y[t, i] (dequantisation multiplies, it does
+    not round)."""
+    t, d_in, d_out, k, i = 4, 16, 24, 5, 17
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((t, d_in))
+    y = rng.standard_normal((t, d_out))
+    for kind, one in (("fp8", 0x38), ("int4", 1)):
+        if kind == "fp8":
+            a = np.zeros((1, d_in), np.uint8); a[0, k] = one
+            b = np.zeros((1, d_out), np.uint8); b[0, i] = one
+        else:
+            a = np.zeros((1, d_in // 2), np.uint8); a[0, k // 2] = one << (4 * (k % 2))
+            b = np.zeros((1, d_out // 2), np.uint8); b[0, i // 2] = one << (4 * (i % 2))
+        ad = oracle.Adapters.from_quantized(kind, [a], [np.array([0.25], np.float32)], [b],
+                                            [np.array([8.0], np.float32)])
+        out = oracle.apply(x, y, np.zeros(t, np.int32), ad)
+        want = y.copy()
+        want[:, i] += x[:, k] * 2.0
+        assert np.array_equal(out, want), kind
+
+
+def test_int4_quantizer_rounds_and_clamps():
+    rows = np.array([[7.0, -7.0, 3.5, 2.5, -0.5, 0.0, 6.9, -3.49]], np.float32)
+    codes, scales = wl.quantize_rows(rows, "int4")
+    assert scales[0] == 1.0
+    vals = oracle.widen_codes(codes, "int4")
+    assert vals.tolist() == [7, -7, 4, 2, -0.0, 0, 7, -3]
