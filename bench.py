@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2,
                     help="1..5 (2 = decode, the default; 5 = the 70B-shape layer)")
     ap.add_argument("--shape", default="q", help="config 3 shape: q or up")
+    ap.add_argument("--wq", choices=("", "fp8", "int4"), default="",
+                    help="adapter rows stored as FP8 E4M3 or INT4 with row scales (configs 2, 4)")
     ap.add_argument("--order", type=int, default=0, help="BGMV order (0 auto, 1 token, 2 adapter)")
     ap.add_argument("--path", choices=("fused", "two"), default="fused",
                     help="per-token (decode) step: one fused launch, or shrink + expand launches")
@@ -71,16 +73,18 @@ def parse():
     return ap.parse_args()
 
 
-def workload(cfg: int, shape: str):
+def workload(cfg: int, shape: str, wq: str = ""):
     from segmented_gather_gemm_segments_amd import workloads as wl
+    if wq and cfg not in (2, 4):
+        raise SystemExit("--wq applies to configs 2 and 4")
     if cfg == 1:
         return wl.tiny_sgmv()
     if cfg == 2:
-        return wl.bgmv_decode()
+        return wl.bgmv_decode(wq=wq)
     if cfg == 3:
         return wl.sgmv_prefill(shape=shape)
     if cfg == 4:
-        return wl.hetero_paged()
+        return wl.hetero_paged(wq=wq)
     raise SystemExit("unknown config")
 
 
@@ -107,7 +111,10 @@ def cpu_baseline(p, budget_s: float):
     """The oracle as it stands (single-threaded C, fp64) on the same batch:
     whole batches repeated until the time budget is used (at least one)."""
     import oracle
-    ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
+    if p.wq:
+        ad = oracle.Adapters.from_quantized(p.wq, p.a_rows, p.a_scales, p.bt_rows, p.bt_scales)
+    else:
+        ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
     ids = p.ids
     # bounded sample: a prefix of the batch sized to the budget
     t0 = time.perf_counter()
@@ -318,7 +325,7 @@ def main():
     B.lib()
     if args.config == 5:
         return bench_layer(args, torch)
-    p = workload(args.config, args.shape)
+    p = workload(args.config, args.shape, args.wq)
     elem = 2 if p.dtype == "bf16" else 4
     mode = "bgmv" if p.mode == "bgmv" else "sgmv"
     stream = torch.cuda.Stream()          # default priority; every launch goes here
@@ -387,10 +394,10 @@ def main():
                          for _ in range(3)])
 
     # ---- accounting
-    timed = {"shrink": (span(0), acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem)),
-             "expand": (span(1), acc.expand_bytes(p.ids, p.ranks, p.d_out, elem))}
+    timed = {"shrink": (span(0), acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem, p.wq)),
+             "expand": (span(1), acc.expand_bytes(p.ids, p.ranks, p.d_out, elem, p.wq))}
     if mode == "bgmv":
-        timed["fused"] = (span(2), acc.fused_bytes(p.ids, p.ranks, p.d_in, p.d_out, elem))
+        timed["fused"] = (span(2), acc.fused_bytes(p.ids, p.ranks, p.d_in, p.d_out, elem, p.wq))
     tokens = int(np.sum(p.ids >= 0))
     ms_per_step = wall / K * 1e3
     kern = {}
@@ -417,6 +424,7 @@ def main():
         "dtype": p.dtype, "data": "synthetic (seeded; random-init adapters)",
         "config": {"workload": p.name, "tokens": p.num_tokens, "adapters": p.num_adapters,
                    "ranks": sorted(set(int(r) for r in p.ranks)), "d_in": p.d_in, "d_out": p.d_out,
+                   "adapter_rows": p.wq or p.dtype,
                    "mode": mode, "path": ("fused" if fused else "shrink+expand"),
                    "replicas": n_rep, "timed": "HIP graph replay of the K steps",
                    "parallelism": "single GPU"},

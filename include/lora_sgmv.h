@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define LORA_ABI_VERSION 1
+#define LORA_ABI_VERSION 2
 
 typedef int32_t lora_status;
 #define LORA_OK 0
@@ -79,6 +79,14 @@ typedef int32_t lora_status;
 
 #define LORA_F32 0
 #define LORA_BF16 1
+
+/* Storage formats of the adapter rows (lora_weights.weight_format). */
+#define LORA_WFMT_PLAIN 0     /* elements of type lora_weights.dtype */
+#define LORA_WFMT_FP8_E4M3 1  /* OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7,
+                                 3 mantissa bits; 0x7f / 0xff are NaN, no infinities),
+                                 one byte per element */
+#define LORA_WFMT_INT4 2      /* two's-complement 4-bit integers in -8..7, two per
+                                 byte, element 2i in the low nibble of byte i */
 
 #define LORA_NO_ADAPTER (-1)
 #define LORA_MAX_RANK 128
@@ -178,12 +186,24 @@ lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
 
 /* ------------------------------------------------------------------------ */
 /* Adapter weights as the kernels read them (the adapter-row gather through the
- * page table).  Row j of adapter a's A lives at
- *     a_pages + ((a_page_table[a*max_pages + j/page_rows]) * page_rows
- *                + j % page_rows) * d_in            (elements)
- * and row j of its B^T likewise in b_pages with width d_out.  With a NULL
- * page table the page index is the adapter id (dense stack: page_rows >= r_max,
- * max_pages ignored).  Rows j >= rank[a] of a page are never read.  */
+ * page table).  Row j of adapter a's A is stored row
+ *     s = a_page_table[a*max_pages + j/page_rows] * page_rows + j % page_rows
+ * of a_pages, at byte offset s * row_bytes(d_in), and row j of its B^T likewise
+ * in b_pages with width d_out.  With a NULL page table the page index is the
+ * adapter id (dense stack: page_rows >= r_max, max_pages ignored).  Rows
+ * j >= rank[a] of a page are never read.
+ *
+ * Quantized rows (weight_format FP8_E4M3 or INT4, with dtype LORA_BF16): each
+ * stored row s holds codes q and has an fp32 scale sc[s] (a_scales, b_scales,
+ * indexed by the same stored-row number s); its values are q * sc[s].  FP8
+ * storage halves an adapter's bytes and INT4 storage quarters them ("Multi-LoRA
+ * Inference Serving: Serving Thousands of Fine-Tuned Models on One GPU",
+ * clusterbid.com, the paragraphs on the adapter memory budget and on adapter
+ * weight quantization); the codes are dequantized inside the kernels, so the
+ * rows cross HBM in their stored size.  The scales factor out of both phases:
+ * v[j] is the row-j sum of codes times x, times A's row scale; the expand uses
+ * v[j] times B^T's row scale.  row_bytes(d) = 2d (bf16), 4d (fp32), d (FP8),
+ * d/2 (INT4).  */
 typedef struct {
   int32_t dtype;         /* LORA_F32 or LORA_BF16: element type of x, y, A, B */
   int32_t d_in, d_out;   /* multiples of 8 */
@@ -193,14 +213,18 @@ typedef struct {
   int32_t max_pages;     /* page-table row length (pages per adapter) */
   int32_t num_pages_a;   /* pages in a_pages (bounds for page ids) */
   int32_t num_pages_b;   /* pages in b_pages */
-  int32_t reserved;      /* must be 0 */
-  const void *a_pages;   /* device [num_pages_a][page_rows][d_in]  */
-  const void *b_pages;   /* device [num_pages_b][page_rows][d_out] (rows of B^T) */
+  int32_t weight_format; /* LORA_WFMT_PLAIN, or (dtype LORA_BF16 only) LORA_WFMT_FP8_E4M3
+                            or LORA_WFMT_INT4 */
+  const void *a_pages;   /* device [num_pages_a][page_rows] rows of row_bytes(d_in) */
+  const void *b_pages;   /* device [num_pages_b][page_rows] rows of row_bytes(d_out) (B^T) */
   const int32_t *rank;   /* device [N]: rank of each adapter (1..r_max) */
   const int32_t *a_page_table; /* device [N][max_pages] or NULL (dense) */
   const int32_t *b_page_table; /* device [N][max_pages] or NULL (dense) */
   const int32_t *host_rank;    /* host [N] copy of rank, or NULL; when given it is
                                   validated (1..r_max) before launch */
+  const float *a_scales;       /* device [num_pages_a * page_rows] row scales; quantized
+                                  formats only (NULL for LORA_WFMT_PLAIN) */
+  const float *b_scales;       /* device [num_pages_b * page_rows] */
 } lora_weights;
 
 /* ------------------------------------------------------------------------ */
@@ -268,7 +292,10 @@ lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
 
 /* ------------------------------------------------------------------------ */
 /* Paged adapter pool (host bookkeeping over caller-owned device storage of
- * [num_pages][page_rows][row_width] elements).  Pages are handed out from a
+ * [num_pages][page_rows] rows of row_width elements in the given dtype and
+ * weight_format (row bytes as for lora_weights), plus, for the quantized
+ * formats, caller-owned device row scales [num_pages * page_rows] that must be
+ * NULL otherwise).  Pages are handed out from a
  * free list shuffled by `shuffle_seed` (0 = in order), so an adapter's pages
  * are scattered through the pool as they are after churn; freed pages return
  * to the back of the list.  Sources: the unified paging of adapter weights
@@ -277,8 +304,8 @@ lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
  * Serving" (clusterbid.com).  A lora_pool object is not thread-safe.        */
 typedef struct lora_pool lora_pool;
 lora_status lora_pool_create(int32_t num_pages, int32_t page_rows, int32_t row_width,
-                             int32_t dtype, void *device_storage, uint64_t shuffle_seed,
-                             lora_pool **out);
+                             int32_t dtype, int32_t weight_format, void *device_storage,
+                             float *device_scales, uint64_t shuffle_seed, lora_pool **out);
 /* Takes ceil(rows / page_rows) pages; ids written to page_ids.  LORA_ENOMEM if
  * too few pages are free (nothing taken). */
 lora_status lora_pool_alloc(lora_pool *pool, int32_t rows, int32_t *page_ids);
@@ -286,11 +313,12 @@ lora_status lora_pool_alloc(lora_pool *pool, int32_t rows, int32_t *page_ids);
  * (nothing freed). */
 lora_status lora_pool_free(lora_pool *pool, const int32_t *page_ids, int32_t num_pages);
 lora_status lora_pool_num_free(const lora_pool *pool, int32_t *num_free);
-/* Copies `rows` rows of row_width elements from src (host or device memory)
- * into the pages, page_rows rows per page, asynchronously on `stream`.  A host
- * source must stay valid until the stream has passed this point. */
+/* Copies `rows` stored rows from src (host or device memory) into the pages,
+ * page_rows rows per page, and for a quantized pool their `rows` scales from
+ * src_scales (NULL for a plain pool), asynchronously on `stream`.  Host
+ * sources must stay valid until the stream has passed this point. */
 lora_status lora_pool_write_rows(lora_pool *pool, const int32_t *page_ids, int32_t rows,
-                                 const void *src, hipStream_t stream);
+                                 const void *src, const float *src_scales, hipStream_t stream);
 void lora_pool_destroy(lora_pool *pool);
 
 /* ------------------------------------------------------------------------ */

@@ -12,7 +12,9 @@ Per launch:
   fused bytes  = T_a*d_in*s + sum_{a used} r_a*(d_in + d_out)*s + 2*T_a*d_out*s
   shrink flops = 2*d_in*sum_t r_{a(t)};  expand flops = 2*d_out*sum_t r_{a(t)}
 where T_a counts tokens that carry an adapter, s is the activation/weight
-element size and v is fp32.  Token ids, segments, plans and page tables are
+element size and v is fp32.  With quantized adapter rows the weight terms use
+the stored size w per element (1 byte for FP8 E4M3, 1/2 for INT4) plus 4 bytes
+of fp32 scale per stored row: r_a*(d*w + 4) per matrix.  Token ids, segments, plans and page tables are
 metadata (< 0.1 %) and are not counted.  Re-reads of an adapter's rows by
 several tokens are cache traffic, not algorithmic bytes.
 """
@@ -41,21 +43,33 @@ def _usage(ids: np.ndarray, ranks: np.ndarray):
     return t_a, sum_r_tok, sum_r_distinct
 
 
-def shrink_bytes(ids, ranks, d_in: int, elem_bytes: int) -> int:
+def _row_bytes(d: int, elem_bytes: int, wq: str) -> int:
+    """Bytes of one stored adapter row of d elements, its scale included."""
+    if wq == "fp8":
+        return d + 4
+    if wq == "int4":
+        return d // 2 + 4
+    return d * elem_bytes
+
+
+def shrink_bytes(ids, ranks, d_in: int, elem_bytes: int, wq: str = "") -> int:
     t_a, sum_r_tok, sum_r_distinct = _usage(ids, ranks)
-    return t_a * d_in * elem_bytes + sum_r_distinct * d_in * elem_bytes + sum_r_tok * 4
+    return (t_a * d_in * elem_bytes + sum_r_distinct * _row_bytes(d_in, elem_bytes, wq)
+            + sum_r_tok * 4)
 
 
-def expand_bytes(ids, ranks, d_out: int, elem_bytes: int) -> int:
+def expand_bytes(ids, ranks, d_out: int, elem_bytes: int, wq: str = "") -> int:
     t_a, sum_r_tok, sum_r_distinct = _usage(ids, ranks)
-    return sum_r_tok * 4 + sum_r_distinct * d_out * elem_bytes + 2 * t_a * d_out * elem_bytes
+    return (sum_r_tok * 4 + sum_r_distinct * _row_bytes(d_out, elem_bytes, wq)
+            + 2 * t_a * d_out * elem_bytes)
 
 
-def fused_bytes(ids, ranks, d_in: int, d_out: int, elem_bytes: int) -> int:
+def fused_bytes(ids, ranks, d_in: int, d_out: int, elem_bytes: int, wq: str = "") -> int:
     """One-launch delta (shrink and expand fused, v kept on chip): x, each used
     adapter's A and B rows, y read and written."""
     t_a, _, sum_r_distinct = _usage(ids, ranks)
-    return (t_a * d_in * elem_bytes + sum_r_distinct * (d_in + d_out) * elem_bytes
+    return (t_a * d_in * elem_bytes
+            + sum_r_distinct * (_row_bytes(d_in, elem_bytes, wq) + _row_bytes(d_out, elem_bytes, wq))
             + 2 * t_a * d_out * elem_bytes)
 
 

@@ -19,6 +19,7 @@ from . import build as _build
 
 LORA_OK, LORA_EINVAL, LORA_ERANGE, LORA_EUNSUPPORTED, LORA_ENOMEM, LORA_EHIP = 0, -1, -2, -3, -4, -5
 LORA_F32, LORA_BF16 = 0, 1
+LORA_WFMT_PLAIN, LORA_WFMT_FP8_E4M3, LORA_WFMT_INT4 = 0, 1, 2
 LORA_NO_ADAPTER = -1
 LORA_MAX_RANK = 128
 LORA_PHASE_SHRINK, LORA_PHASE_EXPAND = 0, 1
@@ -46,10 +47,11 @@ class lora_weights(ctypes.Structure):
                 ("num_adapters", ctypes.c_int32), ("r_max", ctypes.c_int32),
                 ("page_rows", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("num_pages_a", ctypes.c_int32), ("num_pages_b", ctypes.c_int32),
-                ("reserved", ctypes.c_int32),
+                ("weight_format", ctypes.c_int32),
                 ("a_pages", ctypes.c_void_p), ("b_pages", ctypes.c_void_p),
                 ("rank", ctypes.c_void_p), ("a_page_table", ctypes.c_void_p),
-                ("b_page_table", ctypes.c_void_p), ("host_rank", ctypes.c_void_p)]
+                ("b_page_table", ctypes.c_void_p), ("host_rank", ctypes.c_void_p),
+                ("a_scales", ctypes.c_void_p), ("b_scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -66,11 +68,11 @@ EXPORTS = {
     "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_expand": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_fused": ([_P, _P, _I32, _I32, _P, _P, _P, _P], _I32),
-    "lora_pool_create": ([_I32, _I32, _I32, _I32, _P, _U64, _P], _I32),
+    "lora_pool_create": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P], _I32),
     "lora_pool_alloc": ([_P, _I32, _P], _I32),
     "lora_pool_free": ([_P, _P, _I32], _I32),
     "lora_pool_num_free": ([_P, _P], _I32),
-    "lora_pool_write_rows": ([_P, _P, _I32, _P, _P], _I32),
+    "lora_pool_write_rows": ([_P, _P, _I32, _P, _P, _P], _I32),
     "lora_pool_destroy": ([_P], None),
     "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
 }
@@ -173,10 +175,12 @@ def _stream(stream=None):
 class Weights:
     """Device-resident adapter weights plus the lora_weights descriptor.
 
-    ``a_pages`` [num_pages_a, page_rows, d_in] and ``b_pages`` [num_pages_b,
-    page_rows, d_out] are torch tensors (bf16 or fp32); ``rank`` int32 [N] on
-    device; page tables int32 [N, max_pages] on device or None (dense stack:
-    page a = adapter a)."""
+    ``a_pages`` [num_pages_a, page_rows, ...] and ``b_pages`` [num_pages_b,
+    page_rows, ...] are torch tensors: bf16 or fp32 rows of d_in / d_out
+    elements, or, for a quantized ``weight_format``, uint8 rows of the stored
+    codes with fp32 row scales ``a_scales`` [num_pages_a * page_rows] and
+    ``b_scales``; ``rank`` int32 [N] on device; page tables int32 [N,
+    max_pages] on device or None (dense stack: page a = adapter a)."""
     dtype: int
     d_in: int
     d_out: int
@@ -189,6 +193,9 @@ class Weights:
     a_page_table: object = None
     b_page_table: object = None
     max_pages: int = 1
+    weight_format: int = LORA_WFMT_PLAIN
+    a_scales: object = None
+    b_scales: object = None
 
     @property
     def num_adapters(self) -> int:
@@ -198,9 +205,10 @@ class Weights:
         self._host_rank_c = _i32(self.host_rank)
         return lora_weights(
             self.dtype, self.d_in, self.d_out, self.num_adapters, self.r_max, self.page_rows,
-            self.max_pages, int(self.a_pages.shape[0]), int(self.b_pages.shape[0]), 0,
-            _dptr(self.a_pages), _dptr(self.b_pages), _dptr(self.rank), _dptr(self.a_page_table),
-            _dptr(self.b_page_table), self._host_rank_c.ctypes.data)
+            self.max_pages, int(self.a_pages.shape[0]), int(self.b_pages.shape[0]),
+            self.weight_format, _dptr(self.a_pages), _dptr(self.b_pages), _dptr(self.rank),
+            _dptr(self.a_page_table), _dptr(self.b_page_table), self._host_rank_c.ctypes.data,
+            _dptr(self.a_scales), _dptr(self.b_scales))
 
 
 def lora_sgmv_shrink(w: Weights, token_perm, items, x, v, num_tokens: Optional[int] = None,
@@ -247,19 +255,28 @@ def lora_base_gemm(x, w, y, stream=None):
 
 
 class Pool:
-    """lora_pool over caller-owned device storage (a torch tensor
-    [num_pages, page_rows, row_width])."""
+    """lora_pool over caller-owned device storage: a torch tensor [num_pages,
+    page_rows, row_width] of bf16 or fp32, or for a quantized weight_format a
+    uint8 tensor [num_pages, page_rows, row_bytes] with fp32 row scales
+    ``scales`` [num_pages * page_rows]."""
 
-    def __init__(self, storage, page_rows: int, shuffle_seed: int = 0):
+    def __init__(self, storage, page_rows: int, shuffle_seed: int = 0,
+                 weight_format: int = LORA_WFMT_PLAIN, scales=None):
         self.storage = storage
+        self.scales = scales
         num_pages, pr, width = storage.shape
         assert pr == page_rows
         torch = _torch()
-        dtype = LORA_BF16 if storage.dtype == torch.bfloat16 else LORA_F32
+        if weight_format == LORA_WFMT_PLAIN:
+            dtype = LORA_BF16 if storage.dtype == torch.bfloat16 else LORA_F32
+        else:
+            dtype = LORA_BF16
+            width = width * 2 if weight_format == LORA_WFMT_INT4 else width
         self.page_rows = page_rows
         h = ctypes.c_void_p()
-        _check(lib().lora_pool_create(num_pages, page_rows, width, dtype, _dptr(storage),
-                                      shuffle_seed, ctypes.byref(h)))
+        _check(lib().lora_pool_create(num_pages, page_rows, width, dtype, weight_format,
+                                      _dptr(storage), _dptr(scales), shuffle_seed,
+                                      ctypes.byref(h)))
         self._h = h
 
     def alloc(self, rows: int) -> np.ndarray:
@@ -276,11 +293,12 @@ class Pool:
         _check(lib().lora_pool_num_free(self._h, ctypes.byref(n)))
         return n.value
 
-    def write_rows(self, page_ids, src, stream=None):
-        """src: torch tensor [rows, row_width] on device (or pinned host)."""
+    def write_rows(self, page_ids, src, src_scales=None, stream=None):
+        """src: torch tensor [rows, row] on device (or pinned host); src_scales
+        fp32 [rows] for a quantized pool."""
         ids = _i32(page_ids)
         _check(lib().lora_pool_write_rows(self._h, _np_ptr(ids), int(src.shape[0]), _dptr(src),
-                                          _stream(stream)))
+                                          _dptr(src_scales), _stream(stream)))
 
     def close(self):
         if self._h:

@@ -190,8 +190,10 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
 // --------------------------------------------------------------------------
 // Paged pool.
 struct lora_pool {
-  int32_t num_pages, page_rows, row_width, dtype;
+  int32_t num_pages, page_rows, row_width, dtype, weight_format;
+  size_t row_bytes;
   char *storage;
+  float *scales;                    // [num_pages * page_rows], quantized formats only
   std::vector<int32_t> free_list;   // front = next page handed out
   size_t head = 0;                  // free_list[head..] are free
   std::vector<uint8_t> taken;
@@ -205,19 +207,34 @@ static uint64_t splitmix64(uint64_t &s) {
 }
 
 extern "C" lora_status lora_pool_create(int32_t num_pages, int32_t page_rows, int32_t row_width,
-                                        int32_t dtype, void *device_storage,
+                                        int32_t dtype, int32_t weight_format,
+                                        void *device_storage, float *device_scales,
                                         uint64_t shuffle_seed, lora_pool **out) {
   if (!out) return fail(LORA_EINVAL, "null out");
   if (num_pages <= 0 || page_rows <= 0 || row_width <= 0)
     return fail(LORA_EINVAL, "pool sizes must be positive");
   if (dtype != LORA_F32 && dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "dtype %d", dtype);
+  if (weight_format != LORA_WFMT_PLAIN && weight_format != LORA_WFMT_FP8_E4M3 &&
+      weight_format != LORA_WFMT_INT4)
+    return fail(LORA_EUNSUPPORTED, "weight_format %d", weight_format);
+  const bool quant = weight_format != LORA_WFMT_PLAIN;
+  if (quant && dtype != LORA_BF16)
+    return fail(LORA_EUNSUPPORTED, "quantized adapter rows need bf16 activations");
+  if (quant && row_width % 2) return fail(LORA_EINVAL, "INT4 / FP8 rows need an even width");
   if (!device_storage) return fail(LORA_EINVAL, "null storage");
+  if (quant != (device_scales != nullptr))
+    return fail(LORA_EINVAL, "row scales are required for quantized formats and only for them");
   lora_pool *p = new lora_pool();
   p->num_pages = num_pages;
   p->page_rows = page_rows;
   p->row_width = row_width;
   p->dtype = dtype;
+  p->weight_format = weight_format;
+  p->row_bytes = weight_format == LORA_WFMT_FP8_E4M3 ? (size_t)row_width
+                 : weight_format == LORA_WFMT_INT4   ? (size_t)row_width / 2
+                 : (size_t)row_width * (dtype == LORA_BF16 ? 2 : 4);
   p->storage = (char *)device_storage;
+  p->scales = device_scales;
   p->free_list.resize((size_t)num_pages);
   for (int32_t i = 0; i < num_pages; ++i) p->free_list[(size_t)i] = i;
   if (shuffle_seed != 0) {  // Fisher-Yates with a splitmix64 stream
@@ -276,11 +293,13 @@ extern "C" lora_status lora_pool_num_free(const lora_pool *p, int32_t *num_free)
 }
 
 extern "C" lora_status lora_pool_write_rows(lora_pool *p, const int32_t *page_ids, int32_t rows,
-                                            const void *src, hipStream_t stream) {
+                                            const void *src, const float *src_scales,
+                                            hipStream_t stream) {
   if (!p || !page_ids || !src) return fail(LORA_EINVAL, "null argument");
   if (rows <= 0) return fail(LORA_EINVAL, "rows must be positive");
-  const size_t elem = p->dtype == LORA_BF16 ? 2 : 4;
-  const size_t row_bytes = (size_t)p->row_width * elem;
+  if ((p->scales != nullptr) != (src_scales != nullptr))
+    return fail(LORA_EINVAL, "row scales are required for quantized pools and only for them");
+  const size_t row_bytes = p->row_bytes;
   const int32_t npages = (rows + p->page_rows - 1) / p->page_rows;
   for (int32_t i = 0; i < npages; ++i) {
     int32_t id = page_ids[i];
@@ -293,6 +312,12 @@ extern "C" lora_status lora_pool_write_rows(lora_pool *p, const int32_t *page_id
     const char *s = (const char *)src + (size_t)i * p->page_rows * row_bytes;
     hipError_t e = hipMemcpyAsync(dst, s, (size_t)nr * row_bytes, hipMemcpyDefault, stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (pool rows)");
+    if (p->scales) {
+      e = hipMemcpyAsync(p->scales + (size_t)page_ids[i] * p->page_rows,
+                         src_scales + (size_t)i * p->page_rows, (size_t)nr * sizeof(float),
+                         hipMemcpyDefault, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (pool row scales)");
+    }
   }
   return ok();
 }

@@ -34,25 +34,45 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 constexpr int kThreads = 256;  // 4 waves of 64
 
 // ----------------------------------------------------------------- weights
+// Adapter rows are stored in one of four element types W: bf16 (uint16_t) or
+// fp32 (float) like the activations, or -- with bf16 activations only -- OCP
+// FP8 E4M3 (Fp8) or two's-complement INT4 (Int4), each row with an fp32 scale.
+// A row's value is code * scale ("Multi-LoRA Inference Serving": FP8 adapter
+// storage halves the adapter bytes, INT4 adapters are dequantised in the
+// layer).  The scales factor out of both phases exactly: the shrink multiplies
+// v[j] by A row j's scale after its sum, the expand multiplies v[j] by B^T
+// row j's scale before use, and the codes themselves convert exactly to fp32
+// (and to bf16).
+struct Fp8 {};
+struct Int4 {};
+
+template <typename W> struct WT;  // bytes per 8-element chunk; per-row scale?
+template <> struct WT<uint16_t> { static constexpr int kChunk = 16; static constexpr bool kScaled = false; };
+template <> struct WT<float> { static constexpr int kChunk = 32; static constexpr bool kScaled = false; };
+template <> struct WT<Fp8> { static constexpr int kChunk = 8; static constexpr bool kScaled = true; };
+template <> struct WT<Int4> { static constexpr int kChunk = 4; static constexpr bool kScaled = true; };
+
 struct DevW {
   const char *a_pages;
   const char *b_pages;
   const int32_t *rank;
   const int32_t *a_pt;
   const int32_t *b_pt;
+  const float *a_sc;   // per stored row (page * page_rows + row in page); quantized rows only
+  const float *b_sc;
+  int64_t a_row_bytes, b_row_bytes;
   int32_t d_in, d_out, num_adapters, r_max, page_rows, max_pages, num_pages_a, num_pages_b;
 };
 
-// Row j of adapter a through the page table; nullptr when the page id is out
-// of range (the row then contributes nothing).
-template <typename T>
-__device__ __forceinline__ const T *page_row(const char *base, const int32_t *pt, int32_t num_pages,
-                                             const DevW &w, int a, int j, int width) {
+// Storage index (page * page_rows + row in page) of row j of adapter a through
+// the page table, or -1 when the page id is out of range (the row then
+// contributes nothing).  The page-id load is unconditional (clamped index) so
+// that several rows' lookups can be in flight together.
+__device__ __forceinline__ int64_t row_index(const DevW &w, const int32_t *pt, int32_t num_pages,
+                                             int a, int j) {
   int page, r_in;
   if (pt) {
     const int pi = j / w.page_rows;
-    // the page-id load is unconditional (clamped index) so that several rows'
-    // lookups can be in flight together
     page = pt[(int64_t)a * w.max_pages + (pi < w.max_pages ? pi : w.max_pages - 1)];
     if (pi >= w.max_pages) page = -1;
     r_in = j - pi * w.page_rows;
@@ -60,28 +80,43 @@ __device__ __forceinline__ const T *page_row(const char *base, const int32_t *pt
     page = a;
     r_in = j;
   }
-  if ((unsigned)page >= (unsigned)num_pages) return nullptr;
-  return reinterpret_cast<const T *>(base) + ((int64_t)page * w.page_rows + r_in) * width;
+  if ((unsigned)page >= (unsigned)num_pages) return -1;
+  return (int64_t)page * w.page_rows + r_in;
 }
 
-template <typename T>
-__device__ __forceinline__ const T *a_row(const DevW &w, int a, int j) {
-  return page_row<T>(w.a_pages, w.a_pt, w.num_pages_a, w, a, j, w.d_in);
+// Byte address of row j of adapter a's A (or B^T); nullptr when out of range.
+__device__ __forceinline__ const char *a_row(const DevW &w, int a, int j) {
+  const int64_t i = row_index(w, w.a_pt, w.num_pages_a, a, j);
+  return i < 0 ? nullptr : w.a_pages + i * w.a_row_bytes;
 }
-template <typename T>
-__device__ __forceinline__ const T *b_row(const DevW &w, int a, int j) {
-  return page_row<T>(w.b_pages, w.b_pt, w.num_pages_b, w, a, j, w.d_out);
+__device__ __forceinline__ const char *b_row(const DevW &w, int a, int j) {
+  const int64_t i = row_index(w, w.b_pt, w.num_pages_b, a, j);
+  return i < 0 ? nullptr : w.b_pages + i * w.b_row_bytes;
+}
+// Scale of row j (1 for unquantized rows or an out-of-range page).
+template <typename W>
+__device__ __forceinline__ float a_scale(const DevW &w, int a, int j) {
+  if constexpr (!WT<W>::kScaled) return 1.f;
+  const int64_t i = row_index(w, w.a_pt, w.num_pages_a, a, j);
+  return i < 0 ? 0.f : w.a_sc[i];
+}
+template <typename W>
+__device__ __forceinline__ float b_scale(const DevW &w, int a, int j) {
+  if constexpr (!WT<W>::kScaled) return 1.f;
+  const int64_t i = row_index(w, w.b_pt, w.num_pages_b, a, j);
+  return i < 0 ? 0.f : w.b_sc[i];
 }
 
-// Addresses of rows j0 .. j0+15 of adapter a's B^T, offset by `col` (rows at
-// or past the rank, or on an out-of-range page, get `safe`).  When the 16 rows
-// lie in one page (the usual case: 16-row pages, j0 a multiple of 16) a single
-// page lookup serves them all; a dense stack needs none.
-template <typename T>
-__device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, int col, const T *safe,
-                                         const T *(&rp)[16]) {
-  const T *base = reinterpret_cast<const T *>(w.b_pages);
+// Addresses of rows j0 .. j0+15 of adapter a's B^T, offset to element `col`
+// (rows at or past the rank, or on an out-of-range page, get `safe`), and
+// their scales (0 for those rows).  When the 16 rows lie in one page (the
+// usual case: 16-row pages, j0 a multiple of 16) a single page lookup serves
+// them all; a dense stack needs none.
+template <typename W>
+__device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, int col, const char *safe,
+                                         const char *(&rp)[16], float (&sc)[16]) {
   const int pr = w.page_rows;
+  const int64_t cofs = (int64_t)(col >> 3) * WT<W>::kChunk;
   if (!w.b_pt || (pr >= 16 && j0 % pr + 16 <= pr)) {
     int page, r0;
     if (w.b_pt) {
@@ -94,15 +129,21 @@ __device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, in
       r0 = j0;
     }
     const bool ok = (unsigned)page < (unsigned)w.num_pages_b;
-    const T *p0 = base + ((int64_t)(ok ? page : 0) * pr + r0) * w.d_out + col;
+    const int64_t i0 = (int64_t)(ok ? page : 0) * pr + r0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rp[i] = (ok && j0 + i < r) ? p0 + (int64_t)i * w.d_out : safe;
+    for (int i = 0; i < 16; ++i) {
+      const bool in = ok && j0 + i < r;
+      rp[i] = in ? w.b_pages + (i0 + i) * w.b_row_bytes + cofs : safe;
+      if constexpr (WT<W>::kScaled) sc[i] = in ? w.b_sc[i0 + i] : 0.f;
+      else sc[i] = 1.f;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const T *p = j0 + i < r ? page_row<T>(w.b_pages, w.b_pt, w.num_pages_b, w, a, j0 + i, w.d_out)
-                              : nullptr;
-      rp[i] = p ? p + col : safe;
+      const int64_t idx = j0 + i < r ? row_index(w, w.b_pt, w.num_pages_b, a, j0 + i) : -1;
+      rp[i] = idx >= 0 ? w.b_pages + idx * w.b_row_bytes + cofs : safe;
+      if constexpr (WT<W>::kScaled) sc[i] = idx >= 0 ? w.b_sc[idx] : 0.f;
+      else sc[i] = 1.f;
     }
   }
 }
@@ -260,6 +301,87 @@ __device__ __forceinline__ float raw_elem(const Raw8<float> &r, int e) {
   return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
 }
 
+// Quantized weight chunks: 8 FP8 E4M3 codes (8 bytes) or 8 INT4 codes (4 bytes).
+template <> struct Raw8<Fp8> { uint2 u; };
+template <> struct Raw8<Int4> { uint32_t u; };
+
+// Loads of one 8-element weight chunk from a byte address.
+__device__ __forceinline__ void wload(Raw8<uint16_t> &r, const char *p) {
+  r.u = *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void wload(Raw8<float> &r, const char *p) {
+  raw_load(r, reinterpret_cast<const float *>(p));
+}
+__device__ __forceinline__ void wload(Raw8<Fp8> &r, const char *p) {
+  r.u = *reinterpret_cast<const uint2 *>(p);
+}
+__device__ __forceinline__ void wload(Raw8<Int4> &r, const char *p) {
+  r.u = *reinterpret_cast<const uint32_t *>(p);
+}
+__device__ __forceinline__ void raw_zero(Raw8<Fp8> &r) { r.u = make_uint2(0, 0); }
+__device__ __forceinline__ void raw_zero(Raw8<Int4> &r) { r.u = 0; }
+
+// Codes to fp32, exactly: FP8 E4M3 through the converter (gfx950 decodes the
+// OCP encoding), INT4 by sign extension of each nibble (element e in bits
+// 4e .. 4e+3).
+__device__ __forceinline__ void raw_cvt(const Raw8<Fp8> &r, float (&o)[8]) {
+  const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(r.u.x, false);
+  const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(r.u.x, true);
+  const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8(r.u.y, false);
+  const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8(r.u.y, true);
+  o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+  o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+}
+__device__ __forceinline__ void raw_cvt(const Raw8<Int4> &r, float (&o)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (float)((int32_t)(r.u << (28 - 4 * e)) >> 28);
+}
+
+// The 8 elements as bf16 bit patterns (exact for every weight type used with
+// bf16 activations: FP8 E4M3 and INT4 values are bf16 values).
+__device__ __forceinline__ uint4 raw_bf16(const Raw8<uint16_t> &r) { return r.u; }
+template <typename W>
+__device__ __forceinline__ uint4 raw_bf16(const Raw8<W> &r) {
+  float f[8];
+  raw_cvt(r, f);
+  return make_uint4((__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u),
+                    (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u),
+                    (__float_as_uint(f[4]) >> 16) | (__float_as_uint(f[5]) & 0xffff0000u),
+                    (__float_as_uint(f[6]) >> 16) | (__float_as_uint(f[7]) & 0xffff0000u));
+}
+
+// Element e of a weight chunk in the activation type T's representation (bf16
+// bits for T = uint16_t, the value for T = float), for LDS staging.
+template <typename T, typename W>
+__device__ __forceinline__ T w_as_t(const Raw8<W> &r, int e) {
+  if constexpr (sizeof(T) == 4) {
+    return raw_elem(r, e);
+  } else {
+    const uint4 b = raw_bf16(r);
+    const uint32_t wd = e < 2 ? b.x : e < 4 ? b.y : e < 6 ? b.z : b.w;
+    return (uint16_t)(e & 1 ? wd >> 16 : wd & 0xffffu);
+  }
+}
+
+// Byte offset of element k (a multiple of 8) within a weight row.
+template <typename W>
+__device__ __forceinline__ int64_t wofs(int k) { return (int64_t)(k >> 3) * WT<W>::kChunk; }
+
+// MFMA A-operand fragment (8 consecutive k of one weight row) from a byte
+// address: loaded as is for bf16 / fp32 rows, converted exactly to bf16 for
+// quantized rows (whose codes are bf16 values; the row scale is applied to the
+// MFMA result).
+template <typename T, typename W>
+__device__ __forceinline__ void wfrag_load(Frag<T> &f, const char *p) {
+  if constexpr (sizeof(T) == 4) {
+    frag_load(f, reinterpret_cast<const float *>(p));
+  } else {
+    Raw8<W> r;
+    wload(r, p);
+    f.u = raw_bf16(r);
+  }
+}
+
 // ----------------------------------------------------------------- shrink cores
 // Token list of the current item in LDS: toks[0..cnt).  Tokens outside
 // [0, num_tokens) are skipped.
@@ -306,7 +428,7 @@ struct alignas(16) ShrinkSmem {
 // reduce-scattered over the wave and the NW wave results summed in wave order,
 // so a token's result does not depend on TG or on which other tokens share the
 // tile (for a given NW).
-template <typename T, int TG, int RB, int NW>
+template <typename T, typename W, int TG, int RB, int NW>
 __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
                                  int ntok, int num_tokens, const T *__restrict__ x,
                                  float *__restrict__ v, ShrinkSmem<NW> &sm) {
@@ -321,11 +443,11 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
     const int tok = t < ntok ? uniform(toks[g0 + t]) : -1;
     xr[t] = (tok >= 0 && tok < num_tokens) ? x + (int64_t)tok * w.d_in : safe;
   }
-  const T *ar[RB];
+  const char *ar[RB];
 #pragma unroll
   for (int jj = 0; jj < RB; ++jj) {
-    const T *p = jj < nr ? a_row<T>(w, a, j0 + jj) : nullptr;
-    ar[jj] = p ? p : safe;
+    const char *p = jj < nr ? a_row(w, a, j0 + jj) : nullptr;
+    ar[jj] = p ? p : reinterpret_cast<const char *>(safe);
   }
   float acc[NV];
 #pragma unroll
@@ -337,15 +459,16 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
     const int k0 = base + tid * 8, k1 = k0 + kStep;
     const bool one = k0 < w.d_in, two = k1 < w.d_in;
     const int c0 = one ? k0 : 0, c1 = two ? k1 : 0;
-    Raw8<T> xa[TG], aa[RB], xb[TG], ab[RB];
+    Raw8<T> xa[TG], xb[TG];
+    Raw8<W> aa[RB], ab[RB];
 #pragma unroll
     for (int t = 0; t < TG; ++t) raw_load(xa[t], xr[t] + c0);
 #pragma unroll
-    for (int jj = 0; jj < RB; ++jj) raw_load(aa[jj], ar[jj] + c0);
+    for (int jj = 0; jj < RB; ++jj) wload(aa[jj], ar[jj] + wofs<W>(c0));
 #pragma unroll
     for (int t = 0; t < TG; ++t) raw_load(xb[t], xr[t] + c1);
 #pragma unroll
-    for (int jj = 0; jj < RB; ++jj) raw_load(ab[jj], ar[jj] + c1);
+    for (int jj = 0; jj < RB; ++jj) wload(ab[jj], ar[jj] + wofs<W>(c1));
     float xv[TG][8];
     if (one) {
 #pragma unroll
@@ -384,7 +507,8 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
     const int t = tid / RB, jj = tid % RB;
     if (t < ntok && jj < nr) {
       const int tok = toks[g0 + t];
-      if (tok >= 0 && tok < num_tokens) v[(int64_t)tok * w.r_max + j0 + jj] = s;
+      if (tok >= 0 && tok < num_tokens)
+        v[(int64_t)tok * w.r_max + j0 + jj] = WT<W>::kScaled ? s * a_scale<W>(w, a, j0 + jj) : s;
     }
   }
   __syncthreads();
@@ -392,17 +516,17 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
 
 // Gather/GEMV shrink of tokens toks[0..cnt) of adapter a over its row group
 // [j0, j0 + nr), nr <= RB: groups of up to 4 tokens, one group of 1 to 3 at the end.
-template <typename T, int RB, int NW>
+template <typename T, typename W, int RB, int NW>
 __device__ __forceinline__ void shrink_gemv(const DevW &w, int a, int j0, int nr, const int *toks, int cnt,
                             int num_tokens, const T *__restrict__ x, float *__restrict__ v,
                             ShrinkSmem<NW> &sm) {
   int g0 = 0;
   for (; g0 + 4 <= cnt; g0 += 4)
-    shrink_rows_tile<T, 4, RB, NW>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
+    shrink_rows_tile<T, W, 4, RB, NW>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
   const int rest = cnt - g0;
-  if (rest == 1) shrink_rows_tile<T, 1, RB, NW>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
-  else if (rest == 2) shrink_rows_tile<T, 2, RB, NW>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
-  else if (rest == 3) shrink_rows_tile<T, 4, RB, NW>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
+  if (rest == 1) shrink_rows_tile<T, W, 1, RB, NW>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
+  else if (rest == 2) shrink_rows_tile<T, W, 2, RB, NW>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
+  else if (rest == 3) shrink_rows_tile<T, W, 4, RB, NW>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
 }
 
 // One MFMA shrink tile: 16 tokens (this lane's token row xp, or a safe row)
@@ -411,18 +535,18 @@ __device__ __forceinline__ void shrink_gemv(const DevW &w, int a, int j0, int nr
 // MFMAs.  Lanes beyond the rank or the tile read safe rows whose outputs are
 // dropped; the last, partial k-step zeroes both operands past d_in.  The wave
 // results are summed in wave order.
-template <typename T, int RT, int NW>
+template <typename T, typename W, int RT, int NW>
 __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, int j0, const T *xp, int tok,
                                  const T *__restrict__ x, float *__restrict__ v, ShrinkSmem<NW> &sm) {
   constexpr int U = RT == 1 ? 8 : 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
-  const T *safe = x;
-  const T *ap[RT];
+  const char *safe = reinterpret_cast<const char *>(x);
+  const char *ap[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = j0 + rt * 16 + m;
-    const T *p = row < r ? a_row<T>(w, a, row) : nullptr;
+    const char *p = row < r ? a_row(w, a, row) : nullptr;
     ap[rt] = p ? p : safe;
   }
   f32x4_t acc[RT];
@@ -438,7 +562,7 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
       const int k = (s + NW * u) * 32 + g * 8;
       frag_load(xf[u], xp + k);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) frag_load(af[u][rt], ap[rt] + k);
+      for (int rt = 0; rt < RT; ++rt) wfrag_load<T, W>(af[u][rt], ap[rt] + wofs<W>(k));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -454,7 +578,7 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
     if (!kin) frag_zero(xf);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      frag_load(af[rt], ap[rt] + kc);
+      wfrag_load<T, W>(af[rt], ap[rt] + wofs<W>(kc));
       if (!kin) frag_zero(af[rt]);
     }
 #pragma unroll
@@ -474,7 +598,8 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
 #pragma unroll
       for (int wv = 1; wv < NW; ++wv) s4 += sm.red_mfma[((wv * 4 + rt) * 4 + e) * 64 + lane];
       const int j = j0 + rt * 16 + 4 * g + e;
-      if (tok >= 0 && j < r) v[(int64_t)tok * w.r_max + j] = s4;
+      if (tok >= 0 && j < r)
+        v[(int64_t)tok * w.r_max + j] = WT<W>::kScaled ? s4 * a_scale<W>(w, a, j) : s4;
     }
   }
   __syncthreads();
@@ -482,7 +607,7 @@ __device__ __forceinline__ void shrink_mfma_tile(const DevW &w, int a, int r, in
 
 // MFMA shrink for tokens toks[0..cnt) of adapter a: 16-token tiles, passes of
 // up to 64 rows.
-template <typename T, int NW>
+template <typename T, typename W, int NW>
 __device__ __forceinline__ void shrink_mfma(const DevW &w, int a, int r, const int *toks, int cnt, int num_tokens,
                             const T *__restrict__ x, float *__restrict__ v, ShrinkSmem<NW> &sm) {
   const int m = threadIdx.x & 15;
@@ -493,10 +618,10 @@ __device__ __forceinline__ void shrink_mfma(const DevW &w, int a, int r, const i
     for (int j0 = 0; j0 < r; j0 += 64) {
       const int nrt = min(4, (r - j0 + 15) >> 4);
       switch (nrt) {
-        case 1: shrink_mfma_tile<T, 1, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
-        case 2: shrink_mfma_tile<T, 2, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
-        case 3: shrink_mfma_tile<T, 3, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
-        default: shrink_mfma_tile<T, 4, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 1: shrink_mfma_tile<T, W, 1, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 2: shrink_mfma_tile<T, W, 2, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
+        case 3: shrink_mfma_tile<T, W, 3, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
+        default: shrink_mfma_tile<T, W, 4, NW>(w, a, r, j0, xp, tok, x, v, sm); break;
       }
     }
   }
@@ -523,7 +648,7 @@ struct alignas(16) ExpandSmem {
 // (16-byte loads, all issued before the first FMA); the y chunks of the tile's
 // tokens are fetched at the start; v is read as uniform values.  Every output
 // is y + sum_j v_j b_j summed in ascending j, independent of TG.
-template <typename T, int TG, int NT>
+template <typename T, typename W, int TG, int NT>
 __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, int cb, const int *toks, int g0,
                                  int ntok, int num_tokens, const float *__restrict__ v,
                                  T *__restrict__ y) {
@@ -540,7 +665,7 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
   Raw8<T> yraw[TG];
 #pragma unroll
   for (int t = 0; t < TG; ++t) raw_load(yraw[t], y + (int64_t)(tk[t] >= 0 ? tk[t] : 0) * w.d_out + col);
-  const T *safe = reinterpret_cast<const T *>(w.b_pages);
+  const char *safe = w.b_pages;
   const bool vec_v = (w.r_max & 3) == 0;
   float acc[TG][8];
 #pragma unroll
@@ -550,11 +675,12 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
   for (int j0 = 0; j0 < r; j0 += 16) {
     // all 16 row addresses first (their page lookups in flight together), then
     // all 16 row loads
-    const T *rp[16];
-    b_rows16<T>(w, a, j0, r, col, safe, rp);
-    Raw8<T> braw[16];
+    const char *rp[16];
+    float bsc[16];
+    b_rows16<W>(w, a, j0, r, col, safe, rp, bsc);
+    Raw8<W> braw[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) raw_load(braw[i], rp[i]);
+    for (int i = 0; i < 16; ++i) wload(braw[i], rp[i]);
     // v[tok][j0 .. j0+16): the same address in every lane, read with 16-byte
     // vector loads (one request per wave) where r_max keeps them aligned
     float vj[TG][16];
@@ -576,10 +702,12 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
         for (int i = 0; i < 16; ++i) vj[t][i] = vr[min(j0 + i, w.r_max - 1)];
       }
     }
+    // B^T row scales fold into v (quantized rows; 1 otherwise)
 #pragma unroll
     for (int t = 0; t < TG; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vj[t][i] = (tk[t] >= 0 && j0 + i < r) ? vj[t][i] : 0.f;
+      for (int i = 0; i < 16; ++i)
+        vj[t][i] = (tk[t] >= 0 && j0 + i < r) ? (WT<W>::kScaled ? vj[t][i] * bsc[i] : vj[t][i]) : 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (j0 + i < r) {
@@ -604,15 +732,15 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
   }
 }
 
-template <typename T, int NT>
+template <typename T, typename W, int NT>
 __device__ __forceinline__ void expand_gemv(const DevW &w, int a, int r, int cb, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y) {
   int g0 = 0;
-  for (; g0 + 4 <= cnt; g0 += 4) expand_cols_tile<T, 4, NT>(w, a, r, cb, toks, g0, 4, num_tokens, v, y);
+  for (; g0 + 4 <= cnt; g0 += 4) expand_cols_tile<T, W, 4, NT>(w, a, r, cb, toks, g0, 4, num_tokens, v, y);
   const int rest = cnt - g0;
-  if (rest == 1) expand_cols_tile<T, 1, NT>(w, a, r, cb, toks, g0, 1, num_tokens, v, y);
-  else if (rest == 2) expand_cols_tile<T, 2, NT>(w, a, r, cb, toks, g0, 2, num_tokens, v, y);
-  else if (rest == 3) expand_cols_tile<T, 4, NT>(w, a, r, cb, toks, g0, 3, num_tokens, v, y);
+  if (rest == 1) expand_cols_tile<T, W, 1, NT>(w, a, r, cb, toks, g0, 1, num_tokens, v, y);
+  else if (rest == 2) expand_cols_tile<T, W, 2, NT>(w, a, r, cb, toks, g0, 2, num_tokens, v, y);
+  else if (rest == 3) expand_cols_tile<T, W, 4, NT>(w, a, r, cb, toks, g0, 3, num_tokens, v, y);
 }
 
 // Column of the wave's 64-column slab that MFMA row `rho` of sub-tile `t`
@@ -640,29 +768,29 @@ __device__ __forceinline__ void load_v8(const float *vr, int jb, int nj, bool ve
 // 8 (l & 7) .. +7.  Rows past nj (the rank) and columns past d_out are zero.
 // The NR loads are issued unconditionally (safe address, zero-selected) before
 // the first store.
-template <typename T, int NR>
+template <typename T, typename W, int NR>
 __device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj, int c0, T *bt, int lane) {
   constexpr int RS = ExpandCfg<T>::kRowStride;
-  const T *safe = reinterpret_cast<const T *>(w.b_pages);
+  const char *safe = w.b_pages;
   const int cc = (lane & 7) * 8;
-  const T *rp[NR];
+  const char *rp[NR];
   bool ok[NR];
 #pragma unroll
   for (int it = 0; it < NR; ++it) {
     const int jr = (lane >> 3) + 8 * it;
-    const T *br = (jr < nj && c0 + cc < w.d_out) ? b_row<T>(w, a, jc + jr) : nullptr;
+    const char *br = (jr < nj && c0 + cc < w.d_out) ? b_row(w, a, jc + jr) : nullptr;
     ok[it] = br != nullptr;
-    rp[it] = br ? br + c0 + cc : safe;
+    rp[it] = br ? br + wofs<W>(c0 + cc) : safe;
   }
-  Raw8<T> braw[NR];
+  Raw8<W> braw[NR];
 #pragma unroll
-  for (int it = 0; it < NR; ++it) raw_load(braw[it], rp[it]);
+  for (int it = 0; it < NR; ++it) wload(braw[it], rp[it]);
 #pragma unroll
   for (int it = 0; it < NR; ++it) {
     const int jr = (lane >> 3) + 8 * it;
     if (!ok[it]) raw_zero(braw[it]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bt[(cc + e) * RS + jr] = raw_elem(braw[it], e);
+    for (int e = 0; e < 8; ++e) bt[(cc + e) * RS + jr] = w_as_t<T, W>(braw[it], e);
   }
 }
 
@@ -675,7 +803,7 @@ __device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj,
 // 16-index K block are read once and used by all four token tiles.  bf16: v is
 // split into hi + lo bf16 so each K=32 MFMA covers 16 rank indices exactly;
 // fp32: 16x16x4 steps.
-template <typename T>
+template <typename T, typename W>
 __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y,
                             ExpandSmem<T> &sm) {
@@ -741,12 +869,18 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
         vq[it].y = ok && j + 1 < r ? vq[it].y : 0.f;
         vq[it].z = ok && j + 2 < r ? vq[it].z : 0.f;
         vq[it].w = ok && j + 3 < r ? vq[it].w : 0.f;
+        if constexpr (WT<W>::kScaled) {  // B^T row scales fold into v
+          vq[it].x *= j < r ? b_scale<W>(w, a, j) : 0.f;
+          vq[it].y *= j + 1 < r ? b_scale<W>(w, a, j + 1) : 0.f;
+          vq[it].z *= j + 2 < r ? b_scale<W>(w, a, j + 2) : 0.f;
+          vq[it].w *= j + 3 < r ? b_scale<W>(w, a, j + 3) : 0.f;
+        }
       }
       switch (nj16 >> 3) {
-        case 2: stage_slab<T, 2>(w, a, jc, nj, c0, bt, lane); break;
-        case 4: stage_slab<T, 4>(w, a, jc, nj, c0, bt, lane); break;
-        case 6: stage_slab<T, 6>(w, a, jc, nj, c0, bt, lane); break;
-        default: stage_slab<T, 8>(w, a, jc, nj, c0, bt, lane); break;
+        case 2: stage_slab<T, W, 2>(w, a, jc, nj, c0, bt, lane); break;
+        case 4: stage_slab<T, W, 4>(w, a, jc, nj, c0, bt, lane); break;
+        case 6: stage_slab<T, W, 6>(w, a, jc, nj, c0, bt, lane); break;
+        default: stage_slab<T, W, 8>(w, a, jc, nj, c0, bt, lane); break;
       }
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -843,7 +977,7 @@ __device__ __forceinline__ bool decode_item(const lora_item &it, const DevW &w, 
   return true;
 }
 
-template <typename T, int NT>
+template <typename T, typename W, int NT>
 __global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *__restrict__ perm,
                                                          int32_t num_perm,
                                                          const lora_item *__restrict__ items,
@@ -861,12 +995,12 @@ __global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *
   for (int i = threadIdx.x; i < cnt; i += NT) sm.toks[i] = perm[pb + i];
   __syncthreads();
   if (path == LORA_PATH_MFMA)
-    shrink_mfma<T, NW>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
+    shrink_mfma<T, W, NW>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
   else
-    shrink_gemv<T, kRowGroup, NW>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
+    shrink_gemv<T, W, kRowGroup, NW>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
 }
 
-template <typename T>
+template <typename T, typename W>
 __global__ __launch_bounds__(kThreads) void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
                                                                int32_t num_perm,
                                                                const lora_item *__restrict__ items,
@@ -883,9 +1017,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_expand_kernel(DevW w, const int
   __syncthreads();
   const int r = adapter_rank(w, a);
   if (path == LORA_PATH_MFMA)
-    expand_mfma<T>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+    expand_mfma<T, W>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
   else
-    expand_gemv<T, kThreads>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
+    expand_gemv<T, W, kThreads>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
 }
 
 // Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups to
@@ -923,7 +1057,7 @@ __device__ __forceinline__ int gather_adapter_tokens(const int32_t *__restrict__
 
 // Per-token (BGMV) shrink.  Work unit u is a token (token-major) or an adapter
 // (adapter-major); each unit is split into groups of RB rows, one per workgroup.
-template <typename T, int RB>
+template <typename T, typename W, int RB>
 __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int32_t *__restrict__ ids,
                                                                int32_t num_tokens, int32_t adapter_major,
                                                                int32_t units, int32_t groups,
@@ -942,14 +1076,14 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
     if (j0 >= r) return;
     if (threadIdx.x == 0) sm.toks[0] = t;
     __syncthreads();
-    shrink_gemv<T, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
+    shrink_gemv<T, W, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
     if (j0 >= r) return;
     for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
       const int n = gather_adapter_tokens<kThreads>(ids, num_tokens, c0, a, sm.toks, wave_cnt);
-      if (n > 0) shrink_gemv<T, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
+      if (n > 0) shrink_gemv<T, W, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
       __syncthreads();
     }
   }
@@ -957,7 +1091,7 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
 
 // Per-token (BGMV) expand.  Work unit u as above, split into column blocks of
 // 8 NT columns, one per workgroup of NT threads.
-template <typename T, int NT>
+template <typename T, typename W, int NT>
 __global__ __launch_bounds__(NT) void bgmv_expand_kernel(DevW w, const int32_t *__restrict__ ids,
                                                          int32_t num_tokens, int32_t adapter_major,
                                                          int32_t units, int32_t groups,
@@ -973,13 +1107,13 @@ __global__ __launch_bounds__(NT) void bgmv_expand_kernel(DevW w, const int32_t *
     const int a = ids[t];
     if (a < 0 || a >= w.num_adapters) return;
     const int tok1[1] = {t};
-    expand_cols_tile<T, 1, NT>(w, a, adapter_rank(w, a), cb, tok1, 0, 1, num_tokens, v, y);
+    expand_cols_tile<T, W, 1, NT>(w, a, adapter_rank(w, a), cb, tok1, 0, 1, num_tokens, v, y);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
     for (int c0 = 0; c0 < num_tokens; c0 += NT) {
       const int n = gather_adapter_tokens<NT>(ids, num_tokens, c0, a, toks, wave_cnt);
-      if (n > 0) expand_gemv<T, NT>(w, a, r, cb, toks, n, num_tokens, v, y);
+      if (n > 0) expand_gemv<T, W, NT>(w, a, r, cb, toks, n, num_tokens, v, y);
       __syncthreads();
     }
   }
@@ -1006,18 +1140,18 @@ struct alignas(16) FusedSmem {
 
 // Addresses of rows j0 .. j0+15 of adapter a's A (offset k), `safe` past the
 // rank or on an out-of-range page.
-template <typename T>
-__device__ __forceinline__ void a_rows16(const DevW &w, int a, int j0, int r, int k, const T *safe,
-                                         const T *(&rp)[16]) {
+template <typename W>
+__device__ __forceinline__ void a_rows16(const DevW &w, int a, int j0, int r, int k, const char *safe,
+                                         const char *(&rp)[16]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const T *p = j0 + i < r ? a_row<T>(w, a, j0 + i) : nullptr;
-    rp[i] = p ? p + k : safe;
+    const char *p = j0 + i < r ? a_row(w, a, j0 + i) : nullptr;
+    rp[i] = p ? p + wofs<W>(k) : safe;
   }
 }
 
 // One token t (adapter a) of the fused kernel over columns [c_begin, c_end).
-template <typename T>
+template <typename T, typename W>
 __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb, int c_begin,
                                            int c_end, const T *__restrict__ x,
                                            float *__restrict__ v, T *__restrict__ y,
@@ -1026,7 +1160,7 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T *xr = x + (int64_t)t * w.d_in;
   T *yr = y + (int64_t)t * w.d_out;
-  const T *safe_a = x, *safe_b = reinterpret_cast<const T *>(w.b_pages);
+  const char *safe_a = reinterpret_cast<const char *>(x), *safe_b = w.b_pages;
 
   // ---- first expand pass: y chunk and B^T rows 0..15, issued up front
   const int col0 = c_begin + tid * 8;
@@ -1034,11 +1168,12 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
   const int colc0 = cin0 ? col0 : c_begin;
   Raw8<T> y0;
   raw_load(y0, yr + colc0);
-  const T *bp0[16];
-  b_rows16<T>(w, a, 0, r, colc0, safe_b, bp0);
-  Raw8<T> b0[16];
+  const char *bp0[16];
+  float bsc0[16];
+  b_rows16<W>(w, a, 0, r, colc0, safe_b, bp0, bsc0);
+  Raw8<W> b0[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) raw_load(b0[i], bp0[i]);
+  for (int i = 0; i < 16; ++i) wload(b0[i], bp0[i]);
 
   // ---- shrink: v[j] = sum_k A[j][k] x[k], 16 rows at a time
   for (int jc = 0; jc < r; jc += 16) {
@@ -1049,12 +1184,13 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
       const int k = k0 + tid * 8;
       const bool kin = k < w.d_in;
       const int kc = kin ? k : 0;
-      const T *ap[16];
-      a_rows16<T>(w, a, jc, r, kc, safe_a, ap);
-      Raw8<T> xraw, araw[16];
+      const char *ap[16];
+      a_rows16<W>(w, a, jc, r, kc, safe_a, ap);
+      Raw8<T> xraw;
+      Raw8<W> araw[16];
       raw_load(xraw, xr + kc);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) raw_load(araw[i], ap[i]);
+      for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
       if (kin) {
         float xv[8];
         raw_cvt(xraw, xv);
@@ -1076,6 +1212,7 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
       float sum = sm.red[tid];
 #pragma unroll
       for (int wv = 1; wv < kFusedWaves; ++wv) sum += sm.red[wv * 16 + tid];
+      if constexpr (WT<W>::kScaled) sum *= jc + tid < r ? a_scale<W>(w, a, jc + tid) : 0.f;
       sm.vs[jc + tid] = sum;
       if (v && cb == 0 && jc + tid < r) v[(int64_t)t * w.r_max + jc + tid] = sum;
     }
@@ -1094,20 +1231,24 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int j0 = 0; j0 < r; j0 += 16) {
-      Raw8<T> braw[16];
+      Raw8<W> braw[16];
+      float bsc[16];
       if (c0 == c_begin && j0 == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) braw[i] = b0[i];
+        for (int i = 0; i < 16; ++i) {
+          braw[i] = b0[i];
+          bsc[i] = bsc0[i];
+        }
       } else {
-        const T *bp[16];
-        b_rows16<T>(w, a, j0, r, colc, safe_b, bp);
+        const char *bp[16];
+        b_rows16<W>(w, a, j0, r, colc, safe_b, bp, bsc);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) raw_load(braw[i], bp[i]);
+        for (int i = 0; i < 16; ++i) wload(braw[i], bp[i]);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (j0 + i < r) {
-          const float vj = sm.vs[j0 + i];
+          const float vj = WT<W>::kScaled ? sm.vs[j0 + i] * bsc[i] : sm.vs[j0 + i];
           float bv[8];
           raw_cvt(braw[i], bv);
 #pragma unroll
@@ -1126,7 +1267,7 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
 }
 
 // Work unit u = (token u / nblk, column block u % nblk).
-template <typename T>
+template <typename T, typename W>
 __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const int32_t *__restrict__ ids,
                                                                    int32_t num_tokens, int32_t nblk,
                                                                    int32_t block_cols,
@@ -1140,7 +1281,7 @@ __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const
   const int a = ids[t];
   if (a < 0 || a >= w.num_adapters) return;
   const int c_begin = cb * block_cols, c_end = min(w.d_out, c_begin + block_cols);
-  fused_token<T>(w, t, a, cb, c_begin, c_end, x, v, y, sm);
+  fused_token<T, W>(w, t, a, cb, c_begin, c_end, x, v, y, sm);
 }
 
 // Fused per-token delta, adapter-major: work unit (adapter a, column block
@@ -1159,7 +1300,7 @@ struct alignas(16) FusedAmSmem {
   float vs[4][LORA_MAX_RANK];
 };
 
-template <typename T, int TG>
+template <typename T, typename W, int TG>
 __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int c_begin, int c_end,
                                                const int *toks, int g0, int ntok,
                                                const T *__restrict__ x, float *__restrict__ v,
@@ -1168,7 +1309,7 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
   int tk[TG];
 #pragma unroll
   for (int t = 0; t < TG; ++t) tk[t] = t < ntok ? uniform(toks[g0 + t]) : toks[g0];
-  const T *safe_a = x, *safe_b = reinterpret_cast<const T *>(w.b_pages);
+  const char *safe_a = reinterpret_cast<const char *>(x), *safe_b = w.b_pages;
   // shrink: acc[t][i] = sum over this thread's k chunks of A[jc+i][k] x_t[k]
   for (int jc = 0; jc < r; jc += 16) {
     float acc[TG * 16];
@@ -1178,13 +1319,14 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
       const int k = k0 + tid * 8;
       const bool kin = k < w.d_in;
       const int kc = kin ? k : 0;
-      const T *ap[16];
-      a_rows16<T>(w, a, jc, r, kc, safe_a, ap);
-      Raw8<T> xraw[TG], araw[16];
+      const char *ap[16];
+      a_rows16<W>(w, a, jc, r, kc, safe_a, ap);
+      Raw8<T> xraw[TG];
+      Raw8<W> araw[16];
 #pragma unroll
       for (int t = 0; t < TG; ++t) raw_load(xraw[t], x + (int64_t)tk[t] * w.d_in + kc);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) raw_load(araw[i], ap[i]);
+      for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
       if (kin) {
         float xv[TG][8];
 #pragma unroll
@@ -1209,6 +1351,7 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
 #pragma unroll
       for (int wv = 1; wv < kFusedWaves; ++wv) sum += sm.red[wv * 64 + tid];
       const int t = tid >> 4, i = tid & 15;
+      if constexpr (WT<W>::kScaled) sum *= jc + i < r ? a_scale<W>(w, a, jc + i) : 0.f;
       sm.vs[t][jc + i] = sum;
       if (write_v && t < ntok && jc + i < r) v[(int64_t)tk[t] * w.r_max + jc + i] = sum;
     }
@@ -1229,11 +1372,12 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
     for (int j0 = 0; j0 < r; j0 += 16) {
-      const T *bp[16];
-      b_rows16<T>(w, a, j0, r, colc, safe_b, bp);
-      Raw8<T> braw[16];
+      const char *bp[16];
+      float bsc[16];
+      b_rows16<W>(w, a, j0, r, colc, safe_b, bp, bsc);
+      Raw8<W> braw[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) raw_load(braw[i], bp[i]);
+      for (int i = 0; i < 16; ++i) wload(braw[i], bp[i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (j0 + i < r) {
@@ -1241,7 +1385,7 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
           raw_cvt(braw[i], bv);
 #pragma unroll
           for (int t = 0; t < TG; ++t) {
-            const float vj = sm.vs[t][j0 + i];
+            const float vj = WT<W>::kScaled ? sm.vs[t][j0 + i] * bsc[i] : sm.vs[t][j0 + i];
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vj, bv[e], acc[t][e]);
           }
@@ -1264,7 +1408,7 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
   __syncthreads();  // vs is rewritten by the next group
 }
 
-template <typename T>
+template <typename T, typename W>
 __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_am_kernel(DevW w, const int32_t *__restrict__ ids,
                                                                       int32_t num_tokens, int32_t nblk,
                                                                       int32_t block_cols,
@@ -1281,20 +1425,38 @@ __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_am_kernel(DevW w, co
     const int n = gather_adapter_tokens<kFusedThreads>(ids, num_tokens, c0, a, sm.toks, sm.wave_cnt);
     int g0 = 0;
     for (; g0 + 4 <= n; g0 += 4)
-      fused_am_group<T, 4>(w, a, r, c_begin, c_end, sm.toks, g0, 4, x, v, y, v && cb == 0, sm);
+      fused_am_group<T, W, 4>(w, a, r, c_begin, c_end, sm.toks, g0, 4, x, v, y, v && cb == 0, sm);
     const int rest = n - g0;
     if (rest == 1)
-      fused_am_group<T, 1>(w, a, r, c_begin, c_end, sm.toks, g0, 1, x, v, y, v && cb == 0, sm);
+      fused_am_group<T, W, 1>(w, a, r, c_begin, c_end, sm.toks, g0, 1, x, v, y, v && cb == 0, sm);
     else if (rest == 2)
-      fused_am_group<T, 2>(w, a, r, c_begin, c_end, sm.toks, g0, 2, x, v, y, v && cb == 0, sm);
+      fused_am_group<T, W, 2>(w, a, r, c_begin, c_end, sm.toks, g0, 2, x, v, y, v && cb == 0, sm);
     else if (rest == 3)
-      fused_am_group<T, 4>(w, a, r, c_begin, c_end, sm.toks, g0, 3, x, v, y, v && cb == 0, sm);
+      fused_am_group<T, W, 4>(w, a, r, c_begin, c_end, sm.toks, g0, 3, x, v, y, v && cb == 0, sm);
     __syncthreads();
   }
 }
 
 // ----------------------------------------------------------------- validation
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Bytes of one stored adapter row of d elements.
+int64_t row_bytes(int32_t dtype, int32_t wf, int32_t d) {
+  if (wf == LORA_WFMT_FP8_E4M3) return d;
+  if (wf == LORA_WFMT_INT4) return d / 2;
+  return (int64_t)d * (dtype == LORA_BF16 ? 2 : 4);
+}
+
+// Calls f(T{}, W{}) with the activation type T and the adapter-row type W of w
+// (validated by to_dev): (bf16, bf16), (fp32, fp32), (bf16, FP8 E4M3) or
+// (bf16, INT4).
+template <typename F>
+void with_types(const lora_weights *w, F &&f) {
+  if (w->dtype == LORA_F32) f(float{}, float{});
+  else if (w->weight_format == LORA_WFMT_FP8_E4M3) f(uint16_t{}, Fp8{});
+  else if (w->weight_format == LORA_WFMT_INT4) f(uint16_t{}, Int4{});
+  else f(uint16_t{}, uint16_t{});
+}
 
 lora_status to_dev(const lora_weights *w, DevW *d) {
   if (!w) return fail(LORA_EINVAL, "null weights");
@@ -1308,7 +1470,16 @@ lora_status to_dev(const lora_weights *w, DevW *d) {
   if (w->num_adapters < 0) return fail(LORA_EINVAL, "negative num_adapters");
   if (w->page_rows <= 0) return fail(LORA_EINVAL, "page_rows must be positive");
   if (w->num_pages_a <= 0 || w->num_pages_b <= 0) return fail(LORA_EINVAL, "empty page pool");
-  if (w->reserved != 0) return fail(LORA_EINVAL, "reserved field must be 0");
+  const int32_t wf = w->weight_format;
+  if (wf != LORA_WFMT_PLAIN && wf != LORA_WFMT_FP8_E4M3 && wf != LORA_WFMT_INT4)
+    return fail(LORA_EUNSUPPORTED, "unknown weight_format %d", wf);
+  if (wf != LORA_WFMT_PLAIN) {
+    if (w->dtype != LORA_BF16)
+      return fail(LORA_EUNSUPPORTED, "quantized adapter rows need bf16 activations");
+    if (!w->a_scales || !w->b_scales) return fail(LORA_EINVAL, "quantized rows need row scales");
+    if (((uintptr_t)w->a_scales & 3u) || ((uintptr_t)w->b_scales & 3u))
+      return fail(LORA_EINVAL, "row scales must be 4-byte aligned");
+  }
   if (!w->a_pages || !w->b_pages || !w->rank) return fail(LORA_EINVAL, "null weight pointer");
   if (!aligned16(w->a_pages) || !aligned16(w->b_pages))
     return fail(LORA_EINVAL, "page storage must be 16-byte aligned");
@@ -1332,6 +1503,10 @@ lora_status to_dev(const lora_weights *w, DevW *d) {
                     w->host_rank[a], w->r_max);
   d->a_pages = (const char *)w->a_pages;
   d->b_pages = (const char *)w->b_pages;
+  d->a_sc = wf == LORA_WFMT_PLAIN ? nullptr : w->a_scales;
+  d->b_sc = wf == LORA_WFMT_PLAIN ? nullptr : w->b_scales;
+  d->a_row_bytes = row_bytes(w->dtype, wf, w->d_in);
+  d->b_row_bytes = row_bytes(w->dtype, wf, w->d_out);
   d->rank = w->rank;
   d->a_pt = w->a_page_table;
   d->b_pt = w->b_page_table;
@@ -1389,14 +1564,13 @@ extern "C" lora_status lora_sgmv_shrink(const lora_weights *w, const int32_t *to
   if ((st = check_sgmv_args(token_perm, num_perm, items, num_items, num_tokens, x, v)) != LORA_OK)
     return st;
   if (num_items == 0 || num_tokens == 0) return ok();
-  if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL((sgmv_shrink_kernel<uint16_t, kSgmvShrinkThreads>), dim3(num_items),
-                       dim3(kSgmvShrinkThreads), 0, stream, d,
-                       token_perm, num_perm, items, num_tokens, (const uint16_t *)x, v);
-  else
-    hipLaunchKernelGGL((sgmv_shrink_kernel<float, kSgmvShrinkThreads>), dim3(num_items),
-                       dim3(kSgmvShrinkThreads), 0, stream, d,
-                       token_perm, num_perm, items, num_tokens, (const float *)x, v);
+  with_types(w, [&](auto t, auto wt) {
+    using T = decltype(t);
+    using W = decltype(wt);
+    hipLaunchKernelGGL((sgmv_shrink_kernel<T, W, kSgmvShrinkThreads>), dim3(num_items),
+                       dim3(kSgmvShrinkThreads), 0, stream, d, token_perm, num_perm, items,
+                       num_tokens, (const T *)x, v);
+  });
   return check_launch("sgmv shrink launch");
 }
 
@@ -1410,12 +1584,12 @@ extern "C" lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *to
   if ((st = check_sgmv_args(token_perm, num_perm, items, num_items, num_tokens, v, y)) != LORA_OK)
     return st;
   if (num_items == 0 || num_tokens == 0) return ok();
-  if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL(sgmv_expand_kernel<uint16_t>, dim3(num_items), dim3(kThreads), 0, stream, d,
-                       token_perm, num_perm, items, num_tokens, v, (uint16_t *)y);
-  else
-    hipLaunchKernelGGL(sgmv_expand_kernel<float>, dim3(num_items), dim3(kThreads), 0, stream, d,
-                       token_perm, num_perm, items, num_tokens, v, (float *)y);
+  with_types(w, [&](auto t, auto wt) {
+    using T = decltype(t);
+    using W = decltype(wt);
+    hipLaunchKernelGGL((sgmv_expand_kernel<T, W>), dim3(num_items), dim3(kThreads), 0, stream, d,
+                       token_perm, num_perm, items, num_tokens, v, (T *)y);
+  });
   return check_launch("sgmv expand launch");
 }
 
@@ -1437,12 +1611,12 @@ extern "C" lora_status lora_bgmv_shrink(const lora_weights *w, const int32_t *to
   const int groups = (w->r_max + kBgmvRows - 1) / kBgmvRows;
   if ((int64_t)units * groups > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
   const dim3 grid(pad8(units * groups));
-  if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL((bgmv_shrink_kernel<uint16_t, kBgmvRows>), grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, units, groups, (const uint16_t *)x, v);
-  else
-    hipLaunchKernelGGL((bgmv_shrink_kernel<float, kBgmvRows>), grid, dim3(kThreads), 0, stream, d,
-                       token_adapter, num_tokens, am, units, groups, (const float *)x, v);
+  with_types(w, [&](auto t, auto wt) {
+    using T = decltype(t);
+    using W = decltype(wt);
+    hipLaunchKernelGGL((bgmv_shrink_kernel<T, W, kBgmvRows>), grid, dim3(kThreads), 0, stream, d,
+                       token_adapter, num_tokens, am, units, groups, (const T *)x, v);
+  });
   return check_launch("bgmv shrink launch");
 }
 
@@ -1465,14 +1639,13 @@ extern "C" lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *to
   const int groups = (w->d_out + cols - 1) / cols;
   if ((int64_t)units * groups > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
   const dim3 grid(pad8(units * groups));
-  if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL((bgmv_expand_kernel<uint16_t, kBgmvExpandThreads>), grid,
+  with_types(w, [&](auto t, auto wt) {
+    using T = decltype(t);
+    using W = decltype(wt);
+    hipLaunchKernelGGL((bgmv_expand_kernel<T, W, kBgmvExpandThreads>), grid,
                        dim3(kBgmvExpandThreads), 0, stream, d, token_adapter, num_tokens, am, units,
-                       groups, v, (uint16_t *)y);
-  else
-    hipLaunchKernelGGL((bgmv_expand_kernel<float, kBgmvExpandThreads>), grid,
-                       dim3(kBgmvExpandThreads), 0, stream, d, token_adapter, num_tokens, am, units,
-                       groups, v, (float *)y);
+                       groups, v, (T *)y);
+  });
   return check_launch("bgmv expand launch");
 }
 
@@ -1506,23 +1679,20 @@ extern "C" lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *tok
   if ((int64_t)units * nblk > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
   if (am) {
     const dim3 grid(pad8(units * nblk));
-    if (w->dtype == LORA_BF16)
-      hipLaunchKernelGGL(bgmv_fused_am_kernel<uint16_t>, grid, dim3(kFusedThreads), 0, stream, d,
-                         token_adapter, num_tokens, nblk, block_cols, (const uint16_t *)x, v,
-                         (uint16_t *)y);
-    else
-      hipLaunchKernelGGL(bgmv_fused_am_kernel<float>, grid, dim3(kFusedThreads), 0, stream, d,
-                         token_adapter, num_tokens, nblk, block_cols, (const float *)x, v,
-                         (float *)y);
+    with_types(w, [&](auto t, auto wt) {
+      using T = decltype(t);
+      using W = decltype(wt);
+      hipLaunchKernelGGL((bgmv_fused_am_kernel<T, W>), grid, dim3(kFusedThreads), 0, stream, d,
+                         token_adapter, num_tokens, nblk, block_cols, (const T *)x, v, (T *)y);
+    });
     return check_launch("bgmv fused launch");
   }
   const dim3 grid(num_tokens * nblk);
-  if (w->dtype == LORA_BF16)
-    hipLaunchKernelGGL(bgmv_fused_kernel<uint16_t>, grid, dim3(kFusedThreads), 0, stream, d,
-                       token_adapter, num_tokens, nblk, block_cols, (const uint16_t *)x, v,
-                       (uint16_t *)y);
-  else
-    hipLaunchKernelGGL(bgmv_fused_kernel<float>, grid, dim3(kFusedThreads), 0, stream, d,
-                       token_adapter, num_tokens, nblk, block_cols, (const float *)x, v, (float *)y);
+  with_types(w, [&](auto t, auto wt) {
+    using T = decltype(t);
+    using W = decltype(wt);
+    hipLaunchKernelGGL((bgmv_fused_kernel<T, W>), grid, dim3(kFusedThreads), 0, stream, d,
+                       token_adapter, num_tokens, nblk, block_cols, (const T *)x, v, (T *)y);
+  });
   return check_launch("bgmv fused launch");
 }

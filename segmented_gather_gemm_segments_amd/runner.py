@@ -44,6 +44,9 @@ class DeviceProblem:
     layout: "dense" -- [N, r_max, d] stacks, rows r_a..r_max-1 filled with NaN;
             "paged" -- a lora_pool of 16-row pages, shuffled, unused page rows
                        NaN, A and B^T rows sharing one pool when d_in == d_out.
+    Quantized rows (p.wq "fp8" / "int4") are stored as uint8 codes with fp32
+    row scales; unused rows hold FP8 NaN codes (0x7f) or INT4 7s and NaN
+    scales, so a stray read shows up in the results.
     """
 
     def __init__(self, p: LoraProblem, device="cuda", layout: Optional[str] = None,
@@ -54,6 +57,9 @@ class DeviceProblem:
         self.layout = layout or ("paged" if p.paged else "dense")
         self.tdtype = torch.bfloat16 if p.dtype == "bf16" else torch.float32
         self.cdtype = B.LORA_BF16 if p.dtype == "bf16" else B.LORA_F32
+        self.wfmt = {"": B.LORA_WFMT_PLAIN, "fp8": B.LORA_WFMT_FP8_E4M3,
+                     "int4": B.LORA_WFMT_INT4}[p.wq]
+        assert self.wfmt == B.LORA_WFMT_PLAIN or p.dtype == "bf16"
         self.x = to_device(p.x, p.dtype, self.device)
         self.y0 = to_device(p.y, p.dtype, self.device)
         self.ids = torch.from_numpy(p.ids).to(self.device)
@@ -68,20 +74,44 @@ class DeviceProblem:
         self._seg = None
 
     # ------------------------------------------------------------- weights
-    def _stack(self, rows, width):
-        torch = self._torch = _torch()
+    def _row_width(self, d: int) -> int:
+        """Last dimension of a stored row: d elements, or its bytes when quantized."""
+        return d // 2 if self.wfmt == B.LORA_WFMT_INT4 else d
+
+    def _empty_rows(self, shape):
+        torch = _torch()
+        if self.wfmt == B.LORA_WFMT_PLAIN:
+            return torch.full(shape, float("nan"), dtype=self.tdtype, device=self.device)
+        fill = 0x7F if self.wfmt == B.LORA_WFMT_FP8_E4M3 else 0x77
+        return torch.full(shape, fill, dtype=torch.uint8, device=self.device)
+
+    def _rows_dev(self, rows):
+        torch = _torch()
+        if self.wfmt == B.LORA_WFMT_PLAIN:
+            return to_device(rows, self.p.dtype, self.device)
+        return torch.from_numpy(np.ascontiguousarray(rows, dtype=np.uint8)).to(self.device)
+
+    def _stack(self, rows, scales, d):
+        torch = _torch()
         n = len(rows)
-        st = torch.full((n, self.r_max, width), float("nan"), dtype=self.tdtype, device=self.device)
+        st = self._empty_rows((n, self.r_max, self._row_width(d)))
+        sc = None
+        if self.wfmt != B.LORA_WFMT_PLAIN:
+            sc = torch.full((n * self.r_max,), float("nan"), dtype=torch.float32, device=self.device)
         for a, r in enumerate(rows):
-            st[a, : r.shape[0]] = to_device(r, self.p.dtype, self.device)
-        return st
+            st[a, : r.shape[0]] = self._rows_dev(r)
+            if sc is not None:
+                sc[a * self.r_max: a * self.r_max + r.shape[0]] = torch.from_numpy(
+                    np.asarray(scales[a], np.float32)).to(self.device)
+        return st, sc
 
     def _dense(self):
         p = self.p
-        self.a_pages = self._stack(p.a_rows, p.d_in)
-        self.b_pages = self._stack(p.bt_rows, p.d_out)
+        self.a_pages, a_sc = self._stack(p.a_rows, p.a_scales, p.d_in)
+        self.b_pages, b_sc = self._stack(p.bt_rows, p.bt_scales, p.d_out)
         self.weights = B.Weights(self.cdtype, p.d_in, p.d_out, self.r_max, self.r_max,
-                                 self.a_pages, self.b_pages, self.rank, p.ranks.astype(np.int32))
+                                 self.a_pages, self.b_pages, self.rank, p.ranks.astype(np.int32),
+                                 weight_format=self.wfmt, a_scales=a_sc, b_scales=b_sc)
 
     def _paged(self, page_rows, slack, seed):
         torch = _torch()
@@ -90,12 +120,23 @@ class DeviceProblem:
         shared = p.d_in == p.d_out
         max_pages = (self.r_max + page_rows - 1) // page_rows
 
-        def make_pool(n_pages, width, s):
-            storage = torch.full((n_pages, page_rows, width), float("nan"), dtype=self.tdtype,
-                                 device=self.device)
-            pool = B.Pool(storage, page_rows, shuffle_seed=s)
+        quant = self.wfmt != B.LORA_WFMT_PLAIN
+
+        def make_pool(n_pages, d, s):
+            storage = self._empty_rows((n_pages, page_rows, self._row_width(d)))
+            scales = None
+            if quant:
+                scales = torch.full((n_pages * page_rows,), float("nan"), dtype=torch.float32,
+                                    device=self.device)
+            pool = B.Pool(storage, page_rows, shuffle_seed=s, weight_format=self.wfmt,
+                          scales=scales)
             self._pools.append(pool)
             return pool
+
+        def scales_dev(lst, a):
+            if not quant:
+                return None
+            return torch.from_numpy(np.asarray(lst[a], np.float32)).to(self.device)
 
         if shared:
             cap = int(np.ceil(2 * pages_a * slack))
@@ -109,9 +150,9 @@ class DeviceProblem:
         for a in range(p.num_adapters):
             r = int(p.ranks[a])
             ia = pool_a.alloc(r)
-            pool_a.write_rows(ia, to_device(p.a_rows[a], p.dtype, self.device))
+            pool_a.write_rows(ia, self._rows_dev(p.a_rows[a]), scales_dev(p.a_scales, a))
             ib = pool_b.alloc(r)
-            pool_b.write_rows(ib, to_device(p.bt_rows[a], p.dtype, self.device))
+            pool_b.write_rows(ib, self._rows_dev(p.bt_rows[a]), scales_dev(p.bt_scales, a))
             a_pt[a, : ia.size] = ia
             b_pt[a, : ib.size] = ib
         torch.cuda.synchronize(self.device)
@@ -120,7 +161,9 @@ class DeviceProblem:
         self.weights = B.Weights(self.cdtype, p.d_in, p.d_out, self.r_max, page_rows,
                                  self.a_pages, self.b_pages, self.rank, p.ranks.astype(np.int32),
                                  torch.from_numpy(a_pt).to(self.device),
-                                 torch.from_numpy(b_pt).to(self.device), max_pages)
+                                 torch.from_numpy(b_pt).to(self.device), max_pages,
+                                 weight_format=self.wfmt, a_scales=pool_a.scales,
+                                 b_scales=pool_b.scales)
 
     # ------------------------------------------------------------- segments, plans
     def segments(self):

@@ -245,6 +245,16 @@ def hetero_paged(seed: int = 4, num_tokens: int = 4096, num_segments: int = 64, 
                         seg_ids, ranks, d, d, "bf16", seed, paged=True, page_rows=16, wq=wq)
 
 
+def quant_mixed(wq: str, seed: int = 6, paged: bool = False) -> LoraProblem:
+    """Small mixed batch for the quantized-row formats: requests of 40, 1, 3,
+    17, 70, 2 and 5 tokens (the last without an adapter) on five resident
+    adapters of ranks 8, 16, 40, 64, 72; 776 -> 1288, ragged against every k
+    step and column block; bf16 activations, adapter rows FP8 E4M3 or INT4."""
+    return make_problem(f"quant_mixed_{wq}{'_paged' if paged else ''}",
+                        [40, 1, 3, 17, 70, 2, 5], [3, 0, 4, 1, 2, 3, -1], [8, 16, 40, 64, 72],
+                        776, 1288, "bf16", seed, paged=paged, page_rows=16, wq=wq)
+
+
 LAYER_70B = [  # (name, d_in, d_out): Llama-3-70B projections, rank-16 table
     ("q", 8192, 8192), ("k", 8192, 1024), ("v", 8192, 1024), ("o", 8192, 8192),
     ("gate", 8192, 28672), ("up", 8192, 28672), ("down", 28672, 8192),

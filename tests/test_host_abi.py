@@ -2,6 +2,7 @@
 build (bit-exact against the oracle's different algorithm), the planner's
 coverage, the page pool's bookkeeping and the error conventions."""
 import ctypes
+import types
 import os
 import re
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(h, n), n
     assert set(names) == set(B.EXPORTS), "binding and header disagree"
-    assert B.lib().lora_abi_version() == 1
+    assert B.lib().lora_abi_version() == 2
 
 
 # ------------------------------------------------------------------ segments
@@ -245,11 +246,39 @@ def test_pool_alloc_free_and_shuffle():
     assert p.num_free() == 0 and rest.size == 57
 
 
+def test_pool_formats():
+    """Quantized pools need row scales (and bf16), plain pools take none; the
+    bookkeeping is the same for every format."""
+    lib, h = B.lib(), ctypes.c_void_p()
+    buf = np.zeros(4, np.float32)
+    sc = buf.ctypes.data
+    assert lib.lora_pool_create(8, 16, 64, B.LORA_BF16, B.LORA_WFMT_FP8_E4M3, 16, None, 0,
+                                ctypes.byref(h)) == B.LORA_EINVAL
+    assert lib.lora_pool_create(8, 16, 64, B.LORA_BF16, B.LORA_WFMT_PLAIN, 16, sc, 0,
+                                ctypes.byref(h)) == B.LORA_EINVAL
+    assert lib.lora_pool_create(8, 16, 64, B.LORA_F32, B.LORA_WFMT_INT4, 16, sc, 0,
+                                ctypes.byref(h)) == B.LORA_EUNSUPPORTED
+    assert lib.lora_pool_create(8, 16, 63, B.LORA_BF16, B.LORA_WFMT_INT4, 16, sc, 0,
+                                ctypes.byref(h)) == B.LORA_EINVAL
+    assert lib.lora_pool_create(8, 16, 64, B.LORA_BF16, 7, 16, sc, 0,
+                                ctypes.byref(h)) == B.LORA_EUNSUPPORTED
+    s = _FakeStorage(8, 16, 32)
+    p = B.Pool(s, 16, shuffle_seed=3, weight_format=B.LORA_WFMT_INT4, scales=_FakeStorage(1, 1, 1))
+    ids = p.alloc(20)
+    assert ids.size == 2 and p.num_free() == 6
+    with pytest.raises(B.LoraError) as e:   # a quantized pool needs the rows' scales
+        p.write_rows(ids, _FakeStorage(20, 1, 32), stream=types.SimpleNamespace(cuda_stream=0))
+    assert e.value.status == B.LORA_EINVAL
+    p.free(ids)
+    assert p.num_free() == 8
+
+
 # ------------------------------------------------------------------ ABI errors
 def _desc(**kw):
     base = dict(dtype=1, d_in=64, d_out=64, num_adapters=2, r_max=16, page_rows=16, max_pages=1,
-                num_pages_a=2, num_pages_b=2, reserved=0, a_pages=16, b_pages=16, rank=16,
-                a_page_table=None, b_page_table=None, host_rank=None)
+                num_pages_a=2, num_pages_b=2, weight_format=0, a_pages=16, b_pages=16, rank=16,
+                a_page_table=None, b_page_table=None, host_rank=None, a_scales=None,
+                b_scales=None)
     base.update(kw)
     return B.lora_weights(*[base[f] for f, _ in B.lora_weights._fields_])
 
@@ -263,7 +292,12 @@ def _desc(**kw):
     (dict(a_pages=None), B.LORA_EINVAL),
     (dict(a_pages=18), B.LORA_EINVAL),            # misaligned
     (dict(page_rows=8), B.LORA_EINVAL),           # dense stack needs page_rows >= r_max
-    (dict(reserved=1), B.LORA_EINVAL),
+    (dict(weight_format=3), B.LORA_EUNSUPPORTED),
+    (dict(weight_format=-1), B.LORA_EUNSUPPORTED),
+    (dict(weight_format=1, dtype=0, a_scales=16, b_scales=16), B.LORA_EUNSUPPORTED),  # fp32 + FP8
+    (dict(weight_format=1), B.LORA_EINVAL),                                 # no row scales
+    (dict(weight_format=2, a_scales=16), B.LORA_EINVAL),                    # one scale array
+    (dict(weight_format=2, a_scales=18, b_scales=16), B.LORA_EINVAL),       # misaligned scales
     (dict(a_page_table=64), B.LORA_EINVAL),       # one table without the other
 ])
 def test_weight_validation_errors(kw, status):

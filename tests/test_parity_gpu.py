@@ -75,8 +75,7 @@ def check_y(dp, y_gpu, want, label):
 
 def check_v(dp, v_gpu, label):
     p = dp.p
-    ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
-    want = oracle.shrink(p.x, p.ids, ad, dp.r_max)
+    want = oracle.shrink(p.x, p.ids, oracle_adapters(p), dp.r_max)
     got = v_gpu.cpu().numpy().astype(np.float64)
     rows = p.ids >= 0
     mask = np.zeros_like(got, dtype=bool)
@@ -88,8 +87,15 @@ def check_v(dp, v_gpu, label):
     assert err <= V_TOL[p.dtype], f"{label}: v {err}"
 
 
+def oracle_adapters(p):
+    """The problem's adapters in fp64 (quantized rows dequantized exactly)."""
+    if p.wq:
+        return oracle.Adapters.from_quantized(p.wq, p.a_rows, p.a_scales, p.bt_rows, p.bt_scales)
+    return oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
+
+
 def oracle_y(p):
-    return oracle.apply(p.x, p.y, p.ids, oracle.Adapters.from_stacks(p.a_rows, p.bt_rows))
+    return oracle.apply(p.x, p.y, p.ids, oracle_adapters(p))
 
 
 POLICIES = [("auto", B.LORA_PATH_AUTO), ("gather", B.LORA_PATH_GATHER), ("mfma", B.LORA_PATH_MFMA)]
@@ -340,3 +346,74 @@ def test_adapter_serial_comparator_matches_one_launch():
     torch.cuda.synchronize()
     assert torch.equal(v1, v2)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ quantized adapter rows
+WQ = ["fp8", "int4"]
+
+
+@pytest.mark.parametrize("layout", ["dense", "paged"])
+@pytest.mark.parametrize("name,policy", POLICIES)
+@pytest.mark.parametrize("wq", WQ)
+def test_quant_sgmv_mixed(wq, name, policy, layout):
+    """FP8 E4M3 / INT4 rows with per-row scales on both SGMV paths, dense and
+    paged, against the oracle on the exactly dequantized rows."""
+    R = runner()
+    p = wl.quant_mixed(wq, paged=layout == "paged")
+    say(f"quant sgmv {wq} policy={name} layout={layout}")
+    dp = R.DeviceProblem(p)
+    y, v = dp.run_sgmv(policy)
+    torch.cuda.synchronize()
+    check_v(dp, v, f"quant/{wq}/{name}/{layout}")
+    check_y(dp, y, oracle_y(p), f"quant/{wq}/{name}/{layout}")
+
+
+@pytest.mark.parametrize("wq", WQ)
+def test_quant_bgmv_mixed(wq):
+    """Per-token paths (two-launch in both orders, fused in both orders) on the
+    mixed quantized batch, paged."""
+    R = runner()
+    p = wl.quant_mixed(wq, paged=True)
+    dp = R.DeviceProblem(p)
+    want = oracle_y(p)
+    for label, run in [("bgmv-tm", lambda: dp.run_bgmv(B.LORA_BGMV_TOKEN_MAJOR)),
+                       ("bgmv-am", lambda: dp.run_bgmv(B.LORA_BGMV_ADAPTER_MAJOR)),
+                       ("fused-tm", lambda: dp.run_bgmv_fused(B.LORA_BGMV_TOKEN_MAJOR)),
+                       ("fused-am", lambda: dp.run_bgmv_fused(B.LORA_BGMV_ADAPTER_MAJOR))]:
+        say(f"quant bgmv {wq} {label}")
+        y, v = run()
+        torch.cuda.synchronize()
+        check_v(dp, v, f"quant/{wq}/{label}")
+        check_y(dp, y, want, f"quant/{wq}/{label}")
+
+
+@pytest.mark.parametrize("wq", WQ)
+def test_quant_bgmv_decode_full_size(wq):
+    """The decode batch (256 tokens, 128 rank-16 adapters, 4096 -> 4096) with
+    quantized rows: fused (the default decode path) and two-launch."""
+    R = runner()
+    p = wl.bgmv_decode(wq=wq)
+    say(f"quant bgmv decode full size {wq}")
+    dp = R.DeviceProblem(p)
+    want = oracle_y(p)
+    y, v = dp.run_bgmv_fused()
+    y2, v2 = dp.run_bgmv()
+    torch.cuda.synchronize()
+    check_v(dp, v, f"quant-decode/{wq}/fused")
+    check_y(dp, y, want, f"quant-decode/{wq}/fused")
+    check_v(dp, v2, f"quant-decode/{wq}/two")
+    check_y(dp, y2, want, f"quant-decode/{wq}/two")
+
+
+@pytest.mark.parametrize("wq", WQ)
+def test_quant_hetero_paged_full_size(wq):
+    """The heterogeneous paged batch (4096 tokens, 64 requests, ranks 8..64,
+    8192 -> 8192) with quantized rows, one launch per phase."""
+    R = runner()
+    p = wl.hetero_paged(wq=wq)
+    say(f"quant hetero paged full size {wq}")
+    dp = R.DeviceProblem(p)
+    y, v = dp.run_sgmv()
+    torch.cuda.synchronize()
+    check_v(dp, v, f"quant-hetero/{wq}")
+    check_y(dp, y, oracle_y(p), f"quant-hetero/{wq}")
