@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--order", type=int, default=0, help="BGMV order (0 auto, 1 token, 2 adapter)")
     ap.add_argument("--path", choices=("fused", "two"), default="fused",
                     help="per-token (decode) step: one fused launch, or shrink + expand launches")
+    ap.add_argument("--placement", choices=("grouped", "index"), default="grouped",
+                    help="fused decode: workgroups take tokens in the batch's segment order "
+                         "(host-built once per batch, shared by all layers) or in index order")
     ap.add_argument("--policy", type=int, default=0, help="SGMV path policy (0 auto, 1 gather, 2 mfma)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU time (0 disables the CPU baseline)")
@@ -341,7 +344,9 @@ def main():
         y, v = dp.y0.clone(), dp.new_v()
         if mode == "bgmv":
             sh, ex = B.prepare_bgmv(dp.weights, dp.ids, dp.x, v, y, args.order, stream=stream)
-            fu = B.prepare_bgmv_fused(dp.weights, dp.ids, dp.x, y, None, args.order, stream=stream)
+            tord = dp.segments()[3] if args.placement == "grouped" else None
+            fu = B.prepare_bgmv_fused(dp.weights, dp.ids, dp.x, y, None, args.order, stream=stream,
+                                      token_order=tord)
             calls.append((sh, ex, fu))
         else:
             _, _, _, perm_d = dp.segments()
@@ -426,6 +431,7 @@ def main():
                    "ranks": sorted(set(int(r) for r in p.ranks)), "d_in": p.d_in, "d_out": p.d_out,
                    "adapter_rows": p.wq or p.dtype,
                    "mode": mode, "path": ("fused" if fused else "shrink+expand"),
+                   "placement": (args.placement if fused else None),
                    "replicas": n_rep, "timed": "HIP graph replay of the K steps",
                    "parallelism": "single GPU"},
         "roofline": roofline,

@@ -279,15 +279,27 @@ lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *token_adapter
  * arithmetic as lora_bgmv_shrink + lora_bgmv_expand (fp32 v, one rounding of
  * y); v [num_tokens, r_max] receives the rank-space values when non-NULL.
  * The fused and two-launch paths sum in different orders, so their results
- * agree to rounding, not bit for bit; the fused path's two orders give
- * identical bits.  token_adapter, x, y as for lora_bgmv_shrink/expand.
+ * agree to rounding, not bit for bit; the fused path's orders and placements
+ * all give identical bits.  token_adapter, x, y as for lora_bgmv_shrink/expand.
+ *   token_order [num_ordered]  device, or NULL.  Token-major order only: the
+ *          tokens to process, in placement order (each an index in
+ *          [0, num_tokens); others are skipped; tokens not listed keep their y).
+ *          Consecutive entries run on the same XCD and share its L2, so an
+ *          order that groups the tokens of each adapter -- the token_perm of
+ *          lora_segments_build, built once per batch on the host and reused by
+ *          every layer, like a plan -- reads each adapter's rows from memory
+ *          about once instead of once per token.  NULL: every token, in index
+ *          order (no host step; adapter ids stay on the device).
  *   order  LORA_BGMV_TOKEN_MAJOR (and LORA_BGMV_AUTO): one workgroup per
  *          token and column block;
  *          LORA_BGMV_ADAPTER_MAJOR: one workgroup per adapter and column block,
  *          finding its tokens by scanning token_adapter and processing them
- *          four at a time (for few tokens per adapter).                     */
+ *          four at a time (for few tokens per adapter); token_order ignored.
+ * Errors as for lora_bgmv_shrink, and LORA_EINVAL for num_ordered outside
+ * 0..num_tokens with a token_order.                                        */
 lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
-                            int32_t num_tokens, int32_t order, const void *x, float *v,
+                            int32_t num_tokens, const int32_t *token_order,
+                            int32_t num_ordered, int32_t order, const void *x, float *v,
                             void *y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */

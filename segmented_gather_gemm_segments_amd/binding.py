@@ -67,7 +67,7 @@ EXPORTS = {
     "lora_sgmv_expand": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_expand": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
-    "lora_bgmv_fused": ([_P, _P, _I32, _I32, _P, _P, _P, _P], _I32),
+    "lora_bgmv_fused": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P], _I32),
     "lora_pool_create": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P], _I32),
     "lora_pool_alloc": ([_P, _I32, _P], _I32),
     "lora_pool_free": ([_P, _P, _I32], _I32),
@@ -242,10 +242,14 @@ def lora_bgmv_expand(w: Weights, token_adapter, v, y, order: int = LORA_BGMV_AUT
 
 
 def lora_bgmv_fused(w: Weights, token_adapter, x, y, v=None, order: int = LORA_BGMV_AUTO,
-                    stream=None):
+                    stream=None, token_order=None):
+    """token_order: optional device int32 placement order (e.g. the segment
+    permutation of the batch)."""
     d = w.desc()
+    n_ord = 0 if token_order is None else int(token_order.numel())
     _check(lib().lora_bgmv_fused(ctypes.byref(d), _dptr(token_adapter), int(token_adapter.numel()),
-                                 order, _dptr(x), _dptr(v), _dptr(y), _stream(stream)))
+                                 _dptr(token_order), n_ord, order, _dptr(x), _dptr(v), _dptr(y),
+                                 _stream(stream)))
 
 
 def lora_base_gemm(x, w, y, stream=None):
@@ -364,10 +368,11 @@ def prepare_base_gemm(x, w, y, stream=None):
 
 
 def prepare_bgmv_fused(w: Weights, token_adapter, x, y, v=None, order: int = LORA_BGMV_AUTO,
-                       stream=None):
+                       stream=None, token_order=None):
     """Prepared fused BGMV launch (shrink + expand in one kernel) on `stream`."""
     d = w.desc()
-    keep = (d, w, token_adapter, x, v, y)
+    keep = (d, w, token_adapter, x, v, y, token_order)
+    n_ord = 0 if token_order is None else int(token_order.numel())
     return Prepared("lora_bgmv_fused", (ctypes.byref(d), _dptr(token_adapter),
-                                        int(token_adapter.numel()), order, _dptr(x), _dptr(v),
-                                        _dptr(y), _stream(stream)), keep)
+                                        int(token_adapter.numel()), _dptr(token_order), n_ord,
+                                        order, _dptr(x), _dptr(v), _dptr(y), _stream(stream)), keep)

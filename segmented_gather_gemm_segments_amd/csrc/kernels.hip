@@ -107,45 +107,81 @@ __device__ __forceinline__ float b_scale(const DevW &w, int a, int j) {
   return i < 0 ? 0.f : w.b_sc[i];
 }
 
-// Addresses of rows j0 .. j0+15 of adapter a's B^T, offset to element `col`
-// (rows at or past the rank, or on an out-of-range page, get `safe`), and
-// their scales (0 for those rows).  When the 16 rows lie in one page (the
-// usual case: 16-row pages, j0 a multiple of 16) a single page lookup serves
-// them all; a dense stack needs none.
-template <typename W>
-__device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, int col, const char *safe,
-                                         const char *(&rp)[16], float (&sc)[16]) {
+// One side of the adapter storage: A rows or B^T rows.
+struct Side {
+  const char *pages;
+  const int32_t *pt;
+  const float *sc;
+  int64_t row_bytes;
+  int32_t num_pages;
+};
+__device__ __forceinline__ Side side_a(const DevW &w) {
+  return {w.a_pages, w.a_pt, w.a_sc, w.a_row_bytes, w.num_pages_a};
+}
+__device__ __forceinline__ Side side_b(const DevW &w) {
+  return {w.b_pages, w.b_pt, w.b_sc, w.b_row_bytes, w.num_pages_b};
+}
+
+// Branch-free pointer select (a conditional expression on pointers tends to
+// become a branch per row).
+__device__ __forceinline__ const char *sel_ptr(bool c, const char *p, const char *q) {
+  const uintptr_t m = (uintptr_t)0 - (uintptr_t)c;
+  return reinterpret_cast<const char *>((reinterpret_cast<uintptr_t>(p) & m) |
+                                        (reinterpret_cast<uintptr_t>(q) & ~m));
+}
+
+// Addresses of rows j0 .. j0+15 of adapter a on one side, offset to element
+// `col` (rows at or past `r`, or on an out-of-range page, get `safe`), and,
+// when SC, their scales (0 for those rows; 1 for unquantized rows).  When the
+// 16 rows lie in one page (the usual case: 16-row pages, j0 a multiple of 16)
+// a single page lookup serves them all; a dense stack needs none.  AL: the
+// caller guarantees that case (dense rows, or pages of a multiple of 16 rows
+// with j0 a multiple of 16), and the per-row fallback is not compiled.  The
+// scale loads are unconditional (index 0 stands in for rows without one).
+template <typename W, bool SC = true, bool AL = false>
+__device__ __forceinline__ void rows16(const DevW &w, const Side &sd, int a, int j0, int r, int col,
+                                       const char *safe, const char *(&rp)[16], float (&sc)[16]) {
   const int pr = w.page_rows;
   const int64_t cofs = (int64_t)(col >> 3) * WT<W>::kChunk;
-  if (!w.b_pt || (pr >= 16 && j0 % pr + 16 <= pr)) {
+  if (AL || !sd.pt || (pr >= 16 && j0 % pr + 16 <= pr)) {
     int page, r0;
-    if (w.b_pt) {
+    if (sd.pt) {
       const int pi = j0 / pr;
-      page = w.b_pt[(int64_t)a * w.max_pages + (pi < w.max_pages ? pi : w.max_pages - 1)];
-      if (pi >= w.max_pages) page = -1;
+      page = sd.pt[(int64_t)a * w.max_pages + (pi < w.max_pages ? pi : w.max_pages - 1)];
+      page = pi < w.max_pages ? page : -1;
       r0 = j0 - pi * pr;
     } else {
       page = a;
       r0 = j0;
     }
-    const bool ok = (unsigned)page < (unsigned)w.num_pages_b;
+    const bool ok = (unsigned)page < (unsigned)sd.num_pages;
     const int64_t i0 = (int64_t)(ok ? page : 0) * pr + r0;
+    const char *base = sd.pages + i0 * sd.row_bytes + cofs;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool in = ok && j0 + i < r;
-      rp[i] = in ? w.b_pages + (i0 + i) * w.b_row_bytes + cofs : safe;
-      if constexpr (WT<W>::kScaled) sc[i] = in ? w.b_sc[i0 + i] : 0.f;
-      else sc[i] = 1.f;
+      rp[i] = sel_ptr(in, base + i * sd.row_bytes, safe);
+      if constexpr (SC && WT<W>::kScaled) {
+        const float s = sd.sc[in ? i0 + i : 0];
+        sc[i] = in ? s : 0.f;
+      } else {
+        sc[i] = 1.f;
+      }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int64_t idx = j0 + i < r ? row_index(w, w.b_pt, w.num_pages_b, a, j0 + i) : -1;
-      rp[i] = idx >= 0 ? w.b_pages + idx * w.b_row_bytes + cofs : safe;
-      if constexpr (WT<W>::kScaled) sc[i] = idx >= 0 ? w.b_sc[idx] : 0.f;
+      const int64_t idx = j0 + i < r ? row_index(w, sd.pt, sd.num_pages, a, j0 + i) : -1;
+      rp[i] = idx >= 0 ? sd.pages + idx * sd.row_bytes + cofs : safe;
+      if constexpr (SC && WT<W>::kScaled) sc[i] = idx >= 0 ? sd.sc[idx] : 0.f;
       else sc[i] = 1.f;
     }
   }
+}
+template <typename W, bool AL = false>
+__device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, int col, const char *safe,
+                                         const char *(&rp)[16], float (&sc)[16]) {
+  rows16<W, true, AL>(w, side_b(w), a, j0, r, col, safe, rp, sc);
 }
 
 __device__ __forceinline__ int adapter_rank(const DevW &w, int a) {
@@ -1132,51 +1168,105 @@ __global__ __launch_bounds__(NT) void bgmv_expand_kernel(DevW w, const int32_t *
 constexpr int kFusedThreads = 512;
 constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kFusedPass = kFusedThreads * 8;  // d elements per pass of the workgroup
+constexpr int kFusedMinGroups = 256;             // workgroups a launch aims for (one per CU)
 
 struct alignas(16) FusedSmem {
   float red[kFusedWaves * 16];
   float vs[LORA_MAX_RANK];
 };
 
-// Addresses of rows j0 .. j0+15 of adapter a's A (offset k), `safe` past the
-// rank or on an out-of-range page.
-template <typename W>
+// Addresses of rows j0 .. j0+15 of adapter a's A (offset k), `safe` past `r`
+// or on an out-of-range page.
+template <typename W, bool AL = false>
 __device__ __forceinline__ void a_rows16(const DevW &w, int a, int j0, int r, int k, const char *safe,
                                          const char *(&rp)[16]) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const char *p = j0 + i < r ? a_row(w, a, j0 + i) : nullptr;
-    rp[i] = p ? p + wofs<W>(k) : safe;
-  }
+  float unused[16];
+  rows16<W, false, AL>(w, side_a(w), a, j0, r, k, safe, rp, unused);
 }
 
-// One token t (adapter a) of the fused kernel over columns [c_begin, c_end).
-template <typename T, typename W>
-__device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb, int c_begin,
-                                           int c_end, const T *__restrict__ x,
-                                           float *__restrict__ v, T *__restrict__ y,
-                                           FusedSmem &sm) {
-  const int r = adapter_rank(w, a);
+// Scale of row j of adapter a's A, loaded unconditionally (index 0 stands in
+// when `use` is false or the page is out of range; the result is then 0).
+template <typename W>
+__device__ __forceinline__ float a_scale_any(const DevW &w, int a, int j, bool use) {
+  const int64_t i = row_index(w, w.a_pt, w.num_pages_a, a, j);
+  const bool in = use && i >= 0;
+  const float s = w.a_sc[in ? i : 0];
+  return in ? s : 0.f;
+}
+
+// Work unit u = (entry u / nblk of the token order, column block u % nblk):
+// one token's shrink and expand over columns [c_begin, c_end).  Units are
+// placed XCD-aware (consecutive units on one XCD), so when the token order
+// groups the tokens of an adapter (the segment order of the batch) those
+// tokens run on one XCD and read the adapter's rows through its L2 once.  The prologue is arranged so that
+// the whole first pass costs as few dependent round trips as possible: the x
+// and y chunks need only the token and are requested before its adapter id
+// arrives; the first 16 A and B^T rows need only the adapter id and are
+// requested before its rank arrives (rows below min(16, r_max) exist in
+// storage, in a dense stack and, through the page table, in a pool; rows at or
+// past the rank are fetched but never used).  Nothing branches on the adapter
+// id or the rank before these loads are consumed -- a token without a valid
+// adapter takes rank 0 and safe addresses, and its first pass runs on them
+// with every store suppressed -- so the compiler cannot sink the loads past
+// the id or rank wait.
+template <typename T, typename W, bool AL>
+__global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const int32_t *__restrict__ ids,
+                                                                   int32_t num_tokens,
+                                                                   const int32_t *__restrict__ torder,
+                                                                   int32_t units, int32_t nblk,
+                                                                   int32_t block_cols,
+                                                                   const T *__restrict__ x,
+                                                                   float *__restrict__ v,
+                                                                   T *__restrict__ y) {
+  __shared__ FusedSmem sm;
+  const int u = xcd_logical(blockIdx.x, gridDim.x);
+  const int slot = u / nblk, cb = u - slot * nblk;
+  if (slot >= units) return;
+  const int t = torder ? torder[slot] : slot;
+  if ((unsigned)t >= (unsigned)num_tokens) return;
+  const int c_begin = cb * block_cols, c_end = min(w.d_out, c_begin + block_cols);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T *xr = x + (int64_t)t * w.d_in;
   T *yr = y + (int64_t)t * w.d_out;
-  const char *safe_a = reinterpret_cast<const char *>(x), *safe_b = w.b_pages;
 
-  // ---- first expand pass: y chunk and B^T rows 0..15, issued up front
+  // ---- token-only loads: first x chunk and first y chunk
+  const int kc0 = tid * 8 < w.d_in ? tid * 8 : 0;
   const int col0 = c_begin + tid * 8;
-  const bool cin0 = col0 < c_end;
-  const int colc0 = cin0 ? col0 : c_begin;
-  Raw8<T> y0;
+  const int colc0 = col0 < c_end ? col0 : c_begin;
+  Raw8<T> x0, y0;
+  raw_load(x0, xr + kc0);
   raw_load(y0, yr + colc0);
-  const char *bp0[16];
-  float bsc0[16];
-  b_rows16<W>(w, a, 0, r, colc0, safe_b, bp0, bsc0);
-  Raw8<W> b0[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) wload(b0[i], bp0[i]);
 
-  // ---- shrink: v[j] = sum_k A[j][k] x[k], 16 rows at a time
-  for (int jc = 0; jc < r; jc += 16) {
+  const int a_id = ids[t];
+  const bool valid = a_id >= 0 && a_id < w.num_adapters;
+  const int a = valid ? a_id : 0;
+
+  // ---- adapter-only loads: A and B^T rows 0 .. rs-1 (and their scales);
+  // not for fp32 rows, whose 32 chunks would not fit in registers
+  constexpr bool PF = WT<W>::kChunk <= 16;
+  const int rs = valid ? min(16, w.r_max) : 0;
+  const char *safe_a = reinterpret_cast<const char *>(x), *safe_b = w.b_pages;
+  Raw8<W> a0[16], b0[16];
+  float bsc0[16];
+  if constexpr (PF) {
+    const char *ap0[16], *bp0[16];
+    a_rows16<W, AL>(w, a, 0, rs, kc0, safe_a, ap0);
+    b_rows16<W, AL>(w, a, 0, rs, colc0, safe_b, bp0, bsc0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wload(a0[i], ap0[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wload(b0[i], bp0[i]);
+  }
+  float asc = 1.f;  // scale of A row jc + tid (threads 0..15)
+  if constexpr (WT<W>::kScaled) asc = a_scale_any<W>(w, a, tid, tid < rs);
+
+  const int r = valid ? adapter_rank(w, a) : 0;
+
+  // ---- shrink: v[j] = sum_k A[j][k] x[k], 16 rows at a time (the first
+  // 16 always, see above)
+  for (int jc = 0; jc == 0 || jc < r; jc += 16) {
+    if constexpr (WT<W>::kScaled)
+      if (jc > 0) asc = a_scale_any<W>(w, a, jc + tid, tid < 16 && jc + tid < r);
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -1184,13 +1274,19 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
       const int k = k0 + tid * 8;
       const bool kin = k < w.d_in;
       const int kc = kin ? k : 0;
-      const char *ap[16];
-      a_rows16<W>(w, a, jc, r, kc, safe_a, ap);
       Raw8<T> xraw;
       Raw8<W> araw[16];
-      raw_load(xraw, xr + kc);
+      if (jc == 0 && k0 == 0) xraw = x0;
+      else raw_load(xraw, xr + kc);
+      if (PF && jc == 0 && k0 == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
+        for (int i = 0; i < 16; ++i) araw[i] = a0[i];
+      } else {
+        const char *ap[16];
+        a_rows16<W, AL>(w, a, jc, r, kc, safe_a, ap);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
+      }
       if (kin) {
         float xv[8];
         raw_cvt(xraw, xv);
@@ -1204,7 +1300,7 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
       }
     }
     // reduce the 16 row sums over the workgroup: reduce-scatter in each wave,
-    // then the waves in order
+    // then the waves in order (rows at or past the rank are never used)
     const float part = wave_reduce_scatter<16>(acc);
     if ((lane & 3) == 0) sm.red[wave * 16 + (lane >> 2)] = part;
     __syncthreads();
@@ -1212,7 +1308,7 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
       float sum = sm.red[tid];
 #pragma unroll
       for (int wv = 1; wv < kFusedWaves; ++wv) sum += sm.red[wv * 16 + tid];
-      if constexpr (WT<W>::kScaled) sum *= jc + tid < r ? a_scale<W>(w, a, jc + tid) : 0.f;
+      if constexpr (WT<W>::kScaled) sum *= asc;
       sm.vs[jc + tid] = sum;
       if (v && cb == 0 && jc + tid < r) v[(int64_t)t * w.r_max + jc + tid] = sum;
     }
@@ -1230,10 +1326,10 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int j0 = 0; j0 < r; j0 += 16) {
+    for (int j0 = 0; j0 == 0 || j0 < r; j0 += 16) {
       Raw8<W> braw[16];
       float bsc[16];
-      if (c0 == c_begin && j0 == 0) {
+      if (PF && c0 == c_begin && j0 == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           braw[i] = b0[i];
@@ -1241,7 +1337,7 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
         }
       } else {
         const char *bp[16];
-        b_rows16<W>(w, a, j0, r, colc, safe_b, bp, bsc);
+        b_rows16<W, AL>(w, a, j0, r, colc, safe_b, bp, bsc);
 #pragma unroll
         for (int i = 0; i < 16; ++i) wload(braw[i], bp[i]);
       }
@@ -1256,7 +1352,7 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
         }
       }
     }
-    if (cin) {
+    if (cin && r > 0) {
       float yv[8];
       raw_cvt(yraw, yv);
 #pragma unroll
@@ -1264,24 +1360,6 @@ __device__ __forceinline__ void fused_token(const DevW &w, int t, int a, int cb,
       store8(yr + col, yv);
     }
   }
-}
-
-// Work unit u = (token u / nblk, column block u % nblk).
-template <typename T, typename W>
-__global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const int32_t *__restrict__ ids,
-                                                                   int32_t num_tokens, int32_t nblk,
-                                                                   int32_t block_cols,
-                                                                   const T *__restrict__ x,
-                                                                   float *__restrict__ v,
-                                                                   T *__restrict__ y) {
-  __shared__ FusedSmem sm;
-  const int u = blockIdx.x;
-  const int t = u / nblk, cb = u - t * nblk;
-  if (t >= num_tokens) return;
-  const int a = ids[t];
-  if (a < 0 || a >= w.num_adapters) return;
-  const int c_begin = cb * block_cols, c_end = min(w.d_out, c_begin + block_cols);
-  fused_token<T, W>(w, t, a, cb, c_begin, c_end, x, v, y, sm);
 }
 
 // Fused per-token delta, adapter-major: work unit (adapter a, column block
@@ -1650,7 +1728,8 @@ extern "C" lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *to
 }
 
 extern "C" lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
-                                       int32_t num_tokens, int32_t order, const void *x, float *v,
+                                       int32_t num_tokens, const int32_t *token_order,
+                                       int32_t num_ordered, int32_t order, const void *x, float *v,
                                        void *y, hipStream_t stream) {
   DevW d;
   lora_status st = to_dev(w, &d);
@@ -1662,17 +1741,19 @@ extern "C" lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *tok
     return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
   if (order < LORA_BGMV_AUTO || order > LORA_BGMV_ADAPTER_MAJOR)
     return fail(LORA_EINVAL, "unknown order %d", order);
-  // automatic order: token-major (with the sorted placement above it shares
-  // an adapter's rows through L2 without serialising its tokens)
+  if (token_order && (num_ordered < 0 || num_ordered > num_tokens))
+    return fail(LORA_EINVAL, "num_ordered %d outside 0..num_tokens", num_ordered);
+  // automatic order: token-major
   const bool am = order == LORA_BGMV_ADAPTER_MAJOR;
-  const int units = am ? w->num_adapters : num_tokens;
+  const int units = am ? w->num_adapters : (token_order ? num_ordered : num_tokens);
+  if (units == 0) return ok();
   // enough column blocks that the launch has at least ~256 workgroups, one
   // per compute unit: token-major blocks are whole 4096-column passes of the
   // 512 threads; adapter-major blocks are 2048 columns (an adapter-major unit
   // already repeats its shrink per block, so finer blocks add parallelism)
   const int pass = am ? kFusedPass / 2 : kFusedPass;
   const int passes = (w->d_out + pass - 1) / pass;
-  int nblk = (256 + units - 1) / units;
+  int nblk = (kFusedMinGroups + units - 1) / units;
   nblk = nblk < 1 ? 1 : (nblk > passes ? passes : nblk);
   const int block_cols = ((passes + nblk - 1) / nblk) * pass;
   nblk = (w->d_out + block_cols - 1) / block_cols;
@@ -1687,12 +1768,20 @@ extern "C" lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *tok
     });
     return check_launch("bgmv fused launch");
   }
-  const dim3 grid(num_tokens * nblk);
+  const dim3 grid(pad8(units * nblk));
+  // 16-row groups never straddle a page: dense rows, or whole multiples of 16
+  const bool aligned = !w->a_page_table || w->page_rows % 16 == 0;
   with_types(w, [&](auto t, auto wt) {
     using T = decltype(t);
     using W = decltype(wt);
-    hipLaunchKernelGGL((bgmv_fused_kernel<T, W>), grid, dim3(kFusedThreads), 0, stream, d,
-                       token_adapter, num_tokens, nblk, block_cols, (const T *)x, v, (T *)y);
+    if (aligned)
+      hipLaunchKernelGGL((bgmv_fused_kernel<T, W, true>), grid, dim3(kFusedThreads), 0, stream, d,
+                         token_adapter, num_tokens, token_order, units, nblk, block_cols,
+                         (const T *)x, v, (T *)y);
+    else
+      hipLaunchKernelGGL((bgmv_fused_kernel<T, W, false>), grid, dim3(kFusedThreads), 0, stream, d,
+                         token_adapter, num_tokens, token_order, units, nblk, block_cols,
+                         (const T *)x, v, (T *)y);
   });
   return check_launch("bgmv fused launch");
 }

@@ -208,11 +208,16 @@ class DeviceProblem:
         B.lora_bgmv_expand(self.weights, self.ids, v, y, order)
         return y, v
 
-    def run_bgmv_fused(self, order: int = B.LORA_BGMV_AUTO, y=None, v=None):
-        """Fused per-token delta (one launch); returns (y, v)."""
+    def run_bgmv_fused(self, order: int = B.LORA_BGMV_AUTO, y=None, v=None, grouped: bool = False,
+                       token_order=None):
+        """Fused per-token delta (one launch); returns (y, v).  grouped: place
+        the tokens in the batch's segment order (tokens of an adapter together);
+        token_order: an explicit device placement order instead."""
         y = self.y0.clone() if y is None else y
         v = self.new_v() if v is None else v
-        B.lora_bgmv_fused(self.weights, self.ids, self.x, y, v, order)
+        if grouped:
+            token_order = self.segments()[3]
+        B.lora_bgmv_fused(self.weights, self.ids, self.x, y, v, order, token_order=token_order)
         return y, v
 
     def run_base(self, y=None):

@@ -320,10 +320,14 @@ def test_empty_batches_are_noops():
     assert lib.lora_sgmv_shrink(ctypes.byref(d), None, 0, None, 0, 0, None, None, None) == B.LORA_OK
     assert lib.lora_sgmv_expand(ctypes.byref(d), 16, 4, 16, 0, 8, 16, 16, None) == B.LORA_OK
     assert lib.lora_bgmv_shrink(ctypes.byref(d), None, 0, 0, None, None, None) == B.LORA_OK
-    assert lib.lora_bgmv_fused(ctypes.byref(d), None, 0, 0, None, None, None, None) == B.LORA_OK
-    assert lib.lora_bgmv_fused(ctypes.byref(d), 16, 1, 0, None, None, 16, None) == B.LORA_EINVAL
-    assert lib.lora_bgmv_fused(ctypes.byref(d), 16, 1, 0, 16, 20, 16, None) == B.LORA_EINVAL  # misaligned v
-    assert lib.lora_bgmv_fused(ctypes.byref(d), 16, -1, 0, 16, None, 16, None) == B.LORA_EINVAL
-    assert lib.lora_bgmv_fused(ctypes.byref(d), 16, 1, 7, 16, None, 16, None) == B.LORA_EINVAL  # order
+    fused = lib.lora_bgmv_fused
+    assert fused(ctypes.byref(d), None, 0, None, 0, 0, None, None, None, None) == B.LORA_OK
+    assert fused(ctypes.byref(d), 16, 1, None, 0, 0, None, None, 16, None) == B.LORA_EINVAL
+    assert fused(ctypes.byref(d), 16, 1, None, 0, 0, 16, 20, 16, None) == B.LORA_EINVAL  # misaligned v
+    assert fused(ctypes.byref(d), 16, -1, None, 0, 0, 16, None, 16, None) == B.LORA_EINVAL
+    assert fused(ctypes.byref(d), 16, 1, None, 0, 7, 16, None, 16, None) == B.LORA_EINVAL  # order
+    assert fused(ctypes.byref(d), 16, 4, 16, 5, 0, 16, None, 16, None) == B.LORA_EINVAL  # order too long
+    assert fused(ctypes.byref(d), 16, 4, 16, -1, 0, 16, None, 16, None) == B.LORA_EINVAL
+    assert fused(ctypes.byref(d), 16, 4, 16, 0, 0, 16, None, 16, None) == B.LORA_OK      # empty order
     assert lib.lora_bgmv_expand(ctypes.byref(d), 16, 1, 9, 16, 16, None) == B.LORA_EINVAL  # bad order
     assert lib.lora_sgmv_shrink(ctypes.byref(d), None, 4, 16, 2, 8, 16, 16, None) == B.LORA_EINVAL

@@ -147,6 +147,34 @@ def test_bgmv_fused_decode_full_size():
     assert normwise(host_y(dp, y), host_y(dp, y2)) <= 2e-2
 
 
+def test_bgmv_fused_token_order():
+    """Placement order of the fused kernel: the segment order (tokens of an
+    adapter together) and an arbitrary partial order give the same bits for
+    every listed token as index order; unlisted and out-of-range entries are
+    skipped (y unchanged)."""
+    R = runner()
+    p = wl.bgmv_decode()
+    say("bgmv fused token order")
+    dp = R.DeviceProblem(p)
+    y0, v0 = dp.run_bgmv_fused()
+    yg, vg = dp.run_bgmv_fused(grouped=True)
+    rng = np.random.default_rng(7)
+    listed = rng.permutation(p.num_tokens)[: p.num_tokens // 2]
+    order = np.concatenate([listed, [-1, p.num_tokens, 10**6]]).astype(np.int32)
+    rng.shuffle(order)
+    yp, vp = dp.run_bgmv_fused(token_order=torch.from_numpy(order).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), yg.view(torch.int16))
+    assert torch.equal(v0, vg)
+    lt = torch.from_numpy(np.sort(listed)).cuda()
+    unl = np.setdiff1d(np.arange(p.num_tokens), listed)
+    ut = torch.from_numpy(unl).cuda()
+    assert torch.equal(yp[lt].view(torch.int16), y0[lt].view(torch.int16))
+    assert torch.equal(vp[lt], v0[lt])
+    assert torch.equal(yp[ut].view(torch.int16), dp.y0[ut].view(torch.int16))
+    check_y(dp, yg, oracle_y(p), "fused grouped")
+
+
 def test_bgmv_orders_and_sgmv_gather_bit_identical():
     """Per-token results do not depend on grouping: token-major, adapter-major
     and the segmented gather path give the same bits."""
