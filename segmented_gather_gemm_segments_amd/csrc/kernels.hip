@@ -132,17 +132,21 @@ __device__ __forceinline__ const char *sel_ptr(bool c, const char *p, const char
 
 // Addresses of rows j0 .. j0+15 of adapter a on one side, offset to element
 // `col` (rows at or past `r`, or on an out-of-range page, get `safe`), and,
-// when SC, their scales (0 for those rows; 1 for unquantized rows).  When the
-// 16 rows lie in one page (the usual case: 16-row pages, j0 a multiple of 16)
-// a single page lookup serves them all; a dense stack needs none.  AL: the
+// when SC, the lane scale `lsc`: lane l holds the scale of row j0 + (l & 15)
+// (0 for rows without one; 1 for unquantized rows), read back per row with
+// row_sc -- one vector load for the 16 scales instead of 16 dependent scalar
+// loads.  Lanes 0..15 of the wave must all execute this call.  When the 16
+// rows lie in one page (the usual case: 16-row pages, j0 a multiple of 16) a
+// single page lookup serves them all; a dense stack needs none.  AL: the
 // caller guarantees that case (dense rows, or pages of a multiple of 16 rows
 // with j0 a multiple of 16), and the per-row fallback is not compiled.  The
-// scale loads are unconditional (index 0 stands in for rows without one).
+// scale load is unconditional (index 0 stands in for rows without one).
 template <typename W, bool SC = true, bool AL = false>
 __device__ __forceinline__ void rows16(const DevW &w, const Side &sd, int a, int j0, int r, int col,
-                                       const char *safe, const char *(&rp)[16], float (&sc)[16]) {
+                                       const char *safe, const char *(&rp)[16], float &lsc) {
   const int pr = w.page_rows;
   const int64_t cofs = (int64_t)(col >> 3) * WT<W>::kChunk;
+  const int li = threadIdx.x & 15;
   if (AL || !sd.pt || (pr >= 16 && j0 % pr + 16 <= pr)) {
     int page, r0;
     if (sd.pt) {
@@ -158,30 +162,39 @@ __device__ __forceinline__ void rows16(const DevW &w, const Side &sd, int a, int
     const int64_t i0 = (int64_t)(ok ? page : 0) * pr + r0;
     const char *base = sd.pages + i0 * sd.row_bytes + cofs;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool in = ok && j0 + i < r;
-      rp[i] = sel_ptr(in, base + i * sd.row_bytes, safe);
-      if constexpr (SC && WT<W>::kScaled) {
-        const float s = sd.sc[in ? i0 + i : 0];
-        sc[i] = in ? s : 0.f;
-      } else {
-        sc[i] = 1.f;
-      }
+    for (int i = 0; i < 16; ++i) rp[i] = sel_ptr(ok && j0 + i < r, base + i * sd.row_bytes, safe);
+    if constexpr (SC && WT<W>::kScaled) {
+      const bool in = ok && j0 + li < r;
+      const float s = sd.sc[in ? i0 + li : 0];
+      lsc = in ? s : 0.f;
+    } else {
+      lsc = 1.f;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t idx = j0 + i < r ? row_index(w, sd.pt, sd.num_pages, a, j0 + i) : -1;
       rp[i] = idx >= 0 ? sd.pages + idx * sd.row_bytes + cofs : safe;
-      if constexpr (SC && WT<W>::kScaled) sc[i] = idx >= 0 ? sd.sc[idx] : 0.f;
-      else sc[i] = 1.f;
+    }
+    if constexpr (SC && WT<W>::kScaled) {
+      const int64_t idx = j0 + li < r ? row_index(w, sd.pt, sd.num_pages, a, j0 + li) : -1;
+      const float s = sd.sc[idx >= 0 ? idx : 0];
+      lsc = idx >= 0 ? s : 0.f;
+    } else {
+      lsc = 1.f;
     }
   }
 }
+// Scale of row j0 + i from a lane scale of rows16 (i uniform, 0..15).
+template <typename W>
+__device__ __forceinline__ float row_sc(float lsc, int i) {
+  if constexpr (!WT<W>::kScaled) return 1.f;
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsc), i));
+}
 template <typename W, bool AL = false>
 __device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, int col, const char *safe,
-                                         const char *(&rp)[16], float (&sc)[16]) {
-  rows16<W, true, AL>(w, side_b(w), a, j0, r, col, safe, rp, sc);
+                                         const char *(&rp)[16], float &lsc) {
+  rows16<W, true, AL>(w, side_b(w), a, j0, r, col, safe, rp, lsc);
 }
 
 __device__ __forceinline__ int adapter_rank(const DevW &w, int a) {
@@ -688,8 +701,11 @@ template <typename T, typename W, int TG, int NT>
 __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, int cb, const int *toks, int g0,
                                  int ntok, int num_tokens, const float *__restrict__ v,
                                  T *__restrict__ y) {
-  const int col = (cb * NT + (int)threadIdx.x) * 8;
-  if (col >= w.d_out) return;
+  // columns past d_out compute on column 0 and store nothing (the whole wave
+  // stays active: rows16's lane scales need lanes 0..15)
+  const int col_t = (cb * NT + (int)threadIdx.x) * 8;
+  const bool cin = col_t < w.d_out;
+  const int col = cin ? col_t : 0;
   int tk[TG];
 #pragma unroll
   for (int t = 0; t < TG; ++t) {
@@ -712,8 +728,8 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
     // all 16 row addresses first (their page lookups in flight together), then
     // all 16 row loads
     const char *rp[16];
-    float bsc[16];
-    b_rows16<W>(w, a, j0, r, col, safe, rp, bsc);
+    float lsc;
+    b_rows16<W>(w, a, j0, r, col, safe, rp, lsc);
     Raw8<W> braw[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) wload(braw[i], rp[i]);
@@ -743,7 +759,7 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
     for (int t = 0; t < TG; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        vj[t][i] = (tk[t] >= 0 && j0 + i < r) ? (WT<W>::kScaled ? vj[t][i] * bsc[i] : vj[t][i]) : 0.f;
+        vj[t][i] = (tk[t] >= 0 && j0 + i < r) ? (WT<W>::kScaled ? vj[t][i] * row_sc<W>(lsc, i) : vj[t][i]) : 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (j0 + i < r) {
@@ -758,7 +774,7 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
   }
 #pragma unroll
   for (int t = 0; t < TG; ++t) {
-    if (tk[t] >= 0) {
+    if (cin && tk[t] >= 0) {
       float yv[8];
       raw_cvt(yraw[t], yv);
 #pragma unroll
@@ -1180,8 +1196,14 @@ struct alignas(16) FusedSmem {
 template <typename W, bool AL = false>
 __device__ __forceinline__ void a_rows16(const DevW &w, int a, int j0, int r, int k, const char *safe,
                                          const char *(&rp)[16]) {
-  float unused[16];
+  float unused;
   rows16<W, false, AL>(w, side_a(w), a, j0, r, k, safe, rp, unused);
+}
+// As a_rows16, with the lane scale of the 16 A rows (see rows16).
+template <typename W, bool AL = false>
+__device__ __forceinline__ void a_rows16_sc(const DevW &w, int a, int j0, int r, int k, const char *safe,
+                                            const char *(&rp)[16], float &lsc) {
+  rows16<W, true, AL>(w, side_a(w), a, j0, r, k, safe, rp, lsc);
 }
 
 // Scale of row j of adapter a's A, loaded unconditionally (index 0 stands in
@@ -1247,18 +1269,19 @@ __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const
   const int rs = valid ? min(16, w.r_max) : 0;
   const char *safe_a = reinterpret_cast<const char *>(x), *safe_b = w.b_pages;
   Raw8<W> a0[16], b0[16];
-  float bsc0[16];
+  float lsc_b0 = 1.f;
+  float asc = 1.f;  // scale of A row jc + tid (threads 0..15: lane == tid)
   if constexpr (PF) {
     const char *ap0[16], *bp0[16];
-    a_rows16<W, AL>(w, a, 0, rs, kc0, safe_a, ap0);
-    b_rows16<W, AL>(w, a, 0, rs, colc0, safe_b, bp0, bsc0);
+    a_rows16_sc<W, AL>(w, a, 0, rs, kc0, safe_a, ap0, asc);
+    b_rows16<W, AL>(w, a, 0, rs, colc0, safe_b, bp0, lsc_b0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) wload(a0[i], ap0[i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) wload(b0[i], bp0[i]);
+  } else if constexpr (WT<W>::kScaled) {
+    asc = a_scale_any<W>(w, a, tid, tid < rs);
   }
-  float asc = 1.f;  // scale of A row jc + tid (threads 0..15)
-  if constexpr (WT<W>::kScaled) asc = a_scale_any<W>(w, a, tid, tid < rs);
 
   const int r = valid ? adapter_rank(w, a) : 0;
 
@@ -1328,23 +1351,21 @@ __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int j0 = 0; j0 == 0 || j0 < r; j0 += 16) {
       Raw8<W> braw[16];
-      float bsc[16];
+      float lsc;
       if (PF && c0 == c_begin && j0 == 0) {
+        lsc = lsc_b0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          braw[i] = b0[i];
-          bsc[i] = bsc0[i];
-        }
+        for (int i = 0; i < 16; ++i) braw[i] = b0[i];
       } else {
         const char *bp[16];
-        b_rows16<W, AL>(w, a, j0, r, colc, safe_b, bp, bsc);
+        b_rows16<W, AL>(w, a, j0, r, colc, safe_b, bp, lsc);
 #pragma unroll
         for (int i = 0; i < 16; ++i) wload(braw[i], bp[i]);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (j0 + i < r) {
-          const float vj = WT<W>::kScaled ? sm.vs[j0 + i] * bsc[i] : sm.vs[j0 + i];
+          const float vj = WT<W>::kScaled ? sm.vs[j0 + i] * row_sc<W>(lsc, i) : sm.vs[j0 + i];
           float bv[8];
           raw_cvt(braw[i], bv);
 #pragma unroll
@@ -1451,8 +1472,8 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
       for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
     for (int j0 = 0; j0 < r; j0 += 16) {
       const char *bp[16];
-      float bsc[16];
-      b_rows16<W>(w, a, j0, r, colc, safe_b, bp, bsc);
+      float lsc;
+      b_rows16<W>(w, a, j0, r, colc, safe_b, bp, lsc);
       Raw8<W> braw[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) wload(braw[i], bp[i]);
@@ -1463,7 +1484,7 @@ __device__ __forceinline__ void fused_am_group(const DevW &w, int a, int r, int 
           raw_cvt(braw[i], bv);
 #pragma unroll
           for (int t = 0; t < TG; ++t) {
-            const float vj = WT<W>::kScaled ? sm.vs[t][j0 + i] * bsc[i] : sm.vs[t][j0 + i];
+            const float vj = WT<W>::kScaled ? sm.vs[t][j0 + i] * row_sc<W>(lsc, i) : sm.vs[t][j0 + i];
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(vj, bv[e], acc[t][e]);
           }
