@@ -413,8 +413,13 @@ __device__ __forceinline__ T w_as_t(const Raw8<W> &r, int e) {
 }
 
 // Byte offset of element k (a multiple of 8) within a weight row.
+// (k * bytes-per-element with a compile-time factor, so that offsets of
+// unrolled steps fold into the load instructions' immediates)
 template <typename W>
-__device__ __forceinline__ int64_t wofs(int k) { return (int64_t)(k >> 3) * WT<W>::kChunk; }
+__device__ __forceinline__ int wofs(int k) {
+  if constexpr (WT<W>::kChunk >= 8) return k * (WT<W>::kChunk / 8);
+  else return k >> 1;  // INT4: two elements per byte (k is a multiple of 8)
+}
 
 // MFMA A-operand fragment (8 consecutive k of one weight row) from a byte
 // address: loaded as is for bf16 / fp32 rows, converted exactly to bf16 for
