@@ -682,11 +682,18 @@ __device__ __forceinline__ void shrink_mfma(const DevW &w, int a, int r, const i
 }
 
 // ----------------------------------------------------------------- expand cores
+// The MFMA expand stages the rank dimension kExpandK indices at a time, so the
+// LDS of a workgroup (about 31 KiB) lets several workgroups share a CU.
+#ifndef LORA_EXPAND_K
+#define LORA_EXPAND_K 32
+#endif
+constexpr int kExpandK = LORA_EXPAND_K;
+static_assert(kExpandK % 16 == 0 && kExpandK <= 64, "rank chunk: 16, 32, 48 or 64");
 template <typename T> struct ExpandCfg;
-template <> struct ExpandCfg<uint16_t> { static constexpr int kRowStride = 72; };  // 64 j + pad
-template <> struct ExpandCfg<float> { static constexpr int kRowStride = 68; };
+template <> struct ExpandCfg<uint16_t> { static constexpr int kRowStride = kExpandK + 8; };  // j + pad
+template <> struct ExpandCfg<float> { static constexpr int kRowStride = kExpandK + 4; };
 
-constexpr int kVStride = 68;  // LDS row stride (floats) of the staged v rows: 64 j + pad
+constexpr int kVStride = kExpandK + 4;  // LDS row stride (floats) of the staged v rows: j + pad
 
 template <typename T>
 struct alignas(16) ExpandSmem {
@@ -896,17 +903,18 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int jc = 0; jc < r; jc += 64) {
-      const int nj = min(64, r - jc);
+    for (int jc = 0; jc < r; jc += kExpandK) {
+      const int nj = min(kExpandK, r - jc);
       const int nj16 = (nj + 15) & ~15;
       const int nq = nj16 >> 2;  // float4 groups per staged v row
       __syncthreads();  // previous users of the slab and of the v rows are done
       // v rows of the 64 tokens (issued first), then this wave's B^T rows
       // jc .. jc+nj16; all loads unconditional (safe addresses, zero-selected),
       // so they are in flight together before the first LDS store
-      float4 vq[4];
+      constexpr int kVIt = 64 * (kExpandK / 4) / kThreads;  // float4 groups per thread
+      float4 vq[kVIt];
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
+      for (int it = 0; it < kVIt; ++it) {
         const int idx = tid + kThreads * it;     // (token, float4 group) pairs
         const int ti = idx / nq, q = idx - ti * nq;
         const int i = m0 + ti;
@@ -936,11 +944,11 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
       switch (nj16 >> 3) {
         case 2: stage_slab<T, W, 2>(w, a, jc, nj, c0, bt, lane); break;
         case 4: stage_slab<T, W, 4>(w, a, jc, nj, c0, bt, lane); break;
-        case 6: stage_slab<T, W, 6>(w, a, jc, nj, c0, bt, lane); break;
-        default: stage_slab<T, W, 8>(w, a, jc, nj, c0, bt, lane); break;
+        case 6: if constexpr (kExpandK >= 48) stage_slab<T, W, 6>(w, a, jc, nj, c0, bt, lane); break;
+        default: if constexpr (kExpandK >= 64) stage_slab<T, W, 8>(w, a, jc, nj, c0, bt, lane); break;
       }
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
+      for (int it = 0; it < kVIt; ++it) {
         const int idx = tid + kThreads * it;
         const int ti = idx / nq, q = idx - ti * nq;
         if (ti < 64) *reinterpret_cast<float4 *>(&sm.vs[ti * kVStride + 4 * q]) = vq[it];
@@ -1058,7 +1066,10 @@ __global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *
 }
 
 template <typename T, typename W>
-__global__ __launch_bounds__(kThreads) void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
+// bf16 activations: registers bounded so that three waves share a SIMD (three
+// workgroups per CU; the staged rank chunk keeps LDS within that too).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 1)))
+void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
                                                                int32_t num_perm,
                                                                const lora_item *__restrict__ items,
                                                                int32_t num_tokens,
