@@ -444,7 +444,7 @@ constexpr int kRowGroup = LORA_SHRINK_GATHER_ROWS;    // rows of A per segmented
 constexpr int kGatherCols = LORA_EXPAND_GATHER_COLS;  // columns of y per segmented gather item
 static_assert(kGatherCols == kThreads * 8, "one 8-column chunk per thread");
 #ifndef LORA_SGMV_SHRINK_THREADS
-#define LORA_SGMV_SHRINK_THREADS 256
+#define LORA_SGMV_SHRINK_THREADS 512
 #endif
 constexpr int kSgmvShrinkThreads = LORA_SGMV_SHRINK_THREADS;  // threads of a segmented shrink workgroup
 static_assert(kSgmvShrinkThreads % 64 == 0 && kSgmvShrinkThreads <= 1024, "whole waves, <= 1024");
@@ -1099,16 +1099,18 @@ __device__ __forceinline__ int xcd_logical(int b, int grid) { return (b & 7) * (
 
 inline int pad8(int n) { return (n + 7) & ~7; }
 
-// Collects, in token order, the tokens of ids[c0 .. c0+NT) whose adapter is
-// `a` into toks[]; returns their count.  All NT threads must call it.
-template <int NT>
+// Collects, in token order, the tokens of ids[c0 .. c0+CH) whose adapter is
+// `a` into toks[] (room for CH entries); returns their count.  All NT threads
+// must call it; threads CH.. take no token.
+template <int NT, int CH = NT>
 __device__ __forceinline__ int gather_adapter_tokens(const int32_t *__restrict__ ids, int num_tokens, int c0, int a,
                                      int *toks, int *wave_cnt) {
+  static_assert(CH <= NT, "one token per thread");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = c0 + tid;
   const int id = ids[t < num_tokens ? t : num_tokens - 1];  // unconditional load
-  const bool hit = t < num_tokens && id == a;
+  const bool hit = tid < CH && t < num_tokens && id == a;
   const unsigned long long mask = __ballot(hit);
   if (lane == 0) wave_cnt[wave] = __popcll(mask);
   __syncthreads();
@@ -1124,15 +1126,19 @@ __device__ __forceinline__ int gather_adapter_tokens(const int32_t *__restrict__
 }
 
 // Per-token (BGMV) shrink.  Work unit u is a token (token-major) or an adapter
-// (adapter-major); each unit is split into groups of RB rows, one per workgroup.
+// (adapter-major); each unit is split into groups of RB rows, one per workgroup
+// of kThreads threads.  (The segmented shrink runs wider workgroups; a token's
+// v then agrees between the two paths to rounding, not bit for bit, since the
+// k split and the wave reduction depend on the number of waves.)
 template <typename T, typename W, int RB>
 __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int32_t *__restrict__ ids,
                                                                int32_t num_tokens, int32_t adapter_major,
                                                                int32_t units, int32_t groups,
                                                                const T *__restrict__ x,
                                                                float *__restrict__ v) {
-  __shared__ ShrinkSmem<4> sm;
-  __shared__ int wave_cnt[4];
+  constexpr int NW = kThreads / 64;
+  __shared__ ShrinkSmem<NW> sm;
+  __shared__ int wave_cnt[NW];
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   if (L >= units * groups) return;
   const int u = L / groups, j0 = (L - u * groups) * RB;
@@ -1144,14 +1150,15 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
     if (j0 >= r) return;
     if (threadIdx.x == 0) sm.toks[0] = t;
     __syncthreads();
-    shrink_gemv<T, W, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
+    shrink_gemv<T, W, RB, NW>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
     if (j0 >= r) return;
-    for (int c0 = 0; c0 < num_tokens; c0 += kThreads) {
-      const int n = gather_adapter_tokens<kThreads>(ids, num_tokens, c0, a, sm.toks, wave_cnt);
-      if (n > 0) shrink_gemv<T, W, RB, 4>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
+    constexpr int CH = kThreads < kMaxItemTokens ? kThreads : kMaxItemTokens;
+    for (int c0 = 0; c0 < num_tokens; c0 += CH) {
+      const int n = gather_adapter_tokens<kThreads, CH>(ids, num_tokens, c0, a, sm.toks, wave_cnt);
+      if (n > 0) shrink_gemv<T, W, RB, NW>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
       __syncthreads();
     }
   }

@@ -102,7 +102,9 @@ def test_layer70b_projection(name):
     adapter 0): the base GEMM, then the SGMV delta (segmented mode, automatic
     path: one 1025-token MFMA segment, 255 gather segments) added to the GPU's
     base output, both checked on full rows; and the per-token (BGMV) delta
-    equals the segmented gather delta bit for bit."""
+    and the segmented gather delta agree on full rows (the two shrinks split
+    d_in over different numbers of waves, so within one bf16 rounding, not
+    bit for bit)."""
     R = runner()
     p = wl.layer_projection(name)
     say(f"layer70b {name}: {p.d_in} -> {p.d_out}")
@@ -122,8 +124,11 @@ def test_layer70b_projection(name):
     ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
     want = oracle.apply(p.x[rows], yb[rows], p.ids[rows], ad)
     _rows_close(got[rows], want, f"{name} base+delta")
-    # per-token mode on the same batch gives the gather path's bits
+    # per-token mode and the segmented gather path on the same batch
     y2, _ = dp.run_bgmv(B.LORA_BGMV_AUTO, y=y_base.clone())
     y3, _ = dp.run_sgmv(B.LORA_PATH_GATHER, y=y_base.clone())
     torch.cuda.synchronize()
-    assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
+    g2, g3 = bf16_host(y2), bf16_host(y3)
+    _rows_close(g2[rows], want, f"{name} bgmv base+delta")
+    scale = np.max(np.abs(g3), axis=1, keepdims=True)
+    assert np.all(np.abs(g2 - g3) <= np.abs(g3) * 2.0**-7 + 1e-4 * scale), f"{name} bgmv vs gather"

@@ -175,20 +175,24 @@ def test_bgmv_fused_token_order():
     check_y(dp, yg, oracle_y(p), "fused grouped")
 
 
-def test_bgmv_orders_and_sgmv_gather_bit_identical():
-    """Per-token results do not depend on grouping: token-major, adapter-major
-    and the segmented gather path give the same bits."""
+def test_bgmv_orders_bit_identical_and_sgmv_gather_agrees():
+    """Per-token results do not depend on grouping: token-major and
+    adapter-major give the same bits.  The segmented gather path splits d_in
+    over twice as many waves, so its v agrees to fp32 rounding and its y
+    within the bf16 bound."""
     R = runner()
     p = wl.bgmv_decode(num_tokens=200, num_adapters=32, d_in=1024, d_out=1536, seed=7)
-    say("bgmv vs sgmv-gather bit identity")
+    say("bgmv orders bit identity; sgmv-gather agreement")
     dp = R.DeviceProblem(p)
     y1, v1 = dp.run_bgmv(B.LORA_BGMV_TOKEN_MAJOR)
     y2, v2 = dp.run_bgmv(B.LORA_BGMV_ADAPTER_MAJOR)
     y3, v3 = dp.run_sgmv(B.LORA_PATH_GATHER)
     torch.cuda.synchronize()
-    assert torch.equal(v1, v2) and torch.equal(v1, v3)
+    assert torch.equal(v1, v2)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    rel = float((v3 - v1).abs().max() / v1.abs().max())
+    assert rel <= 1e-5, rel
+    check_y(dp, y3, oracle_y(p), "sgmv gather")
 
 
 # ------------------------------------------------------------------ config 3: prefill (reduced)
