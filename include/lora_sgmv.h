@@ -332,6 +332,68 @@ lora_status lora_pool_num_free(const lora_pool *pool, int32_t *num_free);
 lora_status lora_pool_write_rows(lora_pool *pool, const int32_t *page_ids, int32_t rows,
                                  const void *src, const float *src_scales, hipStream_t stream);
 void lora_pool_destroy(lora_pool *pool);
+/* The pool's geometry as created (any output may be NULL). */
+lora_status lora_pool_info(const lora_pool *pool, int32_t *num_pages, int32_t *page_rows,
+                           int32_t *row_width, int32_t *dtype, int32_t *weight_format);
+
+/* ------------------------------------------------------------------------ */
+/* Adapter residency: an LRU cache of adapters over two page pools (A rows and
+ * B^T rows; the same pool twice when d_in == d_out), filled from caller-owned
+ * host copies -- the hot HBM pool and warm host tier of "Multi-LoRA serving
+ * ..." (TL;DR; section "Operational pitfalls": cold start, fragmentation; its
+ * figure of the serving stack: LRU eviction, asynchronous host-to-device copy
+ * on use) and the fixed-size adapter pool of "Multi-LoRA Inference Serving"
+ * (clusterbid.com, vLLM paragraph: adapters swapped in and out as requests
+ * arrive).  The cache owns the contents of three caller-owned device arrays
+ * that a lora_weights descriptor then names: page tables [num_ids][max_pages]
+ * (max_pages = ceil(r_max / page_rows)) and ranks [num_ids], where num_ids is
+ * the size of the adapter id space (resident or not).  Non-resident adapters
+ * have page ids -1 and rank 0 there.  A lora_cache is not thread-safe.
+ *
+ * lora_cache_prepare makes every adapter of a batch resident before the
+ * batch's kernels run on `compute`: misses take pages (evicting the least
+ * recently used adapters the batch does not use), their rows, row scales,
+ * page-table rows and ranks are copied on the cache's own stream, and
+ * `compute` waits for those copies with an event (the call itself does not
+ * block).  A page freed by an eviction is rewritten only once the last batch
+ * that used the evicted adapter has completed on `compute`; use one compute
+ * stream per cache.  Host rows must stay valid and unchanged while their
+ * adapter is registered; pinned host memory (hipHostMalloc) lets the copies
+ * run on the DMA engines alongside the kernels.                             */
+#define LORA_CACHE_HOST_ONLY 1  /* flag: bookkeeping only, no device work (tests) */
+typedef struct lora_cache lora_cache;
+typedef struct {
+  int64_t hits;            /* batch adapters found resident (cumulative) */
+  int64_t misses;          /* batch adapters uploaded (cumulative) */
+  int64_t evictions;       /* adapters evicted (cumulative) */
+  int64_t bytes_uploaded;  /* rows and row scales copied to the pools (cumulative) */
+  int32_t resident;        /* adapters resident now */
+  int32_t scattered;       /* resident adapters whose pages are not consecutive ids */
+  int32_t free_pages_a, free_pages_b;
+} lora_cache_stats;
+/* Errors: LORA_EINVAL (null pointer, unknown flag, pools of different page
+ * size, dtype or format), LORA_EUNSUPPORTED (r_max), LORA_EHIP. */
+lora_status lora_cache_create(lora_pool *pool_a, lora_pool *pool_b, int32_t num_ids, int32_t r_max,
+                              int32_t *device_page_table_a, int32_t *device_page_table_b,
+                              int32_t *device_rank, int32_t flags, lora_cache **out);
+/* Host copies of adapter `id`: rank rows of A (d_in) and of B^T (d_out) in the
+ * pools' format, and for quantized pools their row scales (else NULL).
+ * Errors: LORA_ERANGE (id or rank), LORA_EINVAL (null rows, scales that do
+ * not match the format, a resident adapter). */
+lora_status lora_cache_register(lora_cache *cache, int32_t id, int32_t rank,
+                                const void *host_a_rows, const void *host_b_rows,
+                                const float *host_a_scales, const float *host_b_scales);
+/* ids [n] host (-1 entries skipped).  Errors: LORA_ERANGE (an id outside the
+ * space or not registered), LORA_ENOMEM (the batch's adapters alone exceed
+ * the pools; nothing changed), LORA_EHIP. */
+lora_status lora_cache_prepare(lora_cache *cache, const int32_t *ids, int32_t n, hipStream_t compute);
+lora_status lora_cache_get_stats(const lora_cache *cache, lora_cache_stats *stats);
+/* Page ids of a resident adapter (capacity max_pages each; NULL allowed);
+ * *num_pages = 0 when it is not resident. */
+lora_status lora_cache_pages(const lora_cache *cache, int32_t id, int32_t *pages_a,
+                             int32_t *pages_b, int32_t *num_pages);
+/* Waits for the cache's copies, then frees it (not the pools or arrays). */
+void lora_cache_destroy(lora_cache *cache);
 
 /* ------------------------------------------------------------------------ */
 /* Base projection y = x W^T computed once for every token of the batch, the

@@ -20,6 +20,7 @@ from . import build as _build
 LORA_OK, LORA_EINVAL, LORA_ERANGE, LORA_EUNSUPPORTED, LORA_ENOMEM, LORA_EHIP = 0, -1, -2, -3, -4, -5
 LORA_F32, LORA_BF16 = 0, 1
 LORA_WFMT_PLAIN, LORA_WFMT_FP8_E4M3, LORA_WFMT_INT4 = 0, 1, 2
+LORA_CACHE_HOST_ONLY = 1
 LORA_NO_ADAPTER = -1
 LORA_MAX_RANK = 128
 LORA_PHASE_SHRINK, LORA_PHASE_EXPAND = 0, 1
@@ -54,6 +55,13 @@ class lora_weights(ctypes.Structure):
                 ("a_scales", ctypes.c_void_p), ("b_scales", ctypes.c_void_p)]
 
 
+class lora_cache_stats(ctypes.Structure):
+    _fields_ = [("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
+                ("evictions", ctypes.c_int64), ("bytes_uploaded", ctypes.c_int64),
+                ("resident", ctypes.c_int32), ("scattered", ctypes.c_int32),
+                ("free_pages_a", ctypes.c_int32), ("free_pages_b", ctypes.c_int32)]
+
+
 _lib = None
 _P, _I32, _U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
 
@@ -74,6 +82,13 @@ EXPORTS = {
     "lora_pool_num_free": ([_P, _P], _I32),
     "lora_pool_write_rows": ([_P, _P, _I32, _P, _P, _P], _I32),
     "lora_pool_destroy": ([_P], None),
+    "lora_pool_info": ([_P, _P, _P, _P, _P, _P], _I32),
+    "lora_cache_create": ([_P, _P, _I32, _I32, _P, _P, _P, _I32, _P], _I32),
+    "lora_cache_register": ([_P, _I32, _I32, _P, _P, _P, _P], _I32),
+    "lora_cache_prepare": ([_P, _P, _I32, _P], _I32),
+    "lora_cache_get_stats": ([_P, _P], _I32),
+    "lora_cache_pages": ([_P, _I32, _P, _P, _P], _I32),
+    "lora_cache_destroy": ([_P], None),
     "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
 }
 
@@ -203,11 +218,12 @@ class Weights:
 
     def desc(self) -> lora_weights:
         self._host_rank_c = _i32(self.host_rank)
+        hr = self._host_rank_c.ctypes.data if getattr(self, "host_rank_valid", True) else None
         return lora_weights(
             self.dtype, self.d_in, self.d_out, self.num_adapters, self.r_max, self.page_rows,
             self.max_pages, int(self.a_pages.shape[0]), int(self.b_pages.shape[0]),
             self.weight_format, _dptr(self.a_pages), _dptr(self.b_pages), _dptr(self.rank),
-            _dptr(self.a_page_table), _dptr(self.b_page_table), self._host_rank_c.ctypes.data,
+            _dptr(self.a_page_table), _dptr(self.b_page_table), hr,
             _dptr(self.a_scales), _dptr(self.b_scales))
 
 
@@ -307,6 +323,69 @@ class Pool:
     def close(self):
         if self._h:
             lib().lora_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Cache:
+    """lora_cache: LRU residency of adapters (ids 0..num_ids-1) in two pools,
+    owning the device page tables and ranks (torch int32 tensors it is given,
+    or none in host-only mode).  ``weights(dtype, d_in, d_out)`` is the
+    descriptor the kernels read through it."""
+
+    def __init__(self, pool_a: Pool, pool_b: Pool, num_ids: int, r_max: int, page_table_a=None,
+                 page_table_b=None, rank=None, host_only: bool = False):
+        self.pool_a, self.pool_b = pool_a, pool_b
+        self.num_ids, self.r_max = num_ids, r_max
+        self.page_rows = pool_a.page_rows
+        self.max_pages = (r_max + self.page_rows - 1) // self.page_rows
+        self.pt_a, self.pt_b, self.rank = page_table_a, page_table_b, rank
+        self._keep = {}
+        h = ctypes.c_void_p()
+        _check(lib().lora_cache_create(pool_a._h, pool_b._h, num_ids, r_max, _dptr(page_table_a),
+                                       _dptr(page_table_b), _dptr(rank),
+                                       LORA_CACHE_HOST_ONLY if host_only else 0, ctypes.byref(h)))
+        self._h = h
+
+    def register(self, id_: int, rank: int, rows_a, rows_b, scales_a=None, scales_b=None):
+        """Host rows (numpy or torch CPU, ideally pinned) kept alive by the cache."""
+        self._keep[id_] = (rows_a, rows_b, scales_a, scales_b)
+        ptr = lambda t: None if t is None else (t.ctypes.data if isinstance(t, np.ndarray) else t.data_ptr())
+        _check(lib().lora_cache_register(self._h, id_, rank, ptr(rows_a), ptr(rows_b), ptr(scales_a),
+                                         ptr(scales_b)))
+
+    def prepare(self, ids, stream=None, host_only: bool = False):
+        a = _i32(ids)
+        s = None if host_only else _stream(stream)
+        _check(lib().lora_cache_prepare(self._h, _np_ptr(a), a.size, s))
+
+    def stats(self) -> dict:
+        st = lora_cache_stats()
+        _check(lib().lora_cache_get_stats(self._h, ctypes.byref(st)))
+        return {f: getattr(st, f) for f, _ in lora_cache_stats._fields_}
+
+    def pages(self, id_: int):
+        pa = np.empty(self.max_pages, np.int32)
+        pb = np.empty(self.max_pages, np.int32)
+        n = ctypes.c_int32(0)
+        _check(lib().lora_cache_pages(self._h, id_, _np_ptr(pa), _np_ptr(pb), ctypes.byref(n)))
+        return pa[: n.value].copy(), pb[: n.value].copy()
+
+    def weights(self, dtype: int, d_in: int, d_out: int, weight_format: int = LORA_WFMT_PLAIN) -> "Weights":
+        w = Weights(dtype, d_in, d_out, self.r_max, self.page_rows, self.pool_a.storage,
+                    self.pool_b.storage, self.rank, np.ones(self.num_ids, np.int32), self.pt_a,
+                    self.pt_b, self.max_pages, weight_format, self.pool_a.scales, self.pool_b.scales)
+        w.host_rank_valid = False
+        return w
+
+    def close(self):
+        if self._h:
+            lib().lora_cache_destroy(self._h)
             self._h = None
 
     def __del__(self):

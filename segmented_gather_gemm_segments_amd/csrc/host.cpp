@@ -323,3 +323,14 @@ extern "C" lora_status lora_pool_write_rows(lora_pool *p, const int32_t *page_id
 }
 
 extern "C" void lora_pool_destroy(lora_pool *p) { delete p; }
+
+extern "C" lora_status lora_pool_info(const lora_pool *p, int32_t *num_pages, int32_t *page_rows,
+                                      int32_t *row_width, int32_t *dtype, int32_t *weight_format) {
+  if (!p) return fail(LORA_EINVAL, "null pool");
+  if (num_pages) *num_pages = p->num_pages;
+  if (page_rows) *page_rows = p->page_rows;
+  if (row_width) *row_width = p->row_width;
+  if (dtype) *dtype = p->dtype;
+  if (weight_format) *weight_format = p->weight_format;
+  return ok();
+}

@@ -255,6 +255,34 @@ def quant_mixed(wq: str, seed: int = 6, paged: bool = False) -> LoraProblem:
                         776, 1288, "bf16", seed, paged=paged, page_rows=16, wq=wq)
 
 
+def churn(num_ids: int = 1024, batches: int = 64, tokens: int = 256, rank_choices=(16,),
+          d_in: int = 4096, d_out: int = 4096, seed: int = 8, wq: str = "",
+          no_adapter: float = 0.0, zipf_s: float = 1.1):
+    """Adapter churn: a universe of ``num_ids`` adapters (host copies; ranks
+    drawn from ``rank_choices``) and a sequence of decode batches whose ids
+    follow a Zipf(``zipf_s``) popularity over a random ranking of the adapters,
+    a fraction ``no_adapter`` of tokens without one.  Returns (universe, list of
+    (ids, x, y)): ``universe`` is a LoraProblem holding every adapter and the
+    first batch."""
+    r_rank, r_pop, r_ids, r_xy = _seeds(seed + 2000, 4)
+    ranks = r_rank.choice(np.asarray(rank_choices), size=num_ids).astype(np.int32)
+    order = r_pop.permutation(num_ids)
+    p = 1.0 / np.arange(1, num_ids + 1, dtype=np.float64) ** zipf_s
+    p /= p.sum()
+    seq = []
+    for b in range(batches):
+        ids = order[r_ids.choice(num_ids, size=tokens, p=p)].astype(np.int32)
+        if no_adapter > 0:
+            ids[r_ids.random(tokens) < no_adapter] = -1
+        rx, ry = _seeds(seed * 1000 + b, 2)
+        seq.append((ids, _normal(rx, (tokens, d_in), 1.0, "bf16"), _normal(ry, (tokens, d_out), 1.0, "bf16")))
+    suffix = f"_{wq}" if wq else ""
+    uni = make_problem(f"churn_{num_ids}ids_{tokens}tok_{d_in}x{d_out}{suffix}", None, None, ranks, d_in,
+                       d_out, "bf16", seed, mode="bgmv", ids=seq[0][0], wq=wq)
+    uni.x, uni.y = seq[0][1], seq[0][2]
+    return uni, seq
+
+
 LAYER_70B = [  # (name, d_in, d_out): Llama-3-70B projections, rank-16 table
     ("q", 8192, 8192), ("k", 8192, 1024), ("v", 8192, 1024), ("o", 8192, 8192),
     ("gate", 8192, 28672), ("up", 8192, 28672), ("down", 28672, 8192),
