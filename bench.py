@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU time (0 disables the CPU baseline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the LLC")
+    ap.add_argument("--churn", type=int, default=0, metavar="POOL_ADAPTERS",
+                    help="adapter churn: decode batches over 1024 adapters through an LRU cache "
+                         "whose pools hold POOL_ADAPTERS rank-16 adapters (uploads timed in)")
     ap.add_argument("--serial", action="store_true",
                     help="also time the adapter-serial comparator (one shrink + expand launch "
                          "per adapter sub-batch, same kernels)")
@@ -186,6 +189,105 @@ def serial_comparator(torch, stream, steps_calls, tokens: int, one_launch_s: flo
             "launches_per_step": launches, "ms_per_step": round(wall / K * 1e3, 5),
             "value": round(tokens * K / wall, 1), "unit": "delta tokens/s",
             "one_launch_speedup": round((wall / K) / one_launch_s, 3), "steps": K}
+
+
+def bench_churn(args, torch):
+    """Decode steps under adapter churn: each step makes its batch's adapters
+    resident through the LRU cache (uploads from pinned host copies on the
+    cache's copy stream) and runs the fused delta.  Timed eagerly, since a
+    step has host logic; the same steps are also timed with a host
+    synchronisation after each (no overlap of uploads with compute)."""
+    from segmented_gather_gemm_segments_amd import binding as B
+    from segmented_gather_gemm_segments_amd import workloads as wl
+    num_ids, tokens, d, pr = 1024, 256, 4096, 16
+    K, W = args.steps, args.warmup
+    uni, seq = wl.churn(num_ids=num_ids, batches=W + K, tokens=tokens, d_in=d, d_out=d,
+                        wq=args.wq)
+    dev = torch.device("cuda:0")
+    wf = {"": B.LORA_WFMT_PLAIN, "fp8": B.LORA_WFMT_FP8_E4M3, "int4": B.LORA_WFMT_INT4}[args.wq]
+    n_pages = args.churn * ((16 + pr - 1) // pr)
+
+    def pool(seed):
+        if wf == B.LORA_WFMT_PLAIN:
+            st = torch.empty((n_pages, pr, d), dtype=torch.bfloat16, device=dev)
+            return B.Pool(st, pr, shuffle_seed=seed)
+        w = d // 2 if wf == B.LORA_WFMT_INT4 else d
+        st = torch.empty((n_pages, pr, w), dtype=torch.uint8, device=dev)
+        sc = torch.empty((n_pages * pr,), dtype=torch.float32, device=dev)
+        return B.Pool(st, pr, shuffle_seed=seed, weight_format=wf, scales=sc)
+
+    def pinned(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).pin_memory()
+
+    hosts = [(pinned(uni.a_rows[a]), pinned(uni.bt_rows[a]),
+              pinned(uni.a_scales[a]) if args.wq else None,
+              pinned(uni.bt_scales[a]) if args.wq else None) for a in range(num_ids)]
+    stream = torch.cuda.Stream()
+    dev_batches = []
+    with torch.cuda.stream(stream):
+        for ids, x, y in seq:
+            perm, _, _ = B.lora_segments_build(ids, num_ids)
+            dev_batches.append((ids, torch.from_numpy(ids).to(dev),
+                                torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16),
+                                torch.from_numpy(y.view(np.int16)).to(dev).view(torch.bfloat16),
+                                torch.from_numpy(perm).to(dev)))
+    torch.cuda.synchronize()
+
+    def run(steps, sync_each):
+        pa, pb = pool(11), pool(12)
+        mp = (16 + pr - 1) // pr
+        pt_a = torch.empty((num_ids, mp), dtype=torch.int32, device=dev)
+        pt_b = torch.empty((num_ids, mp), dtype=torch.int32, device=dev)
+        rank = torch.empty(num_ids, dtype=torch.int32, device=dev)
+        cache = B.Cache(pa, pb, num_ids, 16, pt_a, pt_b, rank)
+        for a in range(num_ids):
+            cache.register(a, int(uni.ranks[a]), *hosts[a])
+        w = cache.weights(B.LORA_BF16, d, d, wf)
+        calls = []
+        for ids, ids_d, x_d, y_d, perm_d in dev_batches:
+            calls.append((ids, B.prepare_bgmv_fused(w, ids_d, x_d, y_d, None, B.LORA_BGMV_AUTO,
+                                                    stream=stream, token_order=perm_d)))
+        for ids, fu in calls[:W]:
+            cache.prepare(ids, stream=stream)
+            fu()
+        torch.cuda.synchronize()
+        s0 = cache.stats()
+        t0 = time.perf_counter()
+        for ids, fu in calls[W:W + steps]:
+            cache.prepare(ids, stream=stream)
+            fu()
+            if sync_each:
+                stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        s1 = cache.stats()
+        cache.close()
+        return wall, {k: s1[k] - s0[k] for k in ("hits", "misses", "evictions", "bytes_uploaded")}, s1
+
+    wall, dlt, final = run(K, False)
+    wall_sync, _, _ = run(K, True)
+    tokens_k = int(sum(int(np.sum(ids >= 0)) for ids, *_ in dev_batches[W:W + K]))
+    out = {
+        "metric": "LoRA delta tokens/sec per layer under adapter churn",
+        "value": round(tokens_k / wall, 1), "unit": "delta tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(wall / K * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; random-init adapters; Zipf(1.1) adapter popularity)",
+        "config": {"workload": uni.name.replace("_" + str(tokens) + "tok", f"_{tokens}tok_pool{args.churn}"),
+                   "adapters": num_ids, "pool_adapters": args.churn, "tokens": tokens, "rank": 16,
+                   "d_in": d, "d_out": d, "adapter_rows": args.wq or "bf16",
+                   "timed": "eager steps: lora_cache_prepare + fused delta", "parallelism": "single GPU"},
+        "churn": {"hit_rate": round(dlt["hits"] / max(1, dlt["hits"] + dlt["misses"]), 4),
+                  "misses_per_step": round(dlt["misses"] / K, 2),
+                  "evictions_per_step": round(dlt["evictions"] / K, 2),
+                  "mb_uploaded_per_step": round(dlt["bytes_uploaded"] / K / 1e6, 3),
+                  "upload_gbs_effective": round(dlt["bytes_uploaded"] / wall / 1e9, 2),
+                  "ms_per_step_sync_each_step": round(wall_sync / K * 1e3, 5),
+                  "resident_adapters": final["resident"], "scattered_adapters": final["scattered"]},
+        "kernel_sources_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def bench_layer(args, torch):
@@ -326,6 +428,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     B.lib()
+    if args.churn > 0:
+        return bench_churn(args, torch)
     if args.config == 5:
         return bench_layer(args, torch)
     p = workload(args.config, args.shape, args.wq)

@@ -352,7 +352,8 @@ lora_status lora_pool_info(const lora_pool *pool, int32_t *num_pages, int32_t *p
  *
  * lora_cache_prepare makes every adapter of a batch resident before the
  * batch's kernels run on `compute`: misses take pages (evicting the least
- * recently used adapters the batch does not use), their rows, row scales,
+ * recently used adapters the batch does not use, those whose last batch has
+ * completed before those still in flight), their rows, row scales,
  * page-table rows and ranks are copied on the cache's own stream, and
  * `compute` waits for those copies with an event (the call itself does not
  * block).  A page freed by an eviction is rewritten only once the last batch

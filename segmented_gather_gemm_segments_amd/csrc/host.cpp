@@ -189,15 +189,6 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
 
 // --------------------------------------------------------------------------
 // Paged pool.
-struct lora_pool {
-  int32_t num_pages, page_rows, row_width, dtype, weight_format;
-  size_t row_bytes;
-  char *storage;
-  float *scales;                    // [num_pages * page_rows], quantized formats only
-  std::vector<int32_t> free_list;   // front = next page handed out
-  size_t head = 0;                  // free_list[head..] are free
-  std::vector<uint8_t> taken;
-};
 
 static uint64_t splitmix64(uint64_t &s) {
   uint64_t z = (s += 0x9E3779B97F4A7C15ull);

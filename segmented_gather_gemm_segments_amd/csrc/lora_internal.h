@@ -4,7 +4,23 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
 #include "lora_sgmv.h"
+
+// Page pool bookkeeping (host.cpp); the residency cache reads its geometry and
+// storage to address pages.
+struct lora_pool {
+  int32_t num_pages, page_rows, row_width, dtype, weight_format;
+  size_t row_bytes;
+  char *storage;
+  float *scales;                    // [num_pages * page_rows], quantized formats only
+  std::vector<int32_t> free_list;   // front = next page handed out
+  size_t head = 0;                  // free_list[head..] are free
+  std::vector<uint8_t> taken;
+};
 
 namespace lora {
 

@@ -14,7 +14,8 @@
 //   * hits only refresh their LRU stamp;
 //   * misses take pages from the pools, evicting least-recently-used adapters
 //     that the batch does not use until the pages fit (or fail with nothing
-//     changed);
+//     changed) -- among them first those whose last batch has completed, so
+//     that an upload rarely has to wait for a batch still in flight;
 //   * uploads (rows, row scales, page-table rows, ranks) go on the cache's own
 //     copy stream, so they overlap with kernels already queued on the compute
 //     stream; the compute stream then waits for them with an event;
@@ -27,7 +28,12 @@
 //     normally long completed, so the wait costs nothing.
 // Page-table rows and ranks are written by a small kernel whose entries travel
 // as kernel arguments, so no host staging buffer can change under a pending
-// copy.
+// copy.  The rows themselves are gathered by one copy kernel per prepare that
+// reads the pinned host copies directly (pinned host memory is addressable from
+// the GPU) and writes every page -- one launch instead of one DMA request per
+// page and pool, whose per-request cost dominated; host copies that are not
+// device-addressable (pageable memory) are uploaded with plain asynchronous
+// copies instead.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -69,6 +75,43 @@ __global__ __launch_bounds__(kTableBatch * kEntryPages) void table_update_kernel
   if (p == 0 && e.rank >= 0) u.rank[e.id] = e.rank;
 }
 
+// Upload jobs: `bytes` (a multiple of 4) from src (device-addressable host
+// memory) to dst (a page of a pool, or its scales).  Block b of the launch
+// copies slice b % kSlices of job b / kSlices.
+struct CopyJob {
+  const char *src;
+  char *dst;
+  int64_t bytes;
+};
+constexpr int kCopyJobs = 64;
+constexpr int kSlices = 8;
+struct CopyBatch {
+  int32_t n;
+  CopyJob j[kCopyJobs];
+};
+
+__global__ __launch_bounds__(256) void upload_kernel(CopyBatch b) {
+  const int ji = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
+  if (ji >= b.n) return;
+  const CopyJob &j = b.j[ji];
+  const bool vec = (((uintptr_t)j.src | (uintptr_t)j.dst) & 15u) == 0;
+  const int64_t n16 = vec ? j.bytes >> 4 : 0;
+  // 16-byte units, four in flight per thread
+  const int64_t stride = (int64_t)kSlices * blockDim.x;
+  int64_t i = (int64_t)sl * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    uint4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = reinterpret_cast<const uint4 *>(j.src)[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) reinterpret_cast<uint4 *>(j.dst)[i + u * stride] = q[u];
+  }
+  for (; i < n16; i += stride) reinterpret_cast<uint4 *>(j.dst)[i] = reinterpret_cast<const uint4 *>(j.src)[i];
+  // the rest (or everything, unaligned) in 4-byte words
+  for (int64_t k = (n16 << 2) + (int64_t)sl * blockDim.x + threadIdx.x; k < (j.bytes >> 2); k += stride)
+    reinterpret_cast<uint32_t *>(j.dst)[k] = reinterpret_cast<const uint32_t *>(j.src)[k];
+}
+
 __global__ void fill_kernel(int32_t *p, int64_t n, int32_t value) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = value;
@@ -83,9 +126,11 @@ struct Event {
 
 struct Entry {
   bool registered = false, resident = false;
+  bool mapped = false;                // host copies readable by the GPU (pinned)
   int32_t rank = 0;
   const void *host_a = nullptr, *host_b = nullptr;
   const float *sc_a = nullptr, *sc_b = nullptr;
+  const char *dev_a = nullptr, *dev_b = nullptr, *dev_sa = nullptr, *dev_sb = nullptr;
   std::vector<int32_t> pages_a, pages_b;
   uint64_t stamp = 0;                 // LRU: last batch that used it
   std::shared_ptr<Event> last_use;    // completes after that batch's kernels
@@ -152,6 +197,33 @@ void table_entries(const lora_cache *c, int32_t id, int32_t rank, const std::vec
     }
     out.push_back(e);
   }
+}
+
+// Device address of host memory, or nullptr when it is not device-addressable
+// (pageable).  Clears the error a failed query leaves behind.
+const char *device_view(const void *p) {
+  if (!p) return nullptr;
+  hipPointerAttribute_t at;
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (at.type != hipMemoryTypeHost || !at.devicePointer) return nullptr;
+  return (const char *)at.devicePointer;
+}
+
+lora_status flush_copies(lora_cache *c, std::vector<CopyJob> &jobs) {
+  for (size_t i0 = 0; i0 < jobs.size(); i0 += kCopyJobs) {
+    CopyBatch b{};
+    b.n = (int32_t)std::min<size_t>(kCopyJobs, jobs.size() - i0);
+    for (int i = 0; i < b.n; ++i) b.j[i] = jobs[i0 + (size_t)i];
+    hipLaunchKernelGGL(upload_kernel, dim3(b.n * kSlices), dim3(256), 0, c->copy, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "upload launch");
+  }
+  jobs.clear();
+  return LORA_OK;
 }
 
 bool consecutive(const std::vector<int32_t> &p) {
@@ -230,6 +302,14 @@ extern "C" lora_status lora_cache_register(lora_cache *c, int32_t id, int32_t ra
   e.host_b = host_b_rows;
   e.sc_a = host_a_scales;
   e.sc_b = host_b_scales;
+  e.mapped = false;
+  if (!c->host_only()) {
+    e.dev_a = device_view(host_a_rows);
+    e.dev_b = device_view(host_b_rows);
+    e.dev_sa = device_view(host_a_scales);
+    e.dev_sb = device_view(host_b_scales);
+    e.mapped = e.dev_a && e.dev_b && (!quant || (e.dev_sa && e.dev_sb));
+  }
   return ok();
 }
 
@@ -276,6 +356,14 @@ extern "C" lora_status lora_cache_prepare(lora_cache *c, const int32_t *ids, int
       if (e.resident && !std::binary_search(batch.begin(), batch.end(), a)) lru.push_back({e.stamp, a});
     }
     std::sort(lru.begin(), lru.end());
+    // least recently used first, but adapters whose last batch has already
+    // completed before those still queued on the compute stream: evicting a
+    // queued adapter makes the upload wait for that batch
+    auto done = [&](int32_t a) {
+      const Entry &e = c->ids[(size_t)a];
+      return !e.last_use || hipEventQuery(e.last_use->e) == hipSuccess;
+    };
+    std::stable_partition(lru.begin(), lru.end(), [&](const std::pair<uint64_t, int32_t> &q) { return done(q.second); });
     int64_t fa = free_a, fb = free_b;
     for (const auto &q : lru) {
       if (fits(fa, fb)) break;
@@ -320,6 +408,7 @@ extern "C" lora_status lora_cache_prepare(lora_cache *c, const int32_t *ids, int
     enqueued = true;
   }
   // misses: pages, row uploads, table rows
+  std::vector<CopyJob> jobs;
   for (int32_t a : misses) {
     Entry &e = c->ids[(size_t)a];
     const int32_t np = (e.rank + c->page_rows - 1) / c->page_rows;
@@ -328,7 +417,26 @@ extern "C" lora_status lora_cache_prepare(lora_cache *c, const int32_t *ids, int
     lora_status st = lora_pool_alloc(c->pool_a, e.rank, e.pages_a.data());
     if (st == LORA_OK) st = lora_pool_alloc(c->pool_b, e.rank, e.pages_b.data());
     if (st != LORA_OK) return st;  // cannot happen after the plan above
-    if (!c->host_only()) {
+    if (!c->host_only() && e.mapped) {
+      // one job per page and pool (rows, then scales)
+      for (int32_t i = 0; i < np; ++i) {
+        const int32_t r0 = i * c->page_rows, nr = std::min(c->page_rows, e.rank - r0);
+        const lora_pool *ps[2] = {c->pool_a, c->pool_b};
+        const char *src[2] = {e.dev_a, e.dev_b};
+        const char *ssrc[2] = {e.dev_sa, e.dev_sb};
+        const int32_t pg[2] = {e.pages_a[(size_t)i], e.pages_b[(size_t)i]};
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const lora_pool *p = ps[s2];
+          const int64_t rb = (int64_t)p->row_bytes;
+          jobs.push_back({src[s2] + (int64_t)r0 * rb,
+                          p->storage + ((int64_t)pg[s2] * p->page_rows) * rb, (int64_t)nr * rb});
+          if (p->scales)
+            jobs.push_back({ssrc[s2] + (int64_t)r0 * 4,
+                            reinterpret_cast<char *>(p->scales + (int64_t)pg[s2] * p->page_rows),
+                            (int64_t)nr * 4});
+        }
+      }
+    } else if (!c->host_only()) {
       st = lora_pool_write_rows(c->pool_a, e.pages_a.data(), e.rank, e.host_a, e.sc_a, c->copy);
       if (st == LORA_OK)
         st = lora_pool_write_rows(c->pool_b, e.pages_b.data(), e.rank, e.host_b, e.sc_b, c->copy);
@@ -341,8 +449,9 @@ extern "C" lora_status lora_cache_prepare(lora_cache *c, const int32_t *ids, int
                                (e.sc_a ? (int64_t)e.rank * 8 : 0);
     enqueued = true;
   }
-  lora_status st = flush_updates(c, pending);
+  lora_status st = c->host_only() ? LORA_OK : flush_copies(c, jobs);
   if (st != LORA_OK) return st;
+  if ((st = flush_updates(c, pending)) != LORA_OK) return st;
   if (enqueued && !c->host_only()) {
     hipEvent_t up;
     hipError_t e = hipEventCreateWithFlags(&up, hipEventDisableTiming);

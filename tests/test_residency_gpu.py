@@ -38,8 +38,10 @@ def _pinned(a):
     return torch.from_numpy(a).pin_memory()
 
 
-@pytest.mark.parametrize("wq", ["", "fp8"])
-def test_churn_sequence_matches_oracle(wq):
+@pytest.mark.parametrize("wq,pinned", [("", True), ("fp8", True), ("", False)])
+def test_churn_sequence_matches_oracle(wq, pinned):
+    """pinned: host copies in pinned memory (gathered by the upload kernel);
+    otherwise pageable numpy arrays (uploaded by asynchronous copies)."""
     num_ids, d_in, d_out = 24, 512, 776
     u, seq = wl.churn(num_ids=num_ids, batches=14, tokens=10, rank_choices=(8, 16, 32), d_in=d_in,
                       d_out=d_out, seed=21, wq=wq, no_adapter=0.1)
@@ -47,7 +49,7 @@ def test_churn_sequence_matches_oracle(wq):
     need = max(sum(pages(a) for a in set(ids[ids >= 0].tolist())) for ids, _, _ in seq)
     n_pages = need + 2                     # far below the universe's pages: churn
     assert n_pages < sum(pages(a) for a in range(num_ids))
-    print(f"[case] churn wq={wq or 'bf16'}: {n_pages} pages per pool", flush=True)
+    print(f"[case] churn wq={wq or 'bf16'} pinned={pinned}: {n_pages} pages per pool", flush=True)
     dev = torch.device("cuda:0")
     wf = {"": B.LORA_WFMT_PLAIN, "fp8": B.LORA_WFMT_FP8_E4M3}[wq]
 
@@ -66,10 +68,11 @@ def test_churn_sequence_matches_oracle(wq):
     pt_b = torch.empty((num_ids, mp), dtype=torch.int32, device=dev)
     rank = torch.empty(num_ids, dtype=torch.int32, device=dev)
     cache = B.Cache(pa, pb, num_ids, r_max, pt_a, pt_b, rank)
+    host = _pinned if pinned else np.ascontiguousarray
     for a in range(num_ids):
-        sa = _pinned(u.a_scales[a]) if wq else None
-        sb = _pinned(u.bt_scales[a]) if wq else None
-        cache.register(a, int(u.ranks[a]), _pinned(u.a_rows[a]), _pinned(u.bt_rows[a]), sa, sb)
+        sa = host(u.a_scales[a]) if wq else None
+        sb = host(u.bt_scales[a]) if wq else None
+        cache.register(a, int(u.ranks[a]), host(u.a_rows[a]), host(u.bt_rows[a]), sa, sb)
     w = cache.weights(B.LORA_BF16, d_in, d_out, wf)
     st = torch.cuda.Stream()
     outs = []
