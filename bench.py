@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--churn", type=int, default=0, metavar="POOL_ADAPTERS",
                     help="adapter churn: decode batches over 1024 adapters through an LRU cache "
                          "whose pools hold POOL_ADAPTERS rank-16 adapters (uploads timed in)")
+    ap.add_argument("--multi", action="store_true",
+                    help="decode q, k, v of the 70B layer (256 tokens, 256 rank-16 adapters) as one "
+                         "fused multi-projection launch vs three fused launches")
     ap.add_argument("--serial", action="store_true",
                     help="also time the adapter-serial comparator (one shrink + expand launch "
                          "per adapter sub-batch, same kernels)")
@@ -290,6 +293,84 @@ def bench_churn(args, torch):
     print(json.dumps(out), flush=True)
 
 
+def bench_multi(args, torch):
+    """Decode deltas of the q, k and v projections of the 70B-shape layer (256
+    tokens on a permutation of 256 rank-16 adapters, 8192 -> 8192 / 1024 /
+    1024): one lora_bgmv_fused_multi launch per step against three
+    lora_bgmv_fused launches, both in segment order, both graph-replayed over
+    cache-defeating replicas."""
+    from segmented_gather_gemm_segments_amd import accounting as acc
+    from segmented_gather_gemm_segments_amd import binding as B
+    from segmented_gather_gemm_segments_amd import runner as R
+    from segmented_gather_gemm_segments_amd import workloads as wl
+    names = ["q", "k", "v"]
+    small = {}
+    for nt in (32,):
+        b2 = [wl.layer_projection(n, decode=nt, prefill=0, with_base=False) for n in names]
+        for p in b2[1:]:
+            p.x = b2[0].x
+        st2 = torch.cuda.Stream()
+        reps2 = []
+        for _ in range(8):
+            dps = [R.DeviceProblem(p) for p in b2]
+            order = dps[0].segments()[3]
+            ys = [dp.y0.clone() for dp in dps]
+            reps2.append((B.prepare_bgmv_fused_multi([dp.weights for dp in dps], dps[0].ids, dps[0].x, ys,
+                                                     stream=st2, token_order=order),
+                          [B.prepare_bgmv_fused(dp.weights, dps[0].ids, dps[0].x, y, None,
+                                                B.LORA_BGMV_AUTO, stream=st2, token_order=order)
+                           for dp, y in zip(dps, ys)]))
+        torch.cuda.synchronize()
+        tm = graph_span(torch, st2, [reps2[i % 8][0] for i in range(args.steps)], 3)
+        t3 = graph_span(torch, st2, [f for i in range(args.steps) for f in reps2[i % 8][1]], 3) * 3
+        small[str(nt)] = {"us_one_launch": round(tm * 1e6, 3), "us_three_launches": round(t3 * 1e6, 3),
+                          "speedup": round(t3 / tm, 3)}
+        del reps2
+    base = [wl.layer_projection(n, decode=256, prefill=0, with_base=False) for n in names]
+    for p in base[1:]:
+        p.x = base[0].x
+    stream = torch.cuda.Stream()
+    per_rep = sum(p.x.nbytes / 3 + p.y.nbytes + sum(a.nbytes + b.nbytes for a, b in zip(p.a_rows, p.bt_rows))
+                  for p in base)
+    n_rep = args.replicas or min(32, max(2, int(np.ceil(2 * LLC_BYTES / per_rep))))
+    reps = []
+    for _ in range(n_rep):
+        dps = [R.DeviceProblem(p) for p in base]
+        for dp in dps[1:]:
+            dp.x = dps[0].x
+        order = dps[0].segments()[3]
+        ys = [dp.y0.clone() for dp in dps]
+        multi = B.prepare_bgmv_fused_multi([dp.weights for dp in dps], dps[0].ids, dps[0].x, ys,
+                                           stream=stream, token_order=order)
+        singles = [B.prepare_bgmv_fused(dp.weights, dps[0].ids, dps[0].x, y, None, B.LORA_BGMV_AUTO,
+                                        stream=stream, token_order=order) for dp, y in zip(dps, ys)]
+        reps.append((multi, singles))
+    torch.cuda.synchronize()
+    K = args.steps
+    t_multi = graph_span(torch, stream, [reps[i % n_rep][0] for i in range(K)], 3)
+    t_three = graph_span(torch, stream, [f for i in range(K) for f in reps[i % n_rep][1]], 3) * 3
+    tokens = int(np.sum(base[0].ids >= 0))
+    nbytes = sum(acc.fused_bytes(p.ids, p.ranks, p.d_in, p.d_out, 2) for p in base) - 2 * tokens * base[0].d_in * 2
+    out = {
+        "metric": "LoRA delta tokens/sec per layer (q, k, v decode deltas)",
+        "value": round(tokens / t_multi, 1), "unit": "delta tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(t_multi * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; random-init adapters)",
+        "config": {"workload": "layer70b_qkv_decode_256tok_256ad_r16", "projections": names,
+                   "replicas": n_rep, "timed": "HIP graph of K steps, per-step span",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / t_multi / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / t_multi / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "bgmv_fused_multi", "algorithmic_bytes_per_launch": int(nbytes),
+                     "avg_launch_us": round(t_multi * 1e6, 3)},
+        "multi_projection": {"256": {"us_one_launch": round(t_multi * 1e6, 3),
+                                     "us_three_launches": round(t_three * 1e6, 3),
+                                     "speedup": round(t_three / t_multi, 3)}, **small},
+        "kernel_sources_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_layer(args, torch):
     """The 70B-shape decoder layer: seven projections, each the base GEMM
     y = x W^T followed by the SGMV delta (segmented mode, automatic paths)."""
@@ -430,6 +511,8 @@ def main():
     B.lib()
     if args.churn > 0:
         return bench_churn(args, torch)
+    if args.multi:
+        return bench_multi(args, torch)
     if args.config == 5:
         return bench_layer(args, torch)
     p = workload(args.config, args.shape, args.wq)

@@ -302,6 +302,29 @@ lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
                             int32_t num_ordered, int32_t order, const void *x, float *v,
                             void *y, hipStream_t stream);
 
+/* Several projections of the same input in ONE fused launch: the q, k and v
+ * (or gate and up) projections of a layer, each with its own adapter matrices
+ * (w[p]) and output (y[p] [num_tokens, w[p]->d_out]; v[p] optional, as for
+ * lora_bgmv_fused), all reading x ("Multi-LoRA serving ...", section "The
+ * maths that matters": every targeted projection of a layer carries its own
+ * A and B; x is shared).  The work units of one token are placed on one XCD,
+ * so x crosses the fabric once for all projections, and one launch replaces
+ * num_proj.  Per projection the arithmetic is lora_bgmv_fused's (token-major),
+ * so the bits equal those of separate lora_bgmv_fused calls.  It pays where
+ * launches dominate (small decode batches: 2.3x for q/k/v of a 70B layer at
+ * 32 tokens); at 256 tokens separate launches balance better (0.93x).
+ *   w [num_proj]  host array of descriptors with equal dtype, weight_format,
+ *                 d_in and num_adapters (their d_out may differ); num_proj in 1..4
+ *   v [num_proj]  host array of device pointers (entries may be NULL), or NULL
+ *   y [num_proj]  host array of device pointers
+ *   token_adapter, token_order, num_ordered, x as for lora_bgmv_fused.
+ * Errors: as lora_bgmv_fused; LORA_EINVAL for num_proj or mismatched
+ * descriptors.                                                            */
+lora_status lora_bgmv_fused_multi(const lora_weights *const *w, int32_t num_proj,
+                                  const int32_t *token_adapter, int32_t num_tokens,
+                                  const int32_t *token_order, int32_t num_ordered, const void *x,
+                                  float *const *v, void *const *y, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Paged adapter pool (host bookkeeping over caller-owned device storage of
  * [num_pages][page_rows] rows of row_width elements in the given dtype and

@@ -76,6 +76,7 @@ EXPORTS = {
     "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_expand": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_fused": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P], _I32),
+    "lora_bgmv_fused_multi": ([_P, _I32, _P, _I32, _P, _I32, _P, _P, _P, _P], _I32),
     "lora_pool_create": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _U64, _P], _I32),
     "lora_pool_alloc": ([_P, _I32, _P], _I32),
     "lora_pool_free": ([_P, _P, _I32], _I32),
@@ -266,6 +267,33 @@ def lora_bgmv_fused(w: Weights, token_adapter, x, y, v=None, order: int = LORA_B
     _check(lib().lora_bgmv_fused(ctypes.byref(d), _dptr(token_adapter), int(token_adapter.numel()),
                                  _dptr(token_order), n_ord, order, _dptr(x), _dptr(v), _dptr(y),
                                  _stream(stream)))
+
+
+def _multi_args(ws, ys, vs):
+    descs = [w.desc() for w in ws]
+    n = len(descs)
+    warr = (ctypes.POINTER(lora_weights) * n)(*[ctypes.pointer(d) for d in descs])
+    yarr = (ctypes.c_void_p * n)(*[_dptr(y) for y in ys])
+    varr = None if vs is None else (ctypes.c_void_p * n)(*[_dptr(v) for v in vs])
+    return descs, warr, yarr, varr
+
+
+def lora_bgmv_fused_multi(ws, token_adapter, x, ys, vs=None, stream=None, token_order=None):
+    """Fused per-token deltas of several projections sharing x, one launch."""
+    descs, warr, yarr, varr = _multi_args(ws, ys, vs)
+    n_ord = 0 if token_order is None else int(token_order.numel())
+    _check(lib().lora_bgmv_fused_multi(warr, len(ws), _dptr(token_adapter), int(token_adapter.numel()),
+                                       _dptr(token_order), n_ord, _dptr(x), varr, yarr,
+                                       _stream(stream)))
+
+
+def prepare_bgmv_fused_multi(ws, token_adapter, x, ys, vs=None, stream=None, token_order=None):
+    descs, warr, yarr, varr = _multi_args(ws, ys, vs)
+    n_ord = 0 if token_order is None else int(token_order.numel())
+    keep = (descs, warr, yarr, varr, ws, token_adapter, x, ys, vs, token_order)
+    return Prepared("lora_bgmv_fused_multi", (warr, len(ws), _dptr(token_adapter),
+                                              int(token_adapter.numel()), _dptr(token_order), n_ord,
+                                              _dptr(x), varr, yarr, _stream(stream)), keep)
 
 
 def lora_base_gemm(x, w, y, stream=None):

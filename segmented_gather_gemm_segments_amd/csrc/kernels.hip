@@ -1255,20 +1255,9 @@ __device__ __forceinline__ float a_scale_any(const DevW &w, int a, int j, bool u
 // with every store suppressed -- so the compiler cannot sink the loads past
 // the id or rank wait.
 template <typename T, typename W, bool AL>
-__global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const int32_t *__restrict__ ids,
-                                                                   int32_t num_tokens,
-                                                                   const int32_t *__restrict__ torder,
-                                                                   int32_t units, int32_t nblk,
-                                                                   int32_t block_cols,
-                                                                   const T *__restrict__ x,
-                                                                   float *__restrict__ v,
-                                                                   T *__restrict__ y) {
-  __shared__ FusedSmem sm;
-  const int u = xcd_logical(blockIdx.x, gridDim.x);
-  const int slot = u / nblk, cb = u - slot * nblk;
-  if (slot >= units) return;
-  const int t = torder ? torder[slot] : slot;
-  if ((unsigned)t >= (unsigned)num_tokens) return;
+__device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restrict__ ids, int t, int cb,
+                                           int block_cols, const T *__restrict__ x,
+                                           float *__restrict__ v, T *__restrict__ y, FusedSmem &sm) {
   const int c_begin = cb * block_cols, c_end = min(w.d_out, c_begin + block_cols);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const T *xr = x + (int64_t)t * w.d_in;
@@ -1404,6 +1393,73 @@ __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const
       store8(yr + col, yv);
     }
   }
+}
+
+template <typename T, typename W, bool AL>
+__global__ __launch_bounds__(kFusedThreads) void bgmv_fused_kernel(DevW w, const int32_t *__restrict__ ids,
+                                                                   int32_t num_tokens,
+                                                                   const int32_t *__restrict__ torder,
+                                                                   int32_t units, int32_t nblk,
+                                                                   int32_t block_cols,
+                                                                   const T *__restrict__ x,
+                                                                   float *__restrict__ v,
+                                                                   T *__restrict__ y) {
+  __shared__ FusedSmem sm;
+  const int u = xcd_logical(blockIdx.x, gridDim.x);
+  const int slot = u / nblk, cb = u - slot * nblk;
+  if (slot >= units) return;
+  const int t = torder ? torder[slot] : slot;
+  if ((unsigned)t >= (unsigned)num_tokens) return;
+  fused_unit<T, W, AL>(w, ids, t, cb, block_cols, x, v, y, sm);
+}
+
+// Several projections of the same input in one launch (the q, k and v of an
+// attention layer: each with its own adapter matrices and output, all reading
+// the token's x).  Work unit = (entry of the token order, projection p, column
+// block of p); the units of one token are consecutive and placed on one XCD,
+// so x is fetched once for all its projections.  Each unit's arithmetic is the
+// single-projection kernel's, so results are bit-identical to separate
+// launches.
+constexpr int kMaxProj = 4;
+template <typename T>
+struct MultiArgs {
+  DevW w[kMaxProj];
+  T *y[kMaxProj];
+  float *v[kMaxProj];
+  int32_t block_cols[kMaxProj];
+  int32_t first[kMaxProj + 1];  // units of projections 0 .. p-1 within a token
+};
+
+template <typename T, typename W, bool AL>
+__global__ __launch_bounds__(kFusedThreads) void bgmv_fused_multi_kernel(MultiArgs<T> m, int32_t np,
+                                                                         const int32_t *__restrict__ ids,
+                                                                         int32_t num_tokens,
+                                                                         const int32_t *__restrict__ torder,
+                                                                         int32_t units,
+                                                                         const T *__restrict__ x) {
+  __shared__ FusedSmem sm;
+  const int per = m.first[np];
+  const int u = xcd_logical(blockIdx.x, gridDim.x);
+  const int slot = u / per, k = u - slot * per;
+  if (slot >= units) return;
+  const int t = torder ? torder[slot] : slot;
+  if ((unsigned)t >= (unsigned)num_tokens) return;
+  // the unit's projection, and its arguments chosen by uniform selects with
+  // constant indices (a computed index into the argument block would copy it
+  // to scratch; a call per projection would inline the body four times)
+  const int p = (np > 1 && k >= m.first[1]) + (np > 2 && k >= m.first[2]) + (np > 3 && k >= m.first[3]);
+  DevW w;
+#define LORA_SEL(f) w.f = p == 0 ? m.w[0].f : p == 1 ? m.w[1].f : p == 2 ? m.w[2].f : m.w[3].f
+  LORA_SEL(a_pages); LORA_SEL(b_pages); LORA_SEL(rank); LORA_SEL(a_pt); LORA_SEL(b_pt);
+  LORA_SEL(a_sc); LORA_SEL(b_sc); LORA_SEL(a_row_bytes); LORA_SEL(b_row_bytes);
+  LORA_SEL(d_in); LORA_SEL(d_out); LORA_SEL(num_adapters); LORA_SEL(r_max); LORA_SEL(page_rows);
+  LORA_SEL(max_pages); LORA_SEL(num_pages_a); LORA_SEL(num_pages_b);
+#undef LORA_SEL
+  const int first = p == 0 ? m.first[0] : p == 1 ? m.first[1] : p == 2 ? m.first[2] : m.first[3];
+  const int bc = p == 0 ? m.block_cols[0] : p == 1 ? m.block_cols[1] : p == 2 ? m.block_cols[2] : m.block_cols[3];
+  float *vp = p == 0 ? m.v[0] : p == 1 ? m.v[1] : p == 2 ? m.v[2] : m.v[3];
+  T *yp = p == 0 ? m.y[0] : p == 1 ? m.y[1] : p == 2 ? m.y[2] : m.y[3];
+  fused_unit<T, W, AL>(w, ids, t, k - first, bc, x, vp, yp, sm);
 }
 
 // Fused per-token delta, adapter-major: work unit (adapter a, column block
@@ -1828,4 +1884,68 @@ extern "C" lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *tok
                          (const T *)x, v, (T *)y);
   });
   return check_launch("bgmv fused launch");
+}
+
+extern "C" lora_status lora_bgmv_fused_multi(const lora_weights *const *w, int32_t num_proj,
+                                             const int32_t *token_adapter, int32_t num_tokens,
+                                             const int32_t *token_order, int32_t num_ordered,
+                                             const void *x, float *const *v, void *const *y,
+                                             hipStream_t stream) {
+  if (!w || !y) return fail(LORA_EINVAL, "null pointer");
+  if (num_proj < 1 || num_proj > kMaxProj)
+    return fail(LORA_EINVAL, "num_proj %d outside 1..%d", num_proj, kMaxProj);
+  if (num_tokens < 0) return fail(LORA_EINVAL, "negative num_tokens");
+  if (token_order && (num_ordered < 0 || num_ordered > num_tokens))
+    return fail(LORA_EINVAL, "num_ordered %d outside 0..num_tokens", num_ordered);
+  MultiArgs<uint16_t> mb{};  // pointers are retyped per element type below
+  bool aligned = true;
+  for (int p = 0; p < num_proj; ++p) {
+    lora_status st = to_dev(w[p], &mb.w[p]);
+    if (st != LORA_OK) return st;
+    if (w[p]->dtype != w[0]->dtype || w[p]->weight_format != w[0]->weight_format ||
+        w[p]->d_in != w[0]->d_in || w[p]->num_adapters != w[0]->num_adapters)
+      return fail(LORA_EINVAL, "projection %d differs from projection 0 in dtype, format, d_in "
+                  "or adapter count", p);
+    if (!y[p] || !aligned16(y[p]) || (v && v[p] && !aligned16(v[p])))
+      return fail(LORA_EINVAL, "projection %d: null or misaligned output", p);
+    aligned = aligned && (!w[p]->a_page_table || w[p]->page_rows % 16 == 0);
+  }
+  if (num_tokens == 0 || w[0]->num_adapters == 0) return ok();
+  if (!token_adapter || !x) return fail(LORA_EINVAL, "null pointer");
+  if (!aligned16(x)) return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
+  const int units = token_order ? num_ordered : num_tokens;
+  if (units == 0) return ok();
+  // column blocks: whole 4096-column passes, enough units in all for ~256
+  // workgroups
+  mb.first[0] = 0;
+  for (int p = 0; p < num_proj; ++p) {
+    const int passes = (w[p]->d_out + kFusedPass - 1) / kFusedPass;
+    int nblk = (kFusedMinGroups + units * num_proj - 1) / (units * num_proj);
+    nblk = nblk < 1 ? 1 : (nblk > passes ? passes : nblk);
+    mb.block_cols[p] = ((passes + nblk - 1) / nblk) * kFusedPass;
+    nblk = (w[p]->d_out + mb.block_cols[p] - 1) / mb.block_cols[p];
+    mb.first[p + 1] = mb.first[p] + nblk;
+  }
+  for (int p = num_proj + 1; p <= kMaxProj; ++p) mb.first[p] = mb.first[num_proj];
+  if ((int64_t)units * mb.first[num_proj] > INT32_MAX - 8) return fail(LORA_EINVAL, "batch too large");
+  const dim3 grid(pad8(units * mb.first[num_proj]));
+  with_types(w[0], [&](auto t, auto wt) {
+    using T = decltype(t);
+    using W = decltype(wt);
+    MultiArgs<T> m{};
+    for (int p = 0; p < kMaxProj; ++p) {
+      m.w[p] = mb.w[p];
+      m.y[p] = p < num_proj ? (T *)y[p] : nullptr;
+      m.v[p] = (p < num_proj && v) ? v[p] : nullptr;
+      m.block_cols[p] = mb.block_cols[p];
+    }
+    for (int p = 0; p <= kMaxProj; ++p) m.first[p] = mb.first[p];
+    if (aligned)
+      hipLaunchKernelGGL((bgmv_fused_multi_kernel<T, W, true>), grid, dim3(kFusedThreads), 0, stream,
+                         m, num_proj, token_adapter, num_tokens, token_order, units, (const T *)x);
+    else
+      hipLaunchKernelGGL((bgmv_fused_multi_kernel<T, W, false>), grid, dim3(kFusedThreads), 0, stream,
+                         m, num_proj, token_adapter, num_tokens, token_order, units, (const T *)x);
+  });
+  return check_launch("bgmv fused multi launch");
 }

@@ -449,3 +449,36 @@ def test_quant_hetero_paged_full_size(wq):
     torch.cuda.synchronize()
     check_v(dp, v, f"quant-hetero/{wq}")
     check_y(dp, y, oracle_y(p), f"quant-hetero/{wq}")
+
+
+# ------------------------------------------------------------------ several projections, one launch
+@pytest.mark.parametrize("wq", ["", "fp8"])
+def test_fused_multi_projection(wq):
+    """q, k and v deltas of one batch in one launch: bit-identical to three
+    single-projection fused launches (index order and segment order), and each
+    within the bf16 bound of the oracle."""
+    R = runner()
+    shapes = [("q", 1024), ("k", 256), ("v", 264)]
+    p0 = wl.bgmv_decode(num_tokens=96, num_adapters=40, d_in=1024, d_out=1024, seed=31, wq=wq)
+    probs = [p0]
+    for i, (_, d_out) in enumerate(shapes[1:]):
+        p = wl.make_problem(f"multi_{i}", None, None, [16] * 40, 1024, d_out, "bf16", 40 + i,
+                            mode="bgmv", ids=p0.ids, wq=wq)
+        p.x = p0.x
+        probs.append(p)
+    say(f"fused multi-projection wq={wq or 'bf16'}")
+    dps = [R.DeviceProblem(p) for p in probs]
+    x = dps[0].x
+    ids = dps[0].ids
+    for grouped in (False, True):
+        order = dps[0].segments()[3] if grouped else None
+        ys = [dp.y0.clone() for dp in dps]
+        vs = [dp.new_v() for dp in dps]
+        B.lora_bgmv_fused_multi([dp.weights for dp in dps], ids, x, ys, vs, token_order=order)
+        singles = [dp.run_bgmv_fused(token_order=order) for dp in dps]
+        torch.cuda.synchronize()
+        for (y1, v1), y, v in zip(singles, ys, vs):
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+            assert torch.equal(v, v1)
+    for dp, p, y in zip(dps, probs, ys):
+        check_y(dp, y, oracle_y(p), f"multi {p.name}")
