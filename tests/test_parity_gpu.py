@@ -482,3 +482,54 @@ def test_fused_multi_projection(wq):
             assert torch.equal(v, v1)
     for dp, p, y in zip(dps, probs, ys):
         check_y(dp, y, oracle_y(p), f"multi {p.name}")
+
+
+# ------------------------------------------------------------------ configs 3 and 4 at full size
+def _sample_rows(p, n_random=32, seed=0):
+    """Token rows to check: the first and last token of every segment (in batch
+    order) plus random ones."""
+    ids = p.ids
+    edges = np.flatnonzero(np.diff(ids) != 0)
+    rows = set([0, ids.size - 1] + edges.tolist() + (edges + 1).tolist())
+    rng = np.random.default_rng(seed)
+    rows.update(rng.choice(ids.size, size=n_random, replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _check_rows(dp, y_gpu, rows, label):
+    p = dp.p
+    got = host_y(dp, y_gpu)[rows]
+    y_in = p.y[rows]
+    want = oracle.apply(p.x[rows], y_in, p.ids[rows], oracle_adapters(p))
+    err = normwise(got, want)
+    say(f"{label}: normwise y error {err:.3e} over {rows.size} full rows")
+    assert err <= TOL[p.dtype], label
+    scale = np.max(np.abs(want), axis=1, keepdims=True)
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0**-8 + 1e-4 * scale), label
+
+
+@pytest.mark.parametrize("shape", ["q", "up"])
+def test_sgmv_prefill_full_size(shape):
+    """The prefill batch as benchmarked: 8192 tokens in 32 Zipf-length requests,
+    automatic path policy, dense stacks; full output rows checked at every
+    segment boundary and at random tokens."""
+    R = runner()
+    p = wl.sgmv_prefill(shape=shape)
+    say(f"prefill full size {shape}: {p.num_tokens} tokens, {p.d_in} -> {p.d_out}")
+    dp = R.DeviceProblem(p)
+    y, _ = dp.run_sgmv()
+    torch.cuda.synchronize()
+    _check_rows(dp, y, _sample_rows(p), f"prefill {shape}")
+
+
+def test_hetero_paged_full_size():
+    """The heterogeneous paged batch as benchmarked (bf16 rows, ranks 8..64,
+    shuffled 16-row pages, automatic policy), every row against the oracle."""
+    R = runner()
+    p = wl.hetero_paged()
+    say(f"hetero paged full size: {p.num_tokens} tokens, ranks {sorted(set(p.ranks.tolist()))}")
+    dp = R.DeviceProblem(p)
+    y, v = dp.run_sgmv()
+    torch.cuda.synchronize()
+    check_v(dp, v, "hetero full")
+    check_y(dp, y, oracle_y(p), "hetero full")
