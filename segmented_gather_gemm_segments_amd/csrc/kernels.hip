@@ -694,12 +694,19 @@ template <> struct ExpandCfg<uint16_t> { static constexpr int kRowStride = kExpa
 template <> struct ExpandCfg<float> { static constexpr int kRowStride = kExpandK + 4; };
 
 constexpr int kVStride = kExpandK + 4;  // LDS row stride (floats) of the staged v rows: j + pad
+// bf16 activations: each staged v row holds the chunk's bf16 hi parts, then
+// its bf16 lo parts (v = hi + lo exactly to fp32 rounding), then a pad; the
+// split is done once per staged chunk instead of in every wave's MFMA loop.
+constexpr int kVhlStride = 2 * kExpandK + 8;  // bf16 elements
 
 template <typename T>
 struct alignas(16) ExpandSmem {
   int toks[kMaxItemTokens];
   T bt[4 * 64 * ExpandCfg<T>::kRowStride];  // MFMA path, per wave: [64 cols][j]
-  float vs[64 * kVStride];                   // MFMA path: [token][j] of the 64 tokens
+  union {
+    float vs[64 * kVStride];       // MFMA path, fp32: [token][j] of the 64 tokens
+    uint16_t vhl[64 * kVhlStride];  // MFMA path, bf16: [token][hi j | lo j | pad]
+  };
 };
 
 // One gather/GEMV expand tile: tokens toks[g0 .. g0+ntok) (ntok <= TG) over
@@ -951,7 +958,24 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
       for (int it = 0; it < kVIt; ++it) {
         const int idx = tid + kThreads * it;
         const int ti = idx / nq, q = idx - ti * nq;
-        if (ti < 64) *reinterpret_cast<float4 *>(&sm.vs[ti * kVStride + 4 * q]) = vq[it];
+        if (ti < 64) {
+          if constexpr (sizeof(T) == 2) {
+            // v = hi + lo, each a bf16: hi = RNE(v), lo = RNE(v - hi)
+            const float f[4] = {vq[it].x, vq[it].y, vq[it].z, vq[it].w};
+            uint32_t hb[4], lb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hb[e] = bf16_rne(f[e]);
+              lb[e] = bf16_rne(f[e] - __uint_as_float(hb[e] << 16));
+            }
+            uint16_t *row = &sm.vhl[ti * kVhlStride + 4 * q];
+            *reinterpret_cast<uint2 *>(row) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+            *reinterpret_cast<uint2 *>(row + kExpandK) =
+                make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+          } else {
+            *reinterpret_cast<float4 *>(&sm.vs[ti * kVStride + 4 * q]) = vq[it];
+          }
+        }
       }
       __syncthreads();
       for (int kb = 0; kb * 16 < nj; ++kb) {
@@ -967,20 +991,9 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             if (tt < ntt) {
-              const float *vl = &sm.vs[(tt * 16 + m) * kVStride + jb];
-              const float4 p0 = *reinterpret_cast<const float4 *>(vl);
-              const float4 p1 = *reinterpret_cast<const float4 *>(vl + 4);
-              const float f[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-              uint32_t h[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                uint32_t hb = bf16_rne(f[e]);
-                if (g >= 2) hb = bf16_rne(f[e] - __uint_as_float(hb << 16));
-                h[e] = hb;
-              }
-              const bf16x8_t bop = __builtin_bit_cast(
-                  bf16x8_t, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                       h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
+              // lanes g < 2 take the hi parts, g >= 2 the lo parts of v[tok][jb .. jb+7]
+              const bf16x8_t bop = *reinterpret_cast<const bf16x8_t *>(
+                  &sm.vhl[(tt * 16 + m) * kVhlStride + (g >> 1) * kExpandK + jb]);
 #pragma unroll
               for (int t = 0; t < 4; ++t)
                 acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop, acc[tt][t], 0, 0, 0);
