@@ -197,6 +197,45 @@ __device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, in
   rows16<W, true, AL>(w, side_b(w), a, j0, r, col, safe, rp, lsc);
 }
 
+// Byte addresses of N rows j[i] (>= 0) of adapter a on one side, each plus
+// `ofs`, or `safe` where !use[i] or the row's page is past the page table or
+// out of range; stored[i] gets the row's storage index (page * page_rows + row
+// in page), or -1 where `safe` is returned.  All N page-id loads are issued
+// (clamped indices, unconditional) before any is used, and the rest is
+// selects, not branches: the lookups overlap each other and do not wait for
+// loads issued before them.  Storage indices fit int32 (checked on the host).
+template <int N>
+__device__ __forceinline__ void rows_addr(const DevW &w, const Side &sd, int a, const int (&j)[N],
+                                          const bool (&use)[N], int64_t ofs, const char *safe,
+                                          const char *(&p)[N], int (&stored)[N]) {
+  const int pr = w.page_rows;
+  int page[N], r_in[N];
+  if (sd.pt) {
+    const int32_t *row = sd.pt + (int64_t)a * w.max_pages;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int pi = j[i] / pr;
+      page[i] = row[min(pi, w.max_pages - 1)];
+      r_in[i] = j[i] - pi * pr;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) page[i] = j[i] / pr < w.max_pages ? page[i] : -1;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      page[i] = a;
+      r_in[i] = j[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool ok = use[i] && (unsigned)page[i] < (unsigned)sd.num_pages;
+    const int idx = (int)((unsigned)page[i] * (unsigned)pr + (unsigned)r_in[i]);
+    stored[i] = ok ? idx : -1;
+    p[i] = sel_ptr(ok, sd.pages + (int64_t)(ok ? idx : 0) * sd.row_bytes + ofs, safe);
+  }
+}
+
 __device__ __forceinline__ int adapter_rank(const DevW &w, int a) {
   int r = w.rank[a];
   return r < 0 ? 0 : (r > w.r_max ? w.r_max : r);
@@ -835,33 +874,54 @@ __device__ __forceinline__ void load_v8(const float *vr, int jb, int nj, bool ve
 }
 
 // Stages rows jc .. jc + 8 NR of this wave's 64-column B^T slab into LDS,
-// transposed ([column][j]); lane l takes row (l >> 3) + 8 i and columns
-// 8 (l & 7) .. +7.  Rows past nj (the rank) and columns past d_out are zero.
-// The NR loads are issued unconditionally (safe address, zero-selected) before
-// the first store.
+// transposed ([column][j]); lane l takes the row pairs 2p, 2p + 1 with
+// p = (l >> 3) + 8 i, columns 8 (l & 7) .. +7, and writes each column's two
+// rank indices as one 4-byte (bf16) or 8-byte (fp32) LDS word.  Rows past nj
+// (the rank) and columns past d_out are zero.  The row addresses come from
+// one batch of page lookups and the NR loads are issued unconditionally (safe
+// address, zero-selected) before the first store.
 template <typename T, typename W, int NR>
 __device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj, int c0, T *bt, int lane) {
+  static_assert(NR % 2 == 0, "row pairs");
   constexpr int RS = ExpandCfg<T>::kRowStride;
-  const char *safe = w.b_pages;
+  static_assert(RS % 2 == 0, "pair words stay aligned");
   const int cc = (lane & 7) * 8;
+  int jrow[NR], stored[NR];
+  bool use[NR];
   const char *rp[NR];
-  bool ok[NR];
 #pragma unroll
   for (int it = 0; it < NR; ++it) {
-    const int jr = (lane >> 3) + 8 * it;
-    const char *br = (jr < nj && c0 + cc < w.d_out) ? b_row(w, a, jc + jr) : nullptr;
-    ok[it] = br != nullptr;
-    rp[it] = br ? br + wofs<W>(c0 + cc) : safe;
+    const int jr = 2 * ((lane >> 3) + 8 * (it >> 1)) + (it & 1);
+    jrow[it] = jc + jr;
+    use[it] = jr < nj && c0 + cc < w.d_out;
   }
+  rows_addr<NR>(w, side_b(w), a, jrow, use, wofs<W>(c0 + cc), w.b_pages, rp, stored);
   Raw8<W> braw[NR];
 #pragma unroll
   for (int it = 0; it < NR; ++it) wload(braw[it], rp[it]);
 #pragma unroll
-  for (int it = 0; it < NR; ++it) {
-    const int jr = (lane >> 3) + 8 * it;
-    if (!ok[it]) raw_zero(braw[it]);
+  for (int ip = 0; ip < NR / 2; ++ip) {
+    const int jr = 2 * ((lane >> 3) + 8 * ip);
+    Raw8<W> b0 = braw[2 * ip], b1 = braw[2 * ip + 1];
+    if (stored[2 * ip] < 0) raw_zero(b0);
+    if (stored[2 * ip + 1] < 0) raw_zero(b1);
+    if constexpr (sizeof(T) == 2) {
+      // bf16 bits of the two rows; column e's pair is (row 2p: element e, row
+      // 2p + 1: element e) = the low or high halves of word e / 2 of each
+      const uint4 u0 = raw_bf16(b0), u1 = raw_bf16(b1);
+      const uint32_t w0[4] = {u0.x, u0.y, u0.z, u0.w}, w1[4] = {u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bt[(cc + e) * RS + jr] = w_as_t<T, W>(braw[it], e);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t pair = (e & 1) ? __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], 0x07060302u)
+                                      : __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], 0x05040100u);
+        *reinterpret_cast<uint32_t *>(bt + (cc + e) * RS + jr) = pair;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<float2 *>(bt + (cc + e) * RS + jr) =
+            make_float2(w_as_t<T, W>(b0, e), w_as_t<T, W>(b1, e));
+    }
   }
 }
 
@@ -942,10 +1002,26 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
         vq[it].z = ok && j + 2 < r ? vq[it].z : 0.f;
         vq[it].w = ok && j + 3 < r ? vq[it].w : 0.f;
         if constexpr (WT<W>::kScaled) {  // B^T row scales fold into v
-          vq[it].x *= j < r ? b_scale<W>(w, a, j) : 0.f;
-          vq[it].y *= j + 1 < r ? b_scale<W>(w, a, j + 1) : 0.f;
-          vq[it].z *= j + 2 < r ? b_scale<W>(w, a, j + 2) : 0.f;
-          vq[it].w *= j + 3 < r ? b_scale<W>(w, a, j + 3) : 0.f;
+          // the four rows' page lookups in one batch, the scale loads unconditional
+          int jrow[4], stored[4];
+          bool use[4];
+          const char *unused[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            jrow[e] = min(j + e, r - 1);
+            use[e] = j + e < r;
+          }
+          rows_addr<4>(w, side_b(w), a, jrow, use, 0, w.b_pages, unused, stored);
+          float sc[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sl = w.b_sc[stored[e] >= 0 ? stored[e] : 0];
+            sc[e] = stored[e] >= 0 ? sl : 0.f;
+          }
+          vq[it].x *= sc[0];
+          vq[it].y *= sc[1];
+          vq[it].z *= sc[2];
+          vq[it].w *= sc[3];
         }
       }
       switch (nj16 >> 3) {
