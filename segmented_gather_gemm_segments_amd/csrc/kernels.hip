@@ -1834,9 +1834,19 @@ extern "C" lora_status lora_sgmv_shrink(const lora_weights *w, const int32_t *to
   with_types(w, [&](auto t, auto wt) {
     using T = decltype(t);
     using W = decltype(wt);
-    hipLaunchKernelGGL((sgmv_shrink_kernel<T, W, kSgmvShrinkThreads>), dim3(num_items),
-                       dim3(kSgmvShrinkThreads), 0, stream, d, token_perm, num_perm, items,
-                       num_tokens, (const T *)x, v);
+    // bf16 rows with ranks above 32: an MFMA item reads up to four 16-row
+    // tiles of A per k-step against one of x, and twice the waves per item
+    // keep twice the k-steps in flight (the other element types would spill
+    // registers at 1024 threads)
+    constexpr bool kWide = sizeof(T) == 2 && !WT<W>::kScaled;
+    if (kWide && w->r_max > 32)
+      hipLaunchKernelGGL((sgmv_shrink_kernel<T, W, kWide ? 2 * kSgmvShrinkThreads : kSgmvShrinkThreads>),
+                         dim3(num_items), dim3(kWide ? 2 * kSgmvShrinkThreads : kSgmvShrinkThreads), 0,
+                         stream, d, token_perm, num_perm, items, num_tokens, (const T *)x, v);
+    else
+      hipLaunchKernelGGL((sgmv_shrink_kernel<T, W, kSgmvShrinkThreads>), dim3(num_items),
+                         dim3(kSgmvShrinkThreads), 0, stream, d, token_perm, num_perm, items,
+                         num_tokens, (const T *)x, v);
   });
   return check_launch("sgmv shrink launch");
 }
