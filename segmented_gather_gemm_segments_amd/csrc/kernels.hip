@@ -879,14 +879,14 @@ __device__ __forceinline__ void load_v8(const float *vr, int jb, int nj, bool ve
 // rank indices as one 4-byte (bf16) or 8-byte (fp32) LDS word.  Rows past nj
 // (the rank) and columns past d_out are zero.  The row addresses come from
 // one batch of page lookups and the NR loads are issued unconditionally (safe
-// address, zero-selected) before the first store.
+// address, zero-selected) before the first store.  slab_issue issues the
+// loads, slab_store writes them, so other loads can be issued in between.
 template <typename T, typename W, int NR>
-__device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj, int c0, T *bt, int lane) {
+__device__ __forceinline__ void slab_issue(const DevW &w, int a, int jc, int nj, int c0, int lane,
+                                           Raw8<W> (&braw)[NR], int (&stored)[NR]) {
   static_assert(NR % 2 == 0, "row pairs");
-  constexpr int RS = ExpandCfg<T>::kRowStride;
-  static_assert(RS % 2 == 0, "pair words stay aligned");
   const int cc = (lane & 7) * 8;
-  int jrow[NR], stored[NR];
+  int jrow[NR];
   bool use[NR];
   const char *rp[NR];
 #pragma unroll
@@ -896,9 +896,16 @@ __device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj,
     use[it] = jr < nj && c0 + cc < w.d_out;
   }
   rows_addr<NR>(w, side_b(w), a, jrow, use, wofs<W>(c0 + cc), w.b_pages, rp, stored);
-  Raw8<W> braw[NR];
 #pragma unroll
   for (int it = 0; it < NR; ++it) wload(braw[it], rp[it]);
+}
+
+template <typename T, typename W, int NR>
+__device__ __forceinline__ void slab_store(const Raw8<W> (&braw)[NR], const int (&stored)[NR], T *bt,
+                                           int lane) {
+  constexpr int RS = ExpandCfg<T>::kRowStride;
+  static_assert(RS % 2 == 0, "pair words stay aligned");
+  const int cc = (lane & 7) * 8;
 #pragma unroll
   for (int ip = 0; ip < NR / 2; ++ip) {
     const int jr = 2 * ((lane >> 3) + 8 * ip);
@@ -923,6 +930,14 @@ __device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj,
             make_float2(w_as_t<T, W>(b0, e), w_as_t<T, W>(b1, e));
     }
   }
+}
+
+template <typename T, typename W, int NR>
+__device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj, int c0, T *bt, int lane) {
+  Raw8<W> braw[NR];
+  int stored[NR];
+  slab_issue<T, W, NR>(w, a, jc, nj, c0, lane, braw, stored);
+  slab_store<T, W, NR>(braw, stored, bt, lane);
 }
 
 // MFMA expand for tokens toks[0..cnt) of adapter a over the 256 columns of
@@ -1117,6 +1132,171 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
   }
 }
 
+// MFMA expand for ranks up to 16 (one staged chunk): the same arithmetic as
+// expand_mfma, with the order of the loads changed.  The chunk's v and B^T
+// loads are issued before the tokens' y chunks, so that waiting for the
+// chunk (loads complete in issue order) does not wait for y: the LDS staging,
+// the barrier and the MFMAs overlap y's flight.  Straight-line within a pass
+// of 64 tokens, so no loop-carried state makes the compiler wait for y early.
+template <typename T, typename W>
+__device__ __forceinline__ void expand_mfma_r16(const DevW &w, int a, int r, int blk, const int *toks,
+                                                int cnt, int num_tokens, const float *__restrict__ v,
+                                                T *__restrict__ y, ExpandSmem<T> &sm) {
+  constexpr int RS = ExpandCfg<T>::kRowStride;
+  static_assert(64 * 4 == kThreads, "one float4 of v (16 rank indices x 64 tokens) per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int c0 = blk * LORA_EXPAND_MFMA_COLS + wave * 64;
+  const bool vec_v = (w.r_max & 3) == 0;
+  T *bt = sm.bt + wave * 64 * RS;
+  for (int m0 = 0; m0 < cnt; m0 += 64) {
+    const int ntt = min(4, (cnt - m0 + 15) >> 4);
+    // ---- this thread's v group: token ti of the pass, indices 4q .. 4q+3
+    const int ti = tid >> 2, q = tid & 3, j = 4 * q;
+    const int iv = m0 + ti;
+    const int tl = toks[min(iv, cnt - 1)];
+    const int tv = iv < cnt ? tl : -1;
+    const bool okv = tv >= 0 && tv < num_tokens;
+    const float *vr = v + (int64_t)(okv ? tv : 0) * w.r_max;
+    float4 vq;
+    if (vec_v) {  // uniform; indices past r_max are zeroed below
+      vq = *reinterpret_cast<const float4 *>(vr + min(j, w.r_max - 4));
+    } else {
+      vq.x = vr[min(j, w.r_max - 1)];
+      vq.y = vr[min(j + 1, w.r_max - 1)];
+      vq.z = vr[min(j + 2, w.r_max - 1)];
+      vq.w = vr[min(j + 3, w.r_max - 1)];
+    }
+    float sc[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (WT<W>::kScaled) {  // B^T row scales, folded into v
+      int jrow[4], stored[4];
+      bool use[4];
+      const char *unused[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        jrow[e] = min(j + e, r - 1);
+        use[e] = j + e < r;
+      }
+      rows_addr<4>(w, side_b(w), a, jrow, use, 0, w.b_pages, unused, stored);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sl = w.b_sc[stored[e] >= 0 ? stored[e] : 0];
+        sc[e] = stored[e] >= 0 ? sl : 0.f;
+      }
+    }
+    // ---- this wave's B^T slab rows 0 .. 15
+    Raw8<W> braw[2];
+    int bstored[2];
+    slab_issue<T, W, 2>(w, a, 0, r, c0, lane, braw, bstored);
+    // ---- then the y chunks: lane (g, m) of tile tt touches columns
+    // c0 + 32q + 8g .. +7 (row 0 / column 0 stand in where there is no token
+    // or column; those values are never stored)
+    int tok[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int i = m0 + tt * 16 + m;
+      const int t = (tt < ntt && i < cnt) ? toks[i] : -1;
+      tok[tt] = (t >= 0 && t < num_tokens) ? t : -1;
+    }
+    Raw8<T> yraw[4][2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int col = c0 + 32 * qq + 8 * g;
+        const int64_t row = tok[tt] >= 0 ? tok[tt] : 0;
+        raw_load(yraw[tt][qq], y + row * w.d_out + (col < w.d_out ? col : 0));
+      }
+    // ---- stage the chunk
+    if (m0 > 0) __syncthreads();  // the previous pass's readers of the slab and v rows are done
+    {
+      const float f[4] = {vq.x, vq.y, vq.z, vq.w};
+      float fv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fv[e] = okv && j + e < r ? f[e] * sc[e] : 0.f;
+      if constexpr (sizeof(T) == 2) {
+        // v = hi + lo, each a bf16: hi = RNE(v), lo = RNE(v - hi)
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hb[e] = bf16_rne(fv[e]);
+          lb[e] = bf16_rne(fv[e] - __uint_as_float(hb[e] << 16));
+        }
+        uint16_t *row = &sm.vhl[ti * kVhlStride + 4 * q];
+        *reinterpret_cast<uint2 *>(row) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        *reinterpret_cast<uint2 *>(row + kExpandK) =
+            make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+      } else {
+        *reinterpret_cast<float4 *>(&sm.vs[ti * kVStride + 4 * q]) =
+            make_float4(fv[0], fv[1], fv[2], fv[3]);
+      }
+    }
+    slab_store<T, W, 2>(braw, bstored, bt, lane);
+    __syncthreads();
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(T) == 2) {
+      // A operand (B^T slab, transposed): sub-tile t, row rho = m -> column
+      // slab_col(t, m), rank indices (g&1)*8 .. +7 for the hi (g < 2) and lo
+      // (g >= 2) halves; B operand: v's hi or lo parts of the same indices
+      const int jb = (g & 1) * 8;
+      bf16x8_t aop[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        aop[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bt + slab_col(t, m) * RS + jb));
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (tt < ntt) {
+          const bf16x8_t bop = *reinterpret_cast<const bf16x8_t *>(
+              &sm.vhl[(tt * 16 + m) * kVhlStride + (g >> 1) * kExpandK + jb]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop, acc[tt][t], 0, 0, 0);
+        }
+      }
+    } else {
+      // four K=4 steps: lane group g takes rank index 4q + g
+#pragma unroll
+      for (int qk = 0; qk < 4; ++qk) {
+        const int jj = 4 * qk + g;
+        float aop[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) aop[t] = bt[slab_col(t, m) * RS + jj];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (tt < ntt) {
+            const float bop = sm.vs[(tt * 16 + m) * kVStride + jj];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[t], bop, acc[tt][t], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // ---- y update: lane (g, m) holds columns c0 + 32q + 8g .. +7 of token tok[tt]
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int col = c0 + 32 * qq + 8 * g;
+        if (tt < ntt && tok[tt] >= 0 && col < w.d_out) {
+          float yv[8];
+          raw_cvt(yraw[tt][qq], yv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            yv[e] += acc[tt][2 * qq][e];
+            yv[4 + e] += acc[tt][2 * qq + 1][e];
+          }
+          store8(y + (int64_t)tok[tt] * w.d_out + col, yv);
+        }
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------- kernels
 __device__ __forceinline__ bool decode_item(const lora_item &it, const DevW &w, int num_perm,
                                             int &pb, int &a, int &cnt, int &path, int &blk) {
@@ -1173,8 +1353,10 @@ void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
   for (int i = threadIdx.x; i < cnt; i += kThreads) sm.toks[i] = perm[pb + i];
   __syncthreads();
   const int r = adapter_rank(w, a);
-  if (path == LORA_PATH_MFMA)
-    expand_mfma<T, W>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+  if (path == LORA_PATH_MFMA) {
+    if (r <= 16) expand_mfma_r16<T, W>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+    else expand_mfma<T, W>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+  }
   else
     expand_gemv<T, W, kThreads>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
 }
