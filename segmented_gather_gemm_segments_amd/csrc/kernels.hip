@@ -1132,18 +1132,20 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
   }
 }
 
-// MFMA expand for ranks up to 16 (one staged chunk): the same arithmetic as
-// expand_mfma, with the order of the loads changed.  The chunk's v and B^T
+// MFMA expand for ranks up to 8 NR (one staged chunk, NR = 2 or 4): the same
+// arithmetic as expand_mfma, with the order of the loads changed.  The chunk's v and B^T
 // loads are issued before the tokens' y chunks, so that waiting for the
 // chunk (loads complete in issue order) does not wait for y: the LDS staging,
 // the barrier and the MFMAs overlap y's flight.  Straight-line within a pass
 // of 64 tokens, so no loop-carried state makes the compiler wait for y early.
-template <typename T, typename W>
-__device__ __forceinline__ void expand_mfma_r16(const DevW &w, int a, int r, int blk, const int *toks,
+template <typename T, typename W, int NR>
+__device__ __forceinline__ void expand_mfma_one(const DevW &w, int a, int r, int blk, const int *toks,
                                                 int cnt, int num_tokens, const float *__restrict__ v,
                                                 T *__restrict__ y, ExpandSmem<T> &sm) {
   constexpr int RS = ExpandCfg<T>::kRowStride;
-  static_assert(64 * 4 == kThreads, "one float4 of v (16 rank indices x 64 tokens) per thread");
+  constexpr int KQ = 2 * NR;                 // float4 groups of v per token (8 NR indices)
+  constexpr int VIT = 64 * KQ / kThreads;    // float4 groups per thread
+  static_assert(VIT * kThreads == 64 * KQ && 8 * NR <= kExpandK, "whole groups; fits the slab");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int c0 = blk * LORA_EXPAND_MFMA_COLS + wave * 64;
@@ -1151,43 +1153,50 @@ __device__ __forceinline__ void expand_mfma_r16(const DevW &w, int a, int r, int
   T *bt = sm.bt + wave * 64 * RS;
   for (int m0 = 0; m0 < cnt; m0 += 64) {
     const int ntt = min(4, (cnt - m0 + 15) >> 4);
-    // ---- this thread's v group: token ti of the pass, indices 4q .. 4q+3
-    const int ti = tid >> 2, q = tid & 3, j = 4 * q;
-    const int iv = m0 + ti;
-    const int tl = toks[min(iv, cnt - 1)];
-    const int tv = iv < cnt ? tl : -1;
-    const bool okv = tv >= 0 && tv < num_tokens;
-    const float *vr = v + (int64_t)(okv ? tv : 0) * w.r_max;
-    float4 vq;
-    if (vec_v) {  // uniform; indices past r_max are zeroed below
-      vq = *reinterpret_cast<const float4 *>(vr + min(j, w.r_max - 4));
-    } else {
-      vq.x = vr[min(j, w.r_max - 1)];
-      vq.y = vr[min(j + 1, w.r_max - 1)];
-      vq.z = vr[min(j + 2, w.r_max - 1)];
-      vq.w = vr[min(j + 3, w.r_max - 1)];
-    }
-    float sc[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (WT<W>::kScaled) {  // B^T row scales, folded into v
-      int jrow[4], stored[4];
-      bool use[4];
-      const char *unused[4];
+    // ---- this thread's v groups: (token ti of the pass, indices 4q .. 4q+3)
+    float4 vq[VIT];
+    float sc[VIT][4];
+    bool okv[VIT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        jrow[e] = min(j + e, r - 1);
-        use[e] = j + e < r;
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = tid + kThreads * it;
+      const int ti = idx / KQ, q = idx % KQ, j = 4 * q;
+      const int iv = m0 + ti;
+      const int tl = toks[min(iv, cnt - 1)];
+      const int tv = iv < cnt ? tl : -1;
+      okv[it] = tv >= 0 && tv < num_tokens;
+      const float *vr = v + (int64_t)(okv[it] ? tv : 0) * w.r_max;
+      if (vec_v) {  // uniform; indices past r_max are zeroed below
+        vq[it] = *reinterpret_cast<const float4 *>(vr + min(j, w.r_max - 4));
+      } else {
+        vq[it].x = vr[min(j, w.r_max - 1)];
+        vq[it].y = vr[min(j + 1, w.r_max - 1)];
+        vq[it].z = vr[min(j + 2, w.r_max - 1)];
+        vq[it].w = vr[min(j + 3, w.r_max - 1)];
       }
-      rows_addr<4>(w, side_b(w), a, jrow, use, 0, w.b_pages, unused, stored);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float sl = w.b_sc[stored[e] >= 0 ? stored[e] : 0];
-        sc[e] = stored[e] >= 0 ? sl : 0.f;
+      for (int e = 0; e < 4; ++e) sc[it][e] = 1.f;
+      if constexpr (WT<W>::kScaled) {  // B^T row scales, folded into v
+        int jrow[4], stored[4];
+        bool use[4];
+        const char *unused[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          jrow[e] = min(j + e, r - 1);
+          use[e] = j + e < r;
+        }
+        rows_addr<4>(w, side_b(w), a, jrow, use, 0, w.b_pages, unused, stored);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sl = w.b_sc[stored[e] >= 0 ? stored[e] : 0];
+          sc[it][e] = stored[e] >= 0 ? sl : 0.f;
+        }
       }
     }
-    // ---- this wave's B^T slab rows 0 .. 15
-    Raw8<W> braw[2];
-    int bstored[2];
-    slab_issue<T, W, 2>(w, a, 0, r, c0, lane, braw, bstored);
+    // ---- this wave's B^T slab rows 0 .. 8 NR - 1
+    Raw8<W> braw[NR];
+    int bstored[NR];
+    slab_issue<T, W, NR>(w, a, 0, r, c0, lane, braw, bstored);
     // ---- then the y chunks: lane (g, m) of tile tt touches columns
     // c0 + 32q + 8g .. +7 (row 0 / column 0 stand in where there is no token
     // or column; those values are never stored)
@@ -1209,11 +1218,14 @@ __device__ __forceinline__ void expand_mfma_r16(const DevW &w, int a, int r, int
       }
     // ---- stage the chunk
     if (m0 > 0) __syncthreads();  // the previous pass's readers of the slab and v rows are done
-    {
-      const float f[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = tid + kThreads * it;
+      const int ti = idx / KQ, q = idx % KQ, j = 4 * q;
+      const float f[4] = {vq[it].x, vq[it].y, vq[it].z, vq[it].w};
       float fv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) fv[e] = okv && j + e < r ? f[e] * sc[e] : 0.f;
+      for (int e = 0; e < 4; ++e) fv[e] = okv[it] && j + e < r ? f[e] * sc[it][e] : 0.f;
       if constexpr (sizeof(T) == 2) {
         // v = hi + lo, each a bf16: hi = RNE(v), lo = RNE(v - hi)
         uint32_t hb[4], lb[4];
@@ -1231,47 +1243,49 @@ __device__ __forceinline__ void expand_mfma_r16(const DevW &w, int a, int r, int
             make_float4(fv[0], fv[1], fv[2], fv[3]);
       }
     }
-    slab_store<T, W, 2>(braw, bstored, bt, lane);
+    slab_store<T, W, NR>(braw, bstored, bt, lane);
     __syncthreads();
     f32x4_t acc[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (sizeof(T) == 2) {
-      // A operand (B^T slab, transposed): sub-tile t, row rho = m -> column
-      // slab_col(t, m), rank indices (g&1)*8 .. +7 for the hi (g < 2) and lo
-      // (g >= 2) halves; B operand: v's hi or lo parts of the same indices
-      const int jb = (g & 1) * 8;
-      bf16x8_t aop[4];
+    for (int kb = 0; kb * 16 < r; ++kb) {
+      if constexpr (sizeof(T) == 2) {
+        // A operand (B^T slab, transposed): sub-tile t, row rho = m -> column
+        // slab_col(t, m), rank indices kb*16 + (g&1)*8 .. +7 for the hi
+        // (g < 2) and lo (g >= 2) halves; B operand: v's hi or lo parts
+        const int jb = kb * 16 + (g & 1) * 8;
+        bf16x8_t aop[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        aop[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bt + slab_col(t, m) * RS + jb));
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (tt < ntt) {
-          const bf16x8_t bop = *reinterpret_cast<const bf16x8_t *>(
-              &sm.vhl[(tt * 16 + m) * kVhlStride + (g >> 1) * kExpandK + jb]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop, acc[tt][t], 0, 0, 0);
-        }
-      }
-    } else {
-      // four K=4 steps: lane group g takes rank index 4q + g
-#pragma unroll
-      for (int qk = 0; qk < 4; ++qk) {
-        const int jj = 4 * qk + g;
-        float aop[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) aop[t] = bt[slab_col(t, m) * RS + jj];
+        for (int t = 0; t < 4; ++t)
+          aop[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bt + slab_col(t, m) * RS + jb));
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           if (tt < ntt) {
-            const float bop = sm.vs[(tt * 16 + m) * kVStride + jj];
+            const bf16x8_t bop = *reinterpret_cast<const bf16x8_t *>(
+                &sm.vhl[(tt * 16 + m) * kVhlStride + (g >> 1) * kExpandK + jb]);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-              acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[t], bop, acc[tt][t], 0, 0, 0);
+              acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[t], bop, acc[tt][t], 0, 0, 0);
+          }
+        }
+      } else {
+        // four K=4 steps: lane group g takes rank index kb*16 + 4q + g
+#pragma unroll
+        for (int qk = 0; qk < 4; ++qk) {
+          const int jj = kb * 16 + 4 * qk + g;
+          float aop[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) aop[t] = bt[slab_col(t, m) * RS + jj];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            if (tt < ntt) {
+              const float bop = sm.vs[(tt * 16 + m) * kVStride + jj];
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[t], bop, acc[tt][t], 0, 0, 0);
+            }
           }
         }
       }
@@ -1354,7 +1368,11 @@ void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
   __syncthreads();
   const int r = adapter_rank(w, a);
   if (path == LORA_PATH_MFMA) {
-    if (r <= 16) expand_mfma_r16<T, W>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+    // one-chunk ranks take the early-load path (up to 32 for unscaled rows;
+    // quantized rows' scale registers would spill there past 16)
+    constexpr int kOne = WT<W>::kScaled ? 16 : kExpandK;
+    if (r <= 16) expand_mfma_one<T, W, 2>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
+    else if (r <= kOne) expand_mfma_one<T, W, kOne / 8>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
     else expand_mfma<T, W>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
   }
   else
