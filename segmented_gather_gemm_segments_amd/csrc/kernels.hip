@@ -1588,43 +1588,37 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
 
   // ---- shrink: v[j] = sum_k A[j][k] x[k], 16 rows at a time (the first
   // 16 always, see above)
-  for (int jc = 0; jc == 0 || jc < r; jc += 16) {
-    if constexpr (WT<W>::kScaled)
-      if (jc > 0) asc = a_scale_any<W>(w, a, jc + tid, tid < 16 && jc + tid < r);
-    float acc[16];
+  // the FMAs of one k pass: acc[i] += A[i][k..k+7] . x[k..k+7]
+  auto fma_pass = [&](float (&acc)[16], const Raw8<T> &xraw, const Raw8<W> (&araw)[16], bool kin) {
+    if (kin) {
+      float xv[8];
+      raw_cvt(xraw, xv);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    for (int k0 = 0; k0 < w.d_in; k0 += kFusedPass) {
-      const int k = k0 + tid * 8;
-      const bool kin = k < w.d_in;
-      const int kc = kin ? k : 0;
-      Raw8<T> xraw;
-      Raw8<W> araw[16];
-      if (jc == 0 && k0 == 0) xraw = x0;
-      else raw_load(xraw, xr + kc);
-      if (PF && jc == 0 && k0 == 0) {
+      for (int i = 0; i < 16; ++i) {
+        float av[8];
+        raw_cvt(araw[i], av);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) araw[i] = a0[i];
-      } else {
-        const char *ap[16];
-        a_rows16<W, AL>(w, a, jc, r, kc, safe_a, ap);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
-      }
-      if (kin) {
-        float xv[8];
-        raw_cvt(xraw, xv);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float av[8];
-          raw_cvt(araw[i], av);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i] = fmaf(av[e], xv[e], acc[i]);
-        }
+        for (int e = 0; e < 8; ++e) acc[i] = fmaf(av[e], xv[e], acc[i]);
       }
     }
-    // reduce the 16 row sums over the workgroup: reduce-scatter in each wave,
-    // then the waves in order (rows at or past the rank are never used)
+  };
+  // one k pass of rows jc .. jc+15 from memory
+  auto load_pass = [&](float (&acc)[16], int jc, int k0) {
+    const int k = k0 + tid * 8;
+    const bool kin = k < w.d_in;
+    const int kc = kin ? k : 0;
+    Raw8<T> xraw;
+    Raw8<W> araw[16];
+    raw_load(xraw, xr + kc);
+    const char *ap[16];
+    a_rows16<W, AL>(w, a, jc, r, kc, safe_a, ap);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
+    fma_pass(acc, xraw, araw, kin);
+  };
+  // reduce the 16 row sums over the workgroup: reduce-scatter in each wave,
+  // then the waves in order (rows at or past the rank are never used)
+  auto reduce_rows = [&](float (&acc)[16], int jc) {
     const float part = wave_reduce_scatter<16>(acc);
     if ((lane & 3) == 0) sm.red[wave * 16 + (lane >> 2)] = part;
     __syncthreads();
@@ -1637,6 +1631,36 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
       if (v && cb == 0 && jc + tid < r) v[(int64_t)t * w.r_max + jc + tid] = sum;
     }
     __syncthreads();
+  };
+  {
+    // rows 0..15 over the first k pass from the prologue's chunks, in
+    // straight-line code: a loop here would merge the prologue's pending
+    // loads with the loop's own at its header, and the compiler would then
+    // wait for all of them (the B^T rows too) before the first FMA
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    Raw8<W> araw[16];
+    if constexpr (PF) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) araw[i] = a0[i];
+    } else {
+      const char *ap[16];
+      a_rows16<W, AL>(w, a, 0, r, kc0, safe_a, ap);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
+    }
+    fma_pass(acc, x0, araw, tid * 8 < w.d_in);
+    for (int k0 = kFusedPass; k0 < w.d_in; k0 += kFusedPass) load_pass(acc, 0, k0);
+    reduce_rows(acc, 0);
+  }
+  for (int jc = 16; jc < r; jc += 16) {
+    if constexpr (WT<W>::kScaled) asc = a_scale_any<W>(w, a, jc + tid, tid < 16 && jc + tid < r);
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < w.d_in; k0 += kFusedPass) load_pass(acc, jc, k0);
+    reduce_rows(acc, jc);
   }
 
   // ---- expand: y[col] += sum_j B^T[j][col] v[j], 8 columns per thread
