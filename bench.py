@@ -593,10 +593,14 @@ def main():
     tokens = int(np.sum(p.ids >= 0))
     ms_per_step = wall / K * 1e3
     kern = {}
+    flops = {"shrink": acc.shrink_flops(p.ids, p.ranks, p.d_in),
+             "expand": acc.expand_flops(p.ids, p.ranks, p.d_out)}
+    flops["fused"] = flops["shrink"] + flops["expand"]
     for name, (t, nbytes) in timed.items():
         kern[name] = {"avg_us": float(t.mean() * 1e6), "min_us": float(t.min() * 1e6),
                       "max_us": float(t.max() * 1e6), "bytes": nbytes,
-                      "gbs": nbytes / t.mean() / 1e9}
+                      "gbs": nbytes / t.mean() / 1e9,
+                      "tflops": flops[name] / t.mean() / 1e12}
     t_shrink, t_expand = timed["shrink"][0], timed["expand"][0]
     dom = "fused" if fused else max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
     kname = f"{mode}_{dom}"
@@ -622,6 +626,11 @@ def main():
                    "replicas": n_rep, "timed": "HIP graph replay of the K steps",
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        # the long segments' matrix-core use (reported, not targeted: the path
+        # is HBM-bound, and algorithmic flops / dense peak stays a few percent)
+        "mfma_utilisation": ({k: round(kern[k]["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
+                              for k in ("shrink", "expand")} | {"peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+                             if mode == "sgmv" and p.dtype == "bf16" else None),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for k, d in kern.items()},
         "gpu_tokens_per_s_kernel_time": round(
