@@ -391,7 +391,7 @@ def bench_layer(args, torch):
         ep = dp.plan(B.LORA_PHASE_EXPAND)
         dp._plans = (sp, ep)
         shrink, expand = B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream)
-        base = B.prepare_base_gemm(dp.x, dp.w, y, stream=stream)
+        base = B.prepare_base_gemm(dp.x, dp.w, y, workspace=dp.base_workspace(), stream=stream)
         projs.append({"name": name, "p": p, "dp": dp, "base": base, "shrink": shrink,
                       "expand": expand, "y": y})
     torch.cuda.synchronize()

@@ -426,9 +426,24 @@ void lora_cache_destroy(lora_cache *cache);
  * R^{d_out x d_in}).  bf16 in, fp32 accumulation (MFMA), bf16 out rounded to
  * nearest even.
  *   x [m][k], w [n][k], y [m][n]: row-major device arrays; k, n multiples of 8.
- * Errors: LORA_EINVAL, LORA_EUNSUPPORTED (dtype other than LORA_BF16), LORA_EHIP. */
+ *   workspace, workspace_bytes: optional device memory owned by the caller
+ *     (NULL / 0: none; 16-byte aligned).  When it holds the size that
+ *     lora_base_gemm_workspace reports for the shape (grids too small to fill
+ *     the device), k is cut into up to 4 slices whose fp32 partial tiles go
+ *     there and are added in slice order by a second launch on the same
+ *     stream; otherwise, or for a smaller workspace, k is not split.  The
+ *     workspace must not be in use by other work on the device until the
+ *     call's work on `stream` is done.
+ * Errors: LORA_EINVAL (sizes, null or misaligned pointers, negative
+ * workspace_bytes), LORA_EUNSUPPORTED (dtype other than LORA_BF16; n or k not
+ * multiples of 8), LORA_EHIP. */
 lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *x,
-                           const void *w, void *y, hipStream_t stream);
+                           const void *w, void *y, void *workspace, int64_t workspace_bytes,
+                           hipStream_t stream);
+/* Workspace bytes with which lora_base_gemm splits k for an m x n x k problem
+ * on the current device (0: it would not split).  *bytes host.  Errors:
+ * LORA_EINVAL (sizes, null bytes). */
+lora_status lora_base_gemm_workspace(int32_t m, int32_t n, int32_t k, int64_t *bytes);
 
 #ifdef __cplusplus
 }

@@ -90,7 +90,8 @@ EXPORTS = {
     "lora_cache_get_stats": ([_P, _P], _I32),
     "lora_cache_pages": ([_P, _I32, _P, _P, _P], _I32),
     "lora_cache_destroy": ([_P], None),
-    "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
+    "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_int64, _P], _I32),
+    "lora_base_gemm_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
 }
 
 
@@ -296,10 +297,31 @@ def prepare_bgmv_fused_multi(ws, token_adapter, x, ys, vs=None, stream=None, tok
                                               _dptr(x), varr, yarr, _stream(stream)), keep)
 
 
-def lora_base_gemm(x, w, y, stream=None):
+def base_gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Workspace bytes with which lora_base_gemm splits k (0: no split)."""
+    out = ctypes.c_int64(0)
+    _check(lib().lora_base_gemm_workspace(m, n, k, ctypes.byref(out)))
+    return int(out.value)
+
+
+def base_gemm_workspace(m: int, n: int, k: int, device="cuda"):
+    """A workspace tensor for lora_base_gemm on this shape, or None."""
+    nbytes = base_gemm_workspace_bytes(m, n, k)
+    if nbytes == 0:
+        return None
+    return _torch().empty((nbytes + 3) // 4, dtype=_torch().float32, device=device)
+
+
+def _ws(workspace):
+    return (_dptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def lora_base_gemm(x, w, y, workspace=None, stream=None):
     m, k = x.shape
     n = w.shape[0]
-    _check(lib().lora_base_gemm(LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y), _stream(stream)))
+    wp, wb = _ws(workspace)
+    _check(lib().lora_base_gemm(LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y), wp, wb,
+                                _stream(stream)))
 
 
 class Pool:
@@ -466,12 +488,13 @@ def prepare_sgmv(w: Weights, token_perm, shrink_items, expand_items, x, v, y, st
     return shrink, expand
 
 
-def prepare_base_gemm(x, w, y, stream=None):
+def prepare_base_gemm(x, w, y, workspace=None, stream=None):
     """Prepared lora_base_gemm launch y = x w^T on `stream` (default: current)."""
     m, k = x.shape
     n = w.shape[0]
-    return Prepared("lora_base_gemm", (LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y),
-                                       _stream(stream)), (x, w, y))
+    wp, wb = _ws(workspace)
+    return Prepared("lora_base_gemm", (LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y), wp, wb,
+                                       _stream(stream)), (x, w, y, workspace))
 
 
 def prepare_bgmv_fused(w: Weights, token_adapter, x, y, v=None, order: int = LORA_BGMV_AUTO,

@@ -10,12 +10,21 @@
 // over k in steps of 64; each wave owns a 64 x 64 sub-tile as 4 x 4 blocks of
 // v_mfma_f32_16x16x32_bf16 with W rows as the A operand and x rows as the B
 // operand, so D[n][m] leaves each lane holding 4 consecutive output columns of
-// one token (one 8-byte store).  The k-tiles of both operands are staged in LDS
-// with padded rows (72 elements) and double-buffered through registers: the
-// global loads of tile t+1 are in flight while tile t is multiplied, and one
-// barrier separates the steps.  Tiles are ordered so that the m-tiles sharing
-// one W tile run on the same XCD (workgroup b runs on XCD b % 8) and share its
-// L2.
+// one token (one 8-byte store).  The k-tiles of both operands are staged in one
+// LDS buffer with padded rows (72 elements, 36 KiB in all) and prefetched
+// through registers: the global loads of tile t+1 are in flight while tile t is
+// multiplied, then a barrier, the stores of tile t+1 into LDS, and a second
+// barrier.  One buffer rather than two, and registers bounded to three waves
+// per SIMD, let three workgroups share a compute unit instead of two; that
+// hides more latency and, with 640-tile grids (1280 tokens x 8192 columns),
+// runs them in one round of 768 slots instead of 1.25 rounds of 512.  Tiles
+// are ordered so that the m-tiles sharing one W tile run on the same XCD
+// (workgroup b runs on XCD b % 8) and share its L2.
+//
+// Grids of few tiles (1280 tokens x 1024 columns is 80 tiles, a third of the
+// compute units) split k when the caller lends an fp32 workspace: S slices of
+// each tile write fp32 partial tiles, and a second launch adds them in slice
+// order and rounds once, so the result does not depend on scheduling.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -44,16 +53,16 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 // Loads this thread's chunks of one k-tile of rows [row0, row0 + 128) of a
-// [rows][k] operand: chunk c = tid + 256 i is row c / 8, elements 8 (c % 8) ..
-// +7 of the tile.  Rows past `rows` and k past `k` read as zero.
-__device__ __forceinline__ void load_tile(const uint16_t *__restrict__ src, int rows, int k, int row0,
-                                          int k0, uint4 (&r)[kChunks]) {
+// [rows][ld] operand: chunk c = tid + 256 i is row c / 8, elements 8 (c % 8) ..
+// +7 of the tile.  Rows past `rows` and k at or past `k_end` read as zero.
+__device__ __forceinline__ void load_tile(const uint16_t *__restrict__ src, int rows, int ld, int k_end,
+                                          int row0, int k0, uint4 (&r)[kChunks]) {
 #pragma unroll
   for (int i = 0; i < kChunks; ++i) {
     const int c = (int)threadIdx.x + kGemmThreads * i;
     const int row = row0 + (c >> 3), kk = k0 + (c & 7) * 8;
-    if (row < rows && kk < k)
-      r[i] = *reinterpret_cast<const uint4 *>(src + (int64_t)row * k + kk);
+    if (row < rows && kk < k_end)
+      r[i] = *reinterpret_cast<const uint4 *>(src + (int64_t)row * ld + kk);
     else
       r[i] = make_uint4(0, 0, 0, 0);
   }
@@ -67,18 +76,20 @@ __device__ __forceinline__ void store_tile(uint16_t *lds, const uint4 (&r)[kChun
   }
 }
 
-__global__ __launch_bounds__(kGemmThreads) void base_gemm_kernel(int m, int n, int k, int tiles_m,
-                                                                 int tiles,
-                                                                 const uint16_t *__restrict__ x,
-                                                                 const uint16_t *__restrict__ w,
-                                                                 uint16_t *__restrict__ y) {
-  __shared__ uint16_t sw[2][kBN * kLd];
-  __shared__ uint16_t sx[2][kBM * kLd];
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void base_gemm_kernel(int m, int n, int k, int tiles_m, int tiles, int splits, int k_slice,
+                      const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                      uint16_t *__restrict__ y, float *__restrict__ part) {
+  __shared__ uint16_t sw[kBN * kLd];
+  __shared__ uint16_t sx[kBM * kLd];
   // XCD-aware order: the grid is a multiple of 8; logical tile L = (b % 8) *
   // (grid / 8) + b / 8 gives each XCD a contiguous run, m fastest.
   const int b = blockIdx.x, g8 = gridDim.x >> 3;
-  const int L = (b & 7) * g8 + (b >> 3);
-  if (L >= tiles) return;
+  const int U = (b & 7) * g8 + (b >> 3);
+  if (U >= tiles * splits) return;
+  // unit U = (tile L, k slice sl), slices of a tile adjacent
+  const int L = U / splits, sl = U - L * splits;
+  const int kb = sl * k_slice, ke = min(k, kb + k_slice);
   const int tm = L % tiles_m, tn = L / tiles_m;
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -91,22 +102,21 @@ __global__ __launch_bounds__(kGemmThreads) void base_gemm_kernel(int m, int n, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (k + kBK - 1) / kBK;
+  const int nk = ke > kb ? (ke - kb + kBK - 1) / kBK : 0;
   uint4 rw[kChunks], rx[kChunks];
-  load_tile(w, n, k, n0, 0, rw);
-  load_tile(x, m, k, m0, 0, rx);
-  store_tile(sw[0], rw);
-  store_tile(sx[0], rx);
+  load_tile(w, n, k, ke, n0, kb, rw);
+  load_tile(x, m, k, ke, m0, kb, rx);
+  store_tile(sw, rw);
+  store_tile(sx, rx);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
-      load_tile(w, n, k, n0, (kt + 1) * kBK, rw);
-      load_tile(x, m, k, m0, (kt + 1) * kBK, rx);
+      load_tile(w, n, k, ke, n0, kb + (kt + 1) * kBK, rw);
+      load_tile(x, m, k, ke, m0, kb + (kt + 1) * kBK, rx);
     }
-    const uint16_t *tw = sw[buf] + (wn * 64 + fr) * kLd + fg * 8;
-    const uint16_t *tx = sx[buf] + (wm * 64 + fr) * kLd + fg * 8;
+    const uint16_t *tw = sw + (wn * 64 + fr) * kLd + fg * 8;
+    const uint16_t *tx = sx + (wm * 64 + fr) * kLd + fg * 8;
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
       bf16x8_t fa[4], fb[4];
@@ -121,14 +131,16 @@ __global__ __launch_bounds__(kGemmThreads) void base_gemm_kernel(int m, int n, i
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
+    __syncthreads();  // every wave is done reading tile kt
     if (more) {
-      store_tile(sw[buf ^ 1], rw);
-      store_tile(sx[buf ^ 1], rx);
+      store_tile(sw, rw);
+      store_tile(sx, rx);
     }
     __syncthreads();
   }
   // D[n][m] of block (i, j): lane (fg, fr) holds columns n0 + 64 wn + 16 i + 4 fg
   // .. +3 of token m0 + 64 wm + 16 j + fr
+  float *pt = splits > 1 ? part + (int64_t)sl * m * n : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int col = n0 + wn * 64 + i * 16 + fg * 4;
@@ -136,36 +148,107 @@ __global__ __launch_bounds__(kGemmThreads) void base_gemm_kernel(int m, int n, i
     for (int j = 0; j < 4; ++j) {
       const int row = m0 + wm * 64 + j * 16 + fr;
       if (row < m && col < n) {
-        uint2 o;
-        o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-        o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2 *>(y + (int64_t)row * n + col) = o;
+        if (pt) {
+          *reinterpret_cast<f32x4_t *>(pt + (int64_t)row * n + col) = acc[i][j];
+        } else {
+          uint2 o;
+          o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+          o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2 *>(y + (int64_t)row * n + col) = o;
+        }
       }
     }
   }
+}
+
+// y = round(sum over slices s = 0 .. splits-1 of part[s]), 4 outputs per thread.
+__global__ __launch_bounds__(256) void base_gemm_reduce_kernel(int64_t mn, int splits,
+                                                               const float *__restrict__ part,
+                                                               uint16_t *__restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  f32x4_t a = *reinterpret_cast<const f32x4_t *>(part + i);
+  for (int s = 1; s < splits; ++s) a += *reinterpret_cast<const f32x4_t *>(part + s * mn + i);
+  uint2 o;
+  o.x = bf16_rne(a[0]) | (bf16_rne(a[1]) << 16);
+  o.y = bf16_rne(a[2]) | (bf16_rne(a[3]) << 16);
+  *reinterpret_cast<uint2 *>(y + i) = o;
+}
+
+constexpr int kMaxSplits = 4;
+constexpr int kSlotsPerCu = 3;       // workgroups of the GEMM kernel one compute unit holds
+constexpr int kMinStepsPerSlice = 4;  // k steps each slice keeps at least
+
+// Slices of k for an m x n x k problem on `cus` compute units: the largest
+// S <= 4 (a power of two) whose S x tiles units still fit in one round of the
+// device's slots and leave every slice at least 4 k-steps; 1 for grids that
+// already fill the device.
+int pick_splits(int64_t tiles, int k, int cus) {
+  const int64_t slots = (int64_t)kSlotsPerCu * cus;
+  int s = 1;
+  while (s < kMaxSplits && tiles * s * 2 <= slots && k >= 2 * s * kMinStepsPerSlice * kBK) s *= 2;
+  return s;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
+extern "C" lora_status lora_base_gemm_workspace(int32_t m, int32_t n, int32_t k, int64_t *bytes) {
+  if (!bytes) return fail(LORA_EINVAL, "null pointer");
+  *bytes = 0;
+  if (m < 0 || n <= 0 || k <= 0) return fail(LORA_EINVAL, "base gemm sizes m=%d n=%d k=%d", m, n, k);
+  if (m == 0) return ok();
+  const int64_t tiles = ((m + kBM - 1) / kBM) * (int64_t)((n + kBN - 1) / kBN);
+  const int s = pick_splits(tiles, k, device_cus());
+  if (s > 1) *bytes = (int64_t)s * m * n * (int64_t)sizeof(float);
+  return ok();
+}
+
 extern "C" lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k,
-                                      const void *x, const void *w, void *y, hipStream_t stream) {
+                                      const void *x, const void *w, void *y, void *workspace,
+                                      int64_t workspace_bytes, hipStream_t stream) {
   if (dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "base gemm supports bf16 only");
   if (m < 0 || n <= 0 || k <= 0) return fail(LORA_EINVAL, "base gemm sizes m=%d n=%d k=%d", m, n, k);
   if (n % 8 || k % 8) return fail(LORA_EUNSUPPORTED, "base gemm needs n and k multiples of 8");
+  if (workspace_bytes < 0) return fail(LORA_EINVAL, "negative workspace size");
   if (m == 0) return ok();
   if (!x || !w || !y) return fail(LORA_EINVAL, "null pointer");
-  if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (workspace && !aligned16(workspace)))
     return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
   const int64_t tiles_m = (m + kBM - 1) / kBM, tiles_n = (n + kBN - 1) / kBN;
   const int64_t tiles = tiles_m * tiles_n;
-  if (tiles > INT32_MAX - 8) return fail(LORA_EINVAL, "base gemm too large");
-  const int grid = (int)((tiles + 7) & ~int64_t(7));
+  // split k only into a workspace that holds every slice's partial tile
+  int splits = 1;
+  if (workspace) {
+    const int s = pick_splits(tiles, k, device_cus());
+    if (s > 1 && workspace_bytes >= (int64_t)s * m * n * (int64_t)sizeof(float)) splits = s;
+  }
+  if (tiles * splits > INT32_MAX - 8) return fail(LORA_EINVAL, "base gemm too large");
+  // slice length in whole k-steps
+  const int k_slice = (int)((((int64_t)k + splits - 1) / splits + kBK - 1) / kBK * kBK);
+  const int grid = (int)((tiles * splits + 7) & ~int64_t(7));
   hipLaunchKernelGGL(base_gemm_kernel, dim3(grid), dim3(kGemmThreads), 0, stream, m, n, k,
-                     (int)tiles_m, (int)tiles, (const uint16_t *)x, (const uint16_t *)w,
-                     (uint16_t *)y);
+                     (int)tiles_m, (int)tiles, splits, k_slice, (const uint16_t *)x,
+                     (const uint16_t *)w, (uint16_t *)y, (float *)workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "base gemm launch");
+  if (splits > 1) {
+    const int64_t mn = (int64_t)m * n;  // a multiple of 8
+    const int64_t blocks = (mn / 4 + 255) / 256;
+    if (blocks > INT32_MAX) return fail(LORA_EINVAL, "base gemm too large");
+    hipLaunchKernelGGL(base_gemm_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mn,
+                       splits, (const float *)workspace, (uint16_t *)y);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "base gemm reduce launch");
+  }
   return ok();
 }

@@ -226,8 +226,16 @@ class DeviceProblem:
         assert self.w is not None, "problem has no base weight"
         if y is None:
             y = torch.empty((self.p.num_tokens, self.p.d_out), dtype=self.tdtype, device=self.device)
-        B.lora_base_gemm(self.x, self.w, y)
+        B.lora_base_gemm(self.x, self.w, y, workspace=self.base_workspace())
         return y
+
+    def base_workspace(self):
+        """The split-k workspace of this problem's base GEMM (None if it does
+        not split), allocated once."""
+        if not hasattr(self, "_base_ws"):
+            self._base_ws = B.base_gemm_workspace(self.p.num_tokens, self.p.d_out, self.p.d_in,
+                                                  device=self.device)
+        return self._base_ws
 
     def serial_calls(self, y, v, stream=None, policy: int = B.LORA_PATH_AUTO):
         """Adapter-serial comparator: one (shrink, expand) pair of prepared

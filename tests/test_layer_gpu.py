@@ -48,18 +48,26 @@ def rand_bf16(rng, shape, std):
     return wl.bf16_bits((rng.standard_normal(shape, dtype=np.float32) * np.float32(std)))
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["whole_k", "split_k"])
 @pytest.mark.parametrize("m,n,k", [(1, 8, 8), (77, 264, 520), (200, 136, 1032), (129, 128, 64),
-                                   (256, 1024, 768)])
-def test_base_gemm_small_full(m, n, k):
-    """Every output of ragged shapes (partial tiles in m, n and k)."""
+                                   (256, 1024, 768), (300, 520, 4104)])
+def test_base_gemm_small_full(m, n, k, split):
+    """Every output of ragged shapes (partial tiles in m, n and k), without and
+    with a workspace (with one, these few-tile grids split k into 2 or 4
+    slices, the last one ragged, except where k is too short to split)."""
     rng = np.random.default_rng(m * 7 + n + k)
     x = rand_bf16(rng, (m, k), 1.0)
     w = rand_bf16(rng, (n, k), 1.0 / np.sqrt(k))
-    say(f"base gemm full m={m} n={n} k={k}")
+    ws = B.base_gemm_workspace(m, n, k) if split else None
+    if split and k >= 512:
+        assert ws is not None, "a few-tile grid with k >= 512 splits k"
+    say(f"base gemm full m={m} n={n} k={k} workspace={0 if ws is None else ws.numel() * 4}")
     xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
     yd = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-    B.lora_base_gemm(xd, wd, yd)
+    if ws is not None:
+        ws.fill_(float("nan"))  # every partial the reduction reads must be written
+    B.lora_base_gemm(xd, wd, yd, workspace=ws)
     torch.cuda.synchronize()
     got = bf16_host(yd)
     tok, col = np.meshgrid(np.arange(m, dtype=np.int32), np.arange(n, dtype=np.int32), indexing="ij")
@@ -70,11 +78,18 @@ def test_base_gemm_small_full(m, n, k):
 
 def test_base_gemm_errors():
     lib = B.lib()
-    assert lib.lora_base_gemm(B.LORA_F32, 8, 8, 8, 16, 16, 16, None) == B.LORA_EUNSUPPORTED
-    assert lib.lora_base_gemm(B.LORA_BF16, 8, 12, 8, 16, 16, 16, None) == B.LORA_EUNSUPPORTED
-    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, None, 16, 16, None) == B.LORA_EINVAL
-    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, 18, 16, 16, None) == B.LORA_EINVAL
-    assert lib.lora_base_gemm(B.LORA_BF16, 0, 8, 8, None, None, None, None) == B.LORA_OK
+    assert lib.lora_base_gemm(B.LORA_F32, 8, 8, 8, 16, 16, 16, None, 0, None) == B.LORA_EUNSUPPORTED
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 12, 8, 16, 16, 16, None, 0, None) == B.LORA_EUNSUPPORTED
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, None, 16, 16, None, 0, None) == B.LORA_EINVAL
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, 18, 16, 16, None, 0, None) == B.LORA_EINVAL
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, 16, 16, 16, 24, 64, None) == B.LORA_EINVAL
+    assert lib.lora_base_gemm(B.LORA_BF16, 8, 8, 8, 16, 16, 16, None, -1, None) == B.LORA_EINVAL
+    assert lib.lora_base_gemm(B.LORA_BF16, 0, 8, 8, None, None, None, None, 0, None) == B.LORA_OK
+    # the 70B shapes: only the 80-tile k/v projections (1280 x 1024) split, 4 ways
+    assert B.base_gemm_workspace_bytes(1280, 1024, 8192) == 4 * 1280 * 1024 * 4
+    assert B.base_gemm_workspace_bytes(1280, 8192, 8192) == 0
+    assert B.base_gemm_workspace_bytes(1280, 28672, 8192) == 0
+    assert B.base_gemm_workspace_bytes(0, 8, 8) == 0
 
 
 # tokens whose full output rows are checked: decode tokens (one-token
