@@ -125,6 +125,9 @@ void base_gemm_kernel(int m, int n, int k, int tiles_m, int tiles, int splits, i
         fa[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(tw + i * 16 * kLd + ks * 32));
         fb[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(tx + i * 16 * kLd + ks * 32));
       }
+      // ask the scheduler to interleave the fragment reads with the MFMAs
+      // (left to itself it waits for every read before each row of 4 MFMAs)
+      __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
