@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "lora_internal.h"
 
@@ -164,6 +165,142 @@ void base_gemm_kernel(int m, int n, int k, int tiles_m, int tiles, int splits, i
   }
 }
 
+// Whole-tile shapes (m, n multiples of 128, k of the k-step): the same tile
+// and wave layout, but the k-tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l of a wave's load writes 16 bytes at the
+// load's LDS base + 16 l), so no registers stage them and no LDS stores are
+// issued, and two LDS buffers alternate with one barrier per step.  Rows are
+// unpadded; the 16-byte chunks of a row are permuted by an XOR of the row
+// index so that the 8 lanes of an LDS read phase (8 consecutive rows, one
+// chunk) hit 8 different bank groups.  A k-step of 64 (64 KiB of LDS, two
+// workgroups per CU) does more work per barrier and suits large grids; a
+// k-step of 32 (32 KiB, three per CU) suits grids of a few rounds, where the
+// slot count decides how full the last round is.
+template <int BK>
+struct LdsTile {
+  static constexpr int kCpr = BK / 8;         // 16-byte chunks per row
+  static constexpr int kRows = 64 / kCpr;     // rows per wave load
+  static constexpr int kLoads = 128 * kCpr / kGemmThreads;  // loads per thread per operand
+  // LDS slot of chunk c of row r (an involution: also the chunk of slot c)
+  __device__ static __forceinline__ int slot(int r, int c) {
+    return BK == 64 ? c ^ (r & 7) : c ^ ((r >> 1) & 3);
+  }
+};
+
+template <int BK>
+__device__ __forceinline__ void issue_tile_lds(const uint16_t *__restrict__ src, int ld, int row0, int k0,
+                                               uint16_t *lds) {
+  using LT = LdsTile<BK>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rl = lane / LT::kCpr, c = LT::slot(rl, lane % LT::kCpr);
+#pragma unroll
+  for (int i = 0; i < LT::kLoads; ++i) {
+    const int g = i * (kGemmThreads / 64) + wave;  // this wave load's rows: g kRows .. +kRows-1
+    const uint16_t *p = src + (int64_t)(row0 + g * LT::kRows + rl) * ld + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void *)(lds + g * LT::kRows * BK),
+                                     16, 0, 0);
+  }
+}
+
+template <int BK>
+__device__ __forceinline__ void base_gemm_lds_body(int m, int n, int k, int tiles_m, int tiles, int splits,
+                                                   int k_slice, const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ w,
+                                                   uint16_t *__restrict__ y, float *__restrict__ part) {
+  using LT = LdsTile<BK>;
+  // four separate arrays rather than two double buffers: the compiler keeps
+  // apart accesses to different LDS variables, so it does not wait for the
+  // loads into one buffer before reading the other
+  __shared__ __attribute__((aligned(16))) uint16_t sw0[128 * BK], sw1[128 * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sx0[128 * BK], sx1[128 * BK];
+  const int b = blockIdx.x, g8 = gridDim.x >> 3;
+  const int U = (b & 7) * g8 + (b >> 3);
+  if (U >= tiles * splits) return;
+  const int L = U / splits, sl = U - L * splits;
+  const int kb = sl * k_slice, ke = min(k, kb + k_slice);
+  const int tm = L % tiles_m, tn = L / tiles_m;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int fr = lane & 15, fg = lane >> 4;
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nk = ke > kb ? (ke - kb) / BK : 0;
+  if (nk > 0) {
+    issue_tile_lds<BK>(w, k, n0, kb, sw0);
+    issue_tile_lds<BK>(x, k, m0, kb, sx0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every counter to zero: this wave's tile is in LDS
+  __syncthreads();
+  // one k-step: loads of step kt+1 into the other buffer, MFMAs on buffer B
+  // (a compile-time constant: the loop below is unrolled by two)
+  auto step = [&](auto bufc, int kt) {
+    constexpr int B = decltype(bufc)::value;
+    uint16_t *rw = B ? sw1 : sw0, *rx = B ? sx1 : sx0;  // read now
+    uint16_t *nw = B ? sw0 : sw1, *nx = B ? sx0 : sx1;  // loaded for the next step
+    if (kt + 1 < nk) {
+      issue_tile_lds<BK>(w, k, n0, kb + (kt + 1) * BK, nw);
+      issue_tile_lds<BK>(x, k, m0, kb + (kt + 1) * BK, nx);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8_t fa[4], fb[4];
+      const int ch = ks * 4 + fg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wn * 64 + i * 16 + fr, rb = wm * 64 + i * 16 + fr;
+        fa[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(rw + ra * BK + LT::slot(ra, ch) * 8));
+        fb[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(rx + rb * BK + LT::slot(rb, ch) * 8));
+      }
+      if (BK == 32) __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile's loads (this wave's share) have landed
+    __syncthreads();                // ... and every wave's, and nobody still reads buffer B
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+  }
+  float *pt = splits > 1 ? part + (int64_t)sl * m * n : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int col = n0 + wn * 64 + i * 16 + fg * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = m0 + wm * 64 + j * 16 + fr;
+      if (pt) {
+        *reinterpret_cast<f32x4_t *>(pt + (int64_t)row * n + col) = acc[i][j];
+      } else {
+        uint2 o;
+        o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2 *>(y + (int64_t)row * n + col) = o;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void base_gemm_lds64_kernel(int m, int n, int k, int tiles_m, int tiles, int splits, int k_slice,
+                            const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                            uint16_t *__restrict__ y, float *__restrict__ part) {
+  base_gemm_lds_body<64>(m, n, k, tiles_m, tiles, splits, k_slice, x, w, y, part);
+}
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void base_gemm_lds32_kernel(int m, int n, int k, int tiles_m, int tiles, int splits, int k_slice,
+                            const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+                            uint16_t *__restrict__ y, float *__restrict__ part) {
+  base_gemm_lds_body<32>(m, n, k, tiles_m, tiles, splits, k_slice, x, w, y, part);
+}
+
 // y = round(sum over slices s = 0 .. splits-1 of part[s]), 4 outputs per thread.
 __global__ __launch_bounds__(256) void base_gemm_reduce_kernel(int64_t mn, int splits,
                                                                const float *__restrict__ part,
@@ -239,9 +376,15 @@ extern "C" lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32
   // slice length in whole k-steps
   const int k_slice = (int)((((int64_t)k + splits - 1) / splits + kBK - 1) / kBK * kBK);
   const int grid = (int)((tiles * splits + 7) & ~int64_t(7));
-  hipLaunchKernelGGL(base_gemm_kernel, dim3(grid), dim3(kGemmThreads), 0, stream, m, n, k,
-                     (int)tiles_m, (int)tiles, splits, k_slice, (const uint16_t *)x,
-                     (const uint16_t *)w, (uint16_t *)y, (float *)workspace);
+  // whole tiles: direct-to-LDS kernels, a k-step of 64 for grids of at least
+  // six tiles per CU (three rounds of two), else 32; otherwise the
+  // register-staged kernel, which reads ragged edges as zeros
+  const bool whole = m % kBM == 0 && n % kBN == 0 && k % 64 == 0;
+  auto kern = base_gemm_kernel;
+  if (whole) kern = tiles * splits >= 6 * (int64_t)device_cus() ? base_gemm_lds64_kernel : base_gemm_lds32_kernel;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), 0, stream, m, n, k, (int)tiles_m,
+                     (int)tiles, splits, k_slice, (const uint16_t *)x, (const uint16_t *)w,
+                     (uint16_t *)y, (float *)workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "base gemm launch");
   if (splits > 1) {

@@ -50,11 +50,14 @@ def rand_bf16(rng, shape, std):
 
 @pytest.mark.parametrize("split", [False, True], ids=["whole_k", "split_k"])
 @pytest.mark.parametrize("m,n,k", [(1, 8, 8), (77, 264, 520), (200, 136, 1032), (129, 128, 64),
-                                   (256, 1024, 768), (300, 520, 4104)])
+                                   (256, 1024, 768), (300, 520, 4104),
+                                   (256, 256, 512), (128, 1024, 4096), (384, 128, 192)])
 def test_base_gemm_small_full(m, n, k, split):
-    """Every output of ragged shapes (partial tiles in m, n and k), without and
-    with a workspace (with one, these few-tile grids split k into 2 or 4
-    slices, the last one ragged, except where k is too short to split)."""
+    """Every output of ragged shapes (partial tiles in m, n and k), and of
+    whole-tile shapes (m, n multiples of 128, k of 64: the direct-to-LDS
+    kernel with a k-step of 32), without and with a workspace (with one, these
+    few-tile grids split k into 2 or 4 slices, except where k is too short to
+    split)."""
     rng = np.random.default_rng(m * 7 + n + k)
     x = rand_bf16(rng, (m, k), 1.0)
     w = rand_bf16(rng, (n, k), 1.0 / np.sqrt(k))
@@ -72,6 +75,28 @@ def test_base_gemm_small_full(m, n, k, split):
     got = bf16_host(yd)
     tok, col = np.meshgrid(np.arange(m, dtype=np.int32), np.arange(n, dtype=np.int32), indexing="ij")
     want = oracle.base_sampled(x, w, tok.ravel(), col.ravel()).reshape(m, n)
+    scale = np.maximum(np.max(np.abs(want), axis=1, keepdims=True), 1e-30)
+    check_sampled(got, want, np.broadcast_to(scale, want.shape), f"gemm {m}x{n}x{k}")
+
+
+def test_base_gemm_large_grid_sampled():
+    """A whole-tile grid of 1536 tiles (six per compute unit: the direct-to-LDS
+    kernel with a k-step of 64), checked on 48 full rows."""
+    m, n, k = 1536, 16384, 192
+    rng = np.random.default_rng(1536)
+    x = rand_bf16(rng, (m, k), 1.0)
+    w = rand_bf16(rng, (n, k), 1.0 / np.sqrt(k))
+    say(f"base gemm large grid m={m} n={n} k={k}")
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+    yd = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    assert B.base_gemm_workspace_bytes(m, n, k) == 0
+    B.lora_base_gemm(xd, wd, yd)
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([[0, 127, 128, m - 1], rng.choice(m, 44, replace=False)]))
+    got = bf16_host(yd)[rows]
+    tok, col = np.meshgrid(rows.astype(np.int32), np.arange(n, dtype=np.int32), indexing="ij")
+    want = oracle.base_sampled(x, w, tok.ravel(), col.ravel()).reshape(rows.size, n)
     scale = np.maximum(np.max(np.abs(want), axis=1, keepdims=True), 1e-30)
     check_sampled(got, want, np.broadcast_to(scale, want.shape), f"gemm {m}x{n}x{k}")
 
