@@ -6,6 +6,10 @@
 // it.  Both operands are contiguous along k (x [m][k], W [n][k]), the layout in
 // which every MFMA operand fragment is a run of 8 consecutive k.
 //
+// Two kernel families share one tiling: the register-staged kernel described
+// here serves any shape (ragged edges read as zeros); whole-tile shapes take
+// the direct-to-LDS kernels further down, which are faster.
+//
 // Tiling for gfx950: a workgroup of four waves computes a 128 x 128 tile of y
 // over k in steps of 64; each wave owns a 64 x 64 sub-tile as 4 x 4 blocks of
 // v_mfma_f32_16x16x32_bf16 with W rows as the A operand and x rows as the B
@@ -321,8 +325,8 @@ constexpr int kMinStepsPerSlice = 4;  // k steps each slice keeps at least
 
 // Slices of k for an m x n x k problem on `cus` compute units: the largest
 // S <= 4 (a power of two) whose S x tiles units still fit in one round of the
-// device's slots and leave every slice at least 4 k-steps; 1 for grids that
-// already fill the device.
+// device's slots (three workgroups per CU) and leave every slice at least 4
+// k-steps of 64; 1 for grids of more than half the slots.
 int pick_splits(int64_t tiles, int k, int cus) {
   const int64_t slots = (int64_t)kSlotsPerCu * cus;
   int s = 1;
