@@ -331,3 +331,28 @@ def test_empty_batches_are_noops():
     assert fused(ctypes.byref(d), 16, 4, 16, 0, 0, 16, None, 16, None) == B.LORA_OK      # empty order
     assert lib.lora_bgmv_expand(ctypes.byref(d), 16, 1, 9, 16, 16, None) == B.LORA_EINVAL  # bad order
     assert lib.lora_sgmv_shrink(ctypes.byref(d), None, 4, 16, 2, 8, 16, 16, None) == B.LORA_EINVAL
+
+
+def test_base_gemm_workspace_rule():
+    """The base GEMM's split-k rule, through the host-only size query (no GPU
+    here: the library then assumes MI355X's 256 compute units, 768 slots of
+    three workgroups): k is split 2 or 4 ways only for grids of at most half
+    the slots, and only while every slice keeps 4 k-steps of 64; the
+    workspace holds one fp32 partial output per slice."""
+    def ws(m, n, k):
+        return B.base_gemm_workspace_bytes(m, n, k)
+
+    out = lambda s, m, n: s * m * n * 4
+    assert ws(1280, 1024, 8192) == out(4, 1280, 1024)   # 80 tiles: the 70B k/v projections
+    assert ws(1280, 2048, 8192) == out(4, 1280, 2048)   # 160 tiles
+    assert ws(1280, 4096, 8192) == out(2, 1280, 4096)   # 320 tiles: 4 slices would overfill
+    assert ws(1280, 8192, 8192) == 0                    # 640 tiles: more than half the slots
+    assert ws(1280, 28672, 8192) == 0
+    assert ws(77, 264, 520) == out(2, 77, 264)          # k of 520: 2 slices keep 4 steps each
+    assert ws(200, 136, 1032) == out(4, 200, 136)
+    assert ws(129, 128, 64) == 0                        # too short to split
+    assert ws(0, 8, 8) == 0
+    with pytest.raises(B.LoraError):
+        ws(-1, 8, 8)
+    with pytest.raises(B.LoraError):
+        ws(8, 0, 8)
