@@ -14,7 +14,8 @@ source pages it follows, is stated beside the C function:
                            ``tests/golden/`` and by property tests.
 * ``shrink``            -- v = A_{a(t)} x_t.
 * ``expand``            -- y_t + B_{a(t)} v_t.
-* ``apply``             -- y_t + B_{a(t)} (A_{a(t)} x_t), token by token.
+* ``apply``             -- y_t + B_{a(t)} (A_{a(t)} x_t), token by token (optionally
+                           with the tokens spread over OpenMP threads).
 * ``apply_segmented``   -- the same, walked segment by segment.
 * ``apply_sampled``     -- ``apply`` restricted to sampled (token, column) pairs.
 * ``base_sampled``      -- W x at sampled (token, column) pairs.
@@ -50,8 +51,8 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-shared", "-fPIC",
-             _SRC, "-o", tmp])
+            ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared",
+             "-fPIC", _SRC, "-o", tmp])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -71,6 +72,8 @@ def _load():
     lib.oracle_shrink.argtypes = [I32, I32, I32, P, P, P, P, I, P, I, P]
     lib.oracle_expand.argtypes = [I32, I32, I32, P, P, P, P, P, I, P, I, P]
     lib.oracle_apply.argtypes = [I32, I32, I32, P, P, P, P, I, P, P, I, P, I, P]
+    lib.oracle_apply_threads.argtypes = [I32, I32, I32, P, P, P, P, I, P, P, I, P, I, P, I]
+    lib.oracle_apply_threads.restype = I
     lib.oracle_apply_segmented.argtypes = [I32, I32, I32, P, P, P, I32, P, P, P, I, P, P, I, P,
                                            I, P]
     lib.oracle_base_sampled.argtypes = [I32, P, I, P, I, I32, P, P, P]
@@ -214,16 +217,27 @@ def expand(v: np.ndarray, y_in: np.ndarray, ids, ad: Adapters) -> np.ndarray:
     return out
 
 
-def apply(x: np.ndarray, y_in: np.ndarray, ids, ad: Adapters) -> np.ndarray:
+def apply(x: np.ndarray, y_in: np.ndarray, ids, ad: Adapters, threads: int = 1) -> np.ndarray:
+    """y_in + B(Ax) per token; threads > 1 spreads the tokens over that many
+    OpenMP threads (same per-token arithmetic, bit-identical output)."""
+    return apply_counted(x, y_in, ids, ad, threads)[0]
+
+
+def apply_counted(x: np.ndarray, y_in: np.ndarray, ids, ad: Adapters, threads: int = 1):
+    """``apply``, returning (y_out, threads that ran)."""
     x, y_in = _c(x), _c(y_in)
     ids = _check_common(x, ids, ad)
     t, d_in = x.shape
     d_out = y_in.shape[1]
     out = np.empty((t, d_out), dtype=np.float64)
-    _load().oracle_apply(t, d_in, d_out, _p(ids), _p(ad.rank), _p(ad.row_off), _p(x),
-                         _dtype_code(x), _p(ad.a_rows), _p(ad.bt_rows), _dtype_code(ad.a_rows),
-                         _p(y_in), _dtype_code(y_in), _p(out))
-    return out
+    args = (t, d_in, d_out, _p(ids), _p(ad.rank), _p(ad.row_off), _p(x), _dtype_code(x),
+            _p(ad.a_rows), _p(ad.bt_rows), _dtype_code(ad.a_rows), _p(y_in), _dtype_code(y_in),
+            _p(out))
+    if threads <= 1:
+        _load().oracle_apply(*args)
+        return out, 1
+    used = _load().oracle_apply_threads(*args, int(threads))
+    return out, int(used)
 
 
 def apply_segmented(x, y_in, perm, starts, adapters, ad: Adapters) -> np.ndarray:

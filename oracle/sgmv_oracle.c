@@ -29,9 +29,10 @@
  *
  * Element types: 0 = fp32, 1 = bf16 (raw 16-bit patterns), 2 = fp64,
  * 3 = FP8 E4M3 (raw bytes), 4 = INT4 (packed nibbles).
- * Build: gcc -O2 -std=c11 -shared -fPIC (no -ffast-math, no BLAS, no SIMD
- * intrinsics).
+ * Build: gcc -O2 -std=c11 -fopenmp -shared -fPIC (no -ffast-math, no BLAS, no
+ * SIMD intrinsics; OpenMP only spreads independent tokens over threads).
  */
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -195,40 +196,75 @@ void oracle_expand(int32_t T, int32_t d_out, int32_t r_max, const int32_t *ids,
   }
 }
 
-/* The whole delta, token by token ([LO0] "The bare mechanism": y = Wx + B(Ax),
+/* The whole delta for one token t ([LO0] "The bare mechanism": y = Wx + B(Ax),
  * BA never formed; "SGMV" section: the per-token adapter a(t)).  y_in plays
- * the role of Wx.  Tokens are independent, so one token's v lives only in a
- * small buffer. */
+ * the role of Wx.  v is caller scratch of at least rank[a(t)] doubles. */
+static void apply_token(int32_t t, int32_t d_in, int32_t d_out, const int32_t *ids,
+                        const int32_t *rank, const int64_t *row_off, const void *x,
+                        int x_dtype, const void *a_rows, const void *bt_rows, int w_dtype,
+                        const void *y_in, int y_dtype, double *y_out, double *v) {
+  int32_t a = ids[t];
+  int32_t r = a >= 0 ? rank[a] : 0;
+  for (int32_t j = 0; j < r; ++j) {
+    double s = 0.0;
+    int64_t arow = (row_off[a] + j) * (int64_t)d_in;
+    for (int32_t k = 0; k < d_in; ++k)
+      s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);
+    v[j] = s;
+  }
+  for (int32_t i = 0; i < d_out; ++i) {
+    double y = elem(y_in, y_dtype, (int64_t)t * d_out + i);
+    if (a >= 0) {
+      double s = 0.0;
+      for (int32_t j = 0; j < r; ++j)
+        s += elem(bt_rows, w_dtype, (row_off[a] + j) * (int64_t)d_out + i) * v[j];
+      y += s;
+    }
+    y_out[(int64_t)t * d_out + i] = y;
+  }
+}
+
+static int32_t max_rank_used(int32_t T, const int32_t *ids, const int32_t *rank) {
+  int32_t r_cap = 1;
+  for (int32_t t = 0; t < T; ++t)
+    if (ids[t] >= 0 && rank[ids[t]] > r_cap) r_cap = rank[ids[t]];
+  return r_cap;
+}
+
+/* The whole delta, token by token, in token order.  Tokens are independent, so
+ * one token's v lives only in a small buffer. */
 void oracle_apply(int32_t T, int32_t d_in, int32_t d_out, const int32_t *ids,
                   const int32_t *rank, const int64_t *row_off, const void *x,
                   int x_dtype, const void *a_rows, const void *bt_rows, int w_dtype,
                   const void *y_in, int y_dtype, double *y_out) {
-  int32_t r_cap = 0;
+  double *v = (double *)malloc(sizeof(double) * (size_t)max_rank_used(T, ids, rank));
   for (int32_t t = 0; t < T; ++t)
-    if (ids[t] >= 0 && rank[ids[t]] > r_cap) r_cap = rank[ids[t]];
-  double *v = (double *)malloc(sizeof(double) * (size_t)(r_cap > 0 ? r_cap : 1));
-  for (int32_t t = 0; t < T; ++t) {
-    int32_t a = ids[t];
-    int32_t r = a >= 0 ? rank[a] : 0;
-    for (int32_t j = 0; j < r; ++j) {
-      double s = 0.0;
-      int64_t arow = (row_off[a] + j) * (int64_t)d_in;
-      for (int32_t k = 0; k < d_in; ++k)
-        s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);
-      v[j] = s;
-    }
-    for (int32_t i = 0; i < d_out; ++i) {
-      double y = elem(y_in, y_dtype, (int64_t)t * d_out + i);
-      if (a >= 0) {
-        double s = 0.0;
-        for (int32_t j = 0; j < r; ++j)
-          s += elem(bt_rows, w_dtype, (row_off[a] + j) * (int64_t)d_out + i) * v[j];
-        y += s;
-      }
-      y_out[(int64_t)t * d_out + i] = y;
-    }
-  }
+    apply_token(t, d_in, d_out, ids, rank, row_off, x, x_dtype, a_rows, bt_rows, w_dtype, y_in,
+                y_dtype, y_out, v);
   free(v);
+}
+
+/* oracle_apply with the tokens shared among `threads` OpenMP threads (each
+ * token's arithmetic is apply_token's, so the output is bit-identical to
+ * oracle_apply).  Returns the number of threads that ran. */
+int oracle_apply_threads(int32_t T, int32_t d_in, int32_t d_out, const int32_t *ids,
+                         const int32_t *rank, const int64_t *row_off, const void *x,
+                         int x_dtype, const void *a_rows, const void *bt_rows, int w_dtype,
+                         const void *y_in, int y_dtype, double *y_out, int threads) {
+  const int32_t r_cap = max_rank_used(T, ids, rank);
+  int used = 1;
+#pragma omp parallel num_threads(threads > 0 ? threads : 1)
+  {
+    double *v = (double *)malloc(sizeof(double) * (size_t)r_cap);
+#pragma omp single
+    used = omp_get_num_threads();
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t)
+      apply_token(t, d_in, d_out, ids, rank, row_off, x, x_dtype, a_rows, bt_rows, w_dtype, y_in,
+                  y_dtype, y_out, v);
+    free(v);
+  }
+  return used;
 }
 
 /* The same delta, walked segment by segment over the output of

@@ -142,6 +142,28 @@ def test_mixed_ranks_against_numpy_per_token():
     assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
 
 
+def test_threaded_apply_is_bit_identical_and_pinned():
+    """The all-cores leg (tokens spread over OpenMP threads) gives the same bits
+    as the one-thread oracle, reports the threads that ran, and is pinned to
+    per-adapter numpy products like the one-thread oracle."""
+    rng = np.random.default_rng(17)
+    ranks = [8, 16, 32, 64, 3]
+    d_in, d_out, t = 120, 88, 203
+    ad, a, bt = _rand_adapters(rng, ranks, d_in, d_out)
+    ids = rng.integers(-1, len(ranks), size=t).astype(np.int32)
+    x = rng.standard_normal((t, d_in))
+    y = rng.standard_normal((t, d_out))
+    one = oracle.apply(x, y, ids, ad)
+    many, used = oracle.apply_counted(x, y, ids, ad, threads=4)
+    assert used == 4
+    assert np.array_equal(one, many)
+    want = y.copy()
+    for i in range(len(ranks)):
+        m = ids == i
+        want[m] += (x[m] @ a[i].T) @ bt[i]
+    assert np.max(np.abs(many - want)) <= 1e-12 * np.max(np.abs(want))
+
+
 def test_rank1_unit_adapter_is_exact_copy():
     """A = e_k^T and B = e_i: the delta at (t, i) is exactly x[t, k], zero elsewhere."""
     rng = np.random.default_rng(8)
@@ -274,11 +296,11 @@ def test_segments_rejects_out_of_range():
 # ------------------------------------------------------------------ planted mistakes
 MUTATIONS = {
     # a dropped term of the shrink sum
-    "drop_last_k": ("for (int32_t k = 0; k < d_in; ++k)\n        s += elem(a_rows",
-                    "for (int32_t k = 0; k < d_in - 1; ++k)\n        s += elem(a_rows"),
+    "drop_last_k": ("for (int32_t k = 0; k < d_in; ++k)\n      s += elem(a_rows",
+                    "for (int32_t k = 0; k < d_in - 1; ++k)\n      s += elem(a_rows"),
     # a wrong sign on the delta
-    "wrong_sign": ("        y += s;\n      }\n      y_out[(int64_t)t * d_out + i] = y;\n    }\n  }\n  free(v);",
-                   "        y -= s;\n      }\n      y_out[(int64_t)t * d_out + i] = y;\n    }\n  }\n  free(v);"),
+    "wrong_sign": ("      y += s;\n    }\n    y_out[(int64_t)t * d_out + i] = y;\n  }\n}",
+                   "      y -= s;\n    }\n    y_out[(int64_t)t * d_out + i] = y;\n  }\n}"),
     # B read untransposed (index of j and i swapped within the row block)
     "transposed_b": ("s += elem(bt_rows, w_dtype, (row_off[a] + j) * (int64_t)d_out + i) * v[j];",
                      "s += elem(bt_rows, w_dtype, (row_off[a] + (i % (r > 0 ? r : 1))) * (int64_t)d_out + j) * v[j];"),
@@ -288,8 +310,8 @@ MUTATIONS = {
     # INT4 nibbles in the wrong order
     "int4_nibbles": ("(base[i >> 1] >> ((i & 1) * 4)) & 15", "(base[i >> 1] >> (((i + 1) & 1) * 4)) & 15"),
     # wrong adapter row offset (adapter a reads adapter 0's rows)
-    "wrong_adapter": ("int64_t arow = (row_off[a] + j) * (int64_t)d_in;\n      for (int32_t k = 0; k < d_in; ++k)\n        s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);\n      v[j] = s;",
-                      "int64_t arow = (row_off[0] + j) * (int64_t)d_in;\n      for (int32_t k = 0; k < d_in; ++k)\n        s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);\n      v[j] = s;"),
+    "wrong_adapter": ("int64_t arow = (row_off[a] + j) * (int64_t)d_in;\n    for (int32_t k = 0; k < d_in; ++k)\n      s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);\n    v[j] = s;",
+                      "int64_t arow = (row_off[0] + j) * (int64_t)d_in;\n    for (int32_t k = 0; k < d_in; ++k)\n      s += elem(a_rows, w_dtype, arow + k) * elem(x, x_dtype, (int64_t)t * d_in + k);\n    v[j] = s;"),
 }
 
 
@@ -315,11 +337,12 @@ def test_planted_mistake_is_caught(name, tmp_path, monkeypatch):
     import subprocess
     src = open(oracle._SRC).read()
     old, new = MUTATIONS[name]
-    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    assert src.count(old) == 1, f"mutation anchor for {name} not found once"
     mutated = tmp_path / "mut.c"
     mutated.write_text(src.replace(old, new))
     so = tmp_path / "libmut.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", str(mutated), "-o", str(so)])
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", str(mutated), "-o",
+                           str(so)])
     real = oracle._load()
     assert _pin_suite_passes()
     monkeypatch.setattr(oracle, "_lib", None)
