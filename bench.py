@@ -1,21 +1,30 @@
 """Benchmark of the multi-LoRA delta hot path on one MI355X.
 
-A step is one pass of the delta path over one batch already resident in HBM:
-shrink then expand.  The default workload is the decode batch (256 tokens, one
-token per request, adapters drawn uniformly from 128 resident rank-16
-adapters, 4096 -> 4096, bf16, per-token mode).  Steps rotate over replicas of
-the inputs and weights whose total exceeds twice the 256 MB last-level
-(Infinity) cache, so every step reads its bytes from HBM.
+A step is one pass of the delta path over one batch already resident in HBM.
+The default run is the 70B-shape decoder layer: 1280 tokens (256 decode tokens
+on 256 distinct rank-16 adapters plus a 1024-token prefill request), the seven
+projections of Llama-3-70B (q, o 8192 -> 8192; k, v 8192 -> 1024; gate, up
+8192 -> 28672; down 28672 -> 8192), each step the SGMV delta (shrink + expand)
+of all seven.  Its line nests the decode batch (256 tokens, one per request,
+128 resident rank-16 adapters, 4096 -> 4096, one fused launch) and the
+heterogeneous-rank paged batch (4096 tokens, 64 Zipf-length requests, ranks
+8..64, 8192 -> 8192, 16-row pages in a shuffled pool), each measured the same
+way with its own roofline and CPU baseline.  ``--config N`` runs one workload
+alone.
+
+Cold caches.  Every kernel's bytes come from HBM: steps rotate over device
+replicas of the inputs and adapter rows (clones at other addresses) whose
+per-kernel footprint summed over the rotation exceeds twice the 256 MB
+last-level (Infinity) cache.
 
 Metric: delta tokens/s (whole job) plus achieved HBM GB/s of the dominant
 kernel against the 8 TB/s peak.  The timed region replays the K steps as one
-HIP graph (as a serving loop replays its decode step), bracketed by device
-synchronisation.  Per-kernel durations come from HIP events on the launch
-stream around a graph of K back-to-back launches of that kernel over the same
-replicas (span / K, three repetitions): HIP events around single launches
-would add several microseconds of event and launch latency to kernels that
-themselves last a few microseconds.  The fp64 CPU oracle is timed beside it
-on a bounded sample.
+HIP graph, bracketed by device synchronisation.  Per-kernel durations come
+from HIP events on the launch stream around a graph of K back-to-back launches
+of that kernel rotating over the replicas (span / K, mean of three replays):
+events around single launches would add microseconds of event latency to
+kernels that last a few.  The fp64 CPU oracle is timed beside it on a bounded
+sample, on one thread and on all the cores the process may use.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
 """
@@ -35,10 +44,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 LLC_BYTES = 256 * 2**20        # Infinity Cache
+METRIC = "LoRA delta tokens/sec per layer + achieved HBM GB/s (% of MI355X peak)"
 KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemm_segments_amd", "csrc", f)
                   for f in ("kernels.hip", "base_gemm.hip", "host.cpp", "lora_internal.h")] + \
                  [os.path.join(ROOT, "include", "lora_sgmv.h")]
+LAYER_WORKLOAD = "layer70b_1280tok_256ad_r16"
 
 
 def kernel_hash() -> str:
@@ -53,8 +65,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2,
-                    help="1..5 (2 = decode, the default; 5 = the 70B-shape layer)")
+    ap.add_argument("--config", type=int, default=0,
+                    help="0 (default): the 70B layer with the decode and heterogeneous batches "
+                         "nested; 1..5: one workload alone (2 decode, 3 prefill, 4 heterogeneous "
+                         "paged, 5 the 70B layer)")
     ap.add_argument("--shape", default="q", help="config 3 shape: q or up")
     ap.add_argument("--wq", choices=("", "fp8", "int4"), default="",
                     help="adapter rows stored as FP8 E4M3 or INT4 with row scales (configs 2, 4)")
@@ -65,8 +79,11 @@ def parse():
                     help="fused decode: workgroups take tokens in the batch's segment order "
                          "(host-built once per batch, shared by all layers) or in index order")
     ap.add_argument("--policy", type=int, default=0, help="SGMV path policy (0 auto, 1 gather, 2 mfma)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="bound on the oracle's CPU time (0 disables the CPU baseline)")
+    ap.add_argument("--mfma-min", type=int, default=0,
+                    help="SGMV plan: segments of at least this many tokens take the MFMA path "
+                         "(0: the library default)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="bound on each workload's one-thread oracle time (0 disables the CPU baseline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the LLC")
     ap.add_argument("--churn", type=int, default=0, metavar="POOL_ADAPTERS",
                     help="adapter churn: decode batches over 1024 adapters through an LRU cache "
@@ -77,6 +94,9 @@ def parse():
     ap.add_argument("--serial", action="store_true",
                     help="also time the adapter-serial comparator (one shrink + expand launch "
                          "per adapter sub-batch, same kernels)")
+    ap.add_argument("--floor", action="store_true",
+                    help="only time bare streaming reads and a read-modify-write of given sizes "
+                         "and workgroup counts (the device's floors for launches of that size)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch device copies of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -116,40 +136,58 @@ def read_traffic(kernel: str, workload_name: str):
         return None
 
 
-def cpu_baseline(p, budget_s: float):
-    """The oracle as it stands (single-threaded C, fp64) on the same batch:
-    whole batches repeated until the time budget is used (at least one)."""
+def profile_path(workload_name: str):
+    path = os.path.join("profiles", f"{workload_name}.md")
+    return path if os.path.exists(os.path.join(ROOT, path)) else None
+
+
+def oracle_threads() -> int:
+    """Threads for the all-cores oracle leg: the cores this process may run on
+    (sched_getaffinity), capped by OMP_NUM_THREADS when the host sets it."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(parts, num_tokens: int, budget_s: float):
+    """The oracle as it stands (C, fp64) on a bounded sample of the same
+    workload: the first n tokens of the batch through every part of a step
+    (one projection, or the seven of the layer), n sized so that the one-thread
+    pass takes about budget_s.  Timed once on one thread and once on all the
+    cores this process may use (the same per-token arithmetic, bit-identical
+    output).  parts: list of (problem, oracle adapters)."""
     import oracle
-    if p.wq:
-        ad = oracle.Adapters.from_quantized(p.wq, p.a_rows, p.a_scales, p.bt_rows, p.bt_scales)
-    else:
-        ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
-    ids = p.ids
-    # bounded sample: a prefix of the batch sized to the budget
-    t0 = time.perf_counter()
-    oracle.apply(p.x[:8], p.y[:8], ids[:8], ad)
-    per_tok = max((time.perf_counter() - t0) / 8, 1e-7)
-    n_tok = int(min(p.num_tokens, max(8, budget_s / per_tok)))
-    reps, elapsed = 0, 0.0
-    t0 = time.perf_counter()
-    while True:
-        oracle.apply(p.x[:n_tok], p.y[:n_tok], ids[:n_tok], ad)
-        reps += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s or n_tok < p.num_tokens or reps >= 1000:
-            break
-    sample = (f"{n_tok} of {p.num_tokens} tokens" if n_tok < p.num_tokens
-              else f"the full {p.num_tokens}-token batch") + f" x {reps} pass(es), {elapsed:.1f} s"
-    return {"value": n_tok * reps / elapsed, "unit": "delta tokens/s", "cores": 1,
-            "kind": "oracle", "sample": sample}
+
+    def run(n, threads):
+        used = 1
+        t0 = time.perf_counter()
+        for p, ad in parts:
+            out, used = oracle.apply_counted(p.x[:n], p.y[:n], p.ids[:n], ad, threads)
+        return time.perf_counter() - t0, used, out
+
+    probe = min(8, num_tokens)
+    t_probe, _, _ = run(probe, 1)
+    per_tok = max(t_probe / probe, 1e-7)
+    n = int(min(num_tokens, max(probe, budget_s / per_tok)))
+    t1, _, out1 = run(n, 1)
+    threads = oracle_threads()
+    tn, used, outn = run(n, threads)
+    assert np.array_equal(out1, outn), "threaded oracle differs from the one-thread oracle"
+    what = f"the first {n} of {num_tokens} tokens" if n < num_tokens else f"all {num_tokens} tokens"
+    if len(parts) > 1:
+        what += f" through all {len(parts)} projections"
+    return {"value": round(n / tn, 2), "unit": "delta tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{what}, one pass, {tn:.2f} s on {used} threads (OpenMP over tokens)",
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "single_thread": {"value": round(n / t1, 2), "unit": "delta tokens/s", "cores": 1,
+                              "sample": f"{what}, one pass, {t1:.2f} s"}}
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
-
-
-def graph_span(torch, stream, fns, reps: int = 3) -> float:
+def graph_span(torch, stream, fns, reps: int = 3, best: bool = False) -> float:
     """Seconds per launch: HIP events on `stream` around a graph of the
-    launches `fns` (one each, back to back), best of `reps` replays."""
+    launches `fns` (one each, back to back); mean (or best) of `reps` replays."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for f in fns:
@@ -157,7 +195,7 @@ def graph_span(torch, stream, fns, reps: int = 3) -> float:
     with torch.cuda.stream(stream):
         g.replay()
     torch.cuda.synchronize()
-    best = None
+    ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
@@ -165,9 +203,40 @@ def graph_span(torch, stream, fns, reps: int = 3) -> float:
             g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / len(fns)
-        best = t if best is None else min(best, t)
-    return best
+        ts.append(e0.elapsed_time(e1) * 1e-3 / len(fns))
+    return min(ts) if best else float(np.mean(ts))
+
+
+def timed_graph(torch, stream, step, K: int, W: int):
+    """W eager warmup steps, then the K steps as one HIP graph: one untimed
+    replay, then the timed replay between device synchronisations.  Returns
+    (wall seconds of the K steps, host seconds per eager step)."""
+    t0 = time.perf_counter()
+    for i in range(W):
+        step(i)
+    host_step_s = (time.perf_counter() - t0) / max(W, 1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(K):
+            step(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, host_step_s
+
+
+def n_replicas(args, footprint: float, cap: int = 64) -> int:
+    """Replicas whose rotation moves at least twice the LLC through a kernel
+    whose one launch touches `footprint` bytes."""
+    if args.replicas:
+        return args.replicas
+    return int(min(cap, max(2, np.ceil(2 * LLC_BYTES / max(footprint, 1.0)))))
 
 
 def serial_comparator(torch, stream, steps_calls, tokens: int, one_launch_s: float, K: int):
@@ -192,6 +261,8 @@ def serial_comparator(torch, stream, steps_calls, tokens: int, one_launch_s: flo
             "launches_per_step": launches, "ms_per_step": round(wall / K * 1e3, 5),
             "value": round(tokens * K / wall, 1), "unit": "delta tokens/s",
             "one_launch_speedup": round((wall / K) / one_launch_s, 3), "steps": K}
+
+
 
 
 def bench_churn(args, torch):
@@ -371,115 +442,299 @@ def bench_multi(args, torch):
     print(json.dumps(out), flush=True)
 
 
-def bench_layer(args, torch):
-    """The 70B-shape decoder layer: seven projections, each the base GEMM
-    y = x W^T followed by the SGMV delta (segmented mode, automatic paths)."""
+
+def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
+    """One of configs 1..4: K steps of shrink + expand (or the fused decode
+    launch) over cache-defeating replicas.  Returns the record."""
+    from segmented_gather_gemm_segments_amd import accounting as acc
+    from segmented_gather_gemm_segments_amd import binding as B
+    from segmented_gather_gemm_segments_amd import runner as R
+
+    p = workload(cfg, shape, wq)
+    elem = 2 if p.dtype == "bf16" else 4
+    mode = "bgmv" if p.mode == "bgmv" else "sgmv"
+    fused = mode == "bgmv" and args.path == "fused"
+    stream = torch.cuda.Stream()          # default priority; every launch goes here
+    nbytes = {"shrink": acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem, p.wq),
+              "expand": acc.expand_bytes(p.ids, p.ranks, p.d_out, elem, p.wq),
+              "fused": acc.fused_bytes(p.ids, p.ranks, p.d_in, p.d_out, elem, p.wq)}
+    footprint = nbytes["fused"] if fused else min(nbytes["shrink"], nbytes["expand"])
+    n_rep = n_replicas(args, footprint)
+    one = R.DeviceProblem(p)
+    reps = [one] + [one.replica() for _ in range(n_rep - 1)]
+    mfma_min = args.mfma_min or B.LORA_DEFAULT_MFMA_MIN_TOKENS
+    calls = []
+    for dp in reps:
+        y, v = dp.y0.clone(), dp.new_v()
+        if mode == "bgmv":
+            sh, ex = B.prepare_bgmv(dp.weights, dp.ids, dp.x, v, y, args.order, stream=stream)
+            tord = dp.segments()[3] if args.placement == "grouped" else None
+            fu = B.prepare_bgmv_fused(dp.weights, dp.ids, dp.x, y, None, args.order, stream=stream,
+                                      token_order=tord)
+            calls.append((sh, ex, fu))
+        else:
+            _, _, _, perm_d = dp.segments()
+            if not hasattr(one, "_bench_plans"):
+                one._bench_plans = (dp.plan(B.LORA_PHASE_SHRINK, args.policy, mfma_min),
+                                    dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min))
+            sp, ep = one._bench_plans
+            calls.append(B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream))
+    torch.cuda.synchronize()
+
+    def step(i):
+        c = calls[i % n_rep]
+        if fused:
+            c[2]()
+        else:
+            c[0]()
+            c[1]()
+
+    K = args.steps
+    wall, host_step_s = timed_graph(torch, stream, step, K, args.warmup)
+
+    # per-launch durations: graphs of K back-to-back launches of one kernel
+    # rotating over the replicas (the same launches as in the timed steps)
+    def span(which):
+        return np.array([graph_span(torch, stream, [calls[i % n_rep][which] for i in range(K)], 1)
+                         for _ in range(3)])
+
+    phases = ["shrink", "expand"] + (["fused"] if mode == "bgmv" else [])
+    timed = {k: span(i) for i, k in enumerate(phases)}
+    flops = {"shrink": acc.shrink_flops(p.ids, p.ranks, p.d_in),
+             "expand": acc.expand_flops(p.ids, p.ranks, p.d_out)}
+    flops["fused"] = flops["shrink"] + flops["expand"]
+    kern = {}
+    for name, t in timed.items():
+        kern[name] = {"avg_us": float(t.mean() * 1e6), "min_us": float(t.min() * 1e6),
+                      "max_us": float(t.max() * 1e6), "bytes": nbytes[name],
+                      "gbs": nbytes[name] / t.mean() / 1e9,
+                      "frac_of_peak": nbytes[name] / t.mean() / 1e9 / HBM_PEAK_GBS,
+                      "tflops": flops[name] / t.mean() / 1e12}
+    tokens = int(np.sum(p.ids >= 0))
+    dom = "fused" if fused else max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
+    kname = f"{mode}_{dom}"
+    achieved = kern[dom]["gbs"]
+    out = {
+        "metric": METRIC,
+        "value": round(tokens * K / wall, 1),
+        "unit": "delta tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": p.dtype, "data": "synthetic (seeded; random-init adapters)",
+        "config": {"workload": p.name, "tokens": p.num_tokens, "adapters": p.num_adapters,
+                   "ranks": sorted(set(int(r) for r in p.ranks)), "d_in": p.d_in, "d_out": p.d_out,
+                   "adapter_rows": p.wq or p.dtype, "layout": one.layout,
+                   "mode": mode, "path": ("fused" if fused else "shrink+expand"),
+                   "placement": (args.placement if fused else None),
+                   "mfma_min_tokens": (mfma_min if mode == "sgmv" else None),
+                   "replicas": n_rep, "timed": "HIP graph replay of the K steps",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(kname, p.name), "kernel": kname,
+                     "algorithmic_bytes_per_launch": kern[dom]["bytes"],
+                     "avg_launch_us": round(kern[dom]["avg_us"], 3), "profile": profile_path(p.name)},
+        # the long segments' matrix-core use (reported, not targeted: the path
+        # is HBM-bound, and algorithmic flops / dense peak stays a few percent)
+        "mfma_utilisation": ({k: round(kern[k]["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
+                              for k in ("shrink", "expand")} | {"peak_tflops": MFMA_BF16_PEAK_TFLOPS}
+                             if mode == "sgmv" and p.dtype == "bf16" else None),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in d.items()}
+                    for k, d in kern.items()},
+        "gpu_tokens_per_s_kernel_time": round(
+            tokens / (kern["fused"]["avg_us"] * 1e-6 if fused
+                      else (timed["shrink"].mean() + timed["expand"].mean())), 1),
+        "host_ms_per_step_eager": round(host_step_s * 1e3, 5),
+        "kernel_sources_sha256_16": kernel_hash(),
+    }
+    if args.serial:
+        Ks = min(K, 50)
+        steps_calls = []
+        for dp in reps[: min(n_rep, Ks)]:
+            y, v = dp.y0.clone(), dp.new_v()
+            steps_calls.append([f for pair in dp.serial_calls(y, v, stream) for f in pair])
+        out["comparator"] = serial_comparator(torch, stream, steps_calls, tokens, wall / K, Ks)
+    if args.cpu_seconds > 0:
+        import oracle
+        if p.wq:
+            ad = oracle.Adapters.from_quantized(p.wq, p.a_rows, p.a_scales, p.bt_rows, p.bt_scales)
+        else:
+            ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
+        out["cpu_baseline"] = cpu_baseline([(p, ad)], p.num_tokens, args.cpu_seconds)
+    del calls, reps, one
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_layer(args, torch):
+    """The 70B-shape decoder layer: a step is the SGMV delta (segmented mode,
+    automatic paths) of all seven projections; each projection's base GEMM
+    y = x W^T is timed beside it for the LoRA overhead fraction.  Each
+    projection rotates over its own replicas (x, y, v and adapter rows), so
+    that every kernel of a step reads cold bytes."""
     from segmented_gather_gemm_segments_amd import accounting as acc
     from segmented_gather_gemm_segments_amd import binding as B
     from segmented_gather_gemm_segments_amd import runner as R
     from segmented_gather_gemm_segments_amd import workloads as wl
 
     stream = torch.cuda.Stream()
+    mfma_min = args.mfma_min or B.LORA_DEFAULT_MFMA_MIN_TOKENS
     projs = []
     for name, _, _ in wl.LAYER_70B:
         p = wl.layer_projection(name)
         dp = R.DeviceProblem(p)
-        y = torch.empty((p.num_tokens, p.d_out), dtype=torch.bfloat16, device="cuda")
-        v = dp.new_v()
+        y_base = torch.empty((p.num_tokens, p.d_out), dtype=torch.bfloat16, device="cuda")
+        base = B.prepare_base_gemm(dp.x, dp.w, y_base, workspace=dp.base_workspace(), stream=stream)
+        with torch.cuda.stream(stream):
+            base()
         _, _, _, perm_d = dp.segments()
-        sp = dp.plan(B.LORA_PHASE_SHRINK)
-        ep = dp.plan(B.LORA_PHASE_EXPAND)
-        dp._plans = (sp, ep)
-        shrink, expand = B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream)
-        base = B.prepare_base_gemm(dp.x, dp.w, y, workspace=dp.base_workspace(), stream=stream)
-        projs.append({"name": name, "p": p, "dp": dp, "base": base, "shrink": shrink,
-                      "expand": expand, "y": y})
-    torch.cuda.synchronize()
-    K = args.steps
-    for _ in range(args.warmup):
-        for q in projs:
-            q["base"](); q["shrink"](); q["expand"]()
-    torch.cuda.synchronize()
-    # timed region: K layer-deltas (all seven projections' shrink + expand) as one graph
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for _ in range(K):
-            for q in projs:
-                q["shrink"](); q["expand"]()
-    with torch.cuda.stream(stream):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        g.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    reps = max(4, min(K, 20))
-    per = {}
-    tot = {"base": 0.0, "shrink": 0.0, "expand": 0.0}
-    for q in projs:
-        p = q["p"]
-        d = {k: graph_span(torch, stream, [q[k]] * reps) for k in ("base", "shrink", "expand")}
+        sp = dp.plan(B.LORA_PHASE_SHRINK, args.policy, mfma_min)
+        ep = dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min)
         sb = acc.shrink_bytes(p.ids, p.ranks, p.d_in, 2)
         eb = acc.expand_bytes(p.ids, p.ranks, p.d_out, 2)
-        bf = acc.base_gemm_flops(p.num_tokens, p.d_out, p.d_in)
-        per[q["name"]] = {"d_in": p.d_in, "d_out": p.d_out,
-                          "base_us": round(d["base"] * 1e6, 2),
-                          "base_tflops": round(bf / d["base"] / 1e12, 1),
-                          "shrink_us": round(d["shrink"] * 1e6, 2),
-                          "shrink_gbs": round(sb / d["shrink"] / 1e9, 1),
-                          "expand_us": round(d["expand"] * 1e6, 2),
-                          "expand_gbs": round(eb / d["expand"] / 1e9, 1),
-                          "_sb": sb, "_eb": eb, "_bf": bf, "_t": d}
-        for k in tot:
-            tot[k] += d[k]
+        n_rep = n_replicas(args, min(sb, eb), cap=48)
+        torch.cuda.synchronize()
+        calls = []
+        for i in range(n_rep):
+            rp = dp if i == 0 else dp.replica()
+            y = y_base.clone()
+            calls.append(B.prepare_sgmv(rp.weights, perm_d, sp, ep, rp.x, rp.new_v(), y, stream=stream))
+        p.extra.pop("w", None)   # the host copy of W is no longer needed
+        projs.append({"name": name, "p": p, "dp": dp, "base": base, "calls": calls, "n_rep": n_rep,
+                      "sb": sb, "eb": eb, "bf": acc.base_gemm_flops(p.num_tokens, p.d_out, p.d_in),
+                      "y_base": y_base, "plans": (sp, ep)})
+    torch.cuda.synchronize()
+    K = args.steps
+
+    def step(i):
+        for q in projs:
+            c = q["calls"][i % q["n_rep"]]
+            c[0]()
+            c[1]()
+
+    wall, host_step_s = timed_graph(torch, stream, step, K, args.warmup)
+
+    # per-kernel durations over each projection's rotation; the base GEMMs as
+    # the layer's sequence of seven (each cold: the others stream 1.7 GB of W
+    # between two uses of one), and one by one (k/v's W then stays cached)
+    per, tot = {}, {"shrink": 0.0, "expand": 0.0}
+    for q in projs:
+        t = {ph: float(np.mean([graph_span(torch, stream, [q["calls"][i % q["n_rep"]][k] for i in range(K)], 1)
+                                for _ in range(3)]))
+             for k, ph in enumerate(("shrink", "expand"))}
+        tb = graph_span(torch, stream, [q["base"]] * 5, 3)
+        p = q["p"]
+        per[q["name"]] = {"d_in": p.d_in, "d_out": p.d_out, "replicas": q["n_rep"],
+                          "shrink_us": round(t["shrink"] * 1e6, 3),
+                          "shrink_gbs": round(q["sb"] / t["shrink"] / 1e9, 1),
+                          "expand_us": round(t["expand"] * 1e6, 3),
+                          "expand_gbs": round(q["eb"] / t["expand"] / 1e9, 1),
+                          "base_us_alone": round(tb * 1e6, 2),
+                          "base_tflops_alone": round(q["bf"] / tb / 1e12, 1)}
+        q["t"] = t
+        tot["shrink"] += t["shrink"]
+        tot["expand"] += t["expand"]
+    base_layer = graph_span(torch, stream, [q["base"] for _ in range(3) for q in projs], 3) * len(projs)
     tokens = projs[0]["p"].num_tokens
     delta = tot["shrink"] + tot["expand"]
-    # dominant delta kernel (HBM-bound) and the base GEMM (MFMA-bound)
-    dom = max(((n, k) for n in per for k in ("shrink", "expand")), key=lambda nk: per[nk[0]]["_t"][nk[1]])
-    dn, dk = dom
-    dbytes = per[dn]["_sb" if dk == "shrink" else "_eb"]
-    dt = per[dn]["_t"][dk]
-    base_flops = sum(per[n]["_bf"] for n in per)
-    for n in per:
-        for k in ("_sb", "_eb", "_bf", "_t"):
-            per[n].pop(k)
+    # dominant kernel: the phase with the larger summed time; achieved = its
+    # bytes per launch / its time per launch, averaged over the seven launches
+    dk = max(("shrink", "expand"), key=lambda k: tot[k])
+    dbytes = sum(q["sb" if dk == "shrink" else "eb"] for q in projs)
+    achieved = dbytes / tot[dk] / 1e9
+    base_flops = sum(q["bf"] for q in projs)
     out = {
-        "metric": "LoRA delta tokens/sec per layer + achieved HBM GB/s (% of MI355X peak)",
+        "metric": METRIC,
         "value": round(tokens * K / wall, 1),
         "unit": "delta tokens/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(wall / K * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded; random-init adapters and base weights)",
-        "config": {"workload": "layer70b_1280tok_256ad_r16", "tokens": tokens, "adapters": 256,
-                   "ranks": [16], "projections": [q["name"] for q in projs], "mode": "sgmv",
+        "config": {"workload": LAYER_WORKLOAD, "tokens": tokens, "adapters": 256, "ranks": [16],
+                   "projections": [q["name"] for q in projs], "mode": "sgmv",
+                   "mfma_min_tokens": mfma_min,
                    "timed": "HIP graph replay of K layer deltas (7 projections x shrink + expand)",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(dbytes / dt / 1e9, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic(f"sgmv_{dk}", f"layer70b_{dn}"),
-                     "kernel": f"sgmv_{dk} ({dn})", "algorithmic_bytes_per_launch": dbytes,
-                     "avg_launch_us": round(dt * 1e6, 3)},
-        "base_roofline": {"bound": "mfma", "achieved": round(base_flops / tot["base"] / 1e12, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(f"sgmv_{dk}", LAYER_WORKLOAD),
+                     "kernel": f"sgmv_{dk} (its 7 launches of a layer step, averaged)",
+                     "algorithmic_bytes_per_launch": int(round(dbytes / len(projs))),
+                     "avg_launch_us": round(tot[dk] / len(projs) * 1e6, 3),
+                     "profile": profile_path(LAYER_WORKLOAD)},
+        "base_roofline": {"bound": "mfma", "achieved": round(base_flops / base_layer / 1e12, 1),
                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(base_flops / tot["base"] / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
-        "layer": {"base_us": round(tot["base"] * 1e6, 2), "delta_us": round(delta * 1e6, 2),
-                  "lora_overhead_fraction": round(delta / tot["base"], 4),
+                          "frac": round(base_flops / base_layer / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "layer": {"base_us": round(base_layer * 1e6, 2), "delta_us_kernels": round(delta * 1e6, 2),
+                  "delta_us_step": round(wall / K * 1e6, 2),
+                  "lora_overhead_fraction": round(delta / base_layer, 4),
                   "delta_tokens_per_s_kernel_time": round(tokens / delta, 1),
+                  "delta_bytes": int(sum(q["sb"] + q["eb"] for q in projs)),
+                  "delta_gbs_step": round(sum(q["sb"] + q["eb"] for q in projs) / (wall / K) / 1e9, 1),
                   "projections": per},
+        "host_ms_per_step_eager": round(host_step_s * 1e3, 5),
         "kernel_sources_sha256_16": kernel_hash(),
     }
     if args.serial:
         Ks = min(K, 5)
-        calls = []
+        scalls = []
         for q in projs:
-            calls += [f for pair in q["dp"].serial_calls(q["y"], q["dp"].new_v(), stream) for f in pair]
-        out["comparator"] = serial_comparator(torch, stream, [calls], tokens, wall / K, Ks)
+            dp = q["dp"]
+            scalls += [f for pair in dp.serial_calls(q["y_base"].clone(), dp.new_v(), stream) for f in pair]
+        out["comparator"] = serial_comparator(torch, stream, [scalls], tokens, wall / K, Ks)
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(projs[0]["p"], args.cpu_seconds)
-        out["cpu_baseline"]["sample"] += " (q projection only)"
-    print(json.dumps(out), flush=True)
+        import oracle
+        parts = [(q["p"], oracle.Adapters.from_stacks(q["p"].a_rows, q["p"].bt_rows)) for q in projs]
+        out["cpu_baseline"] = cpu_baseline(parts, tokens, args.cpu_seconds)
+    del projs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_floor(args, torch):
+    """Bare streaming reads (the library's probe kernel) and a torch
+    read-modify-write, each rotating over buffers totalling more than twice the
+    LLC: the floor that a launch moving that many bytes with that many
+    workgroups cannot beat on this device."""
+    from segmented_gather_gemm_segments_amd import binding as B
+    stream = torch.cuda.Stream()
+    K = args.steps
+    rows = [("empty launch (256 workgroups x 16 B)", 16, 256, 256),
+            ("17 MB read, 2048 workgroups x 256 threads", 17 * 10**6 // 2048 // 16 * 16, 2048, 256),
+            ("36 MB read, 2048 workgroups x 256 threads", 36 * 10**6 // 2048 // 16 * 16, 2048, 256),
+            ("36 MB read, 256 workgroups x 512 threads", 36 * 10**6 // 256 // 16 * 16, 256, 512),
+            ("64 MB read, 2048 workgroups x 256 threads", 64 * 10**6 // 2048 // 16 * 16, 2048, 256),
+            ("256 MB read, 4096 workgroups x 256 threads", 256 * 10**6 // 4096 // 16 * 16, 4096, 256),
+            ("256 workgroups x 34 rows of 8 KiB (71 MB, the decode shape, rows distinct)", 34 * 8192, 256, 512),
+            ("111 workgroups x 34 rows of 8 KiB (31 MB)", 34 * 8192, 111, 512)]
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    table = []
+    for label, bpg, groups, threads in rows:
+        size = bpg * groups
+        n_rep = int(min(64, max(2, np.ceil(2 * LLC_BYTES / max(size, 1)))))
+        buf = torch.empty(size * n_rep // 2 + 16, dtype=torch.int16, device="cuda")
+        buf.fill_(1)
+        fns = [B.prepare_probe_stream_read(buf[(i * size) // 2:], bpg, groups, threads, sink, stream)
+               for i in range(n_rep)]
+        t = graph_span(torch, stream, [fns[i % n_rep] for i in range(K)], 3)
+        table.append({"launch": label, "bytes": size, "us": round(t * 1e6, 3),
+                      "gbs": round(size / t / 1e9, 1), "frac_of_peak": round(size / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del buf, fns
+    for mib in (64, 224):
+        n = mib * 2**20 // 2
+        n_rep = int(max(2, np.ceil(2 * LLC_BYTES / (2 * n))))
+        ts = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(n_rep)]
+        fns = [(lambda t=t: t.add_(1.0)) for t in ts]
+        t = graph_span(torch, stream, [fns[i % n_rep] for i in range(K)], 3)
+        table.append({"launch": f"read-modify-write of {mib} MiB bf16 (torch in-place add)",
+                      "bytes": 4 * n, "us": round(t * 1e6, 3), "gbs": round(4 * n / t / 1e9, 1),
+                      "frac_of_peak": round(4 * n / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del ts, fns
+    print(json.dumps({"floor": table, "steps": K, "peak_gbs": HBM_PEAK_GBS}), flush=True)
 
 
 def main():
@@ -502,151 +757,30 @@ def main():
         print(json.dumps({"calibrate_copy_mib": args.calibrate_copy, "dispatches": 5}), flush=True)
         return
 
-    from segmented_gather_gemm_segments_amd import accounting as acc
     from segmented_gather_gemm_segments_amd import binding as B
-    from segmented_gather_gemm_segments_amd import runner as R
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     B.lib()
+    if args.floor:
+        return run_floor(args, torch)
     if args.churn > 0:
         return bench_churn(args, torch)
     if args.multi:
         return bench_multi(args, torch)
     if args.config == 5:
-        return bench_layer(args, torch)
-    p = workload(args.config, args.shape, args.wq)
-    elem = 2 if p.dtype == "bf16" else 4
-    mode = "bgmv" if p.mode == "bgmv" else "sgmv"
-    stream = torch.cuda.Stream()          # default priority; every launch goes here
-
-    # ---- replicas (each its own x, y, v, weights): defeat the last-level cache
-    one = R.DeviceProblem(p)
-    per_rep = sum(t.numel() * t.element_size() for t in (one.x, one.y0, one.a_pages, one.b_pages))
-    n_rep = args.replicas or max(2, int(np.ceil(2 * LLC_BYTES / per_rep)))
-    n_rep = min(n_rep, 64)
-    reps = [one] + [R.DeviceProblem(p) for _ in range(n_rep - 1)]
-    calls = []
-    for dp in reps:
-        y, v = dp.y0.clone(), dp.new_v()
-        if mode == "bgmv":
-            sh, ex = B.prepare_bgmv(dp.weights, dp.ids, dp.x, v, y, args.order, stream=stream)
-            tord = dp.segments()[3] if args.placement == "grouped" else None
-            fu = B.prepare_bgmv_fused(dp.weights, dp.ids, dp.x, y, None, args.order, stream=stream,
-                                      token_order=tord)
-            calls.append((sh, ex, fu))
-        else:
-            _, _, _, perm_d = dp.segments()
-            sp = dp.plan(B.LORA_PHASE_SHRINK, args.policy)
-            ep = dp.plan(B.LORA_PHASE_EXPAND, args.policy)
-            dp._plans = (sp, ep)
-            calls.append(B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream))
-    torch.cuda.synchronize()
-    fused = mode == "bgmv" and args.path == "fused"
-
-    def step(i):
-        c = calls[i % n_rep]
-        if fused:
-            c[2]()
-        else:
-            c[0]()
-            c[1]()
-
-    # ---- warmup (eager), also measures the host's cost of one step
-    t0 = time.perf_counter()
-    for i in range(args.warmup):
-        step(i)
-    host_step_s = (time.perf_counter() - t0) / max(args.warmup, 1)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    # ---- the K steps as one HIP graph (a decode step is replayed, not re-launched)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(K):
-            step(i)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        graph.replay()                   # untimed replay: first-touch of the graph
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps, bracketed by synchronisation
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        graph.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # ---- per-launch durations: HIP events on the launch stream around a graph
-    # of K back-to-back launches of one kernel (the same launches as in the
-    # timed steps); duration per launch = event span / K
-    def span(which):
-        return np.array([graph_span(torch, stream, [calls[i % n_rep][which] for i in range(K)], 1)
-                         for _ in range(3)])
-
-    # ---- accounting
-    timed = {"shrink": (span(0), acc.shrink_bytes(p.ids, p.ranks, p.d_in, elem, p.wq)),
-             "expand": (span(1), acc.expand_bytes(p.ids, p.ranks, p.d_out, elem, p.wq))}
-    if mode == "bgmv":
-        timed["fused"] = (span(2), acc.fused_bytes(p.ids, p.ranks, p.d_in, p.d_out, elem, p.wq))
-    tokens = int(np.sum(p.ids >= 0))
-    ms_per_step = wall / K * 1e3
-    kern = {}
-    flops = {"shrink": acc.shrink_flops(p.ids, p.ranks, p.d_in),
-             "expand": acc.expand_flops(p.ids, p.ranks, p.d_out)}
-    flops["fused"] = flops["shrink"] + flops["expand"]
-    for name, (t, nbytes) in timed.items():
-        kern[name] = {"avg_us": float(t.mean() * 1e6), "min_us": float(t.min() * 1e6),
-                      "max_us": float(t.max() * 1e6), "bytes": nbytes,
-                      "gbs": nbytes / t.mean() / 1e9,
-                      "tflops": flops[name] / t.mean() / 1e12}
-    t_shrink, t_expand = timed["shrink"][0], timed["expand"][0]
-    dom = "fused" if fused else max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
-    kname = f"{mode}_{dom}"
-    traffic = read_traffic(kname, p.name)
-    achieved = kern[dom]["gbs"]
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kname, "algorithmic_bytes_per_launch": kern[dom]["bytes"],
-                "avg_launch_us": round(kern[dom]["avg_us"], 3)}
-    out = {
-        "metric": "LoRA delta tokens/sec per layer + achieved HBM GB/s (% of MI355X peak)",
-        "value": round(tokens * K / wall, 1),
-        "unit": "delta tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": p.dtype, "data": "synthetic (seeded; random-init adapters)",
-        "config": {"workload": p.name, "tokens": p.num_tokens, "adapters": p.num_adapters,
-                   "ranks": sorted(set(int(r) for r in p.ranks)), "d_in": p.d_in, "d_out": p.d_out,
-                   "adapter_rows": p.wq or p.dtype,
-                   "mode": mode, "path": ("fused" if fused else "shrink+expand"),
-                   "placement": (args.placement if fused else None),
-                   "replicas": n_rep, "timed": "HIP graph replay of the K steps",
-                   "parallelism": "single GPU"},
-        "roofline": roofline,
-        # the long segments' matrix-core use (reported, not targeted: the path
-        # is HBM-bound, and algorithmic flops / dense peak stays a few percent)
-        "mfma_utilisation": ({k: round(kern[k]["tflops"] / MFMA_BF16_PEAK_TFLOPS, 5)
-                              for k in ("shrink", "expand")} | {"peak_tflops": MFMA_BF16_PEAK_TFLOPS}
-                             if mode == "sgmv" and p.dtype == "bf16" else None),
-        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in d.items()}
-                    for k, d in kern.items()},
-        "gpu_tokens_per_s_kernel_time": round(
-            tokens / (kern["fused"]["avg_us"] * 1e-6 if fused else t_shrink.mean() + t_expand.mean()), 1),
-        "host_ms_per_step_eager": round(host_step_s * 1e3, 5),
-        "kernel_sources_sha256_16": kernel_hash(),
-    }
-    if args.serial:
-        Ks = min(K, 50)
-        steps_calls = []
-        for dp in reps[: min(n_rep, Ks)]:
-            y, v = dp.y0.clone(), dp.new_v()
-            steps_calls.append([f for pair in dp.serial_calls(y, v, stream) for f in pair])
-        out["comparator"] = serial_comparator(torch, stream, steps_calls, tokens, wall / K, Ks)
-    if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+        out = run_layer(args, torch)
+    elif args.config:
+        out = run_config(args, torch, args.config, args.shape, args.wq)
+    else:
+        # the default line: the 70B layer, with the decode batch and the
+        # heterogeneous paged batch nested (their own rooflines and baselines)
+        print("[bench] 70B layer", file=sys.stderr, flush=True)
+        out = run_layer(args, torch)
+        out["configs"] = {}
+        for cfg in (2, 4):
+            print(f"[bench] config {cfg}", file=sys.stderr, flush=True)
+            out["configs"][str(cfg)] = run_config(args, torch, cfg)
     print(json.dumps(out), flush=True)
 
 

@@ -445,6 +445,18 @@ lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const
  * LORA_EINVAL (sizes, null bytes). */
 lora_status lora_base_gemm_workspace(int32_t m, int32_t n, int32_t k, int64_t *bytes);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement helper, not part of the delta path: a bare streaming read of
+ * `groups` consecutive regions of bytes_per_group bytes of src, one workgroup
+ * of `threads` threads per region (16-byte loads), writing nothing to sink
+ * [groups] in practice.  The benchmark times it to show the floor that
+ * launches of a given size and workgroup count cannot beat on the device.
+ * src 16-byte aligned with groups * bytes_per_group readable bytes;
+ * bytes_per_group a multiple of 16; threads a multiple of 64 in 64..1024.
+ * Errors: LORA_EINVAL, LORA_EHIP. */
+lora_status lora_probe_stream_read(const void *src, int64_t bytes_per_group, int32_t groups,
+                                   int32_t threads, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

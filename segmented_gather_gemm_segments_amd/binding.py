@@ -92,6 +92,7 @@ EXPORTS = {
     "lora_cache_destroy": ([_P], None),
     "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_int64, _P], _I32),
     "lora_base_gemm_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
+    "lora_probe_stream_read": ([_P, ctypes.c_int64, _I32, _I32, _P, _P], _I32),
 }
 
 
@@ -443,6 +444,14 @@ class Cache:
             self.close()
         except Exception:
             pass
+
+
+def prepare_probe_stream_read(src, bytes_per_group: int, groups: int, threads: int, sink, stream=None):
+    """Prepared bare streaming read (a measurement floor, not the delta path)."""
+    assert src.numel() * src.element_size() >= bytes_per_group * groups
+    assert sink.numel() * sink.element_size() >= 4 * groups
+    return Prepared("lora_probe_stream_read", (_dptr(src), int(bytes_per_group), int(groups),
+                                               int(threads), _dptr(sink), _stream(stream)), (src, sink))
 
 
 # ---------------------------------------------------------------- prepared launches

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblora_sgmv.so")
 SOURCES = [os.path.join(HERE, "csrc", "host.cpp"), os.path.join(HERE, "csrc", "kernels.hip"),
-           os.path.join(HERE, "csrc", "base_gemm.hip"), os.path.join(HERE, "csrc", "residency.hip")]
+           os.path.join(HERE, "csrc", "base_gemm.hip"), os.path.join(HERE, "csrc", "residency.hip"),
+           os.path.join(HERE, "csrc", "probe.hip")]
 HEADERS = [os.path.join(ROOT, "include", "lora_sgmv.h"),
            os.path.join(HERE, "csrc", "lora_internal.h")]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")

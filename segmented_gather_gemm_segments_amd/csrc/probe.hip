@@ -1,0 +1,55 @@
+// Measurement helper, outside the delta path: a bare streaming read of given
+// size and workgroup count.  bench.py times it to show what a kernel that
+// moves a given number of bytes with a given number of workgroups cannot beat
+// on this device (the launch and memory-latency floor of small launches).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+// Workgroup g reads the 16-byte chunks [g n16, (g + 1) n16) of src, eight
+// loads in flight per thread, and folds them into one word that is stored
+// only in the (practically impossible) case that it equals a magic value, so
+// the loads stay live while nothing is written.
+__global__ __launch_bounds__(1024) void stream_read_kernel(const uint4 *__restrict__ src, int64_t n16,
+                                                           uint32_t *__restrict__ sink) {
+  const uint4 *p = src + (int64_t)blockIdx.x * n16;
+  const int nt = blockDim.x;
+  uint32_t acc = 0;
+  int64_t i = threadIdx.x;
+  for (; i + 7 * (int64_t)nt < n16; i += 8 * (int64_t)nt) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * nt];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += nt) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" lora_status lora_probe_stream_read(const void *src, int64_t bytes_per_group, int32_t groups,
+                                              int32_t threads, uint32_t *sink, hipStream_t stream) {
+  if (groups < 0 || bytes_per_group < 0) return fail(LORA_EINVAL, "negative size");
+  if (groups == 0 || bytes_per_group == 0) return ok();
+  if (!src || !sink) return fail(LORA_EINVAL, "null pointer");
+  if (((uintptr_t)src & 15u) || bytes_per_group % 16)
+    return fail(LORA_EINVAL, "src and bytes_per_group must be multiples of 16 bytes");
+  if (threads < 64 || threads > 1024 || threads % 64)
+    return fail(LORA_EINVAL, "threads must be a multiple of 64 in 64..1024");
+  hipLaunchKernelGGL(stream_read_kernel, dim3(groups), dim3(threads), 0, stream, (const uint4 *)src,
+                     bytes_per_group / 16, sink);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}

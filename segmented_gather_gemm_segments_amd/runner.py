@@ -7,6 +7,7 @@ Used by the GPU tests, the benchmark and the smoke check.
 """
 from __future__ import annotations
 
+import dataclasses
 from typing import Optional
 
 import numpy as np
@@ -164,6 +165,28 @@ class DeviceProblem:
                                  torch.from_numpy(b_pt).to(self.device), max_pages,
                                  weight_format=self.wfmt, a_scales=pool_a.scales,
                                  b_scales=pool_b.scales)
+
+    def replica(self, with_base: bool = False):
+        """The same batch at other device addresses: clones of x, y0 and the
+        adapter rows (and row scales), with a descriptor of their own; ids,
+        ranks, page tables, segments and (unless with_base) the base weight are
+        shared.  Replicas let a benchmark rotate over more bytes than the
+        last-level cache holds."""
+        r = object.__new__(DeviceProblem)
+        r.__dict__.update(self.__dict__)
+        r.x = self.x.clone()
+        r.y0 = self.y0.clone()
+        w = self.weights
+        a = w.a_pages.clone()
+        b = a if w.b_pages is w.a_pages else w.b_pages.clone()
+        sa = None if w.a_scales is None else w.a_scales.clone()
+        sb = sa if (w.b_scales is w.a_scales) else (None if w.b_scales is None else w.b_scales.clone())
+        r.a_pages, r.b_pages = a, b
+        r.weights = dataclasses.replace(w, a_pages=a, b_pages=b, a_scales=sa, b_scales=sb)
+        if with_base and self.w is not None:
+            r.w = self.w.clone()
+        r._pools = []
+        return r
 
     # ------------------------------------------------------------- segments, plans
     def segments(self):

@@ -135,15 +135,22 @@ def _rows_close(got, want, label, elementwise=True):
         assert np.all(np.abs(got - want) <= np.abs(want) * 2.0**-8 + 1e-3 * scale), label
 
 
-@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
+def _threads():
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+@pytest.mark.parametrize("name", [n for n, _, _ in wl.LAYER_70B])
 def test_layer70b_projection(name):
     """One projection of the 70B-shape layer at full size (1280 tokens: 256
     decode tokens on 256 rank-16 adapters plus a 1024-token prefill request on
-    adapter 0): the base GEMM, then the SGMV delta (segmented mode, automatic
-    path: one 1025-token MFMA segment, 255 gather segments) added to the GPU's
-    base output, both checked on full rows; and the per-token (BGMV) delta
-    and the segmented gather delta agree on full rows (the two shrinks split
-    d_in over different numbers of waves, so within one bf16 rounding, not
+    adapter 0), for each of the seven projections: the base GEMM checked on
+    sampled full rows; then the SGMV delta (segmented mode, automatic path:
+    one 1025-token MFMA segment, 255 gather segments) added to the GPU's base
+    output, checked on EVERY row against the oracle with that same base output
+    as y_in, and its v on every token; and the per-token (BGMV) delta and the
+    segmented gather delta on every row too (the two shrinks split d_in over
+    different numbers of waves, so they agree within one bf16 rounding, not
     bit for bit)."""
     R = runner()
     p = wl.layer_projection(name)
@@ -158,17 +165,24 @@ def test_layer70b_projection(name):
     want_b = oracle.base_sampled(p.x, p.extra["w"], tok, col).reshape(rows.size, p.d_out)
     _rows_close(yb[rows], want_b, f"{name} base")
     # delta on top of the GPU's base output (the oracle takes the same y_in)
-    y, _ = dp.run_sgmv(B.LORA_PATH_AUTO, y=y_base.clone())
+    y, v = dp.run_sgmv(B.LORA_PATH_AUTO, y=y_base.clone())
     torch.cuda.synchronize()
     got = bf16_host(y)
     ad = oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
-    want = oracle.apply(p.x[rows], yb[rows], p.ids[rows], ad)
-    _rows_close(got[rows], want, f"{name} base+delta")
+    yb_bits = y_base.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = oracle.apply(p.x, yb_bits, p.ids, ad, threads=_threads())
+    _rows_close(got, want, f"{name} base+delta, all {p.num_tokens} rows")
+    want_v = oracle.shrink(p.x, p.ids, ad, dp.r_max)
+    got_v = v.cpu().numpy().astype(np.float64)
+    err_v = float(np.max(np.max(np.abs(got_v - want_v), axis=1) / np.max(np.abs(want_v), axis=1)))
+    say(f"{name} v: normwise error {err_v:.3e} over all {p.num_tokens} tokens")
+    assert err_v <= 1e-4, name
     # per-token mode and the segmented gather path on the same batch
     y2, _ = dp.run_bgmv(B.LORA_BGMV_AUTO, y=y_base.clone())
     y3, _ = dp.run_sgmv(B.LORA_PATH_GATHER, y=y_base.clone())
     torch.cuda.synchronize()
     g2, g3 = bf16_host(y2), bf16_host(y3)
-    _rows_close(g2[rows], want, f"{name} bgmv base+delta")
+    _rows_close(g2, want, f"{name} bgmv base+delta, all rows")
+    _rows_close(g3, want, f"{name} sgmv gather base+delta, all rows")
     scale = np.max(np.abs(g3), axis=1, keepdims=True)
     assert np.all(np.abs(g2 - g3) <= np.abs(g3) * 2.0**-7 + 1e-4 * scale), f"{name} bgmv vs gather"
