@@ -46,8 +46,9 @@
  *     and need no GPU.  Device-side functions enqueue work on `stream` (the
  *     caller's HIP stream; 0 = default) and return without synchronising.
  *   - The library allocates no device memory on any call below; every buffer
- *     is caller-owned.  Pointers to device arrays must be 16-byte aligned, and
- *     d_in and d_out multiples of 8.
+ *     is caller-owned, except the fixed scratch array that the library's code
+ *     object holds for lora_base_gemm_noalloc.  Pointers to device arrays must
+ *     be 16-byte aligned, and d_in and d_out multiples of 8.
  *   - Each y element is written by exactly one GPU thread, with no atomics, so
  *     results are bit-identical from run to run.
  *   - Device-resident indices (token_perm, plan items, page tables, per-token
@@ -444,6 +445,27 @@ lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const
  * on the current device (0: it would not split).  *bytes host.  Errors:
  * LORA_EINVAL (sizes, null bytes). */
 lora_status lora_base_gemm_workspace(int32_t m, int32_t n, int32_t k, int64_t *bytes);
+
+/* lora_base_gemm for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, arithmetic and results as
+ * lora_base_gemm called with the workspace lora_base_gemm_workspace reports
+ * (bit for bit: the same kernels and the same k split), but the split-k
+ * partial tiles go to a scratch array the library holds in device memory:
+ * LORA_BASE_GEMM_SCRATCH_BYTES (24 MiB) on every device it is called on, kept
+ * until the process ends.  Nothing is allocated by the call (no hipMalloc, no
+ * hipFree, no allocating library routine); the scratch's device address is
+ * looked up once per device on the first call there.  Every call on one
+ * device shares that device's scratch, and each split call overwrites every
+ * partial it reads before reading it (nothing needs clearing), so calls that
+ * overlap on one device -- on different streams, or on one stream from
+ * several host threads without ordering -- race and give wrong results.
+ * Errors: as lora_base_gemm, and LORA_ENOMEM when the shape's split needs
+ * more partial-tile bytes than the scratch holds (not for any shape on a
+ * device of up to 256 compute units, where the split rule stays within 24 MiB). */
+#define LORA_BASE_GEMM_SCRATCH_BYTES (24 << 20)
+lora_status lora_base_gemm_noalloc(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *x,
+                                   const void *w, void *y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Measurement helper, not part of the delta path: a bare streaming read of

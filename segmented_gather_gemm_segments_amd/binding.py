@@ -92,6 +92,7 @@ EXPORTS = {
     "lora_cache_destroy": ([_P], None),
     "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_int64, _P], _I32),
     "lora_base_gemm_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
+    "lora_base_gemm_noalloc": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "lora_probe_stream_read": ([_P, ctypes.c_int64, _I32, _I32, _P, _P], _I32),
 }
 
@@ -323,6 +324,15 @@ def lora_base_gemm(x, w, y, workspace=None, stream=None):
     wp, wb = _ws(workspace)
     _check(lib().lora_base_gemm(LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y), wp, wb,
                                 _stream(stream)))
+
+
+def lora_base_gemm_noalloc(x, w, y, stream=None):
+    """lora_base_gemm without a workspace argument: split-k partials go to the
+    library's own device scratch (allocates nothing)."""
+    m, k = x.shape
+    n = w.shape[0]
+    _check(lib().lora_base_gemm_noalloc(LORA_BF16, m, n, k, _dptr(x), _dptr(w), _dptr(y),
+                                        _stream(stream)))
 
 
 class Pool:

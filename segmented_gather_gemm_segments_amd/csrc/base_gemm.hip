@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "lora_internal.h"
@@ -344,6 +345,90 @@ int device_cus() {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Checks the arguments shared by both entry points (LORA_OK, or an error with
+// its message); *tiles_m, *tiles get the grid's tile counts.
+lora_status check_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *x, const void *w,
+                       const void *y, int64_t *tiles_m, int64_t *tiles) {
+  if (dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "base gemm supports bf16 only");
+  if (m < 0 || n <= 0 || k <= 0) return fail(LORA_EINVAL, "base gemm sizes m=%d n=%d k=%d", m, n, k);
+  if (n % 8 || k % 8) return fail(LORA_EUNSUPPORTED, "base gemm needs n and k multiples of 8");
+  *tiles_m = (m + kBM - 1) / kBM;
+  *tiles = *tiles_m * ((n + kBN - 1) / kBN);
+  if (m == 0) return ok();
+  if (!x || !w || !y) return fail(LORA_EINVAL, "null pointer");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+    return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
+  return ok();
+}
+
+// Enqueues the GEMM with k cut into `splits` slices (1: no split; more: their
+// fp32 partial tiles go to `part`, splits * m * n floats, then the reduction).
+lora_status launch_gemm(int32_t m, int32_t n, int32_t k, int64_t tiles_m, int64_t tiles, int splits,
+                        const void *x, const void *w, void *y, float *part, hipStream_t stream) {
+  if (tiles * splits > INT32_MAX - 8) return fail(LORA_EINVAL, "base gemm too large");
+  // slice length in whole k-steps
+  const int k_slice = (int)((((int64_t)k + splits - 1) / splits + kBK - 1) / kBK * kBK);
+  const int grid = (int)((tiles * splits + 7) & ~int64_t(7));
+  // whole tiles: direct-to-LDS kernels, a k-step of 64 for grids of at least
+  // six tiles per CU (three rounds of two), else 32; otherwise the
+  // register-staged kernel, which reads ragged edges as zeros
+  const bool whole = m % kBM == 0 && n % kBN == 0 && k % 64 == 0;
+  auto kern = base_gemm_kernel;
+  if (whole) kern = tiles * splits >= 6 * (int64_t)device_cus() ? base_gemm_lds64_kernel : base_gemm_lds32_kernel;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), 0, stream, m, n, k, (int)tiles_m,
+                     (int)tiles, splits, k_slice, (const uint16_t *)x, (const uint16_t *)w,
+                     (uint16_t *)y, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "base gemm launch");
+  if (splits > 1) {
+    const int64_t mn = (int64_t)m * n;  // a multiple of 8
+    const int64_t blocks = (mn / 4 + 255) / 256;
+    if (blocks > INT32_MAX) return fail(LORA_EINVAL, "base gemm too large");
+    hipLaunchKernelGGL(base_gemm_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mn,
+                       splits, (const float *)part, (uint16_t *)y);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "base gemm reduce launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- scratch
+// Device memory of lora_base_gemm_noalloc's split-k partial tiles, held by
+// the library on every device it runs on until the process ends.  Its size
+// covers every split the rule in pick_splits asks for on a 256-CU device:
+// S x tiles <= 1.5 x CUs units of 128 x 128 fp32 partials, 384 x 64 KiB.
+constexpr int64_t kScratchBytes = LORA_BASE_GEMM_SCRATCH_BYTES;
+static_assert(kScratchBytes == int64_t(24) << 20, "24 MiB");
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current (in host code the array's name is only a host-side
+// stand-in, never a device address).
+lora_status scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LORA_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LORA_EHIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ok();
+}
+
 }  // namespace
 
 extern "C" lora_status lora_base_gemm_workspace(int32_t m, int32_t n, int32_t k, int64_t *bytes) {
@@ -360,45 +445,36 @@ extern "C" lora_status lora_base_gemm_workspace(int32_t m, int32_t n, int32_t k,
 extern "C" lora_status lora_base_gemm(int32_t dtype, int32_t m, int32_t n, int32_t k,
                                       const void *x, const void *w, void *y, void *workspace,
                                       int64_t workspace_bytes, hipStream_t stream) {
-  if (dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "base gemm supports bf16 only");
-  if (m < 0 || n <= 0 || k <= 0) return fail(LORA_EINVAL, "base gemm sizes m=%d n=%d k=%d", m, n, k);
-  if (n % 8 || k % 8) return fail(LORA_EUNSUPPORTED, "base gemm needs n and k multiples of 8");
+  int64_t tiles_m = 0, tiles = 0;
+  lora_status st = check_gemm(dtype, m, n, k, x, w, y, &tiles_m, &tiles);
+  if (st != LORA_OK) return st;
   if (workspace_bytes < 0) return fail(LORA_EINVAL, "negative workspace size");
   if (m == 0) return ok();
-  if (!x || !w || !y) return fail(LORA_EINVAL, "null pointer");
-  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (workspace && !aligned16(workspace)))
-    return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
-  const int64_t tiles_m = (m + kBM - 1) / kBM, tiles_n = (n + kBN - 1) / kBN;
-  const int64_t tiles = tiles_m * tiles_n;
+  if (workspace && !aligned16(workspace)) return fail(LORA_EINVAL, "device arrays must be 16-byte aligned");
   // split k only into a workspace that holds every slice's partial tile
   int splits = 1;
   if (workspace) {
     const int s = pick_splits(tiles, k, device_cus());
     if (s > 1 && workspace_bytes >= (int64_t)s * m * n * (int64_t)sizeof(float)) splits = s;
   }
-  if (tiles * splits > INT32_MAX - 8) return fail(LORA_EINVAL, "base gemm too large");
-  // slice length in whole k-steps
-  const int k_slice = (int)((((int64_t)k + splits - 1) / splits + kBK - 1) / kBK * kBK);
-  const int grid = (int)((tiles * splits + 7) & ~int64_t(7));
-  // whole tiles: direct-to-LDS kernels, a k-step of 64 for grids of at least
-  // six tiles per CU (three rounds of two), else 32; otherwise the
-  // register-staged kernel, which reads ragged edges as zeros
-  const bool whole = m % kBM == 0 && n % kBN == 0 && k % 64 == 0;
-  auto kern = base_gemm_kernel;
-  if (whole) kern = tiles * splits >= 6 * (int64_t)device_cus() ? base_gemm_lds64_kernel : base_gemm_lds32_kernel;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), 0, stream, m, n, k, (int)tiles_m,
-                     (int)tiles, splits, k_slice, (const uint16_t *)x, (const uint16_t *)w,
-                     (uint16_t *)y, (float *)workspace);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "base gemm launch");
-  if (splits > 1) {
-    const int64_t mn = (int64_t)m * n;  // a multiple of 8
-    const int64_t blocks = (mn / 4 + 255) / 256;
-    if (blocks > INT32_MAX) return fail(LORA_EINVAL, "base gemm too large");
-    hipLaunchKernelGGL(base_gemm_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, mn,
-                       splits, (const float *)workspace, (uint16_t *)y);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "base gemm reduce launch");
+  return launch_gemm(m, n, k, tiles_m, tiles, splits, x, w, y, (float *)workspace, stream);
+}
+
+extern "C" lora_status lora_base_gemm_noalloc(int32_t dtype, int32_t m, int32_t n, int32_t k,
+                                              const void *x, const void *w, void *y,
+                                              hipStream_t stream) {
+  int64_t tiles_m = 0, tiles = 0;
+  lora_status st = check_gemm(dtype, m, n, k, x, w, y, &tiles_m, &tiles);
+  if (st != LORA_OK || m == 0) return st;
+  const int s = pick_splits(tiles, k, device_cus());
+  void *part = nullptr;
+  if (s > 1) {
+    const int64_t need = (int64_t)s * m * n * (int64_t)sizeof(float);
+    if (need > kScratchBytes)
+      return fail(LORA_ENOMEM, "base gemm %dx%dx%d splits k %d ways into %lld bytes of partial "
+                  "tiles; the library's scratch holds %lld", m, n, k, s, (long long)need,
+                  (long long)kScratchBytes);
+    if ((st = scratch_address(&part)) != LORA_OK) return st;
   }
-  return ok();
+  return launch_gemm(m, n, k, tiles_m, tiles, s, x, w, y, (float *)part, stream);
 }
