@@ -285,6 +285,9 @@ lora_status lora_bgmv_expand(const lora_weights *w, const int32_t *token_adapter
  *   token_order [num_ordered]  device, or NULL.  Token-major order only: the
  *          tokens to process, in placement order (each an index in
  *          [0, num_tokens); others are skipped; tokens not listed keep their y).
+ *          Each token may be listed at most once: a token listed twice is
+ *          updated by two workgroups that race on its y row (the token_perm
+ *          of lora_segments_build lists every token once).
  *          Consecutive entries run on the same XCD and share its L2, so an
  *          order that groups the tokens of each adapter -- the token_perm of
  *          lora_segments_build, built once per batch on the host and reused by

@@ -13,8 +13,11 @@
 //     four waves;
 //   * MFMA (long segments): the per-adapter product is a dense GEMM and runs on
 //     v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32).
-//     Expand keeps v exact by splitting it into a bf16 pair hi + lo (two MFMA
-//     K-halves), so v never loses precision to bf16.
+//     The bf16 expand feeds the fp32 v to the matrix cores as a pair of bf16
+//     values hi + lo (two MFMA K-halves): hi = RNE(v), lo = RNE(v - hi) keep
+//     about 16 significant bits of v (relative error at most about 2^-17), far
+//     more than one bf16 (8 bits) but fewer than fp32's 24, so the MFMA and
+//     gather expands agree to rounding, not bit for bit.
 // No floating-point atomics: every output element is produced by one thread
 // and summation orders are fixed, so repeated runs are bit-identical.
 #include <hip/hip_runtime.h>
@@ -203,7 +206,8 @@ __device__ __forceinline__ void b_rows16(const DevW &w, int a, int j0, int r, in
 // in page), or -1 where `safe` is returned.  All N page-id loads are issued
 // (clamped indices, unconditional) before any is used, and the rest is
 // selects, not branches: the lookups overlap each other and do not wait for
-// loads issued before them.  Storage indices fit int32 (checked on the host).
+// loads issued before them.  Storage indices fit int32: to_dev rejects pools
+// of more than 2^31 - 1 stored rows.
 template <int N>
 __device__ __forceinline__ void rows_addr(const DevW &w, const Side &sd, int a, const int (&j)[N],
                                           const bool (&use)[N], int64_t ofs, const char *safe,
@@ -734,7 +738,7 @@ template <> struct ExpandCfg<float> { static constexpr int kRowStride = kExpandK
 
 constexpr int kVStride = kExpandK + 4;  // LDS row stride (floats) of the staged v rows: j + pad
 // bf16 activations: each staged v row holds the chunk's bf16 hi parts, then
-// its bf16 lo parts (v = hi + lo exactly to fp32 rounding), then a pad; the
+// its bf16 lo parts (v = hi + lo to about 16 significant bits), then a pad; the
 // split is done once per staged chunk instead of in every wave's MFMA loop.
 constexpr int kVhlStride = 2 * kExpandK + 8;  // bf16 elements
 
@@ -947,7 +951,8 @@ __device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj,
 // up to 64 rank indices, stored transposed in LDS) and the workgroup loads the
 // 64 tokens' v rows (stored in LDS); after one barrier the slab fragments of a
 // 16-index K block are read once and used by all four token tiles.  bf16: v is
-// split into hi + lo bf16 so each K=32 MFMA covers 16 rank indices exactly;
+// split into hi + lo bf16 (about 16 significant bits of v) so each K=32 MFMA
+// covers 16 rank indices;
 // fp32: 16x16x4 steps.
 template <typename T, typename W>
 __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk, const int *toks, int cnt,
@@ -1961,6 +1966,11 @@ lora_status to_dev(const lora_weights *w, DevW *d) {
   if (w->num_adapters < 0) return fail(LORA_EINVAL, "negative num_adapters");
   if (w->page_rows <= 0) return fail(LORA_EINVAL, "page_rows must be positive");
   if (w->num_pages_a <= 0 || w->num_pages_b <= 0) return fail(LORA_EINVAL, "empty page pool");
+  // the kernels form stored-row numbers (page * page_rows + row) in 32 bits
+  if ((int64_t)w->num_pages_a * w->page_rows > INT32_MAX ||
+      (int64_t)w->num_pages_b * w->page_rows > INT32_MAX)
+    return fail(LORA_EINVAL, "page pool of more than 2^31 - 1 stored rows (%d or %d pages of %d rows)",
+                w->num_pages_a, w->num_pages_b, w->page_rows);
   const int32_t wf = w->weight_format;
   if (wf != LORA_WFMT_PLAIN && wf != LORA_WFMT_FP8_E4M3 && wf != LORA_WFMT_INT4)
     return fail(LORA_EUNSUPPORTED, "unknown weight_format %d", wf);

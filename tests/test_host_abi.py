@@ -159,7 +159,8 @@ def test_plan_path_choice_and_order():
     items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 16, mfma_min_tokens=1)
     assert all((cp >> 16) == B.LORA_PATH_MFMA for _, _, cp, _ in items)
     # heaviest first: expand items ordered by the bytes they move (y read and
-    # written per token, plus 16 B^T rows over the item's columns)
+    # written per token, plus the adapter's B^T rows over the item's columns:
+    # 16 rows assumed when no ranks are given)
     items = B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, starts, adapters, 3, 4096)
     cols = np.where((items[:, 2] >> 16) == B.LORA_PATH_MFMA, B.LORA_EXPAND_MFMA_COLS,
                     B.LORA_EXPAND_GATHER_COLS)
@@ -299,12 +300,24 @@ def _desc(**kw):
     (dict(weight_format=2, a_scales=16), B.LORA_EINVAL),                    # one scale array
     (dict(weight_format=2, a_scales=18, b_scales=16), B.LORA_EINVAL),       # misaligned scales
     (dict(a_page_table=64), B.LORA_EINVAL),       # one table without the other
+    # stored-row numbers must fit 32 bits: 2^27 pages of 16 rows is 2^31 rows
+    (dict(a_page_table=64, b_page_table=64, num_pages_a=1 << 27), B.LORA_EINVAL),
+    (dict(a_page_table=64, b_page_table=64, num_pages_b=(1 << 27) + 5), B.LORA_EINVAL),
 ])
 def test_weight_validation_errors(kw, status):
     d = _desc(**kw)
     rc = B.lib().lora_sgmv_shrink(ctypes.byref(d), 16, 1, 16, 1, 1, 16, 16, None)
     assert rc == status, B.lora_last_error()
     assert B.lora_last_error()
+
+
+def test_largest_pool_within_32_bit_rows_is_accepted():
+    """(2^31 - 1) // 16 pages of 16 rows pass validation (zero items: a
+    validated no-op, no GPU needed)."""
+    d = _desc(a_page_table=64, b_page_table=64, num_pages_a=(2**31 - 1) // 16,
+              num_pages_b=(2**31 - 1) // 16)
+    rc = B.lib().lora_sgmv_shrink(ctypes.byref(d), 16, 1, 16, 0, 1, 16, 16, None)
+    assert rc == B.LORA_OK, B.lora_last_error()
 
 
 def test_host_rank_validation():
