@@ -52,9 +52,10 @@
  *   - Each y element is written by exactly one GPU thread, with no atomics, so
  *     results are bit-identical from run to run.
  *   - Device-resident indices (token_perm, plan items, page tables, per-token
- *     adapter ids) are checked by the kernels: an out-of-range value makes the
- *     affected token or row contribute nothing instead of reading out of
- *     bounds.  Outputs for such tokens are then unspecified.
+ *     adapter ids, ranks) are checked by the kernels: an out-of-range value
+ *     makes the affected token or row contribute nothing instead of reading
+ *     out of bounds.  Outputs for such tokens are then unspecified.  The debug
+ *     build of the library reports such values (lora_debug_flags below).
  */
 #ifndef LORA_SGMV_H
 #define LORA_SGMV_H
@@ -469,6 +470,22 @@ lora_status lora_base_gemm_workspace(int32_t m, int32_t n, int32_t k, int64_t *b
 #define LORA_BASE_GEMM_SCRATCH_BYTES (24 << 20)
 lora_status lora_base_gemm_noalloc(int32_t dtype, int32_t m, int32_t n, int32_t k, const void *x,
                                    const void *w, void *y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Debug build.  The library is also built as liblora_sgmv_debug.so, with
+ * LORA_DEBUG: its kernels record the bad device-side values that every build
+ * skips (see "Device-resident indices" above) as bits of a device word, and
+ * still exit normally.  lora_debug_flags waits for the device's work (it reads
+ * the word with a synchronous copy), stores the word in *flags and, when clear
+ * is non-zero, resets it.  The word covers every call on the current device
+ * since the last clear.  Release builds return LORA_EUNSUPPORTED (and *flags =
+ * 0).  Errors: LORA_EINVAL (null flags), LORA_EHIP. */
+#define LORA_DEBUG_BAD_PAGE 1u      /* a page id outside the pool for a row below the rank */
+#define LORA_DEBUG_BAD_ADAPTER 2u   /* a device adapter id outside {-1} U [0, num_adapters) */
+#define LORA_DEBUG_BAD_RANK 4u      /* a used adapter's rank outside 1..r_max */
+#define LORA_DEBUG_BAD_TOKEN 8u     /* a token_perm entry outside [0, num_tokens) */
+#define LORA_DEBUG_BAD_ITEM 16u     /* a plan item that names no valid tokens or adapter */
+lora_status lora_debug_flags(uint32_t *flags, int32_t clear);
 
 /* ------------------------------------------------------------------------ */
 /* Measurement helper, not part of the delta path: a bare streaming read of

@@ -94,27 +94,53 @@ EXPORTS = {
     "lora_base_gemm_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
     "lora_base_gemm_noalloc": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "lora_probe_stream_read": ([_P, ctypes.c_int64, _I32, _I32, _P, _P], _I32),
+    "lora_debug_flags": ([_P, _I32], _I32),
 }
+LORA_DEBUG_BAD_PAGE, LORA_DEBUG_BAD_ADAPTER, LORA_DEBUG_BAD_RANK = 1, 2, 4
+LORA_DEBUG_BAD_TOKEN, LORA_DEBUG_BAD_ITEM = 8, 16
+
+
+_debug = False
+_loaded = {}
 
 
 def lib_path() -> str:
-    return _build.LIB
+    return _build.DEBUG_LIB if _debug else _build.LIB
+
+
+def select_library(debug: bool) -> None:
+    """Route every call of this module to the debug build of the library
+    (kernels record bad device-side values, read by lora_debug_flags) or back
+    to the release build."""
+    global _debug, _lib
+    _debug = bool(debug)
+    _lib = None
 
 
 def lib():
     """Load the built library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            raise RuntimeError(f"{_build.LIB} is missing: build it with "
-                               "`python -m segmented_gather_gemm_segments_amd.build`")
-        h = ctypes.CDLL(_build.LIB)
-        for name, (args, res) in EXPORTS.items():
-            f = getattr(h, name)
-            f.argtypes = args
-            f.restype = res
-        _lib = h
+        path = lib_path()
+        if path not in _loaded:
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is missing: build it with "
+                                   "`python -m segmented_gather_gemm_segments_amd.build`")
+            h = ctypes.CDLL(path)
+            for name, (args, res) in EXPORTS.items():
+                f = getattr(h, name)
+                f.argtypes = args
+                f.restype = res
+            _loaded[path] = h
+        _lib = _loaded[path]
     return _lib
+
+
+def lora_debug_flags(clear: bool = False) -> int:
+    """The debug build's error word (LORA_DEBUG_* bits); waits for the device."""
+    out = ctypes.c_uint32(0)
+    _check(lib().lora_debug_flags(ctypes.byref(out), int(clear)))
+    return int(out.value)
 
 
 def status_name(status: int) -> str:

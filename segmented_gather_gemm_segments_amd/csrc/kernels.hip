@@ -67,6 +67,32 @@ struct DevW {
   int32_t d_in, d_out, num_adapters, r_max, page_rows, max_pages, num_pages_a, num_pages_b;
 };
 
+// ----------------------------------------------------------------- debug checks
+// With LORA_DEBUG (the debug build of the library) the kernels record the bad
+// device-side values they skip -- a page id outside the pool for a row below
+// the rank, an adapter id outside {-1} U [0, N), a rank outside 1..r_max, a
+// token index outside the batch, a malformed plan item -- as LORA_DEBUG_* bits
+// in a device word that lora_debug_flags reads back.  Every kernel still
+// skips such values and exits normally; release builds compile the checks
+// away.
+#ifndef LORA_DEBUG
+#define LORA_DEBUG 0
+#endif
+#if LORA_DEBUG
+__device__ uint32_t g_debug_flags;
+__device__ __forceinline__ void debug_flag(uint32_t bit) {
+  __hip_atomic_fetch_or(&g_debug_flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+#define LORA_CHECK(cond, bit) \
+  do {                        \
+    if (!(cond)) debug_flag(bit); \
+  } while (0)
+#else
+#define LORA_CHECK(cond, bit) \
+  do {                        \
+  } while (0)
+#endif
+
 // Storage index (page * page_rows + row in page) of row j of adapter a through
 // the page table, or -1 when the page id is out of range (the row then
 // contributes nothing).  The page-id load is unconditional (clamped index) so
@@ -88,12 +114,15 @@ __device__ __forceinline__ int64_t row_index(const DevW &w, const int32_t *pt, i
 }
 
 // Byte address of row j of adapter a's A (or B^T); nullptr when out of range.
+// (Called for rows below the adapter's rank only.)
 __device__ __forceinline__ const char *a_row(const DevW &w, int a, int j) {
   const int64_t i = row_index(w, w.a_pt, w.num_pages_a, a, j);
+  LORA_CHECK(i >= 0, LORA_DEBUG_BAD_PAGE);
   return i < 0 ? nullptr : w.a_pages + i * w.a_row_bytes;
 }
 __device__ __forceinline__ const char *b_row(const DevW &w, int a, int j) {
   const int64_t i = row_index(w, w.b_pt, w.num_pages_b, a, j);
+  LORA_CHECK(i >= 0, LORA_DEBUG_BAD_PAGE);
   return i < 0 ? nullptr : w.b_pages + i * w.b_row_bytes;
 }
 // Scale of row j (1 for unquantized rows or an out-of-range page).
@@ -101,12 +130,14 @@ template <typename W>
 __device__ __forceinline__ float a_scale(const DevW &w, int a, int j) {
   if constexpr (!WT<W>::kScaled) return 1.f;
   const int64_t i = row_index(w, w.a_pt, w.num_pages_a, a, j);
+  LORA_CHECK(i >= 0, LORA_DEBUG_BAD_PAGE);
   return i < 0 ? 0.f : w.a_sc[i];
 }
 template <typename W>
 __device__ __forceinline__ float b_scale(const DevW &w, int a, int j) {
   if constexpr (!WT<W>::kScaled) return 1.f;
   const int64_t i = row_index(w, w.b_pt, w.num_pages_b, a, j);
+  LORA_CHECK(i >= 0, LORA_DEBUG_BAD_PAGE);
   return i < 0 ? 0.f : w.b_sc[i];
 }
 
@@ -162,6 +193,7 @@ __device__ __forceinline__ void rows16(const DevW &w, const Side &sd, int a, int
       r0 = j0;
     }
     const bool ok = (unsigned)page < (unsigned)sd.num_pages;
+    LORA_CHECK(ok || j0 >= r, LORA_DEBUG_BAD_PAGE);
     const int64_t i0 = (int64_t)(ok ? page : 0) * pr + r0;
     const char *base = sd.pages + i0 * sd.row_bytes + cofs;
 #pragma unroll
@@ -177,6 +209,7 @@ __device__ __forceinline__ void rows16(const DevW &w, const Side &sd, int a, int
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t idx = j0 + i < r ? row_index(w, sd.pt, sd.num_pages, a, j0 + i) : -1;
+      LORA_CHECK(idx >= 0 || j0 + i >= r, LORA_DEBUG_BAD_PAGE);
       rp[i] = idx >= 0 ? sd.pages + idx * sd.row_bytes + cofs : safe;
     }
     if constexpr (SC && WT<W>::kScaled) {
@@ -234,6 +267,7 @@ __device__ __forceinline__ void rows_addr(const DevW &w, const Side &sd, int a, 
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const bool ok = use[i] && (unsigned)page[i] < (unsigned)sd.num_pages;
+    LORA_CHECK(ok || !use[i], LORA_DEBUG_BAD_PAGE);
     const int idx = (int)((unsigned)page[i] * (unsigned)pr + (unsigned)r_in[i]);
     stored[i] = ok ? idx : -1;
     p[i] = sel_ptr(ok, sd.pages + (int64_t)(ok ? idx : 0) * sd.row_bytes + ofs, safe);
@@ -243,6 +277,16 @@ __device__ __forceinline__ void rows_addr(const DevW &w, const Side &sd, int a, 
 __device__ __forceinline__ int adapter_rank(const DevW &w, int a) {
   int r = w.rank[a];
   return r < 0 ? 0 : (r > w.r_max ? w.r_max : r);
+}
+// The rank of an adapter that a token uses (checked in the debug build).
+__device__ __forceinline__ int used_rank(const DevW &w, int a) {
+  const int r = w.rank[a];
+  LORA_CHECK(r >= 1 && r <= w.r_max, LORA_DEBUG_BAD_RANK);
+  return r < 0 ? 0 : (r > w.r_max ? w.r_max : r);
+}
+// An adapter id read from the device: -1 (no adapter) or in [0, N).
+__device__ __forceinline__ void check_id(const DevW &w, int a) {
+  LORA_CHECK(a == LORA_NO_ADAPTER || (a >= 0 && a < w.num_adapters), LORA_DEBUG_BAD_ADAPTER);
 }
 
 // ----------------------------------------------------------------- elements
@@ -944,6 +988,68 @@ __device__ __forceinline__ void stage_slab(const DevW &w, int a, int jc, int nj,
   slab_store<T, W, NR>(braw, stored, bt, lane);
 }
 
+// Line-complete y access of a wave's 64-column slab (bf16): for token tile tt
+// (16 tokens) and half h, lane l covers token 16 tt + 8 h + (l >> 3) of the
+// pass and columns c0 + 8 (l & 7) .. +7, so eight lanes share each 128-byte
+// line and a wave instruction touches eight whole lines.  (The MFMA layout,
+// lane (g, m) = token m, 64 bytes of each of 16 rows per instruction, reads
+// and writes half lines and runs at a fraction of the bandwidth.)  The MFMA
+// results reach this layout through the wave's own LDS slab region.
+// Token of lane l in half h of token tile tt of the pass at m0 (-1 if none).
+__device__ __forceinline__ int yline_token(const int *toks, int m0, int cnt, int num_tokens, int tt, int h) {
+  const int i = m0 + tt * 16 + 8 * h + ((threadIdx.x & 63) >> 3);
+  const int t = i < cnt ? toks[i] : -1;
+  return (t >= 0 && t < num_tokens) ? t : -1;
+}
+__device__ __forceinline__ void yline_load(const uint16_t *y, int d_out, int c0, const int *toks, int m0,
+                                           int cnt, int num_tokens, Raw8<uint16_t> (&yraw)[4][2]) {
+  const int col = c0 + 8 * (threadIdx.x & 7);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = yline_token(toks, m0, cnt, num_tokens, tt, h);
+      raw_load(yraw[tt][h], y + (int64_t)(t >= 0 ? t : 0) * d_out + (col < d_out ? col : 0));
+    }
+}
+// y += the MFMA results of token tile tt (acc[t]: lane (g, m) holds columns
+// 32q + 8g .. +7 of token m in sub-tiles 2q, 2q + 1), one rounding, stored
+// line-complete.  tr: the wave's LDS region (16 x 68 floats), free for the
+// wave's own use (no other wave reads it).
+__device__ __forceinline__ void yline_update(float *tr, const f32x4_t (&acc)[4], const Raw8<uint16_t> (&yraw)[2],
+                                             const int *toks, int m0, int cnt, int num_tokens, int tt,
+                                             uint16_t *y, int d_out, int c0) {
+  constexpr int kTs = 68;  // row stride (floats): conflict-free writes and reads
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    *reinterpret_cast<f32x4_t *>(&tr[m * kTs + 32 * q + 8 * g]) = acc[2 * q];
+    *reinterpret_cast<f32x4_t *>(&tr[m * kTs + 32 * q + 8 * g + 4]) = acc[2 * q + 1];
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int cl = 8 * (lane & 7), col = c0 + cl;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float *src = &tr[(8 * h + (lane >> 3)) * kTs + cl];
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t *>(src);
+    const f32x4_t hi = *reinterpret_cast<const f32x4_t *>(src + 4);
+    const int t = yline_token(toks, m0, cnt, num_tokens, tt, h);
+    if (t >= 0 && col < d_out) {
+      float yv[8];
+      raw_cvt(yraw[h], yv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        yv[e] += lo[e];
+        yv[4 + e] += hi[e];
+      }
+      store8(y + (int64_t)t * d_out + col, yv);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // the next tile's writes come after these reads
+}
+static_assert(16 * 68 * sizeof(float) <= 64 * ExpandCfg<uint16_t>::kRowStride * sizeof(uint16_t),
+              "a wave's slab region holds one token tile of fp32 results");
+
 // MFMA expand for tokens toks[0..cnt) of adapter a over the 256 columns of
 // block `blk` (wave w: 64 columns), 64 tokens (four 16-token tiles) at a time.
 // D[col][token] = B^T-slab^T · v^T.  The y chunks of the 64 tokens are fetched
@@ -973,18 +1079,23 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
       const int t = (tt < ntt && i < cnt) ? toks[i] : -1;
       tok[tt] = (t >= 0 && t < num_tokens) ? t : -1;
     }
-    // prefetch y: lane (g, m) of tile tt touches columns c0 + 32q + 8g .. +7;
-    // issued unconditionally (row 0 / column 0 stand in where there is no
-    // token or column; those values are never stored)
+    // prefetch y, issued unconditionally (row 0 / column 0 stand in where
+    // there is no token or column; those values are never stored): bf16 in
+    // the line-complete layout, fp32 in the MFMA layout (lane (g, m) of tile
+    // tt touches columns c0 + 32q + 8g .. +7)
     Raw8<T> yraw[4][2];
+    if constexpr (sizeof(T) == 2) {
+      yline_load(y, w.d_out, c0, toks, m0, cnt, num_tokens, yraw);
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = c0 + 32 * q + 8 * g;
-        const int64_t row = tok[tt] >= 0 ? tok[tt] : 0;
-        raw_load(yraw[tt][q], y + row * w.d_out + (col < w.d_out ? col : 0));
-      }
+        for (int q = 0; q < 2; ++q) {
+          const int col = c0 + 32 * q + 8 * g;
+          const int64_t row = tok[tt] >= 0 ? tok[tt] : 0;
+          raw_load(yraw[tt][q], y + row * w.d_out + (col < w.d_out ? col : 0));
+        }
+    }
     f32x4_t acc[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -1116,21 +1227,29 @@ __device__ __forceinline__ void expand_mfma(const DevW &w, int a, int r, int blk
         }
       }
     }
-    // y update: lane (g, m) holds columns c0 + 32q + 8g .. +7 of token tok[tt]
+    // y update
+    if constexpr (sizeof(T) == 2) {
+      float *tr = reinterpret_cast<float *>(bt);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+      for (int tt = 0; tt < 4; ++tt)
+        if (tt < ntt) yline_update(tr, acc[tt], yraw[tt], toks, m0, cnt, num_tokens, tt, y, w.d_out, c0);
+    } else {
+      // lane (g, m) holds columns c0 + 32q + 8g .. +7 of token tok[tt]
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = c0 + 32 * q + 8 * g;
-        if (tt < ntt && tok[tt] >= 0 && col < w.d_out) {
-          float yv[8];
-          raw_cvt(yraw[tt][q], yv);
+      for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            yv[e] += acc[tt][2 * q][e];
-            yv[4 + e] += acc[tt][2 * q + 1][e];
+        for (int q = 0; q < 2; ++q) {
+          const int col = c0 + 32 * q + 8 * g;
+          if (tt < ntt && tok[tt] >= 0 && col < w.d_out) {
+            float yv[8];
+            raw_cvt(yraw[tt][q], yv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              yv[e] += acc[tt][2 * q][e];
+              yv[4 + e] += acc[tt][2 * q + 1][e];
+            }
+            store8(y + (int64_t)tok[tt] * w.d_out + col, yv);
           }
-          store8(y + (int64_t)tok[tt] * w.d_out + col, yv);
         }
       }
     }
@@ -1202,9 +1321,10 @@ __device__ __forceinline__ void expand_mfma_one(const DevW &w, int a, int r, int
     Raw8<W> braw[NR];
     int bstored[NR];
     slab_issue<T, W, NR>(w, a, 0, r, c0, lane, braw, bstored);
-    // ---- then the y chunks: lane (g, m) of tile tt touches columns
-    // c0 + 32q + 8g .. +7 (row 0 / column 0 stand in where there is no token
-    // or column; those values are never stored)
+    // ---- then the y chunks (row 0 / column 0 stand in where there is no
+    // token or column; those values are never stored): bf16 in the
+    // line-complete layout, fp32 in the MFMA layout (lane (g, m) of tile tt
+    // touches columns c0 + 32q + 8g .. +7)
     int tok[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -1213,14 +1333,18 @@ __device__ __forceinline__ void expand_mfma_one(const DevW &w, int a, int r, int
       tok[tt] = (t >= 0 && t < num_tokens) ? t : -1;
     }
     Raw8<T> yraw[4][2];
+    if constexpr (sizeof(T) == 2) {
+      yline_load(y, w.d_out, c0, toks, m0, cnt, num_tokens, yraw);
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const int col = c0 + 32 * qq + 8 * g;
-        const int64_t row = tok[tt] >= 0 ? tok[tt] : 0;
-        raw_load(yraw[tt][qq], y + row * w.d_out + (col < w.d_out ? col : 0));
-      }
+        for (int qq = 0; qq < 2; ++qq) {
+          const int col = c0 + 32 * qq + 8 * g;
+          const int64_t row = tok[tt] >= 0 ? tok[tt] : 0;
+          raw_load(yraw[tt][qq], y + row * w.d_out + (col < w.d_out ? col : 0));
+        }
+    }
     // ---- stage the chunk
     if (m0 > 0) __syncthreads();  // the previous pass's readers of the slab and v rows are done
 #pragma unroll
@@ -1295,21 +1419,29 @@ __device__ __forceinline__ void expand_mfma_one(const DevW &w, int a, int r, int
         }
       }
     }
-    // ---- y update: lane (g, m) holds columns c0 + 32q + 8g .. +7 of token tok[tt]
+    // ---- y update
+    if constexpr (sizeof(T) == 2) {
+      float *tr = reinterpret_cast<float *>(bt);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+      for (int tt = 0; tt < 4; ++tt)
+        if (tt < ntt) yline_update(tr, acc[tt], yraw[tt], toks, m0, cnt, num_tokens, tt, y, w.d_out, c0);
+    } else {
+      // lane (g, m) holds columns c0 + 32q + 8g .. +7 of token tok[tt]
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const int col = c0 + 32 * qq + 8 * g;
-        if (tt < ntt && tok[tt] >= 0 && col < w.d_out) {
-          float yv[8];
-          raw_cvt(yraw[tt][qq], yv);
+      for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            yv[e] += acc[tt][2 * qq][e];
-            yv[4 + e] += acc[tt][2 * qq + 1][e];
+        for (int qq = 0; qq < 2; ++qq) {
+          const int col = c0 + 32 * qq + 8 * g;
+          if (tt < ntt && tok[tt] >= 0 && col < w.d_out) {
+            float yv[8];
+            raw_cvt(yraw[tt][qq], yv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              yv[e] += acc[tt][2 * qq][e];
+              yv[4 + e] += acc[tt][2 * qq + 1][e];
+            }
+            store8(y + (int64_t)tok[tt] * w.d_out + col, yv);
           }
-          store8(y + (int64_t)tok[tt] * w.d_out + col, yv);
         }
       }
     }
@@ -1325,8 +1457,10 @@ __device__ __forceinline__ bool decode_item(const lora_item &it, const DevW &w, 
   path = it.count_path >> 16;
   blk = it.block;
   if (a < 0 || a >= w.num_adapters || pb < 0 || cnt <= 0 || cnt > kMaxItemTokens ||
-      pb + cnt > num_perm || blk < 0)
+      pb + cnt > num_perm || blk < 0) {
+    LORA_CHECK(false, LORA_DEBUG_BAD_ITEM);
     return false;
+  }
   return true;
 }
 
@@ -1342,10 +1476,13 @@ __global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *
   const lora_item it = items[blockIdx.x];
   int pb, a, cnt, path, blk;
   if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
-  const int r = adapter_rank(w, a);
+  const int r = used_rank(w, a);
   if (path != LORA_PATH_MFMA && blk >= (r + kRowGroup - 1) / kRowGroup) return;
   const int j0 = path == LORA_PATH_MFMA ? 0 : blk * kRowGroup;
-  for (int i = threadIdx.x; i < cnt; i += NT) sm.toks[i] = perm[pb + i];
+  for (int i = threadIdx.x; i < cnt; i += NT) {
+    sm.toks[i] = perm[pb + i];
+    LORA_CHECK((unsigned)sm.toks[i] < (unsigned)num_tokens, LORA_DEBUG_BAD_TOKEN);
+  }
   __syncthreads();
   if (path == LORA_PATH_MFMA)
     shrink_mfma<T, W, NW>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
@@ -1369,9 +1506,12 @@ void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
   if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
   const int cols = path == LORA_PATH_MFMA ? LORA_EXPAND_MFMA_COLS : kGatherCols;
   if ((int64_t)blk * cols >= w.d_out) return;
-  for (int i = threadIdx.x; i < cnt; i += kThreads) sm.toks[i] = perm[pb + i];
+  for (int i = threadIdx.x; i < cnt; i += kThreads) {
+    sm.toks[i] = perm[pb + i];
+    LORA_CHECK((unsigned)sm.toks[i] < (unsigned)num_tokens, LORA_DEBUG_BAD_TOKEN);
+  }
   __syncthreads();
-  const int r = adapter_rank(w, a);
+  const int r = used_rank(w, a);
   if (path == LORA_PATH_MFMA) {
     // one-chunk ranks take the early-load path (up to 32 for unscaled rows;
     // quantized rows' scale registers would spill there past 16)
@@ -1398,12 +1538,14 @@ inline int pad8(int n) { return (n + 7) & ~7; }
 // must call it; threads CH.. take no token.
 template <int NT, int CH = NT>
 __device__ __forceinline__ int gather_adapter_tokens(const int32_t *__restrict__ ids, int num_tokens, int c0, int a,
-                                     int *toks, int *wave_cnt) {
+                                     int *toks, int *wave_cnt, int num_adapters) {
   static_assert(CH <= NT, "one token per thread");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = c0 + tid;
   const int id = ids[t < num_tokens ? t : num_tokens - 1];  // unconditional load
+  LORA_CHECK(a != 0 || t >= num_tokens || id == LORA_NO_ADAPTER || (id >= 0 && id < num_adapters),
+             LORA_DEBUG_BAD_ADAPTER);
   const bool hit = tid < CH && t < num_tokens && id == a;
   const unsigned long long mask = __ballot(hit);
   if (lane == 0) wave_cnt[wave] = __popcll(mask);
@@ -1439,8 +1581,9 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
   if (!adapter_major) {
     const int t = u;
     const int a = ids[t];
+    check_id(w, a);
     if (a < 0 || a >= w.num_adapters) return;
-    const int r = adapter_rank(w, a);
+    const int r = used_rank(w, a);
     if (j0 >= r) return;
     if (threadIdx.x == 0) sm.toks[0] = t;
     __syncthreads();
@@ -1451,7 +1594,9 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
     if (j0 >= r) return;
     constexpr int CH = kThreads < kMaxItemTokens ? kThreads : kMaxItemTokens;
     for (int c0 = 0; c0 < num_tokens; c0 += CH) {
-      const int n = gather_adapter_tokens<kThreads, CH>(ids, num_tokens, c0, a, sm.toks, wave_cnt);
+      const int n = gather_adapter_tokens<kThreads, CH>(ids, num_tokens, c0, a, sm.toks, wave_cnt,
+                                                          w.num_adapters);
+      if (n > 0) used_rank(w, a);
       if (n > 0) shrink_gemv<T, W, RB, NW>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
       __syncthreads();
     }
@@ -1474,14 +1619,16 @@ __global__ __launch_bounds__(NT) void bgmv_expand_kernel(DevW w, const int32_t *
   if (!adapter_major) {
     const int t = u;
     const int a = ids[t];
+    check_id(w, a);
     if (a < 0 || a >= w.num_adapters) return;
     const int tok1[1] = {t};
-    expand_cols_tile<T, W, 1, NT>(w, a, adapter_rank(w, a), cb, tok1, 0, 1, num_tokens, v, y);
+    expand_cols_tile<T, W, 1, NT>(w, a, used_rank(w, a), cb, tok1, 0, 1, num_tokens, v, y);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
     for (int c0 = 0; c0 < num_tokens; c0 += NT) {
-      const int n = gather_adapter_tokens<NT>(ids, num_tokens, c0, a, toks, wave_cnt);
+      const int n = gather_adapter_tokens<NT>(ids, num_tokens, c0, a, toks, wave_cnt, w.num_adapters);
+      if (n > 0) used_rank(w, a);
       if (n > 0) expand_gemv<T, W, NT>(w, a, r, cb, toks, n, num_tokens, v, y);
       __syncthreads();
     }
@@ -1528,6 +1675,7 @@ __device__ __forceinline__ void a_rows16_sc(const DevW &w, int a, int j0, int r,
 template <typename W>
 __device__ __forceinline__ float a_scale_any(const DevW &w, int a, int j, bool use) {
   const int64_t i = row_index(w, w.a_pt, w.num_pages_a, a, j);
+  LORA_CHECK(!use || i >= 0, LORA_DEBUG_BAD_PAGE);
   const bool in = use && i >= 0;
   const float s = w.a_sc[in ? i : 0];
   return in ? s : 0.f;
@@ -1567,6 +1715,7 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
 
   const int a_id = ids[t];
   const bool valid = a_id >= 0 && a_id < w.num_adapters;
+  check_id(w, a_id);
   const int a = valid ? a_id : 0;
 
   // ---- adapter-only loads: A and B^T rows 0 .. rs-1 (and their scales);
@@ -1589,7 +1738,7 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
     asc = a_scale_any<W>(w, a, tid, tid < rs);
   }
 
-  const int r = valid ? adapter_rank(w, a) : 0;
+  const int r = valid ? used_rank(w, a) : 0;
 
   // ---- shrink: v[j] = sum_k A[j][k] x[k], 16 rows at a time (the first
   // 16 always, see above)
@@ -1918,7 +2067,9 @@ __global__ __launch_bounds__(kFusedThreads) void bgmv_fused_am_kernel(DevW w, co
   const int r = adapter_rank(w, a);
   const int c_begin = cb * block_cols, c_end = min(w.d_out, c_begin + block_cols);
   for (int c0 = 0; c0 < num_tokens; c0 += kFusedThreads) {
-    const int n = gather_adapter_tokens<kFusedThreads>(ids, num_tokens, c0, a, sm.toks, sm.wave_cnt);
+    const int n = gather_adapter_tokens<kFusedThreads>(ids, num_tokens, c0, a, sm.toks, sm.wave_cnt,
+                                                         w.num_adapters);
+    if (n > 0) used_rank(w, a);
     int g0 = 0;
     for (; g0 + 4 <= n; g0 += 4)
       fused_am_group<T, W, 4>(w, a, r, c_begin, c_end, sm.toks, g0, 4, x, v, y, v && cb == 0, sm);
@@ -2053,6 +2204,26 @@ int bgmv_order(int phase, int order, int num_tokens, int num_adapters) {
 }
 
 }  // namespace
+
+// ----------------------------------------------------------------- debug word
+extern "C" lora_status lora_debug_flags(uint32_t *flags, int32_t clear) {
+  if (!flags) return fail(LORA_EINVAL, "null flags");
+  *flags = 0;
+#if LORA_DEBUG
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_debug_flags), sizeof(uint32_t), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the debug word");
+  if (clear) {
+    const uint32_t zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &zero, sizeof(uint32_t), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "clearing the debug word");
+  }
+  return ok();
+#else
+  (void)clear;
+  return fail(LORA_EUNSUPPORTED, "library built without LORA_DEBUG (load liblora_sgmv_debug.so)");
+#endif
+}
 
 // ----------------------------------------------------------------- C ABI
 extern "C" lora_status lora_sgmv_shrink(const lora_weights *w, const int32_t *token_perm,
