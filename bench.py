@@ -79,6 +79,15 @@ def parse():
                     help="fused decode: workgroups take tokens in the batch's segment order "
                          "(host-built once per batch, shared by all layers) or in index order")
     ap.add_argument("--policy", type=int, default=0, help="SGMV path policy (0 auto, 1 gather, 2 mfma)")
+    ap.add_argument("--shrink", choices=("auto", "tiled", "plain"), default="auto",
+                    help="SGMV shrink: tiled (64-token tiles of x and A streamed through LDS, d_in cut "
+                         "into slices whose partials a second launch adds), the one-launch shrink, or "
+                         "auto: tiled where segments of at least --tile-min tokens carry most of the "
+                         "shrink's bytes")
+    ap.add_argument("--tile-min", type=int, default=0,
+                    help="tiled shrink: segments of at least this many tokens take tile items "
+                         "(0: the library default)")
+    ap.add_argument("--max-splits", type=int, default=0, help="tiled shrink: at most this many d_in slices")
     ap.add_argument("--mfma-min", type=int, default=0,
                     help="SGMV plan: segments of at least this many tokens take the MFMA path "
                          "(0: the library default)")
@@ -463,6 +472,7 @@ def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
     one = R.DeviceProblem(p)
     reps = [one] + [one.replica() for _ in range(n_rep - 1)]
     mfma_min = args.mfma_min or B.LORA_DEFAULT_MFMA_MIN_TOKENS
+    tiled = mode == "sgmv" and (args.shrink == "tiled" or (args.shrink == "auto" and one.tiled_pays(args.tile_min)))
     calls = []
     for dp in reps:
         y, v = dp.y0.clone(), dp.new_v()
@@ -476,9 +486,14 @@ def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
             _, _, _, perm_d = dp.segments()
             if not hasattr(one, "_bench_plans"):
                 one._bench_plans = (dp.plan(B.LORA_PHASE_SHRINK, args.policy, mfma_min),
-                                    dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min))
-            sp, ep = one._bench_plans
-            calls.append(B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream))
+                                    dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min),
+                                    dp.plan_tiled(args.policy, args.tile_min, args.max_splits) if tiled else None)
+            sp, ep, tp = one._bench_plans
+            if tiled:
+                calls.append(B.prepare_sgmv_tiled(dp.weights, perm_d, tp[0], tp[1], tp[2], ep, dp.x, v, y,
+                                                  stream=stream))
+            else:
+                calls.append(B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v, y, stream=stream))
     torch.cuda.synchronize()
 
     def step(i):
@@ -528,6 +543,8 @@ def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
                    "mode": mode, "path": ("fused" if fused else "shrink+expand"),
                    "placement": (args.placement if fused else None),
                    "mfma_min_tokens": (mfma_min if mode == "sgmv" else None),
+                   "shrink": ((f"tiled: 64-token tiles, {one._bench_plans[2][1]} d_in slices" if tiled
+                               else "one launch") if mode == "sgmv" else None),
                    "replicas": n_rep, "timed": "HIP graph replay of the K steps",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -592,6 +609,8 @@ def run_layer(args, torch):
         _, _, _, perm_d = dp.segments()
         sp = dp.plan(B.LORA_PHASE_SHRINK, args.policy, mfma_min)
         ep = dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min)
+        use_tiled = args.shrink == "tiled" or (args.shrink == "auto" and dp.tiled_pays(args.tile_min))
+        tp = dp.plan_tiled(args.policy, args.tile_min, args.max_splits) if use_tiled else None
         sb = acc.shrink_bytes(p.ids, p.ranks, p.d_in, 2)
         eb = acc.expand_bytes(p.ids, p.ranks, p.d_out, 2)
         n_rep = n_replicas(args, min(sb, eb), cap=48)
@@ -600,11 +619,16 @@ def run_layer(args, torch):
         for i in range(n_rep):
             rp = dp if i == 0 else dp.replica()
             y = y_base.clone()
-            calls.append(B.prepare_sgmv(rp.weights, perm_d, sp, ep, rp.x, rp.new_v(), y, stream=stream))
+            if tp is not None:
+                calls.append(B.prepare_sgmv_tiled(rp.weights, perm_d, tp[0], tp[1], tp[2], ep, rp.x, rp.new_v(),
+                                                  y, stream=stream))
+            else:
+                calls.append(B.prepare_sgmv(rp.weights, perm_d, sp, ep, rp.x, rp.new_v(), y, stream=stream))
         p.extra.pop("w", None)   # the host copy of W is no longer needed
         projs.append({"name": name, "p": p, "dp": dp, "base": base, "calls": calls, "n_rep": n_rep,
                       "sb": sb, "eb": eb, "bf": acc.base_gemm_flops(p.num_tokens, p.d_out, p.d_in),
-                      "y_base": y_base, "plans": (sp, ep)})
+                      "y_base": y_base, "plans": (sp, ep),
+                      "shrink": (f"tiled ({tp[1]} d_in slices)" if tp is not None else "one launch")})
     torch.cuda.synchronize()
     K = args.steps
 
@@ -626,7 +650,7 @@ def run_layer(args, torch):
              for k, ph in enumerate(("shrink", "expand"))}
         tb = graph_span(torch, stream, [q["base"]] * 5, 3)
         p = q["p"]
-        per[q["name"]] = {"d_in": p.d_in, "d_out": p.d_out, "replicas": q["n_rep"],
+        per[q["name"]] = {"d_in": p.d_in, "d_out": p.d_out, "replicas": q["n_rep"], "shrink": q["shrink"],
                           "shrink_us": round(t["shrink"] * 1e6, 3),
                           "shrink_gbs": round(q["sb"] / t["shrink"] / 1e9, 1),
                           "expand_us": round(t["expand"] * 1e6, 3),
@@ -656,6 +680,7 @@ def run_layer(args, torch):
         "config": {"workload": LAYER_WORKLOAD, "tokens": tokens, "adapters": 256, "ranks": [16],
                    "projections": [q["name"] for q in projs], "mode": "sgmv",
                    "mfma_min_tokens": mfma_min,
+                   "shrink": sorted(set(q["shrink"] for q in projs)),
                    "timed": "HIP graph replay of K layer deltas (7 projections x shrink + expand)",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -249,6 +249,64 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
                              const float *v, void *y, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Tiled segmented shrink: the v of lora_sgmv_shrink for bf16 activations and
+ * bf16 rows, planned for segments whose shrink is a real dense product
+ * ("SGMV ..." section: the shrink phase, d_in -> r through A_{a(t)}; tensor
+ * cores for the long segments).  A tile item is up to LORA_SHRINK_TILE_TOKENS
+ * tokens of one segment and one slice of d_in: its workgroup streams the
+ * tokens' x rows and the adapter's A rows of the slice into LDS once (so A
+ * crosses the compute unit once per 64 tokens instead of once per 16) and
+ * runs the products on MFMA.  With more than one slice the items write fp32
+ * partial products to a caller-owned workspace and a second launch on the
+ * same stream adds each token's partials in slice order (a fixed order:
+ * repeated runs are bit-identical).  Shorter segments keep gather items.
+ *
+ * lora_sgmv_plan_tiled: as lora_sgmv_plan's shrink phase, plus d_in (a
+ * multiple of LORA_SHRINK_TILE_K) and max_splits (1..LORA_MAX_K_SPLITS; <= 0:
+ * no bound but d_in's).  Segments of at least tile_min_tokens tokens (<= 0:
+ * LORA_DEFAULT_TILE_MIN_TOKENS), and shorter ones of rank at least
+ * LORA_TILE_MIN_RANK_SHORT (whose gather items would read each x row r / 4
+ * times), take tile items (path LORA_PATH_TILE, block = slice); the others
+ * gather items as in lora_sgmv_plan (policy GATHER: none tiled; MFMA: all
+ * tiled).  *k_splits receives the number of slices, chosen so
+ * that the heaviest tile item reads about LORA_SHRINK_TILE_ITEM_BYTES; every
+ * slice is a non-empty multiple of LORA_SHRINK_TILE_K elements.  Items
+ * heaviest first.  Errors as lora_sgmv_plan, LORA_EUNSUPPORTED for a d_in
+ * that is not a positive multiple of LORA_SHRINK_TILE_K, or r_max above 64.
+ *
+ * lora_sgmv_shrink_tiled_workspace: bytes of workspace for k_splits
+ * (k_splits * num_perm * r_max floats; 0 when k_splits == 1).
+ *
+ * lora_sgmv_shrink_tiled: runs the plan; k_splits must be the plan's (the
+ * slices are recomputed from d_in and k_splits).  workspace: caller-owned
+ * device memory, 16-byte aligned, of at least the size above (contents on
+ * entry do not matter; NULL with 0 bytes when k_splits == 1); calls that
+ * share it must not overlap (on one stream they do not).  Errors: as
+ * lora_sgmv_shrink; LORA_EUNSUPPORTED unless activations and rows are bf16,
+ * r_max <= 64 and d_in is a multiple of LORA_SHRINK_TILE_K; LORA_EINVAL for
+ * k_splits out of range or leaving an empty slice, or a missing, misaligned
+ * or short workspace.                                                        */
+#define LORA_PATH_TILE 3                    /* plan items only: a tiled shrink item */
+#define LORA_SHRINK_TILE_TOKENS 64
+#define LORA_SHRINK_TILE_K 64               /* slices are multiples of this many elements */
+#define LORA_SHRINK_TILE_ITEM_BYTES 262144  /* bytes of x and A an item aims to read */
+#define LORA_DEFAULT_TILE_MIN_TOKENS 16
+#define LORA_TILE_MIN_RANK_SHORT 32
+#define LORA_MAX_K_SPLITS 64
+lora_status lora_sgmv_plan_tiled(const int32_t *seg_starts, const int32_t *seg_adapter,
+                                 int32_t num_segments, int32_t num_adapters,
+                                 const int32_t *host_rank, int32_t r_max, int32_t d_in,
+                                 int32_t path_policy, int32_t tile_min_tokens, int32_t max_splits,
+                                 lora_item *items, int32_t capacity, int32_t *num_items,
+                                 int32_t *k_splits);
+lora_status lora_sgmv_shrink_tiled_workspace(int32_t num_perm, int32_t r_max, int32_t k_splits,
+                                             int64_t *bytes);
+lora_status lora_sgmv_shrink_tiled(const lora_weights *w, const int32_t *token_perm,
+                                   int32_t num_perm, const lora_item *items, int32_t num_items,
+                                   int32_t num_tokens, int32_t k_splits, const void *x, float *v,
+                                   void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Per-token (BGMV, decode) mode: adapter ids stay on the device, no host
  * planning and no host synchronisation; every token takes the gather/GEMV path
  * (S-LoRA's decode kernel, MBGMV, in the same section: mixed ranks in one

@@ -30,6 +30,9 @@ LORA_DEFAULT_MFMA_MIN_TOKENS = 16
 LORA_SHRINK_GATHER_TOKENS, LORA_SHRINK_GATHER_ROWS, LORA_SHRINK_MFMA_TOKENS = 4, 4, 16
 LORA_EXPAND_GATHER_TOKENS, LORA_EXPAND_MFMA_TOKENS = 4, 64
 LORA_EXPAND_GATHER_COLS, LORA_EXPAND_MFMA_COLS = 2048, 256
+LORA_PATH_TILE = 3
+LORA_SHRINK_TILE_TOKENS, LORA_SHRINK_TILE_K, LORA_SHRINK_TILE_ITEM_BYTES = 64, 64, 262144
+LORA_DEFAULT_TILE_MIN_TOKENS, LORA_TILE_MIN_RANK_SHORT, LORA_MAX_K_SPLITS = 16, 32, 64
 
 
 class LoraError(RuntimeError):
@@ -73,6 +76,10 @@ EXPORTS = {
     "lora_sgmv_plan": ([_I32, _P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, _P], _I32),
     "lora_sgmv_shrink": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_sgmv_expand": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
+    "lora_sgmv_plan_tiled": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
+                             _I32),
+    "lora_sgmv_shrink_tiled_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
+    "lora_sgmv_shrink_tiled": ([_P, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, ctypes.c_int64, _P], _I32),
     "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_expand": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_fused": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P], _I32),
@@ -199,6 +206,27 @@ def lora_sgmv_plan(phase: int, seg_starts, seg_adapter, num_adapters: int, dim: 
     return items[: n.value]
 
 
+def lora_sgmv_plan_tiled(seg_starts, seg_adapter, num_adapters: int, r_max: int, d_in: int,
+                         path_policy: int = LORA_PATH_AUTO, tile_min_tokens: int = 0,
+                         max_splits: int = 0, host_rank=None):
+    """Tiled shrink plan: (int32 items [num_items, 4], k_splits)."""
+    starts, adapters = _i32(seg_starts), _i32(seg_adapter)
+    ranks = None if host_rank is None else _i32(host_rank)
+    n, ks = ctypes.c_int32(0), ctypes.c_int32(0)
+    args = (_np_ptr(starts), _np_ptr(adapters), adapters.size, num_adapters, _np_ptr(ranks), r_max, d_in,
+            path_policy, tile_min_tokens, max_splits)
+    _check(lib().lora_sgmv_plan_tiled(*args, None, 0, ctypes.byref(n), ctypes.byref(ks)))
+    items = np.zeros((max(n.value, 1), 4), np.int32)
+    _check(lib().lora_sgmv_plan_tiled(*args, _np_ptr(items), n.value, ctypes.byref(n), ctypes.byref(ks)))
+    return items[: n.value], int(ks.value)
+
+
+def lora_sgmv_shrink_tiled_workspace(num_perm: int, r_max: int, k_splits: int) -> int:
+    out = ctypes.c_int64(0)
+    _check(lib().lora_sgmv_shrink_tiled_workspace(num_perm, r_max, k_splits, ctypes.byref(out)))
+    return int(out.value)
+
+
 # ---------------------------------------------------------------- device helpers
 def _torch():
     import torch
@@ -273,6 +301,20 @@ def lora_sgmv_expand(w: Weights, token_perm, items, v, y, num_tokens: Optional[i
     _check(lib().lora_sgmv_expand(ctypes.byref(d), _dptr(token_perm), int(token_perm.numel()),
                                   _dptr(items), int(items.shape[0]), n_tok, _dptr(v), _dptr(y),
                                   _stream(stream)))
+
+
+def _ws_args(workspace):
+    return (_dptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def lora_sgmv_shrink_tiled(w: Weights, token_perm, items, k_splits: int, x, v, workspace=None,
+                           num_tokens: Optional[int] = None, stream=None):
+    d = w.desc()
+    n = int(x.shape[0]) if num_tokens is None else num_tokens
+    wp, wb = _ws_args(workspace)
+    _check(lib().lora_sgmv_shrink_tiled(ctypes.byref(d), _dptr(token_perm), int(token_perm.numel()),
+                                        _dptr(items), int(items.shape[0]), n, int(k_splits), _dptr(x),
+                                        _dptr(v), wp, wb, _stream(stream)))
 
 
 def lora_bgmv_shrink(w: Weights, token_adapter, x, v, order: int = LORA_BGMV_AUTO, stream=None):
@@ -527,6 +569,24 @@ def prepare_sgmv(w: Weights, token_perm, shrink_items, expand_items, x, v, y, st
     shrink = Prepared("lora_sgmv_shrink", (ctypes.byref(d), _dptr(token_perm), npm, _dptr(shrink_items),
                                            int(shrink_items.shape[0]), int(x.shape[0]), _dptr(x),
                                            _dptr(v), s), keep)
+    expand = Prepared("lora_sgmv_expand", (ctypes.byref(d), _dptr(token_perm), npm, _dptr(expand_items),
+                                           int(expand_items.shape[0]), int(y.shape[0]), _dptr(v),
+                                           _dptr(y), s), keep)
+    return shrink, expand
+
+
+def prepare_sgmv_tiled(w: Weights, token_perm, tile_items, k_splits: int, workspace, expand_items, x, v, y,
+                       stream=None):
+    """(shrink, expand) prepared launches: the tiled shrink (with its reduce
+    launch when k_splits > 1) and the segmented expand, on `stream`."""
+    d = w.desc()
+    s = _stream(stream)
+    keep = (d, w, token_perm, tile_items, expand_items, x, v, y, workspace)
+    npm = int(token_perm.numel())
+    wp, wb = _ws_args(workspace)
+    shrink = Prepared("lora_sgmv_shrink_tiled", (ctypes.byref(d), _dptr(token_perm), npm, _dptr(tile_items),
+                                                 int(tile_items.shape[0]), int(x.shape[0]), int(k_splits),
+                                                 _dptr(x), _dptr(v), wp, wb, s), keep)
     expand = Prepared("lora_sgmv_expand", (ctypes.byref(d), _dptr(token_perm), npm, _dptr(expand_items),
                                            int(expand_items.shape[0]), int(y.shape[0]), _dptr(v),
                                            _dptr(y), s), keep)

@@ -203,6 +203,97 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
   return ok();
 }
 
+// Slices of a tiled shrink: k_splits slices of tile_slice_len elements (the
+// last one shorter), every one a non-empty multiple of LORA_SHRINK_TILE_K.
+static int32_t tile_slice_count(int32_t d_in, int32_t want) {
+  const int32_t units = d_in / LORA_SHRINK_TILE_K;
+  int32_t s = std::max(1, std::min(want, units));
+  while (s > 1 && (int64_t)(s - 1) * lora::tile_slice_len(d_in, s) >= d_in) --s;
+  return s;
+}
+
+extern "C" lora_status lora_sgmv_plan_tiled(const int32_t *seg_starts, const int32_t *seg_adapter,
+                                            int32_t num_segments, int32_t num_adapters,
+                                            const int32_t *host_rank, int32_t r_max, int32_t d_in,
+                                            int32_t path_policy, int32_t tile_min_tokens,
+                                            int32_t max_splits, lora_item *items, int32_t capacity,
+                                            int32_t *num_items, int32_t *k_splits) {
+  if (!num_items || !k_splits) return fail(LORA_EINVAL, "null num_items or k_splits");
+  if (d_in <= 0 || d_in % LORA_SHRINK_TILE_K)
+    return fail(LORA_EUNSUPPORTED, "d_in %d is not a positive multiple of %d", d_in, LORA_SHRINK_TILE_K);
+  if (r_max > 64) return fail(LORA_EUNSUPPORTED, "tiled shrink needs r_max <= 64 (got %d)", r_max);
+  if (max_splits > LORA_MAX_K_SPLITS)
+    return fail(LORA_EINVAL, "max_splits %d above %d", max_splits, LORA_MAX_K_SPLITS);
+  if (max_splits <= 0) max_splits = LORA_MAX_K_SPLITS;
+  if (tile_min_tokens <= 0) tile_min_tokens = LORA_DEFAULT_TILE_MIN_TOKENS;
+  // the segment checks are the plain shrink plan's
+  int32_t n_plain = 0;
+  lora_status st = lora_sgmv_plan(LORA_PHASE_SHRINK, seg_starts, seg_adapter, num_segments, num_adapters,
+                                  host_rank, r_max, LORA_PATH_GATHER, 1, nullptr, 0, &n_plain);
+  if (st != LORA_OK) return st;
+  // AUTO: long segments, and short ones whose gather items would read each x
+  // row r / LORA_SHRINK_GATHER_ROWS >= 8 times
+  auto tiled = [&](int32_t len, int32_t r) {
+    return path_policy == LORA_PATH_MFMA ||
+           (path_policy == LORA_PATH_AUTO && (len >= tile_min_tokens || r >= LORA_TILE_MIN_RANK_SHORT));
+  };
+  // slices: the heaviest tile item (a full token tile and the largest rank)
+  // reads about LORA_SHRINK_TILE_ITEM_BYTES of x and A
+  int64_t heaviest = 0;
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int32_t len = seg_starts[s + 1] - seg_starts[s];
+    const int32_t r = host_rank ? host_rank[seg_adapter[s]] : r_max;
+    if (!tiled(len, r)) continue;
+    heaviest = std::max(heaviest, (int64_t)(std::min(len, LORA_SHRINK_TILE_TOKENS) + r) * d_in * 2);
+  }
+  const int64_t want = (heaviest + LORA_SHRINK_TILE_ITEM_BYTES - 1) / LORA_SHRINK_TILE_ITEM_BYTES;
+  const int32_t splits = tile_slice_count(d_in, (int32_t)std::min<int64_t>(want, max_splits));
+  std::vector<PlanItem> plan;
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int32_t begin = seg_starts[s], len = seg_starts[s + 1] - seg_starts[s];
+    const int32_t a = seg_adapter[s];
+    const int32_t r = host_rank ? host_rank[a] : r_max;
+    if (tiled(len, r)) {
+      for (int32_t m0 = 0; m0 < len; m0 += LORA_SHRINK_TILE_TOKENS) {
+        const int32_t cnt = std::min(LORA_SHRINK_TILE_TOKENS, len - m0);
+        for (int32_t k = 0; k < splits; ++k)
+          plan.push_back({{begin + m0, a, cnt | (LORA_PATH_TILE << 16), k}, (int64_t)cnt + r});
+      }
+    } else {
+      const int32_t groups = (r + LORA_SHRINK_GATHER_ROWS - 1) / LORA_SHRINK_GATHER_ROWS;
+      for (int32_t m0 = 0; m0 < len; m0 += LORA_SHRINK_GATHER_TOKENS) {
+        const int32_t cnt = std::min(LORA_SHRINK_GATHER_TOKENS, len - m0);
+        for (int32_t g = 0; g < groups; ++g) {
+          // in units of one slice of a row, as the tile items: a gather item
+          // reads its rows over all of d_in
+          const int32_t rows = std::min(LORA_SHRINK_GATHER_ROWS, r - g * LORA_SHRINK_GATHER_ROWS);
+          plan.push_back({{begin + m0, a, cnt | (LORA_PATH_GATHER << 16), g}, (int64_t)(cnt + rows) * splits});
+        }
+      }
+    }
+  }
+  const std::vector<lora_item> order = device_order(plan);
+  if (order.size() > (size_t)INT32_MAX) return fail(LORA_ENOMEM, "plan too large");
+  *num_items = (int32_t)order.size();
+  *k_splits = splits;
+  if (!items) return ok();
+  if ((int32_t)order.size() > capacity)
+    return fail(LORA_ENOMEM, "plan needs %zu items, capacity %d", order.size(), capacity);
+  for (size_t i = 0; i < order.size(); ++i) items[i] = order[i];
+  return ok();
+}
+
+extern "C" lora_status lora_sgmv_shrink_tiled_workspace(int32_t num_perm, int32_t r_max, int32_t k_splits,
+                                                        int64_t *bytes) {
+  if (!bytes) return fail(LORA_EINVAL, "null bytes");
+  *bytes = 0;
+  if (num_perm < 0 || r_max < 1 || r_max > 64 || k_splits < 1 || k_splits > LORA_MAX_K_SPLITS)
+    return fail(LORA_EINVAL, "tiled workspace query: num_perm %d, r_max %d, k_splits %d", num_perm, r_max,
+                k_splits);
+  if (k_splits > 1) *bytes = (int64_t)k_splits * num_perm * r_max * (int64_t)sizeof(float);
+  return ok();
+}
+
 // --------------------------------------------------------------------------
 // Paged pool.
 

@@ -569,10 +569,10 @@ struct alignas(16) ShrinkSmem {
 // reduce-scattered over the wave and the NW wave results summed in wave order,
 // so a token's result does not depend on TG or on which other tokens share the
 // tile (for a given NW).
-template <typename T, typename W, int TG, int RB, int NW>
+template <typename T, typename W, int TG, int RB, int NW, typename SM>
 __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
                                  int ntok, int num_tokens, const T *__restrict__ x,
-                                 float *__restrict__ v, ShrinkSmem<NW> &sm) {
+                                 float *__restrict__ v, SM &sm) {
   constexpr int kStep = NW * 64 * 8;
   constexpr int NV = TG * RB;
   constexpr int SH = 6 - ilog2(NV);
@@ -657,10 +657,9 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
 
 // Gather/GEMV shrink of tokens toks[0..cnt) of adapter a over its row group
 // [j0, j0 + nr), nr <= RB: groups of up to 4 tokens, one group of 1 to 3 at the end.
-template <typename T, typename W, int RB, int NW>
+template <typename T, typename W, int RB, int NW, typename SM>
 __device__ __forceinline__ void shrink_gemv(const DevW &w, int a, int j0, int nr, const int *toks, int cnt,
-                            int num_tokens, const T *__restrict__ x, float *__restrict__ v,
-                            ShrinkSmem<NW> &sm) {
+                            int num_tokens, const T *__restrict__ x, float *__restrict__ v, SM &sm) {
   int g0 = 0;
   for (; g0 + 4 <= cnt; g0 += 4)
     shrink_rows_tile<T, W, 4, RB, NW>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
@@ -1490,6 +1489,317 @@ __global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *
     shrink_gemv<T, W, kRowGroup, NW>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
 }
 
+// ----------------------------------------------------------------- tiled shrink
+// Segmented shrink for bf16 activations and bf16 rows in 64-token tiles: an
+// item is up to 64 tokens of one segment and one slice [kb, ke) of d_in.  Its
+// four waves own one 16-token tile each; the tokens' x rows and the adapter's
+// A rows (up to MAXR) stream through LDS in stages of 64 elements (128 bytes,
+// one cache line per row), loaded by global_load_lds_dwordx4 (lane l of a
+// wave's load lands at the load's LDS base + 16 l: eight lanes per row, each
+// wave load covers eight whole lines), so no registers stage them.  Stages
+// rotate through kTileStages buffers with up to kTileStages - 1 of them in
+// flight; each wave waits only for its own loads of the stage it is about to
+// use, then one barrier makes every wave's share visible.  A rows are read
+// from HBM once per item and shared by the four waves; x rows once.  The
+// chunks of a row are permuted by an XOR of the row index (LDS slot
+// c ^ (row & 7)), so that the eight lanes of an LDS read phase hit eight bank
+// groups.  Rows past the rank and tokens past the item load a row that is
+// loaded anyway (the last valid one); their products are never stored.
+constexpr int kTileTokens = LORA_SHRINK_TILE_TOKENS;
+constexpr int kTileK = LORA_SHRINK_TILE_K;
+#ifndef LORA_TILE_STAGES
+#define LORA_TILE_STAGES 4
+#endif
+constexpr int kTileStages = LORA_TILE_STAGES;
+static_assert(kTileTokens == 64 && kTileK == 64, "four 16-token tiles; eight 16-byte chunks per row");
+static_assert(kTileStages >= 2 && kTileStages <= 4, "two to four stage buffers");
+
+__device__ __forceinline__ int tile_slot(int row, int c) { return c ^ (row & 7); }
+
+// s_waitcnt: at most N vector-memory operations of this wave outstanding,
+// the other counters not waited for (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vm_n(int n) {  // n wave-uniform, 0..8
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    default: wait_vm<8>(); break;
+  }
+}
+
+// Workgroup barrier without a memory fence: __syncthreads() would first wait
+// for every outstanding global load (the later stages too).  Each wave has
+// already waited for its own loads of the stage the barrier publishes (their
+// LDS writes are complete when the wave's vmcnt drops), and the "memory"
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+struct alignas(16) TileSmem {
+  int toks[kTileTokens];
+  float red_gemv[4 * 64];  // gather items of the same launch
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// v rows of the tokens toks[0..cnt) of a chunk = the sum of their k_splits
+// partials part[slice][pb + i][j], added in slice order.  A thread takes four
+// consecutive outputs of one token (a 16-byte load per slice when r_max and r
+// are multiples of 4) and issues the loads of eight slices before adding them.
+__device__ __forceinline__ void tile_sum_slices(const DevW &w, int r, int cnt, int pb, int k_splits, int num_perm,
+                                                int num_tokens, const int *toks, const float *__restrict__ part,
+                                                float *__restrict__ v) {
+  const int q4 = (r + 3) >> 2;
+  const int64_t stride = (int64_t)num_perm * w.r_max;
+  const bool vec = (w.r_max & 3) == 0 && (r & 3) == 0;
+  for (int e = (int)threadIdx.x; e < cnt * q4; e += kThreads) {
+    const int i = e / q4, j = (e - i * q4) * 4;
+    const int t = toks[i];
+    const float *pp = part + (int64_t)(pb + i) * w.r_max + j;
+    auto load4 = [&](int s) {
+      const float *q = pp + s * stride;
+      if (vec) return *reinterpret_cast<const f32x4_t *>(q);
+      f32x4_t o;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = j + c < r ? q[c] : 0.f;
+      return o;
+    };
+    f32x4_t sum = load4(0);
+    int s = 1;
+    for (; s + 8 <= k_splits; s += 8) {
+      f32x4_t q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) q[u] = load4(s + u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += q[u];
+    }
+    for (; s < k_splits; ++s) sum += load4(s);
+    if (t >= 0 && t < num_tokens) {
+      float *dst = v + (int64_t)t * w.r_max + j;
+      if (vec) {
+        *reinterpret_cast<f32x4_t *>(dst) = sum;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (j + c < r) dst[c] = sum[c];
+      }
+    }
+  }
+}
+
+// One tile item with RT row tiles (r <= 16 RT <= MAXR).  Buffers: x0..x3
+// (64 x 64 bf16 each) and a0..a3 (MAXR x 64), separate LDS variables so the
+// compiler tells them apart.
+template <int RT, int MAXR>
+__device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, int kb, int ke, int pb,
+                                          int slice, int k_splits, int num_perm, int num_tokens,
+                                          const int *toks, const uint16_t *__restrict__ x,
+                                          float *__restrict__ v, float *__restrict__ part, uint16_t *x0,
+                                          uint16_t *x1, uint16_t *x2, uint16_t *x3, uint16_t *a0, uint16_t *a1,
+                                          uint16_t *a2, uint16_t *a3) {
+  static_assert(RT >= 1 && 16 * RT <= MAXR, "row tiles");
+  constexpr int NS = kTileStages;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane >> 3, lc = lane & 7;  // row of a wave load, LDS slot
+  const bool xact = 16 * wave < cnt;        // this wave's token tile has tokens
+  // x rows of this wave's two loads per stage: token rows 16 wave + 8 i + lr
+  const char *xp[2];
+  int xrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * wave + 8 * i + lr;
+    const int t = toks[row < cnt ? row : cnt - 1];
+    const bool ok = t >= 0 && t < num_tokens;
+    xrow[i] = row;
+    xp[i] = reinterpret_cast<const char *>(x + (ok ? (int64_t)t * w.d_in : 0));
+  }
+  // A loads: 2 RT per stage (eight rows each); wave takes loads wave, wave + 4
+  constexpr int NA = 2 * RT;
+  const int na = (NA > wave ? 1 : 0) + (NA > wave + 4 ? 1 : 0);
+  const char *ap[2];
+  int arow[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 8 * (wave + 4 * u) + lr;
+    const int rr = row < r ? row : r - 1;
+    const char *p = (wave + 4 * u < NA) ? a_row(w, a, rr) : nullptr;
+    arow[u] = row;
+    ap[u] = p ? p : reinterpret_cast<const char *>(x);
+  }
+  const int nw = (xact ? 2 : 0) + na;  // this wave's loads per stage
+  const int nst = (ke - kb) / kTileK;
+
+  auto issue = [&](auto bc, int s) {
+    constexpr int B = decltype(bc)::value;
+    uint16_t *bx = B == 0 ? x0 : B == 1 ? x1 : B == 2 ? x2 : x3;
+    uint16_t *ba = B == 0 ? a0 : B == 1 ? a1 : B == 2 ? a2 : a3;
+    const int k = kb + s * kTileK;
+    if (xact) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(xp[i] + (int64_t)(k + tile_slot(xrow[i], lc) * 8) * 2,
+                                         (lds_void *)(bx + (16 * wave + 8 * i) * kTileK), 16, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (u < na)
+        __builtin_amdgcn_global_load_lds(ap[u] + (int64_t)(k + tile_slot(arow[u], lc) * 8) * 2,
+                                         (lds_void *)(ba + 8 * (wave + 4 * u) * kTileK), 16, 0, 0);
+  };
+
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int m = lane & 15, g = lane >> 4;
+
+  auto step = [&](auto bc, int t) {
+    constexpr int B = decltype(bc)::value;
+    const uint16_t *bx = B == 0 ? x0 : B == 1 ? x1 : B == 2 ? x2 : x3;
+    const uint16_t *ba = B == 0 ? a0 : B == 1 ? a1 : B == 2 ? a2 : a3;
+    // this wave's loads of stage t have landed once no more than those of the
+    // later issued stages are outstanding
+    const int later = min(NS - 2, nst - 1 - t);
+    wait_vm_n(later * nw);
+    lds_barrier();  // every wave's share of stage t; buffer (t - 1) % NS free
+    if (t + NS - 1 < nst) issue(std::integral_constant<int, (B + NS - 1) % NS>{}, t + NS - 1);
+    if (xact) {
+#pragma unroll
+      for (int ks = 0; ks < kTileK / 32; ++ks) {
+        const int ch = 4 * ks + g;
+        const int xr = 16 * wave + m;
+        const bf16x8_t xf = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4 *>(bx + xr * kTileK + tile_slot(xr, ch) * 8));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int ar = 16 * rt + m;
+          const bf16x8_t af = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4 *>(ba + ar * kTileK + tile_slot(ar, ch) * 8));
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, xf, acc[rt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (NS > 2 && 1 < nst) issue(std::integral_constant<int, 1 % NS>{}, 1);
+  if (NS > 3 && 2 < nst) issue(std::integral_constant<int, 2 % NS>{}, 2);
+  for (int t0 = 0; t0 < nst; t0 += NS) {
+    step(std::integral_constant<int, 0>{}, t0);
+    if (t0 + 1 < nst) step(std::integral_constant<int, 1 % NS>{}, t0 + 1);
+    if (NS > 2 && t0 + 2 < nst) step(std::integral_constant<int, 2 % NS>{}, t0 + 2);
+    if (NS > 3 && t0 + 3 < nst) step(std::integral_constant<int, 3 % NS>{}, t0 + 3);
+  }
+  __syncthreads();  // the next item of this workgroup (none) or the exit: no buffer reuse after this
+  // lane (g, m) of row tile rt holds D[4g + e][m]: row 16 rt + 4g + e of token 16 wave + m
+  const int i = 16 * wave + m;
+  if (xact && i < cnt) {
+    const int t = toks[i];
+    if (t >= 0 && t < num_tokens) {
+      float *dst = k_splits == 1 ? v + (int64_t)t * w.r_max
+                                 : part + ((int64_t)slice * num_perm + pb + i) * w.r_max;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * rt + 4 * g + e;
+          if (j < r) dst[j] = acc[rt][e];
+        }
+    }
+  }
+}
+
+// Launch 1 of the tiled shrink: tile items (block = slice) and the gather
+// items of the short segments (block = row group).
+template <int MAXR>
+__global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_kernel(
+    DevW w, const int32_t *__restrict__ perm, int32_t num_perm, const lora_item *__restrict__ items,
+    int32_t num_tokens, int32_t k_splits, int32_t k_slice, const uint16_t *__restrict__ x,
+    float *__restrict__ v, float *__restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t x0[kTileTokens * kTileK], x1[kTileTokens * kTileK];
+  __shared__ __attribute__((aligned(16))) uint16_t x2[kTileStages > 2 ? kTileTokens * kTileK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t x3[kTileStages > 3 ? kTileTokens * kTileK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t a0[MAXR * kTileK], a1[MAXR * kTileK];
+  __shared__ __attribute__((aligned(16))) uint16_t a2[kTileStages > 2 ? MAXR * kTileK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t a3[kTileStages > 3 ? MAXR * kTileK : 8];
+  __shared__ TileSmem sm;
+  const lora_item it = items[blockIdx.x];
+  int pb, a, cnt, path, blk;
+  if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
+  if (cnt > kTileTokens) {
+    LORA_CHECK(false, LORA_DEBUG_BAD_ITEM);
+    return;
+  }
+  const int r = used_rank(w, a);
+  if (r == 0) return;
+  if (path == LORA_PATH_TILE) {
+    if (blk >= k_splits || r > MAXR) {
+      LORA_CHECK(false, LORA_DEBUG_BAD_ITEM);
+      return;
+    }
+  } else if (blk >= (r + kRowGroup - 1) / kRowGroup) {
+    return;
+  }
+  for (int i = threadIdx.x; i < cnt; i += kThreads) {
+    sm.toks[i] = perm[pb + i];
+    LORA_CHECK((unsigned)sm.toks[i] < (unsigned)num_tokens, LORA_DEBUG_BAD_TOKEN);
+  }
+  __syncthreads();
+  if (path == LORA_PATH_TILE) {
+    const int kb = blk * k_slice, ke = min(w.d_in, kb + k_slice);
+    if (kb >= ke) return;
+    const int nrt = (r + 15) >> 4;
+#define LORA_TILE_CASE(RT)                                                                             \
+  tile_item<RT, MAXR>(w, a, r, cnt, kb, ke, pb, blk, k_splits, num_perm, num_tokens, sm.toks, x, v, part, \
+                      x0, x1, x2, x3, a0, a1, a2, a3)
+    if (nrt == 1) LORA_TILE_CASE(1);
+    else if constexpr (MAXR >= 32) {
+      if (nrt == 2) LORA_TILE_CASE(2);
+      else if constexpr (MAXR >= 64) {
+        if (nrt == 3) LORA_TILE_CASE(3);
+        else LORA_TILE_CASE(4);
+      }
+    }
+#undef LORA_TILE_CASE
+  } else {
+    const int j0 = blk * kRowGroup;
+    shrink_gemv<uint16_t, uint16_t, kRowGroup, kThreads / 64>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt,
+                                                               num_tokens, x, v, sm);
+  }
+}
+
+// Launch 2 of the tiled shrink (k_splits > 1): v = the sum of each token's
+// k_splits partials, added in slice order.  The workgroup of slice s of a
+// tile item takes the s-th of k_splits even shares of the item's tokens' rows
+// (so every workgroup of the launch has work).  (Adding the slices in the
+// last tile item of a chunk to finish, counted with an atomic, was measured
+// 3-6x slower: each arrival needs a device-scope release, which writes back
+// the L2.)
+__global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_reduce_kernel(
+    DevW w, const int32_t *__restrict__ perm, int32_t num_perm, const lora_item *__restrict__ items,
+    int32_t num_tokens, int32_t k_splits, const float *__restrict__ part, float *__restrict__ v) {
+  __shared__ int toks[kTileTokens];
+  const lora_item it = items[blockIdx.x];
+  int pb, a, cnt, path, blk;
+  if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
+  if (path != LORA_PATH_TILE || blk >= k_splits || cnt > kTileTokens) return;
+  const int r = adapter_rank(w, a);
+  const int i0 = (int)((int64_t)cnt * blk / k_splits), i1 = (int)((int64_t)cnt * (blk + 1) / k_splits);
+  if (i0 >= i1 || r == 0) return;
+  for (int i = threadIdx.x; i < i1 - i0; i += kThreads) toks[i] = perm[pb + i0 + i];
+  __syncthreads();
+  tile_sum_slices(w, r, i1 - i0, pb + i0, k_splits, num_perm, num_tokens, toks, part, v);
+}
+
 template <typename T, typename W>
 // bf16 activations: registers bounded so that three waves share a SIMD (three
 // workgroups per CU; the staged rank chunk keeps LDS within that too).
@@ -2254,6 +2564,53 @@ extern "C" lora_status lora_sgmv_shrink(const lora_weights *w, const int32_t *to
                          num_tokens, (const T *)x, v);
   });
   return check_launch("sgmv shrink launch");
+}
+
+extern "C" lora_status lora_sgmv_shrink_tiled(const lora_weights *w, const int32_t *token_perm,
+                                              int32_t num_perm, const lora_item *items,
+                                              int32_t num_items, int32_t num_tokens, int32_t k_splits,
+                                              const void *x, float *v, void *workspace,
+                                              int64_t workspace_bytes, hipStream_t stream) {
+  DevW d;
+  lora_status st = to_dev(w, &d);
+  if (st != LORA_OK) return st;
+  if ((st = check_sgmv_args(token_perm, num_perm, items, num_items, num_tokens, x, v)) != LORA_OK)
+    return st;
+  if (w->dtype != LORA_BF16 || w->weight_format != LORA_WFMT_PLAIN)
+    return fail(LORA_EUNSUPPORTED, "the tiled shrink needs bf16 activations and bf16 rows");
+  if (w->r_max > 64) return fail(LORA_EUNSUPPORTED, "the tiled shrink needs r_max <= 64 (got %d)", w->r_max);
+  if (w->d_in % LORA_SHRINK_TILE_K)
+    return fail(LORA_EUNSUPPORTED, "the tiled shrink needs d_in a multiple of %d (got %d)", LORA_SHRINK_TILE_K,
+                w->d_in);
+  if (k_splits < 1 || k_splits > LORA_MAX_K_SPLITS)
+    return fail(LORA_EINVAL, "k_splits %d outside 1..%d", k_splits, LORA_MAX_K_SPLITS);
+  const int32_t slice = tile_slice_len(w->d_in, k_splits);
+  if ((int64_t)(k_splits - 1) * slice >= w->d_in)
+    return fail(LORA_EINVAL, "k_splits %d leaves an empty slice of d_in %d (a plan built for another d_in)",
+                k_splits, w->d_in);
+  if (workspace_bytes < 0) return fail(LORA_EINVAL, "negative workspace size");
+  const int64_t need = k_splits > 1 ? (int64_t)k_splits * num_perm * w->r_max * (int64_t)sizeof(float) : 0;
+  if (need > 0 && (!workspace || !aligned16(workspace)))
+    return fail(LORA_EINVAL, "the tiled shrink with k_splits > 1 needs a 16-byte aligned workspace");
+  if (workspace_bytes < need)
+    return fail(LORA_EINVAL, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  if (num_items == 0 || num_tokens == 0) return ok();
+  float *part = static_cast<float *>(workspace);
+  const uint16_t *xb = static_cast<const uint16_t *>(x);
+  if (w->r_max <= 16)
+    hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<16>), dim3(num_items), dim3(kThreads), 0, stream, d, token_perm,
+                       num_perm, items, num_tokens, k_splits, slice, xb, v, part);
+  else if (w->r_max <= 32)
+    hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<32>), dim3(num_items), dim3(kThreads), 0, stream, d, token_perm,
+                       num_perm, items, num_tokens, k_splits, slice, xb, v, part);
+  else
+    hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<64>), dim3(num_items), dim3(kThreads), 0, stream, d, token_perm,
+                       num_perm, items, num_tokens, k_splits, slice, xb, v, part);
+  if (k_splits > 1)
+    hipLaunchKernelGGL(sgmv_shrink_tiled_reduce_kernel, dim3(num_items), dim3(kThreads), 0, stream, d,
+                       token_perm, num_perm, items, num_tokens, k_splits, (const float *)part, v);
+  return check_launch("sgmv tiled shrink launch");
 }
 
 extern "C" lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm,

@@ -31,4 +31,12 @@ lora_status ok();
 // LORA_EHIP with the HIP error's text.
 lora_status hip_fail(hipError_t e, const char *what);
 
+// Length of each of the k_splits slices of d_in in a tiled shrink: the even
+// share rounded up to a multiple of LORA_SHRINK_TILE_K (the last slice may be
+// shorter; the planner never makes one empty).
+inline int32_t tile_slice_len(int32_t d_in, int32_t k_splits) {
+  const int32_t even = (d_in + k_splits - 1) / k_splits;
+  return (even + LORA_SHRINK_TILE_K - 1) / LORA_SHRINK_TILE_K * LORA_SHRINK_TILE_K;
+}
+
 }  // namespace lora

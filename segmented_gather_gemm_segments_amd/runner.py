@@ -206,6 +206,38 @@ class DeviceProblem:
                                  mfma_min_tokens, host_rank=self.p.ranks.astype(np.int32))
         return torch.from_numpy(np.ascontiguousarray(items)).to(self.device)
 
+    def tiled_pays(self, tile_min_tokens: int = 0) -> bool:
+        """Whether the tiled shrink suits this batch: it applies (bf16
+        activations and rows, d_in a multiple of LORA_SHRINK_TILE_K, r_max <=
+        64) and the segments it tiles (at least tile_min_tokens tokens) carry
+        at least half of the shrink's algorithmic bytes (x rows plus each
+        segment's adapter rows), counting as tiled what the plan tiles: long
+        segments and short ones of rank >= LORA_TILE_MIN_RANK_SHORT.  Batches
+        dominated by short low-rank segments (decode tokens) keep the
+        one-launch shrink, whose gather items run at higher occupancy and need
+        no second launch."""
+        p = self.p
+        if p.dtype != "bf16" or p.wq or p.d_in % B.LORA_SHRINK_TILE_K or self.r_max > 64:
+            return False
+        tmin = tile_min_tokens or B.LORA_DEFAULT_TILE_MIN_TOKENS
+        _, starts, adapters, _ = self.segments()
+        lens = np.diff(np.asarray(starts, np.int64))
+        ranks = p.ranks[np.asarray(adapters)].astype(np.int64)
+        rows = lens + ranks
+        tiled = (lens >= tmin) | (ranks >= B.LORA_TILE_MIN_RANK_SHORT)
+        return bool(rows[tiled].sum() * 2 >= rows.sum())
+
+    def plan_tiled(self, policy: int = B.LORA_PATH_AUTO, tile_min_tokens: int = 0, max_splits: int = 0):
+        """Tiled shrink plan on the device: (items, k_splits, workspace or None)."""
+        torch = _torch()
+        _, starts, adapters, _ = self.segments()
+        items, ks = B.lora_sgmv_plan_tiled(starts, adapters, self.p.num_adapters, self.r_max, self.p.d_in,
+                                           policy, tile_min_tokens, max_splits,
+                                           host_rank=self.p.ranks.astype(np.int32))
+        nbytes = B.lora_sgmv_shrink_tiled_workspace(int(starts[-1]), self.r_max, ks)
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device=self.device) if nbytes else None
+        return torch.from_numpy(np.ascontiguousarray(items)).to(self.device), ks, ws
+
     # ------------------------------------------------------------- runs
     def new_v(self):
         torch = _torch()
@@ -213,14 +245,20 @@ class DeviceProblem:
                            device=self.device)
 
     def run_sgmv(self, policy: int = B.LORA_PATH_AUTO,
-                 mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS, y=None, v=None):
-        """shrink then expand over the segmented batch; returns (y, v)."""
+                 mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS, y=None, v=None,
+                 tiled: bool = False, tile_min_tokens: int = 0, max_splits: int = 0):
+        """shrink then expand over the segmented batch; returns (y, v).
+        tiled: the tiled shrink (its own plan, threshold and workspace)."""
         _, _, _, perm_d = self.segments()
-        sp = self.plan(B.LORA_PHASE_SHRINK, policy, mfma_min_tokens)
         ep = self.plan(B.LORA_PHASE_EXPAND, policy, mfma_min_tokens)
         y = self.y0.clone() if y is None else y
         v = self.new_v() if v is None else v
-        B.lora_sgmv_shrink(self.weights, perm_d, sp, self.x, v)
+        if tiled:
+            items, ks, ws = self.plan_tiled(policy, tile_min_tokens, max_splits)
+            B.lora_sgmv_shrink_tiled(self.weights, perm_d, items, ks, self.x, v, ws)
+        else:
+            sp = self.plan(B.LORA_PHASE_SHRINK, policy, mfma_min_tokens)
+            B.lora_sgmv_shrink(self.weights, perm_d, sp, self.x, v)
         B.lora_sgmv_expand(self.weights, perm_d, ep, v, y)
         return y, v
 

@@ -369,3 +369,90 @@ def test_base_gemm_workspace_rule():
         ws(-1, 8, 8)
     with pytest.raises(B.LoraError):
         ws(8, 0, 8)
+
+
+# ------------------------------------------------------------------ tiled shrink plan
+def _tile_slice_len(d_in, ks):
+    even = -(-d_in // ks)
+    return -(-even // B.LORA_SHRINK_TILE_K) * B.LORA_SHRINK_TILE_K
+
+
+@pytest.mark.parametrize("policy", [B.LORA_PATH_AUTO, B.LORA_PATH_GATHER, B.LORA_PATH_MFMA])
+def test_tiled_plan_covers_every_output_once(policy):
+    """Every (token, row of its adapter, d_in slice) is covered exactly once:
+    tile items cover (tokens x all rows x one slice), gather items (tokens x
+    row group x all of d_in)."""
+    rng = np.random.default_rng(40 + policy)
+    for trial in range(20):
+        nseg = int(rng.integers(1, 12))
+        lens = rng.integers(1, 200, size=nseg)
+        ranks = rng.choice([1, 8, 13, 16, 32, 50, 64], size=6).astype(np.int32)
+        seg_ad = rng.integers(0, 6, size=nseg).astype(np.int32)
+        starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        d_in = int(rng.choice([64, 512, 4096, 8192, 28672]))
+        items, ks = B.lora_sgmv_plan_tiled(starts, seg_ad, 6, 64, d_in, policy, 0, 0, host_rank=ranks)
+        assert 1 <= ks <= B.LORA_MAX_K_SPLITS
+        sl = _tile_slice_len(d_in, ks)
+        assert (ks - 1) * sl < d_in  # no empty slice
+        n = int(starts[-1])
+        cover = np.zeros((n, 64, ks), np.int32)
+        for pb, a, cp, blk in items:
+            cnt, path = cp & 0xFFFF, cp >> 16
+            seg = int(np.searchsorted(starts, pb, side="right") - 1)
+            assert seg_ad[seg] == a and pb + cnt <= starts[seg + 1]
+            r = int(ranks[a])
+            if path == B.LORA_PATH_TILE:
+                assert cnt <= B.LORA_SHRINK_TILE_TOKENS and 0 <= blk < ks
+                assert policy != B.LORA_PATH_GATHER
+                cover[pb:pb + cnt, :r, blk] += 1
+            else:
+                assert path == B.LORA_PATH_GATHER and policy != B.LORA_PATH_MFMA
+                assert cnt <= B.LORA_SHRINK_GATHER_TOKENS
+                j0 = blk * B.LORA_SHRINK_GATHER_ROWS
+                cover[pb:pb + cnt, j0:min(r, j0 + B.LORA_SHRINK_GATHER_ROWS), :] += 1
+        for s in range(nseg):
+            r = int(ranks[seg_ad[s]])
+            blk = cover[starts[s]:starts[s + 1]]
+            assert np.all(blk[:, :r, :] == 1) and np.all(blk[:, r:, :] == 0)
+            tiled = policy == B.LORA_PATH_MFMA or (policy == B.LORA_PATH_AUTO and (lens[s] >= 16 or r >= 32))
+            is_tile = [it for it in items if it[0] >= starts[s] and it[0] < starts[s + 1]]
+            assert all((it[2] >> 16 == B.LORA_PATH_TILE) == tiled for it in is_tile)
+
+
+def test_tiled_slices_and_workspace():
+    # heaviest item (64 + 64) x 8192 x 2 bytes = 2 MiB -> 8 slices of 1024
+    items, ks = B.lora_sgmv_plan_tiled([0, 100], [0], 1, 64, 8192, host_rank=[64])
+    assert ks == 8 and _tile_slice_len(8192, 8) == 1024
+    assert sum(1 for it in items if it[2] >> 16 == B.LORA_PATH_TILE) == 2 * 8
+    # max_splits bounds it
+    assert B.lora_sgmv_plan_tiled([0, 100], [0], 1, 64, 8192, max_splits=3, host_rank=[64])[1] == 3
+    # rank 16, 1024 tokens on 8192: (64 + 16) x 16 KiB = 1.25 MiB -> 5 slices of 1664 (the last 1536)
+    items, ks = B.lora_sgmv_plan_tiled([0, 1024], [0], 1, 16, 8192, host_rank=[16])
+    assert ks == 5 and _tile_slice_len(8192, 5) == 1664 and 4 * 1664 < 8192
+    assert B.lora_sgmv_shrink_tiled_workspace(1280, 16, 5) == 5 * 1280 * 16 * 4
+    assert B.lora_sgmv_shrink_tiled_workspace(1280, 16, 1) == 0
+    # no tiled segment (short, rank 16): one slice; a short rank-32 segment is tiled
+    assert B.lora_sgmv_plan_tiled([0, 3, 4], [0, 0], 1, 16, 8192, host_rank=[16])[1] == 1
+    items, ks = B.lora_sgmv_plan_tiled([0, 3], [0], 1, 32, 8192, host_rank=[32])
+    assert ks == 3 and all(it[2] >> 16 == B.LORA_PATH_TILE for it in items)  # (3 + 32) x 16 KiB
+
+
+def test_tiled_plan_validation():
+    lib = B.lib()
+    n, ks = ctypes.c_int32(0), ctypes.c_int32(0)
+    starts = np.array([0, 10], np.int32)
+    ad = np.array([0], np.int32)
+    sp, ap = starts.ctypes.data_as(ctypes.c_void_p), ad.ctypes.data_as(ctypes.c_void_p)
+    call = lambda d_in, r_max, ms=0: lib.lora_sgmv_plan_tiled(sp, ap, 1, 1, None, r_max, d_in, 0, 0, ms, None, 0,
+                                                               ctypes.byref(n), ctypes.byref(ks))
+    assert call(4096, 16) == B.LORA_OK
+    assert call(4104, 16) == B.LORA_EUNSUPPORTED      # not a multiple of 64
+    assert call(0, 16) == B.LORA_EUNSUPPORTED
+    assert call(4096, 65) == B.LORA_EUNSUPPORTED      # r_max above 64
+    assert call(4096, 16, 65) == B.LORA_EINVAL        # max_splits above the bound
+    assert lib.lora_sgmv_plan_tiled(sp, ap, 1, 1, None, 16, 4096, 0, 0, 0, None, 0, None,
+                                    ctypes.byref(ks)) == B.LORA_EINVAL
+    out = ctypes.c_int64(0)
+    assert lib.lora_sgmv_shrink_tiled_workspace(10, 16, 0, ctypes.byref(out)) == B.LORA_EINVAL
+    assert lib.lora_sgmv_shrink_tiled_workspace(10, 65, 2, ctypes.byref(out)) == B.LORA_EINVAL
+    assert lib.lora_sgmv_shrink_tiled_workspace(-1, 16, 2, ctypes.byref(out)) == B.LORA_EINVAL
