@@ -301,6 +301,20 @@ lora_status lora_sgmv_plan_tiled(const int32_t *seg_starts, const int32_t *seg_a
                                  int32_t *k_splits);
 lora_status lora_sgmv_shrink_tiled_workspace(int32_t num_perm, int32_t r_max, int32_t k_splits,
                                              int64_t *bytes);
+/* lora_sgmv_tiled_pays: whether to prefer the tiled shrink for a batch (host
+ * only).  *pays = 1 when lora_sgmv_shrink_tiled accepts the weights (dtype
+ * LORA_BF16, weight_format LORA_WFMT_PLAIN, r_max <= 64, d_in a positive
+ * multiple of LORA_SHRINK_TILE_K) and the segments lora_sgmv_plan_tiled would
+ * tile under the AUTO policy carry at least half of the shrink's bytes
+ * (counted as each segment's tokens plus its adapter's rank, in d_in rows);
+ * else 0.  Batches dominated by short low-rank segments (decode tokens) do
+ * better with lora_sgmv_shrink: its gather items run at higher occupancy and
+ * it needs no second launch.  Arguments as lora_sgmv_plan_tiled (host_rank may
+ * be NULL: every adapter at r_max); errors as lora_sgmv_plan. */
+lora_status lora_sgmv_tiled_pays(const int32_t *seg_starts, const int32_t *seg_adapter,
+                                 int32_t num_segments, int32_t num_adapters, const int32_t *host_rank,
+                                 int32_t r_max, int32_t d_in, int32_t dtype, int32_t weight_format,
+                                 int32_t tile_min_tokens, int32_t *pays);
 lora_status lora_sgmv_shrink_tiled(const lora_weights *w, const int32_t *token_perm,
                                    int32_t num_perm, const lora_item *items, int32_t num_items,
                                    int32_t num_tokens, int32_t k_splits, const void *x, float *v,

@@ -79,6 +79,7 @@ EXPORTS = {
     "lora_sgmv_plan_tiled": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
                              _I32),
     "lora_sgmv_shrink_tiled_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
+    "lora_sgmv_tiled_pays": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P], _I32),
     "lora_sgmv_shrink_tiled": ([_P, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, ctypes.c_int64, _P], _I32),
     "lora_bgmv_shrink": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_bgmv_expand": ([_P, _P, _I32, _I32, _P, _P, _P], _I32),
@@ -219,6 +220,18 @@ def lora_sgmv_plan_tiled(seg_starts, seg_adapter, num_adapters: int, r_max: int,
     items = np.zeros((max(n.value, 1), 4), np.int32)
     _check(lib().lora_sgmv_plan_tiled(*args, _np_ptr(items), n.value, ctypes.byref(n), ctypes.byref(ks)))
     return items[: n.value], int(ks.value)
+
+
+def lora_sgmv_tiled_pays(seg_starts, seg_adapter, num_adapters: int, r_max: int, d_in: int, dtype: int,
+                         weight_format: int = LORA_WFMT_PLAIN, tile_min_tokens: int = 0, host_rank=None) -> bool:
+    """Whether the library prefers the tiled shrink for this batch."""
+    starts, adapters = _i32(seg_starts), _i32(seg_adapter)
+    ranks = None if host_rank is None else _i32(host_rank)
+    out = ctypes.c_int32(0)
+    _check(lib().lora_sgmv_tiled_pays(_np_ptr(starts), _np_ptr(adapters), adapters.size, num_adapters,
+                                      _np_ptr(ranks), r_max, d_in, dtype, weight_format, tile_min_tokens,
+                                      ctypes.byref(out)))
+    return bool(out.value)
 
 
 def lora_sgmv_shrink_tiled_workspace(num_perm: int, r_max: int, k_splits: int) -> int:

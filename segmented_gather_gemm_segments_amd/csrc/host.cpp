@@ -283,6 +283,32 @@ extern "C" lora_status lora_sgmv_plan_tiled(const int32_t *seg_starts, const int
   return ok();
 }
 
+extern "C" lora_status lora_sgmv_tiled_pays(const int32_t *seg_starts, const int32_t *seg_adapter,
+                                            int32_t num_segments, int32_t num_adapters,
+                                            const int32_t *host_rank, int32_t r_max, int32_t d_in,
+                                            int32_t dtype, int32_t weight_format, int32_t tile_min_tokens,
+                                            int32_t *pays) {
+  if (!pays) return fail(LORA_EINVAL, "null pays");
+  *pays = 0;
+  int32_t n_plain = 0;
+  lora_status st = lora_sgmv_plan(LORA_PHASE_SHRINK, seg_starts, seg_adapter, num_segments, num_adapters,
+                                  host_rank, r_max, LORA_PATH_GATHER, 1, nullptr, 0, &n_plain);
+  if (st != LORA_OK) return st;
+  if (dtype != LORA_BF16 || weight_format != LORA_WFMT_PLAIN || r_max > 64 || d_in <= 0 ||
+      d_in % LORA_SHRINK_TILE_K)
+    return ok();
+  if (tile_min_tokens <= 0) tile_min_tokens = LORA_DEFAULT_TILE_MIN_TOKENS;
+  int64_t tiled = 0, all = 0;
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int32_t len = seg_starts[s + 1] - seg_starts[s];
+    const int32_t r = host_rank ? host_rank[seg_adapter[s]] : r_max;
+    all += (int64_t)len + r;
+    if (len >= tile_min_tokens || r >= LORA_TILE_MIN_RANK_SHORT) tiled += (int64_t)len + r;
+  }
+  *pays = all > 0 && 2 * tiled >= all;
+  return ok();
+}
+
 extern "C" lora_status lora_sgmv_shrink_tiled_workspace(int32_t num_perm, int32_t r_max, int32_t k_splits,
                                                         int64_t *bytes) {
   if (!bytes) return fail(LORA_EINVAL, "null bytes");

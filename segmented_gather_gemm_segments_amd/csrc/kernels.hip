@@ -1552,7 +1552,7 @@ struct alignas(16) TileSmem {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// v rows of the tokens toks[0..cnt) of a chunk = the sum of their k_splits
+// v rows of the tokens toks[0..cnt) (token_perm entries) of a chunk = the sum of their k_splits
 // partials part[slice][pb + i][j], added in slice order.  A thread takes four
 // consecutive outputs of one token (a 16-byte load per slice when r_max and r
 // are multiples of 4) and issues the loads of eight slices before adding them.
@@ -1787,7 +1787,6 @@ __global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_kernel(
 __global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_reduce_kernel(
     DevW w, const int32_t *__restrict__ perm, int32_t num_perm, const lora_item *__restrict__ items,
     int32_t num_tokens, int32_t k_splits, const float *__restrict__ part, float *__restrict__ v) {
-  __shared__ int toks[kTileTokens];
   const lora_item it = items[blockIdx.x];
   int pb, a, cnt, path, blk;
   if (!decode_item(it, w, num_perm, pb, a, cnt, path, blk)) return;
@@ -1795,9 +1794,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_reduce_kernel(
   const int r = adapter_rank(w, a);
   const int i0 = (int)((int64_t)cnt * blk / k_splits), i1 = (int)((int64_t)cnt * (blk + 1) / k_splits);
   if (i0 >= i1 || r == 0) return;
-  for (int i = threadIdx.x; i < i1 - i0; i += kThreads) toks[i] = perm[pb + i0 + i];
-  __syncthreads();
-  tile_sum_slices(w, r, i1 - i0, pb + i0, k_splits, num_perm, num_tokens, toks, part, v);
+  // token ids straight from token_perm: their loads go out with the partials'
+  tile_sum_slices(w, r, i1 - i0, pb + i0, k_splits, num_perm, num_tokens, perm + pb + i0, part, v);
 }
 
 template <typename T, typename W>

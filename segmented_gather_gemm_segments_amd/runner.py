@@ -207,25 +207,11 @@ class DeviceProblem:
         return torch.from_numpy(np.ascontiguousarray(items)).to(self.device)
 
     def tiled_pays(self, tile_min_tokens: int = 0) -> bool:
-        """Whether the tiled shrink suits this batch: it applies (bf16
-        activations and rows, d_in a multiple of LORA_SHRINK_TILE_K, r_max <=
-        64) and the segments it tiles (at least tile_min_tokens tokens) carry
-        at least half of the shrink's algorithmic bytes (x rows plus each
-        segment's adapter rows), counting as tiled what the plan tiles: long
-        segments and short ones of rank >= LORA_TILE_MIN_RANK_SHORT.  Batches
-        dominated by short low-rank segments (decode tokens) keep the
-        one-launch shrink, whose gather items run at higher occupancy and need
-        no second launch."""
-        p = self.p
-        if p.dtype != "bf16" or p.wq or p.d_in % B.LORA_SHRINK_TILE_K or self.r_max > 64:
-            return False
-        tmin = tile_min_tokens or B.LORA_DEFAULT_TILE_MIN_TOKENS
+        """The library's choice between the tiled and the one-launch shrink
+        for this batch (lora_sgmv_tiled_pays)."""
         _, starts, adapters, _ = self.segments()
-        lens = np.diff(np.asarray(starts, np.int64))
-        ranks = p.ranks[np.asarray(adapters)].astype(np.int64)
-        rows = lens + ranks
-        tiled = (lens >= tmin) | (ranks >= B.LORA_TILE_MIN_RANK_SHORT)
-        return bool(rows[tiled].sum() * 2 >= rows.sum())
+        return B.lora_sgmv_tiled_pays(starts, adapters, self.p.num_adapters, self.r_max, self.p.d_in, self.cdtype,
+                                      self.wfmt, tile_min_tokens, host_rank=self.p.ranks.astype(np.int32))
 
     def plan_tiled(self, policy: int = B.LORA_PATH_AUTO, tile_min_tokens: int = 0, max_splits: int = 0):
         """Tiled shrink plan on the device: (items, k_splits, workspace or None)."""

@@ -75,6 +75,41 @@ static void segments_and_plans(std::mt19937 &rng) {
           CHECK(cnt == 0 || (items[(size_t)i].perm_begin + cnt <= starts[(size_t)ns]));
         }
     }
+  // the tiled planner, its workspace query and the tiled-or-plain choice
+  const int32_t d_in = 64 * (int32_t)(rng() % 500) + (rng() % 8 == 0 ? 8 : 0);  // sometimes not a multiple
+  for (int policy = 0; policy < 3; ++policy) {
+    const int32_t rm = std::min(r_max, (int32_t)(rng() % 2 ? 64 : 128));
+    std::vector<int32_t> rk(ranks);
+    for (auto &r : rk) r = std::min(r, rm);
+    const int32_t tmin = (int32_t)(rng() % 40) - 4, ms = (int32_t)(rng() % 70) - 2;
+    int32_t count = -1, ks = -1;
+    lora_status s = lora_sgmv_plan_tiled(starts.data(), seg.data(), ns, n_adapters, rk.data(), rm, d_in, policy,
+                                         tmin, ms, nullptr, 0, &count, &ks);
+    if (d_in <= 0 || d_in % LORA_SHRINK_TILE_K || rm > 64) {
+      CHECK(s == LORA_EUNSUPPORTED);
+    } else if (ms > LORA_MAX_K_SPLITS) {
+      CHECK(s == LORA_EINVAL);
+    } else {
+      CHECK(s == LORA_OK && count >= 0 && ks >= 1 && ks <= LORA_MAX_K_SPLITS);
+      std::vector<lora_item> items((size_t)count + 1);
+      int32_t count2 = -1, ks2 = -1;
+      s = lora_sgmv_plan_tiled(starts.data(), seg.data(), ns, n_adapters, rk.data(), rm, d_in, policy, tmin, ms,
+                               items.data(), count, &count2, &ks2);
+      CHECK(s == LORA_OK && count2 == count && ks2 == ks);
+      for (int32_t i = 0; i < count; ++i) {
+        const int32_t cnt = items[(size_t)i].count_path & 0xffff, path = items[(size_t)i].count_path >> 16;
+        CHECK(cnt > 0 && items[(size_t)i].perm_begin + cnt <= starts[(size_t)ns]);
+        CHECK(path != LORA_PATH_TILE || (cnt <= LORA_SHRINK_TILE_TOKENS && items[(size_t)i].block < ks));
+      }
+      int64_t bytes = -1;
+      CHECK(lora_sgmv_shrink_tiled_workspace(starts[(size_t)ns], rm, ks, &bytes) == LORA_OK);
+      CHECK(ks == 1 ? bytes == 0 : bytes == (int64_t)ks * starts[(size_t)ns] * rm * 4);
+    }
+    int32_t pays = -1;
+    s = lora_sgmv_tiled_pays(starts.data(), seg.data(), ns, n_adapters, rk.data(), rm, d_in, LORA_BF16,
+                             LORA_WFMT_PLAIN, tmin, &pays);
+    CHECK(s == LORA_OK && (pays == 0 || pays == 1));
+  }
 }
 
 static void pools(std::mt19937 &rng) {

@@ -456,3 +456,27 @@ def test_tiled_plan_validation():
     assert lib.lora_sgmv_shrink_tiled_workspace(10, 16, 0, ctypes.byref(out)) == B.LORA_EINVAL
     assert lib.lora_sgmv_shrink_tiled_workspace(10, 65, 2, ctypes.byref(out)) == B.LORA_EINVAL
     assert lib.lora_sgmv_shrink_tiled_workspace(-1, 16, 2, ctypes.byref(out)) == B.LORA_EINVAL
+
+
+def test_tiled_pays_choice():
+    """The library prefers the tiled shrink where tiled segments carry most of
+    the shrink's bytes: the prefill and heterogeneous batches, not the 70B
+    layer's 256 single-token segments; never for fp32, quantised rows, r_max
+    above 64 or d_in not a multiple of 64."""
+    from segmented_gather_gemm_segments_amd import workloads as wl
+
+    def pays(p, dtype=B.LORA_BF16, wfmt=B.LORA_WFMT_PLAIN, d_in=None):
+        _, st, ad = B.lora_segments_build(p.ids, p.num_adapters)
+        return B.lora_sgmv_tiled_pays(st, ad, p.num_adapters, p.r_max, d_in or p.d_in, dtype, wfmt,
+                                      host_rank=p.ranks.astype(np.int32))
+    pre = wl.sgmv_prefill()
+    het = wl.hetero_paged()
+    lay = wl.layer_projection("q", with_base=False)
+    assert pays(pre) and pays(het) and not pays(lay)
+    assert not pays(het, dtype=B.LORA_F32)
+    assert not pays(het, wfmt=B.LORA_WFMT_FP8_E4M3)
+    assert not pays(het, d_in=8200)
+    # a rank-32 one-token segment alone is tiled; a rank-16 one is not
+    assert B.lora_sgmv_tiled_pays([0, 1], [0], 1, 32, 4096, B.LORA_BF16, host_rank=[32])
+    assert not B.lora_sgmv_tiled_pays([0, 1], [0], 1, 16, 4096, B.LORA_BF16, host_rank=[16])
+    assert not B.lora_sgmv_tiled_pays([0, 1], [0], 1, 80, 4096, B.LORA_BF16, host_rank=[80])
