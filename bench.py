@@ -51,6 +51,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "segmented_gather_gemm_segments_amd", "csrc
                   for f in ("kernels.hip", "base_gemm.hip", "host.cpp", "lora_internal.h")] + \
                  [os.path.join(ROOT, "include", "lora_sgmv.h")]
 LAYER_WORKLOAD = "layer70b_1280tok_256ad_r16"
+LAYER_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
 def kernel_hash() -> str:
@@ -88,6 +89,10 @@ def parse():
                     help="tiled shrink: segments of at least this many tokens take tile items "
                          "(0: the library default)")
     ap.add_argument("--max-splits", type=int, default=0, help="tiled shrink: at most this many d_in slices")
+    ap.add_argument("--layer-streams", choices=("groups", "serial"), default="groups",
+                    help="70B layer step: the deltas of q, k, v (and of gate, up), independent given the "
+                         "layer's inputs, on separate HIP streams with o and down after their groups, "
+                         "or all seven in one stream")
     ap.add_argument("--mfma-min", type=int, default=0,
                     help="SGMV plan: segments of at least this many tokens take the MFMA path "
                          "(0: the library default)")
@@ -598,9 +603,17 @@ def run_layer(args, torch):
 
     stream = torch.cuda.Stream()
     mfma_min = args.mfma_min or B.LORA_DEFAULT_MFMA_MIN_TOKENS
+    # a layer's dependency groups: the deltas inside a group are independent
+    # (q, k and v read the same input, as do gate and up); with
+    # --layer-streams groups each member runs on its own stream (all at the
+    # default priority) and the group joins before the next one starts
+    groups = LAYER_GROUPS if args.layer_streams == "groups" else tuple((n,) for n, _, _ in wl.LAYER_70B)
+    lane_of = {n: j for g in groups for j, n in enumerate(g)}
+    lanes = [stream] + [torch.cuda.Stream() for _ in range(max(len(g) for g in groups) - 1)]
     projs = []
     for name, _, _ in wl.LAYER_70B:
         p = wl.layer_projection(name)
+        ls = lanes[lane_of[name]]
         dp = R.DeviceProblem(p)
         y_base = torch.empty((p.num_tokens, p.d_out), dtype=torch.bfloat16, device="cuda")
         base = B.prepare_base_gemm(dp.x, dp.w, y_base, workspace=dp.base_workspace(), stream=stream)
@@ -621,22 +634,35 @@ def run_layer(args, torch):
             y = y_base.clone()
             if tp is not None:
                 calls.append(B.prepare_sgmv_tiled(rp.weights, perm_d, tp[0], tp[1], tp[2], ep, rp.x, rp.new_v(),
-                                                  y, stream=stream))
+                                                  y, stream=ls))
             else:
-                calls.append(B.prepare_sgmv(rp.weights, perm_d, sp, ep, rp.x, rp.new_v(), y, stream=stream))
+                calls.append(B.prepare_sgmv(rp.weights, perm_d, sp, ep, rp.x, rp.new_v(), y, stream=ls))
         p.extra.pop("w", None)   # the host copy of W is no longer needed
-        projs.append({"name": name, "p": p, "dp": dp, "base": base, "calls": calls, "n_rep": n_rep,
+        projs.append({"name": name, "p": p, "dp": dp, "base": base, "calls": calls, "n_rep": n_rep, "lane": ls,
                       "sb": sb, "eb": eb, "bf": acc.base_gemm_flops(p.num_tokens, p.d_out, p.d_in),
                       "y_base": y_base, "plans": (sp, ep),
                       "shrink": (f"tiled ({tp[1]} d_in slices)" if tp is not None else "one launch")})
     torch.cuda.synchronize()
     K = args.steps
 
+    by_name = {q["name"]: q for q in projs}
+
     def step(i):
-        for q in projs:
-            c = q["calls"][i % q["n_rep"]]
-            c[0]()
-            c[1]()
+        for g in groups:
+            members = [by_name[n] for n in g]
+            if len(members) > 1:
+                fork = torch.cuda.Event()
+                fork.record(stream)
+                for q in members[1:]:
+                    q["lane"].wait_event(fork)
+            for q in members:
+                c = q["calls"][i % q["n_rep"]]
+                c[0]()
+                c[1]()
+            for q in members[1:]:
+                done = torch.cuda.Event()
+                done.record(q["lane"])
+                stream.wait_event(done)
 
     wall, host_step_s = timed_graph(torch, stream, step, K, args.warmup)
 
@@ -645,7 +671,7 @@ def run_layer(args, torch):
     # between two uses of one), and one by one (k/v's W then stays cached)
     per, tot = {}, {"shrink": 0.0, "expand": 0.0}
     for q in projs:
-        t = {ph: float(np.mean([graph_span(torch, stream, [q["calls"][i % q["n_rep"]][k] for i in range(K)], 1)
+        t = {ph: float(np.mean([graph_span(torch, q["lane"], [q["calls"][i % q["n_rep"]][k] for i in range(K)], 1)
                                 for _ in range(3)]))
              for k, ph in enumerate(("shrink", "expand"))}
         tb = graph_span(torch, stream, [q["base"]] * 5, 3)
@@ -682,6 +708,7 @@ def run_layer(args, torch):
                    "mfma_min_tokens": mfma_min,
                    "shrink": sorted(set(q["shrink"] for q in projs)),
                    "timed": "HIP graph replay of K layer deltas (7 projections x shrink + expand)",
+                   "streams": " then ".join("|".join(g) for g in groups),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

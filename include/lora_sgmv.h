@@ -293,6 +293,7 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
 #define LORA_DEFAULT_TILE_MIN_TOKENS 16
 #define LORA_TILE_MIN_RANK_SHORT 32
 #define LORA_MAX_K_SPLITS 64
+#define LORA_TILE_PAYS_BYTES (24 << 20)    /* compute-unit bytes a tiled shrink must save */
 lora_status lora_sgmv_plan_tiled(const int32_t *seg_starts, const int32_t *seg_adapter,
                                  int32_t num_segments, int32_t num_adapters,
                                  const int32_t *host_rank, int32_t r_max, int32_t d_in,
@@ -304,13 +305,13 @@ lora_status lora_sgmv_shrink_tiled_workspace(int32_t num_perm, int32_t r_max, in
 /* lora_sgmv_tiled_pays: whether to prefer the tiled shrink for a batch (host
  * only).  *pays = 1 when lora_sgmv_shrink_tiled accepts the weights (dtype
  * LORA_BF16, weight_format LORA_WFMT_PLAIN, r_max <= 64, d_in a positive
- * multiple of LORA_SHRINK_TILE_K) and the segments lora_sgmv_plan_tiled would
- * tile under the AUTO policy carry at least half of the shrink's bytes
- * (counted as each segment's tokens plus its adapter's rank, in d_in rows);
- * else 0.  Batches dominated by short low-rank segments (decode tokens) do
- * better with lora_sgmv_shrink: its gather items run at higher occupancy and
- * it needs no second launch.  Arguments as lora_sgmv_plan_tiled (host_rank may
- * be NULL: every adapter at r_max); errors as lora_sgmv_plan. */
+ * multiple of LORA_SHRINK_TILE_K) and its tile items, planned under the AUTO
+ * policy, would read at least LORA_TILE_PAYS_BYTES fewer bytes through the
+ * compute units than the items of lora_sgmv_plan (A rows once per 64 tokens
+ * instead of once per 16, x rows once instead of once per row group): about
+ * what the second launch costs.  Else 0 (batches of short low-rank segments,
+ * such as decode tokens, or short d_in).  Arguments as lora_sgmv_plan_tiled
+ * (host_rank may be NULL: every adapter at r_max); errors as lora_sgmv_plan. */
 lora_status lora_sgmv_tiled_pays(const int32_t *seg_starts, const int32_t *seg_adapter,
                                  int32_t num_segments, int32_t num_adapters, const int32_t *host_rank,
                                  int32_t r_max, int32_t d_in, int32_t dtype, int32_t weight_format,

@@ -33,6 +33,7 @@ LORA_EXPAND_GATHER_COLS, LORA_EXPAND_MFMA_COLS = 2048, 256
 LORA_PATH_TILE = 3
 LORA_SHRINK_TILE_TOKENS, LORA_SHRINK_TILE_K, LORA_SHRINK_TILE_ITEM_BYTES = 64, 64, 262144
 LORA_DEFAULT_TILE_MIN_TOKENS, LORA_TILE_MIN_RANK_SHORT, LORA_MAX_K_SPLITS = 16, 32, 64
+LORA_TILE_PAYS_BYTES = 24 << 20
 
 
 class LoraError(RuntimeError):

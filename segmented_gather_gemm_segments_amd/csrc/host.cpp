@@ -298,14 +298,23 @@ extern "C" lora_status lora_sgmv_tiled_pays(const int32_t *seg_starts, const int
       d_in % LORA_SHRINK_TILE_K)
     return ok();
   if (tile_min_tokens <= 0) tile_min_tokens = LORA_DEFAULT_TILE_MIN_TOKENS;
-  int64_t tiled = 0, all = 0;
+  // d_in rows each plan's items read through the compute units: the plain
+  // plan's MFMA items read A once per LORA_SHRINK_MFMA_TOKENS tokens, its
+  // gather items x once per LORA_SHRINK_GATHER_ROWS rows and A once per
+  // LORA_SHRINK_GATHER_TOKENS tokens; tile items read x once and A once per
+  // LORA_SHRINK_TILE_TOKENS tokens
+  auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  int64_t saved = 0;
   for (int32_t s = 0; s < num_segments; ++s) {
-    const int32_t len = seg_starts[s + 1] - seg_starts[s];
-    const int32_t r = host_rank ? host_rank[seg_adapter[s]] : r_max;
-    all += (int64_t)len + r;
-    if (len >= tile_min_tokens || r >= LORA_TILE_MIN_RANK_SHORT) tiled += (int64_t)len + r;
+    const int64_t len = seg_starts[s + 1] - seg_starts[s];
+    const int64_t r = host_rank ? host_rank[seg_adapter[s]] : r_max;
+    if (!(len >= tile_min_tokens || r >= LORA_TILE_MIN_RANK_SHORT)) continue;
+    const int64_t plain = len >= LORA_DEFAULT_MFMA_MIN_TOKENS
+                              ? len + r * cdiv(len, LORA_SHRINK_MFMA_TOKENS)
+                              : len * cdiv(r, LORA_SHRINK_GATHER_ROWS) + r * cdiv(len, LORA_SHRINK_GATHER_TOKENS);
+    saved += plain - (len + r * cdiv(len, LORA_SHRINK_TILE_TOKENS));
   }
-  *pays = all > 0 && 2 * tiled >= all;
+  *pays = saved * d_in * 2 >= (int64_t)LORA_TILE_PAYS_BYTES;
   return ok();
 }
 

@@ -3,8 +3,10 @@ captured once and the graph replayed several times, with the program's own
 eager work and device synchronisations between the replays; every replay must
 equal the eager call bit for bit (the kernels' reduction orders are fixed and
 none of them records a memset).  Covers the fused decode launch, the segmented
-shrink + expand pair on the paged heterogeneous batch, and the base GEMM with
-and without its split-k workspace (two launches per call)."""
+shrink + expand pair and the tiled shrink + expand on the paged heterogeneous
+batch, three projections' deltas forked onto three streams and joined with
+events, and the base GEMM with and without its split-k workspace (two
+launches per call)."""
 import numpy as np
 import pytest
 
@@ -88,6 +90,76 @@ def test_graph_sgmv_paged_hetero():
         v_g.zero_()
 
     replay_and_check(st, capture, reset, [y_g, v_g], [y_e, v_e], "sgmv shrink+expand")
+
+
+def test_graph_sgmv_tiled():
+    """The tiled shrink (tile launch + slice reduction) and the expand."""
+    R = runner()
+    dp = R.DeviceProblem(wl.config(4))
+    say("graph tiled sgmv: 4096 tokens, 64 segments, ranks 8..64, paged pool")
+    y_e, v_e = dp.run_sgmv(tiled=True)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    y_g, v_g = dp.y0.clone(), dp.new_v()
+    _, _, _, perm_d = dp.segments()
+    items, ks, ws = dp.plan_tiled()
+    assert ks > 1
+    ep = dp.plan(B.LORA_PHASE_EXPAND)
+    shrink, expand = B.prepare_sgmv_tiled(dp.weights, perm_d, items, ks, ws, ep, dp.x, v_g, y_g, stream=st)
+
+    def capture():
+        shrink()
+        expand()
+
+    def reset():
+        y_g.copy_(dp.y0)
+        v_g.zero_()
+        ws.fill_(float("nan"))  # the partials of every replay are rewritten before they are read
+
+    replay_and_check(st, capture, reset, [y_g, v_g], [y_e, v_e], "tiled shrink+expand")
+
+
+def test_graph_layer_group_on_three_streams():
+    """The q, k and v deltas of the 70B layer, each on its own stream, forked
+    from and joined back to the capture stream with events (as the bench's
+    layer step runs them): every replay equals the three eager calls."""
+    R = runner()
+    dps = [R.DeviceProblem(wl.layer_projection(n, with_base=False)) for n in ("q", "k", "v")]
+    say("graph layer q|k|v on three streams")
+    wants = []
+    for dp in dps:
+        y, v = dp.run_sgmv()
+        wants += [y, v]
+    torch.cuda.synchronize()
+    main = torch.cuda.Stream()
+    lanes = [main, torch.cuda.Stream(), torch.cuda.Stream()]
+    outs, calls = [], []
+    for dp, ls in zip(dps, lanes):
+        y_g, v_g = dp.y0.clone(), dp.new_v()
+        _, _, _, perm_d = dp.segments()
+        sp, ep = dp.plan(B.LORA_PHASE_SHRINK), dp.plan(B.LORA_PHASE_EXPAND)
+        calls.append(B.prepare_sgmv(dp.weights, perm_d, sp, ep, dp.x, v_g, y_g, stream=ls))
+        outs += [y_g, v_g]
+
+    def capture():
+        fork = torch.cuda.Event()
+        fork.record(main)
+        for ls in lanes[1:]:
+            ls.wait_event(fork)
+        for c in calls:
+            c[0]()
+            c[1]()
+        for ls in lanes[1:]:
+            done = torch.cuda.Event()
+            done.record(ls)
+            main.wait_event(done)
+
+    def reset():
+        for dp, j in zip(dps, range(0, 6, 2)):
+            outs[j].copy_(dp.y0)
+            outs[j + 1].zero_()
+
+    replay_and_check(main, capture, reset, outs, wants, "layer q|k|v streams")
 
 
 @pytest.mark.parametrize("m,n,k,split", [(256, 1024, 4096, True), (300, 520, 4104, True),

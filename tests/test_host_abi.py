@@ -459,10 +459,11 @@ def test_tiled_plan_validation():
 
 
 def test_tiled_pays_choice():
-    """The library prefers the tiled shrink where tiled segments carry most of
-    the shrink's bytes: the prefill and heterogeneous batches, not the 70B
-    layer's 256 single-token segments; never for fp32, quantised rows, r_max
-    above 64 or d_in not a multiple of 64."""
+    """The library prefers the tiled shrink where its tile items save at least
+    24 MiB of compute-unit reads: the prefill and heterogeneous batches and the
+    70B layer's down projection (d_in 28672), not the layer's q projection
+    (d_in 8192: 768 rows x 16 KiB = 12 MiB saved); never for fp32, quantised
+    rows, r_max above 64 or d_in not a multiple of 64."""
     from segmented_gather_gemm_segments_amd import workloads as wl
 
     def pays(p, dtype=B.LORA_BF16, wfmt=B.LORA_WFMT_PLAIN, d_in=None):
@@ -472,11 +473,16 @@ def test_tiled_pays_choice():
     pre = wl.sgmv_prefill()
     het = wl.hetero_paged()
     lay = wl.layer_projection("q", with_base=False)
-    assert pays(pre) and pays(het) and not pays(lay)
+    down = wl.layer_projection("down", with_base=False)
+    assert pays(pre) and pays(het) and not pays(lay) and pays(down)
     assert not pays(het, dtype=B.LORA_F32)
     assert not pays(het, wfmt=B.LORA_WFMT_FP8_E4M3)
     assert not pays(het, d_in=8200)
-    # a rank-32 one-token segment alone is tiled; a rank-16 one is not
-    assert B.lora_sgmv_tiled_pays([0, 1], [0], 1, 32, 4096, B.LORA_BF16, host_rank=[32])
-    assert not B.lora_sgmv_tiled_pays([0, 1], [0], 1, 16, 4096, B.LORA_BF16, host_rank=[16])
+    # the byte rule: 64 one-token rank-64 segments on d_in 8192 save 64 x (16 - 1) rows x 16 KiB = 15 MiB
+    # (no), 128 of them 30 MiB (yes); rank 16 saves nothing on one token (x read 4x vs 1x: 3 rows each)
+    st64 = np.arange(65, dtype=np.int32)
+    st128 = np.arange(129, dtype=np.int32)
+    assert not B.lora_sgmv_tiled_pays(st64, np.arange(64), 64, 64, 8192, B.LORA_BF16, host_rank=[64] * 64)
+    assert B.lora_sgmv_tiled_pays(st128, np.arange(128), 128, 64, 8192, B.LORA_BF16, host_rank=[64] * 128)
+    assert not B.lora_sgmv_tiled_pays(st128, np.arange(128), 128, 16, 8192, B.LORA_BF16, host_rank=[16] * 128)
     assert not B.lora_sgmv_tiled_pays([0, 1], [0], 1, 80, 4096, B.LORA_BF16, host_rank=[80])
