@@ -250,7 +250,9 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
 
 /* ------------------------------------------------------------------------ */
 /* Tiled segmented shrink: the v of lora_sgmv_shrink for bf16 activations and
- * bf16 rows, planned for segments whose shrink is a real dense product
+ * bf16, FP8 E4M3 or INT4 rows (dequantised to bf16 MFMA operands as they leave
+ * LDS; a row's scale multiplies its sums), planned for segments whose shrink
+ * is a real dense product
  * ("SGMV ..." section: the shrink phase, d_in -> r through A_{a(t)}; tensor
  * cores for the long segments).  A tile item is up to LORA_SHRINK_TILE_TOKENS
  * tokens of one segment and one slice of d_in: its workgroup streams the
@@ -282,8 +284,8 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
  * device memory, 16-byte aligned, of at least the size above (contents on
  * entry do not matter; NULL with 0 bytes when k_splits == 1); calls that
  * share it must not overlap (on one stream they do not).  Errors: as
- * lora_sgmv_shrink; LORA_EUNSUPPORTED unless activations and rows are bf16,
- * r_max <= 64 and d_in is a multiple of LORA_SHRINK_TILE_K; LORA_EINVAL for
+ * lora_sgmv_shrink; LORA_EUNSUPPORTED unless activations are bf16, r_max <=
+ * 64 and d_in is a multiple of LORA_SHRINK_TILE_K; LORA_EINVAL for
  * k_splits out of range or leaving an empty slice, or a missing, misaligned
  * or short workspace.                                                        */
 #define LORA_PATH_TILE 3                    /* plan items only: a tiled shrink item */
@@ -304,8 +306,8 @@ lora_status lora_sgmv_shrink_tiled_workspace(int32_t num_perm, int32_t r_max, in
                                              int64_t *bytes);
 /* lora_sgmv_tiled_pays: whether to prefer the tiled shrink for a batch (host
  * only).  *pays = 1 when lora_sgmv_shrink_tiled accepts the weights (dtype
- * LORA_BF16, weight_format LORA_WFMT_PLAIN, r_max <= 64, d_in a positive
- * multiple of LORA_SHRINK_TILE_K) and its tile items, planned under the AUTO
+ * LORA_BF16, any weight_format, r_max <= 64, d_in a positive multiple of
+ * LORA_SHRINK_TILE_K) and its tile items, planned under the AUTO
  * policy, would read at least LORA_TILE_PAYS_BYTES fewer bytes through the
  * compute units than the items of lora_sgmv_plan (A rows once per 64 tokens
  * instead of once per 16, x rows once instead of once per row group): about

@@ -294,13 +294,17 @@ extern "C" lora_status lora_sgmv_tiled_pays(const int32_t *seg_starts, const int
   lora_status st = lora_sgmv_plan(LORA_PHASE_SHRINK, seg_starts, seg_adapter, num_segments, num_adapters,
                                   host_rank, r_max, LORA_PATH_GATHER, 1, nullptr, 0, &n_plain);
   if (st != LORA_OK) return st;
-  if (dtype != LORA_BF16 || weight_format != LORA_WFMT_PLAIN || r_max > 64 || d_in <= 0 ||
-      d_in % LORA_SHRINK_TILE_K)
+  if (dtype != LORA_BF16 || weight_format < LORA_WFMT_PLAIN || weight_format > LORA_WFMT_INT4 || r_max > 64 ||
+      d_in <= 0 || d_in % LORA_SHRINK_TILE_K)
     return ok();
+  // bytes of one d_in row: x rows are bf16, A rows bf16, FP8 or INT4
+  const int64_t x_row = 2 * (int64_t)d_in;
+  const int64_t a_row = weight_format == LORA_WFMT_PLAIN ? 2 * (int64_t)d_in
+                        : weight_format == LORA_WFMT_FP8_E4M3 ? (int64_t)d_in : (int64_t)d_in / 2;
   if (tile_min_tokens <= 0) tile_min_tokens = LORA_DEFAULT_TILE_MIN_TOKENS;
-  // d_in rows each plan's items read through the compute units: the plain
-  // plan's MFMA items read A once per LORA_SHRINK_MFMA_TOKENS tokens, its
-  // gather items x once per LORA_SHRINK_GATHER_ROWS rows and A once per
+  // rows each plan's items read through the compute units: the plain plan's
+  // MFMA items read A once per LORA_SHRINK_MFMA_TOKENS tokens, its gather
+  // items x once per LORA_SHRINK_GATHER_ROWS rows and A once per
   // LORA_SHRINK_GATHER_TOKENS tokens; tile items read x once and A once per
   // LORA_SHRINK_TILE_TOKENS tokens
   auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
@@ -309,12 +313,12 @@ extern "C" lora_status lora_sgmv_tiled_pays(const int32_t *seg_starts, const int
     const int64_t len = seg_starts[s + 1] - seg_starts[s];
     const int64_t r = host_rank ? host_rank[seg_adapter[s]] : r_max;
     if (!(len >= tile_min_tokens || r >= LORA_TILE_MIN_RANK_SHORT)) continue;
-    const int64_t plain = len >= LORA_DEFAULT_MFMA_MIN_TOKENS
-                              ? len + r * cdiv(len, LORA_SHRINK_MFMA_TOKENS)
-                              : len * cdiv(r, LORA_SHRINK_GATHER_ROWS) + r * cdiv(len, LORA_SHRINK_GATHER_TOKENS);
-    saved += plain - (len + r * cdiv(len, LORA_SHRINK_TILE_TOKENS));
+    const bool mfma = len >= LORA_DEFAULT_MFMA_MIN_TOKENS;
+    const int64_t px = mfma ? len : len * cdiv(r, LORA_SHRINK_GATHER_ROWS);
+    const int64_t pa = r * cdiv(len, mfma ? LORA_SHRINK_MFMA_TOKENS : LORA_SHRINK_GATHER_TOKENS);
+    saved += (px - len) * x_row + (pa - r * cdiv(len, LORA_SHRINK_TILE_TOKENS)) * a_row;
   }
-  *pays = saved * d_in * 2 >= (int64_t)LORA_TILE_PAYS_BYTES;
+  *pays = saved >= (int64_t)LORA_TILE_PAYS_BYTES;
   return ok();
 }
 

@@ -1600,7 +1600,34 @@ __device__ __forceinline__ void tile_sum_slices(const DevW &w, int r, int cnt, i
 // One tile item with RT row tiles (r <= 16 RT <= MAXR).  Buffers: x0..x3
 // (64 x 64 bf16 each) and a0..a3 (MAXR x 64), separate LDS variables so the
 // compiler tells them apart.
-template <int RT, int MAXR>
+// Stage geometry of the A rows for row type W: a stage row is kTileK
+// elements, kArb bytes (128 for bf16, 64 for FP8, 32 for INT4); a wave load
+// covers kArpi rows of kAlpr 16-byte chunks each.
+template <typename W>
+struct TileA {
+  static constexpr int kArb = kTileK * WT<W>::kChunk / 8;
+  static constexpr int kAlpr = kArb / 16;
+  static constexpr int kArpi = 64 / kAlpr;
+  // LDS slot of chunk c of row `row` (an involution, as tile_slot)
+  __device__ static __forceinline__ int slot(int row, int c) { return c ^ (row & (kAlpr - 1)); }
+  // the MFMA A fragment of k-step ks for lane group g: 8 elements as bf16
+  __device__ static __forceinline__ bf16x8_t frag(const uint16_t *ba, int row, int ks, int g) {
+    const char *rb = reinterpret_cast<const char *>(ba) + row * kArb;
+    if constexpr (WT<W>::kChunk == 16) {
+      return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(rb + slot(row, 4 * ks + g) * 16));
+    } else if constexpr (WT<W>::kChunk == 8) {
+      Raw8<W> q;
+      q.u = *reinterpret_cast<const uint2 *>(rb + slot(row, 2 * ks + (g >> 1)) * 16 + (g & 1) * 8);
+      return __builtin_bit_cast(bf16x8_t, raw_bf16(q));
+    } else {
+      Raw8<W> q;
+      q.u = *reinterpret_cast<const uint32_t *>(rb + slot(row, ks) * 16 + g * 4);
+      return __builtin_bit_cast(bf16x8_t, raw_bf16(q));
+    }
+  }
+};
+
+template <typename W, int RT, int MAXR>
 __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, int kb, int ke, int pb,
                                           int slice, int k_splits, int num_perm, int num_tokens,
                                           const int *toks, const uint16_t *__restrict__ x,
@@ -1608,9 +1635,10 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
                                           uint16_t *x1, uint16_t *x2, uint16_t *x3, uint16_t *a0, uint16_t *a1,
                                           uint16_t *a2, uint16_t *a3) {
   static_assert(RT >= 1 && 16 * RT <= MAXR, "row tiles");
+  using TA = TileA<W>;
   constexpr int NS = kTileStages;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane >> 3, lc = lane & 7;  // row of a wave load, LDS slot
+  const int lr = lane >> 3, lc = lane & 7;  // x: row of a wave load, LDS slot
   const bool xact = 16 * wave < cnt;        // this wave's token tile has tokens
   // x rows of this wave's two loads per stage: token rows 16 wave + 8 i + lr
   const char *xp[2];
@@ -1623,14 +1651,15 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
     xrow[i] = row;
     xp[i] = reinterpret_cast<const char *>(x + (ok ? (int64_t)t * w.d_in : 0));
   }
-  // A loads: 2 RT per stage (eight rows each); wave takes loads wave, wave + 4
-  constexpr int NA = 2 * RT;
+  // A loads: NA per stage (kArpi rows each); wave takes loads wave, wave + 4
+  constexpr int NA = (16 * RT + TA::kArpi - 1) / TA::kArpi;
   const int na = (NA > wave ? 1 : 0) + (NA > wave + 4 ? 1 : 0);
+  const int alr = lane / TA::kAlpr, alc = lane % TA::kAlpr;
   const char *ap[2];
   int arow[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int row = 8 * (wave + 4 * u) + lr;
+    const int row = TA::kArpi * (wave + 4 * u) + alr;
     const int rr = row < r ? row : r - 1;
     const char *p = (wave + 4 * u < NA) ? a_row(w, a, rr) : nullptr;
     arow[u] = row;
@@ -1650,11 +1679,14 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
         __builtin_amdgcn_global_load_lds(xp[i] + (int64_t)(k + tile_slot(xrow[i], lc) * 8) * 2,
                                          (lds_void *)(bx + (16 * wave + 8 * i) * kTileK), 16, 0, 0);
     }
+    const int64_t kbytes = (int64_t)k * WT<W>::kChunk / 8;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       if (u < na)
-        __builtin_amdgcn_global_load_lds(ap[u] + (int64_t)(k + tile_slot(arow[u], lc) * 8) * 2,
-                                         (lds_void *)(ba + 8 * (wave + 4 * u) * kTileK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ap[u] + kbytes + TA::slot(arow[u], alc) * 16,
+                                         (lds_void *)(reinterpret_cast<char *>(ba) +
+                                                      TA::kArpi * (wave + 4 * u) * TA::kArb),
+                                         16, 0, 0);
   };
 
   f32x4_t acc[RT];
@@ -1681,9 +1713,7 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
             bf16x8_t, *reinterpret_cast<const uint4 *>(bx + xr * kTileK + tile_slot(xr, ch) * 8));
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int ar = 16 * rt + m;
-          const bf16x8_t af = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4 *>(ba + ar * kTileK + tile_slot(ar, ch) * 8));
+          const bf16x8_t af = TA::frag(ba, 16 * rt + m, ks, g);
           acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, xf, acc[rt], 0, 0, 0);
         }
       }
@@ -1700,7 +1730,9 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
     if (NS > 3 && t0 + 3 < nst) step(std::integral_constant<int, 3 % NS>{}, t0 + 3);
   }
   __syncthreads();  // the next item of this workgroup (none) or the exit: no buffer reuse after this
-  // lane (g, m) of row tile rt holds D[4g + e][m]: row 16 rt + 4g + e of token 16 wave + m
+  // lane (g, m) of row tile rt holds D[4g + e][m]: row 16 rt + 4g + e of token 16 wave + m;
+  // quantized rows: each slice's partial times the row's scale (the scale
+  // factors out of the row sum)
   const int i = 16 * wave + m;
   if (xact && i < cnt) {
     const int t = toks[i];
@@ -1712,25 +1744,30 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 16 * rt + 4 * g + e;
-          if (j < r) dst[j] = acc[rt][e];
+          if (j < r) dst[j] = WT<W>::kScaled ? acc[rt][e] * a_scale<W>(w, a, j) : acc[rt][e];
         }
     }
   }
 }
 
 // Launch 1 of the tiled shrink: tile items (block = slice) and the gather
-// items of the short segments (block = row group).
-template <int MAXR>
+// items of the short segments (block = row group).  W: the row type (bf16,
+// FP8 E4M3 or INT4; activations bf16).
+template <typename W, int MAXR>
 __global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_kernel(
     DevW w, const int32_t *__restrict__ perm, int32_t num_perm, const lora_item *__restrict__ items,
     int32_t num_tokens, int32_t k_splits, int32_t k_slice, const uint16_t *__restrict__ x,
     float *__restrict__ v, float *__restrict__ part) {
+  // uint16_t elements of an A stage buffer: whole wave loads of kArpi rows
+  // (one INT4 load covers 32 rows, more than MAXR = 16)
+  constexpr int kArows = (MAXR + TileA<W>::kArpi - 1) / TileA<W>::kArpi * TileA<W>::kArpi;
+  constexpr int kAe = kArows * TileA<W>::kArb / 2;
   __shared__ __attribute__((aligned(16))) uint16_t x0[kTileTokens * kTileK], x1[kTileTokens * kTileK];
   __shared__ __attribute__((aligned(16))) uint16_t x2[kTileStages > 2 ? kTileTokens * kTileK : 8];
   __shared__ __attribute__((aligned(16))) uint16_t x3[kTileStages > 3 ? kTileTokens * kTileK : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t a0[MAXR * kTileK], a1[MAXR * kTileK];
-  __shared__ __attribute__((aligned(16))) uint16_t a2[kTileStages > 2 ? MAXR * kTileK : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t a3[kTileStages > 3 ? MAXR * kTileK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t a0[kAe], a1[kAe];
+  __shared__ __attribute__((aligned(16))) uint16_t a2[kTileStages > 2 ? kAe : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t a3[kTileStages > 3 ? kAe : 8];
   __shared__ TileSmem sm;
   const lora_item it = items[blockIdx.x];
   int pb, a, cnt, path, blk;
@@ -1758,9 +1795,9 @@ __global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_kernel(
     const int kb = blk * k_slice, ke = min(w.d_in, kb + k_slice);
     if (kb >= ke) return;
     const int nrt = (r + 15) >> 4;
-#define LORA_TILE_CASE(RT)                                                                             \
-  tile_item<RT, MAXR>(w, a, r, cnt, kb, ke, pb, blk, k_splits, num_perm, num_tokens, sm.toks, x, v, part, \
-                      x0, x1, x2, x3, a0, a1, a2, a3)
+#define LORA_TILE_CASE(RT)                                                                                \
+  tile_item<W, RT, MAXR>(w, a, r, cnt, kb, ke, pb, blk, k_splits, num_perm, num_tokens, sm.toks, x, v, part, \
+                         x0, x1, x2, x3, a0, a1, a2, a3)
     if (nrt == 1) LORA_TILE_CASE(1);
     else if constexpr (MAXR >= 32) {
       if (nrt == 2) LORA_TILE_CASE(2);
@@ -1772,8 +1809,8 @@ __global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_kernel(
 #undef LORA_TILE_CASE
   } else {
     const int j0 = blk * kRowGroup;
-    shrink_gemv<uint16_t, uint16_t, kRowGroup, kThreads / 64>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt,
-                                                               num_tokens, x, v, sm);
+    shrink_gemv<uint16_t, W, kRowGroup, kThreads / 64>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt,
+                                                        num_tokens, x, v, sm);
   }
 }
 
@@ -2574,8 +2611,7 @@ extern "C" lora_status lora_sgmv_shrink_tiled(const lora_weights *w, const int32
   if (st != LORA_OK) return st;
   if ((st = check_sgmv_args(token_perm, num_perm, items, num_items, num_tokens, x, v)) != LORA_OK)
     return st;
-  if (w->dtype != LORA_BF16 || w->weight_format != LORA_WFMT_PLAIN)
-    return fail(LORA_EUNSUPPORTED, "the tiled shrink needs bf16 activations and bf16 rows");
+  if (w->dtype != LORA_BF16) return fail(LORA_EUNSUPPORTED, "the tiled shrink needs bf16 activations");
   if (w->r_max > 64) return fail(LORA_EUNSUPPORTED, "the tiled shrink needs r_max <= 64 (got %d)", w->r_max);
   if (w->d_in % LORA_SHRINK_TILE_K)
     return fail(LORA_EUNSUPPORTED, "the tiled shrink needs d_in a multiple of %d (got %d)", LORA_SHRINK_TILE_K,
@@ -2596,15 +2632,21 @@ extern "C" lora_status lora_sgmv_shrink_tiled(const lora_weights *w, const int32
   if (num_items == 0 || num_tokens == 0) return ok();
   float *part = static_cast<float *>(workspace);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
-  if (w->r_max <= 16)
-    hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<16>), dim3(num_items), dim3(kThreads), 0, stream, d, token_perm,
-                       num_perm, items, num_tokens, k_splits, slice, xb, v, part);
-  else if (w->r_max <= 32)
-    hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<32>), dim3(num_items), dim3(kThreads), 0, stream, d, token_perm,
-                       num_perm, items, num_tokens, k_splits, slice, xb, v, part);
-  else
-    hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<64>), dim3(num_items), dim3(kThreads), 0, stream, d, token_perm,
-                       num_perm, items, num_tokens, k_splits, slice, xb, v, part);
+  with_types(w, [&](auto t, auto wt) {
+    using T = decltype(t);
+    using W = decltype(wt);
+    if constexpr (sizeof(T) == 2) {
+      if (w->r_max <= 16)
+        hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<W, 16>), dim3(num_items), dim3(kThreads), 0, stream, d,
+                           token_perm, num_perm, items, num_tokens, k_splits, slice, xb, v, part);
+      else if (w->r_max <= 32)
+        hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<W, 32>), dim3(num_items), dim3(kThreads), 0, stream, d,
+                           token_perm, num_perm, items, num_tokens, k_splits, slice, xb, v, part);
+      else
+        hipLaunchKernelGGL((sgmv_shrink_tiled_kernel<W, 64>), dim3(num_items), dim3(kThreads), 0, stream, d,
+                           token_perm, num_perm, items, num_tokens, k_splits, slice, xb, v, part);
+    }
+  });
   if (k_splits > 1)
     hipLaunchKernelGGL(sgmv_shrink_tiled_reduce_kernel, dim3(num_items), dim3(kThreads), 0, stream, d,
                        token_perm, num_perm, items, num_tokens, k_splits, (const float *)part, v);

@@ -460,10 +460,10 @@ def test_tiled_plan_validation():
 
 def test_tiled_pays_choice():
     """The library prefers the tiled shrink where its tile items save at least
-    24 MiB of compute-unit reads: the prefill and heterogeneous batches and the
-    70B layer's down projection (d_in 28672), not the layer's q projection
-    (d_in 8192: 768 rows x 16 KiB = 12 MiB saved); never for fp32, quantised
-    rows, r_max above 64 or d_in not a multiple of 64."""
+    24 MiB of compute-unit reads: the prefill and heterogeneous batches (bf16,
+    FP8 or INT4 rows) and the 70B layer's down projection (d_in 28672), not
+    the layer's q projection (d_in 8192: 768 A rows x 16 KiB = 12 MiB saved);
+    never for fp32 activations, r_max above 64 or d_in not a multiple of 64."""
     from segmented_gather_gemm_segments_amd import workloads as wl
 
     def pays(p, dtype=B.LORA_BF16, wfmt=B.LORA_WFMT_PLAIN, d_in=None):
@@ -476,7 +476,7 @@ def test_tiled_pays_choice():
     down = wl.layer_projection("down", with_base=False)
     assert pays(pre) and pays(het) and not pays(lay) and pays(down)
     assert not pays(het, dtype=B.LORA_F32)
-    assert not pays(het, wfmt=B.LORA_WFMT_FP8_E4M3)
+    assert pays(het, wfmt=B.LORA_WFMT_FP8_E4M3) and pays(het, wfmt=B.LORA_WFMT_INT4)
     assert not pays(het, d_in=8200)
     # the byte rule: 64 one-token rank-64 segments on d_in 8192 save 64 x (16 - 1) rows x 16 KiB = 15 MiB
     # (no), 128 of them 30 MiB (yes); rank 16 saves nothing on one token (x read 4x vs 1x: 3 rows each)

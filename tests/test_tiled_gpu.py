@@ -42,6 +42,9 @@ def _threads():
 
 
 def ad_of(p):
+    """The problem's adapters in fp64 (quantized rows dequantized exactly)."""
+    if p.wq:
+        return oracle.Adapters.from_quantized(p.wq, p.a_rows, p.a_scales, p.bt_rows, p.bt_scales)
     return oracle.Adapters.from_stacks(p.a_rows, p.bt_rows)
 
 
@@ -143,6 +146,37 @@ def test_tiled_none_ids_and_unused_adapters():
     check(dp, y, v, "none ids")
 
 
+@pytest.mark.parametrize("layout", ["dense", "paged"])
+@pytest.mark.parametrize("wq", ["fp8", "int4"])
+def test_tiled_quantized_rows(wq, layout):
+    """FP8 E4M3 and INT4 rows (dequantised from LDS, row scale on the sums):
+    a mixed batch with every rank class and ranks not a multiple of 16, one
+    and several slices, every policy."""
+    R = runner()
+    lens = [150, 1, 64, 17, 3, 90, 33]
+    p = wl.make_problem(f"tiled_{wq}", lens, [i % 5 for i in range(len(lens))], [8, 24, 40, 64, 13], 2048, 520,
+                        "bf16", 60, wq=wq, paged=layout == "paged", page_rows=16)
+    dp = R.DeviceProblem(p, layout=layout)
+    for name, pol in POLICIES:
+        for ms in (1, 0):
+            y, v = dp.run_sgmv(pol, tiled=True, max_splits=ms)
+            torch.cuda.synchronize()
+            check(dp, y, v, f"{wq}/{layout}/{name}/splits {ms}")
+
+
+@pytest.mark.parametrize("wq", ["fp8", "int4"])
+def test_tiled_hetero_quantized_full_size(wq):
+    """The heterogeneous paged batch with FP8 or INT4 rows, every row and v."""
+    R = runner()
+    p = wl.hetero_paged(wq=wq)
+    dp = R.DeviceProblem(p)
+    assert dp.tiled_pays()
+    say(f"tiled hetero full size, {wq} rows")
+    y, v = dp.run_sgmv(tiled=True)
+    torch.cuda.synchronize()
+    check(dp, y, v, f"hetero tiled {wq}")
+
+
 def test_tiled_errors():
     R = runner()
     lib = B.lib()
@@ -164,7 +198,7 @@ def test_tiled_errors():
     assert lib.lora_sgmv_shrink_tiled(*args, 65, B._dptr(dp.x), B._dptr(v), None, 0, None) == B.LORA_EINVAL
     # 1024 / 64 = 16 units: 17 slices would leave one empty
     assert lib.lora_sgmv_shrink_tiled(*args, 17, B._dptr(dp.x), B._dptr(v), None, 0, None) == B.LORA_EINVAL
-    # fp32 activations are not supported by the tiled shrink
+    # fp32 activations are not supported by the tiled shrink (quantized rows are)
     pf = wl.make_problem("tiled_f32", [20], [0], [16], 256, 256, "f32", 3)
     df = R.DeviceProblem(pf)
     it_f, ks_f, _ = df.plan_tiled()
