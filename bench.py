@@ -108,6 +108,9 @@ def parse():
     ap.add_argument("--serial", action="store_true",
                     help="also time the adapter-serial comparator (one shrink + expand launch "
                          "per adapter sub-batch, same kernels)")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time every kernel warm: K launches on one replica, its operands left in "
+                         "cache by the previous launch (the default timings are all cold)")
     ap.add_argument("--floor", action="store_true",
                     help="only time bare streaming reads and a read-modify-write of given sizes "
                          "and workgroup counts (the device's floors for launches of that size)")
@@ -520,6 +523,9 @@ def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
 
     phases = ["shrink", "expand"] + (["fused"] if mode == "bgmv" else [])
     timed = {k: span(i) for i, k in enumerate(phases)}
+    # warm (--warm): K launches on replica 0 only (operands left in cache by the last)
+    warm = {k: graph_span(torch, stream, [calls[0][i]] * K, 3) if args.warm else float("nan")
+            for i, k in enumerate(phases)}
     flops = {"shrink": acc.shrink_flops(p.ids, p.ranks, p.d_in),
              "expand": acc.expand_flops(p.ids, p.ranks, p.d_out)}
     flops["fused"] = flops["shrink"] + flops["expand"]
@@ -530,6 +536,8 @@ def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
                       "gbs": nbytes[name] / t.mean() / 1e9,
                       "frac_of_peak": nbytes[name] / t.mean() / 1e9 / HBM_PEAK_GBS,
                       "tflops": flops[name] / t.mean() / 1e12}
+        if args.warm:
+            kern[name]["warm_us"] = float(warm[name] * 1e6)
     tokens = int(np.sum(p.ids >= 0))
     dom = "fused" if fused else max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
     kname = f"{mode}_{dom}"
@@ -675,12 +683,16 @@ def run_layer(args, torch):
                                 for _ in range(3)]))
              for k, ph in enumerate(("shrink", "expand"))}
         tb = graph_span(torch, stream, [q["base"]] * 5, 3)
+        tw = ({ph: graph_span(torch, q["lane"], [q["calls"][0][k]] * K, 3) for k, ph in enumerate(("shrink", "expand"))}
+              if args.warm else None)
         p = q["p"]
         per[q["name"]] = {"d_in": p.d_in, "d_out": p.d_out, "replicas": q["n_rep"], "shrink": q["shrink"],
                           "shrink_us": round(t["shrink"] * 1e6, 3),
                           "shrink_gbs": round(q["sb"] / t["shrink"] / 1e9, 1),
                           "expand_us": round(t["expand"] * 1e6, 3),
                           "expand_gbs": round(q["eb"] / t["expand"] / 1e9, 1),
+                          **({"shrink_us_warm": round(tw["shrink"] * 1e6, 3),
+                              "expand_us_warm": round(tw["expand"] * 1e6, 3)} if tw else {}),
                           "base_us_alone": round(tb * 1e6, 2),
                           "base_tflops_alone": round(q["bf"] / tb / 1e12, 1)}
         q["t"] = t
