@@ -261,7 +261,8 @@ lora_status lora_sgmv_expand(const lora_weights *w, const int32_t *token_perm, i
  * runs the products on MFMA.  With more than one slice the items write fp32
  * partial products to a caller-owned workspace and a second launch on the
  * same stream adds each token's partials in slice order (a fixed order:
- * repeated runs are bit-identical).  Shorter segments keep gather items.
+ * repeated runs are bit-identical).  Short low-rank segments keep gather
+ * items.
  *
  * lora_sgmv_plan_tiled: as lora_sgmv_plan's shrink phase, plus d_in (a
  * multiple of LORA_SHRINK_TILE_K) and max_splits (1..LORA_MAX_K_SPLITS; <= 0:

@@ -17,7 +17,12 @@
 //     values hi + lo (two MFMA K-halves): hi = RNE(v), lo = RNE(v - hi) keep
 //     about 16 significant bits of v (relative error at most about 2^-17), far
 //     more than one bf16 (8 bits) but fewer than fp32's 24, so the MFMA and
-//     gather expands agree to rounding, not bit for bit.
+//     gather expands agree to rounding, not bit for bit;
+//   * tiled shrink (long segments, bf16 activations): 64-token tiles of x and
+//     A streamed into LDS by direct global-to-LDS loads, over slices of d_in
+//     whose partial products a second launch adds in slice order.
+// The per-token (decode) mode has the same two paths plus a fused kernel that
+// runs one token's shrink and expand in one workgroup.
 // No floating-point atomics: every output element is produced by one thread
 // and summation orders are fixed, so repeated runs are bit-identical.
 #include <hip/hip_runtime.h>
@@ -1490,21 +1495,24 @@ __global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *
 }
 
 // ----------------------------------------------------------------- tiled shrink
-// Segmented shrink for bf16 activations and bf16 rows in 64-token tiles: an
-// item is up to 64 tokens of one segment and one slice [kb, ke) of d_in.  Its
-// four waves own one 16-token tile each; the tokens' x rows and the adapter's
-// A rows (up to MAXR) stream through LDS in stages of 64 elements (128 bytes,
-// one cache line per row), loaded by global_load_lds_dwordx4 (lane l of a
-// wave's load lands at the load's LDS base + 16 l: eight lanes per row, each
-// wave load covers eight whole lines), so no registers stage them.  Stages
+// Segmented shrink for bf16 activations (bf16, FP8 or INT4 rows) in 64-token
+// tiles: an item is up to 64 tokens of one segment and one slice [kb, ke) of
+// d_in.  Its four waves own one 16-token tile each; the tokens' x rows and the
+// adapter's A rows (up to MAXR) stream through LDS in stages of 64 elements
+// (an x row's stage is 128 bytes, one cache line; an A row's 128, 64 or 32
+// bytes), loaded by global_load_lds_dwordx4 (lane l of a wave's load lands at
+// the load's LDS base + 16 l: eight lanes per x row, each wave load covers
+// eight whole lines), so no registers stage them.  Stages
 // rotate through kTileStages buffers with up to kTileStages - 1 of them in
 // flight; each wave waits only for its own loads of the stage it is about to
 // use, then one barrier makes every wave's share visible.  A rows are read
 // from HBM once per item and shared by the four waves; x rows once.  The
 // chunks of a row are permuted by an XOR of the row index (LDS slot
 // c ^ (row & 7)), so that the eight lanes of an LDS read phase hit eight bank
-// groups.  Rows past the rank and tokens past the item load a row that is
-// loaded anyway (the last valid one); their products are never stored.
+// groups (A rows of FP8 or INT4 codes: c ^ (row & 3) or c ^ (row & 1) over
+// their four or two chunks).  Rows past the rank and tokens past the item
+// load a row that is loaded anyway (the last valid one); their products are
+// never stored.
 constexpr int kTileTokens = LORA_SHRINK_TILE_TOKENS;
 constexpr int kTileK = LORA_SHRINK_TILE_K;
 #ifndef LORA_TILE_STAGES
