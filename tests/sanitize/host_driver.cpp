@@ -2,8 +2,8 @@
 // pool bookkeeping, error reporting), built with g++ under AddressSanitizer
 // and UndefinedBehaviorSanitizer by tests/test_sanitizers.py.  The three HIP
 // runtime calls host.cpp makes are stubbed here with host equivalents: pool
-// storage is host memory in this build, so lora_pool_write_rows copies host to
-// host.  Exits non-zero (or the sanitizers abort) on any failure.
+// storage is host memory under the sanitizers, so lora_pool_write_rows copies
+// host to host.  Exits non-zero (or the sanitizers abort) on any failure.
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>

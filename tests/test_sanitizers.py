@@ -1,8 +1,8 @@
 """The library's host half and the C oracle built under AddressSanitizer and
 UndefinedBehaviorSanitizer (g++ / gcc, CPU only), each driven by a randomised
 program in tests/sanitize/: memory errors, leaks and undefined behaviour abort
-the driver.  host.cpp is the library's own source file; its three HIP runtime
-calls are stubbed by the driver."""
+that program.  host.cpp is the library's own source file; its three HIP runtime
+calls are stubbed by the test program."""
 import os
 import shutil
 import subprocess
