@@ -1,5 +1,7 @@
 """Input generators (determinism, shapes, distributions) and the benchmark's
 algorithmic byte counter (pinned to the page's Llama-3-70B rank-16 table).  CPU only."""
+import os
+
 import numpy as np
 
 from conftest import golden_path
@@ -94,3 +96,15 @@ def test_full_size_configs_shapes():
     assert p.num_tokens == 8192 and np.unique(p.ids).size == 32 and p.num_adapters == 64
     ids = wl.layer_batch_ids()
     assert ids.size == 1280 and np.unique(ids[:256]).size == 256 and np.all(ids[256:] == 0)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode != 0
+    assert "one GPU only" in res.stdout + res.stderr
