@@ -1546,12 +1546,14 @@ __device__ __forceinline__ void wait_vm_n(int n) {  // n wave-uniform, 0..8
   }
 }
 
-// Workgroup barrier without a memory fence: __syncthreads() would first wait
-// for every outstanding global load (the later stages too).  Each wave has
-// already waited for its own loads of the stage the barrier publishes (their
-// LDS writes are complete when the wave's vmcnt drops), and the "memory"
-// clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Workgroup barrier without a global-memory fence: __syncthreads() would first
+// wait for every outstanding global load (the later stages too).  Each wave
+// has already waited for its own loads of the stage the barrier publishes
+// (their LDS writes are complete when the wave's vmcnt drops); the barrier
+// waits for the wave's own LDS reads (lgkmcnt), so no wave can start loading
+// into a buffer another wave is still reading, and the "memory" clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct alignas(16) TileSmem {
   int toks[kTileTokens];
