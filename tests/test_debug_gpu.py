@@ -131,3 +131,46 @@ def test_bad_token_and_plan_item_are_reported():
     bad_items[0, 1] = p.num_adapters           # adapter outside [0, N)
     B.lora_sgmv_shrink(dp.weights, perm_d, bad_items, dp.x, v)
     assert _flags() == B.LORA_DEBUG_BAD_ITEM
+
+
+def test_tiled_shrink_reports_bad_values():
+    """The tiled shrink (tile items, its gather items and the slice reduction)
+    records a bad page, token or plan item like the one-launch kernels, and
+    the rows the bad value does not touch keep their bits."""
+    R = runner()
+    p = wl.make_problem("debug_tiled", [70, 3, 1, 25, 7], [0, 3, 1, 2, 4], [16, 8, 32, 16, 24], 2048, 512,
+                        "bf16", 78)
+    dp = R.DeviceProblem(p, layout="paged")
+    say("debug tiled shrink")
+    B.lora_debug_flags(clear=True)
+    items, ks, ws = dp.plan_tiled(tile_min_tokens=2)
+    host_items = items.cpu().numpy()
+    tile = np.flatnonzero((host_items[:, 2] >> 16) == B.LORA_PATH_TILE)
+    assert ks > 1 and tile.size > 0
+    _, _, _, perm_d = dp.segments()
+
+    def shrink(perm, its):
+        v = dp.new_v()
+        B.lora_sgmv_shrink_tiled(dp.weights, perm, its, ks, dp.x, v, ws)
+        return v
+
+    v_ok = shrink(perm_d, items)
+    assert _flags() == 0
+    a = 0                                     # the 70-token request: tile items
+    saved = int(dp.weights.a_page_table[a, 0])
+    dp.weights.a_page_table[a, 0] = dp.a_pages.shape[0] + 5
+    v = shrink(perm_d, items)
+    assert _flags() == B.LORA_DEBUG_BAD_PAGE
+    other = torch.from_numpy(np.flatnonzero(p.ids != a)).cuda()
+    assert torch.equal(v[other].view(torch.int32), v_ok[other].view(torch.int32))
+    dp.weights.a_page_table[a, 0] = saved
+    assert torch.equal(shrink(perm_d, items).view(torch.int32), v_ok.view(torch.int32))
+    assert _flags() == 0
+    bad_perm = perm_d.clone()
+    bad_perm[0] = p.num_tokens + 3
+    shrink(bad_perm, items)
+    assert _flags() == B.LORA_DEBUG_BAD_TOKEN
+    bad_items = items.clone()
+    bad_items[int(tile[0]), 3] = ks            # a d_in slice past the last
+    shrink(perm_d, bad_items)
+    assert _flags() == B.LORA_DEBUG_BAD_ITEM
