@@ -172,34 +172,41 @@ def cpu_baseline(parts, num_tokens: int, budget_s: float):
     """The oracle as it stands (C, fp64) on a bounded sample of the same
     workload: the first n tokens of the batch through every part of a step
     (one projection, or the seven of the layer), n sized so that the one-thread
-    pass takes about budget_s.  Timed once on one thread and once on all the
-    cores this process may use (the same per-token arithmetic, bit-identical
-    output).  parts: list of (problem, oracle adapters)."""
+    pass takes about budget_s; a batch whose whole pass takes less is passed
+    through repeatedly, about budget_s in all.  Timed once on one thread and
+    once on all the cores this process may use, with the same number of passes
+    (the same per-token arithmetic, bit-identical output).  parts: list of
+    (problem, oracle adapters)."""
     import oracle
 
-    def run(n, threads):
+    def run(n, threads, passes=1):
         used = 1
         t0 = time.perf_counter()
-        for p, ad in parts:
-            out, used = oracle.apply_counted(p.x[:n], p.y[:n], p.ids[:n], ad, threads)
+        for _ in range(passes):
+            for p, ad in parts:
+                out, used = oracle.apply_counted(p.x[:n], p.y[:n], p.ids[:n], ad, threads)
         return time.perf_counter() - t0, used, out
 
     probe = min(8, num_tokens)
     t_probe, _, _ = run(probe, 1)
     per_tok = max(t_probe / probe, 1e-7)
     n = int(min(num_tokens, max(probe, budget_s / per_tok)))
-    t1, _, out1 = run(n, 1)
+    passes = 1
+    if n == num_tokens:
+        passes = int(max(1, min(1000, budget_s // (per_tok * num_tokens))))
+    t1, _, out1 = run(n, 1, passes)
     threads = oracle_threads()
-    tn, used, outn = run(n, threads)
+    tn, used, outn = run(n, threads, passes)
     assert np.array_equal(out1, outn), "threaded oracle differs from the one-thread oracle"
     what = f"the first {n} of {num_tokens} tokens" if n < num_tokens else f"all {num_tokens} tokens"
     if len(parts) > 1:
         what += f" through all {len(parts)} projections"
-    return {"value": round(n / tn, 2), "unit": "delta tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{what}, one pass, {tn:.2f} s on {used} threads (OpenMP over tokens)",
+    what += ", one pass" if passes == 1 else f", {passes} passes"
+    return {"value": round(n * passes / tn, 2), "unit": "delta tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{what}, {tn:.2f} s on {used} threads (OpenMP over tokens)",
             "affinity_cores": len(os.sched_getaffinity(0)),
-            "single_thread": {"value": round(n / t1, 2), "unit": "delta tokens/s", "cores": 1,
-                              "sample": f"{what}, one pass, {t1:.2f} s"}}
+            "single_thread": {"value": round(n * passes / t1, 2), "unit": "delta tokens/s", "cores": 1,
+                              "sample": f"{what}, {t1:.2f} s"}}
 
 
 def graph_span(torch, stream, fns, reps: int = 3, best: bool = False) -> float:
@@ -767,22 +774,30 @@ def run_floor(args, torch):
     from segmented_gather_gemm_segments_amd import binding as B
     stream = torch.cuda.Stream()
     K = args.steps
-    rows = [("empty launch (256 workgroups x 16 B)", 16, 256, 256),
-            ("17 MB read, 2048 workgroups x 256 threads", 17 * 10**6 // 2048 // 16 * 16, 2048, 256),
-            ("36 MB read, 2048 workgroups x 256 threads", 36 * 10**6 // 2048 // 16 * 16, 2048, 256),
-            ("36 MB read, 256 workgroups x 512 threads", 36 * 10**6 // 256 // 16 * 16, 256, 512),
-            ("64 MB read, 2048 workgroups x 256 threads", 64 * 10**6 // 2048 // 16 * 16, 2048, 256),
-            ("256 MB read, 4096 workgroups x 256 threads", 256 * 10**6 // 4096 // 16 * 16, 4096, 256),
-            ("256 workgroups x 34 rows of 8 KiB (71 MB, the decode shape, rows distinct)", 34 * 8192, 256, 512),
-            ("111 workgroups x 34 rows of 8 KiB (31 MB)", 34 * 8192, 111, 512)]
+    rows = [("empty launch (256 workgroups x 16 B)", 16, 256, 256, False),
+            ("17 MB read, 2048 workgroups x 256 threads", 17 * 10**6 // 2048 // 16 * 16, 2048, 256, False),
+            ("36 MB read, 2048 workgroups x 256 threads", 36 * 10**6 // 2048 // 16 * 16, 2048, 256, False),
+            ("36 MB read, 2048 workgroups x 256 threads, non-temporal loads",
+             36 * 10**6 // 2048 // 16 * 16, 2048, 256, True),
+            ("36 MB read, 256 workgroups x 512 threads", 36 * 10**6 // 256 // 16 * 16, 256, 512, False),
+            ("64 MB read, 2048 workgroups x 256 threads", 64 * 10**6 // 2048 // 16 * 16, 2048, 256, False),
+            ("96 MB read, 2048 workgroups x 256 threads", 96 * 10**6 // 2048 // 16 * 16, 2048, 256, False),
+            ("96 MB read, 2048 workgroups x 256 threads, non-temporal loads",
+             96 * 10**6 // 2048 // 16 * 16, 2048, 256, True),
+            ("256 MB read, 4096 workgroups x 256 threads", 256 * 10**6 // 4096 // 16 * 16, 4096, 256, False),
+            ("256 MB read, 4096 workgroups x 256 threads, non-temporal loads",
+             256 * 10**6 // 4096 // 16 * 16, 4096, 256, True),
+            ("256 workgroups x 34 rows of 8 KiB (71 MB, the decode shape, rows distinct)", 34 * 8192, 256, 512,
+             False),
+            ("111 workgroups x 34 rows of 8 KiB (31 MB)", 34 * 8192, 111, 512, False)]
     sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
     table = []
-    for label, bpg, groups, threads in rows:
+    for label, bpg, groups, threads, nt in rows:
         size = bpg * groups
         n_rep = int(min(64, max(2, np.ceil(2 * LLC_BYTES / max(size, 1)))))
         buf = torch.empty(size * n_rep // 2 + 16, dtype=torch.int16, device="cuda")
         buf.fill_(1)
-        fns = [B.prepare_probe_stream_read(buf[(i * size) // 2:], bpg, groups, threads, sink, stream)
+        fns = [B.prepare_probe_stream_read(buf[(i * size) // 2:], bpg, groups, threads, sink, stream, nt)
                for i in range(n_rep)]
         t = graph_span(torch, stream, [fns[i % n_rep] for i in range(K)], 3)
         table.append({"launch": label, "bytes": size, "us": round(t * 1e6, 3),

@@ -392,8 +392,8 @@ lora_status lora_bgmv_fused(const lora_weights *w, const int32_t *token_adapter,
  * so x crosses the fabric once for all projections, and one launch replaces
  * num_proj.  Per projection the arithmetic is lora_bgmv_fused's (token-major),
  * so the bits equal those of separate lora_bgmv_fused calls.  It pays where
- * launches dominate (small decode batches: 2.3x for q/k/v of a 70B layer at
- * 32 tokens); at 256 tokens separate launches balance better (0.93x).
+ * launches dominate (small decode batches: 2.6x for q/k/v of a 70B layer at
+ * 32 tokens); at 256 tokens separate launches balance better (0.97x).
  *   w [num_proj]  host array of descriptors with equal dtype, weight_format,
  *                 d_in and num_adapters (their d_out may differ); num_proj in 1..4
  *   v [num_proj]  host array of device pointers (entries may be NULL), or NULL
@@ -570,10 +570,12 @@ lora_status lora_debug_flags(uint32_t *flags, int32_t clear);
  * [groups] in practice.  The benchmark times it to show the floor that
  * launches of a given size and workgroup count cannot beat on the device.
  * src 16-byte aligned with groups * bytes_per_group readable bytes;
- * bytes_per_group a multiple of 16; threads a multiple of 64 in 64..1024.
+ * bytes_per_group a multiple of 16; threads a multiple of 64 in 64..1024;
+ * nontemporal 1: the loads carry the non-temporal hint (0: plain loads).
  * Errors: LORA_EINVAL, LORA_EHIP. */
 lora_status lora_probe_stream_read(const void *src, int64_t bytes_per_group, int32_t groups,
-                                   int32_t threads, uint32_t *sink, hipStream_t stream);
+                                   int32_t threads, int32_t nontemporal, uint32_t *sink,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -102,7 +102,7 @@ EXPORTS = {
     "lora_base_gemm": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_int64, _P], _I32),
     "lora_base_gemm_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
     "lora_base_gemm_noalloc": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
-    "lora_probe_stream_read": ([_P, ctypes.c_int64, _I32, _I32, _P, _P], _I32),
+    "lora_probe_stream_read": ([_P, ctypes.c_int64, _I32, _I32, _I32, _P, _P], _I32),
     "lora_debug_flags": ([_P, _I32], _I32),
 }
 LORA_DEBUG_BAD_PAGE, LORA_DEBUG_BAD_ADAPTER, LORA_DEBUG_BAD_RANK = 1, 2, 4
@@ -538,12 +538,14 @@ class Cache:
             pass
 
 
-def prepare_probe_stream_read(src, bytes_per_group: int, groups: int, threads: int, sink, stream=None):
-    """Prepared bare streaming read (a measurement floor, not the delta path)."""
+def prepare_probe_stream_read(src, bytes_per_group: int, groups: int, threads: int, sink, stream=None,
+                              nontemporal: bool = False):
+    """Prepared bare streaming read (a measurement floor, not the delta path);
+    nontemporal: loads with the non-temporal hint."""
     assert src.numel() * src.element_size() >= bytes_per_group * groups
     assert sink.numel() * sink.element_size() >= 4 * groups
-    return Prepared("lora_probe_stream_read", (_dptr(src), int(bytes_per_group), int(groups),
-                                               int(threads), _dptr(sink), _stream(stream)), (src, sink))
+    return Prepared("lora_probe_stream_read", (_dptr(src), int(bytes_per_group), int(groups), int(threads),
+                                               int(bool(nontemporal)), _dptr(sink), _stream(stream)), (src, sink))
 
 
 # ---------------------------------------------------------------- prepared launches

@@ -446,18 +446,39 @@ __device__ __forceinline__ float raw_elem(const Raw8<float> &r, int e) {
 template <> struct Raw8<Fp8> { uint2 u; };
 template <> struct Raw8<Int4> { uint32_t u; };
 
-// Loads of one 8-element weight chunk from a byte address.
+// Loads of one 8-element weight chunk from a byte address.  ST: the load
+// carries the non-temporal hint, for rows that no later load of the launch
+// reads again (on this device a stream of such loads moves 10-15 % more bytes
+// per second than plain loads once it spans ~100 MB or more; where other
+// items read the same rows later, the hint costs more than it saves).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <bool ST = false>
 __device__ __forceinline__ void wload(Raw8<uint16_t> &r, const char *p) {
-  r.u = *reinterpret_cast<const uint4 *>(p);
+  if constexpr (ST) {
+    const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    r.u = make_uint4(q.x, q.y, q.z, q.w);
+  } else {
+    r.u = *reinterpret_cast<const uint4 *>(p);
+  }
 }
+template <bool ST = false>
 __device__ __forceinline__ void wload(Raw8<float> &r, const char *p) {
   raw_load(r, reinterpret_cast<const float *>(p));
 }
+template <bool ST = false>
 __device__ __forceinline__ void wload(Raw8<Fp8> &r, const char *p) {
-  r.u = *reinterpret_cast<const uint2 *>(p);
+  if constexpr (ST) {
+    const u32x2_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    r.u = make_uint2(q.x, q.y);
+  } else {
+    r.u = *reinterpret_cast<const uint2 *>(p);
+  }
 }
+template <bool ST = false>
 __device__ __forceinline__ void wload(Raw8<Int4> &r, const char *p) {
-  r.u = *reinterpret_cast<const uint32_t *>(p);
+  if constexpr (ST) r.u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+  else r.u = *reinterpret_cast<const uint32_t *>(p);
 }
 __device__ __forceinline__ void raw_zero(Raw8<Fp8> &r) { r.u = make_uint2(0, 0); }
 __device__ __forceinline__ void raw_zero(Raw8<Int4> &r) { r.u = 0; }
@@ -574,7 +595,7 @@ struct alignas(16) ShrinkSmem {
 // reduce-scattered over the wave and the NW wave results summed in wave order,
 // so a token's result does not depend on TG or on which other tokens share the
 // tile (for a given NW).
-template <typename T, typename W, int TG, int RB, int NW, typename SM>
+template <typename T, typename W, int TG, int RB, int NW, bool ST, typename SM>
 __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, int nr, const int *toks, int g0,
                                  int ntok, int num_tokens, const T *__restrict__ x,
                                  float *__restrict__ v, SM &sm) {
@@ -610,11 +631,11 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
 #pragma unroll
     for (int t = 0; t < TG; ++t) raw_load(xa[t], xr[t] + c0);
 #pragma unroll
-    for (int jj = 0; jj < RB; ++jj) wload(aa[jj], ar[jj] + wofs<W>(c0));
+    for (int jj = 0; jj < RB; ++jj) wload<ST>(aa[jj], ar[jj] + wofs<W>(c0));
 #pragma unroll
     for (int t = 0; t < TG; ++t) raw_load(xb[t], xr[t] + c1);
 #pragma unroll
-    for (int jj = 0; jj < RB; ++jj) wload(ab[jj], ar[jj] + wofs<W>(c1));
+    for (int jj = 0; jj < RB; ++jj) wload<ST>(ab[jj], ar[jj] + wofs<W>(c1));
     float xv[TG][8];
     if (one) {
 #pragma unroll
@@ -661,17 +682,19 @@ __device__ __forceinline__ void shrink_rows_tile(const DevW &w, int a, int j0, i
 }
 
 // Gather/GEMV shrink of tokens toks[0..cnt) of adapter a over its row group
-// [j0, j0 + nr), nr <= RB: groups of up to 4 tokens, one group of 1 to 3 at the end.
-template <typename T, typename W, int RB, int NW, typename SM>
+// [j0, j0 + nr), nr <= RB: groups of up to 4 tokens, the last of 1 to 4.
+// LAST: the last group reads the rows non-temporally (the item is the only
+// reader of its row group, and that group its last).
+template <typename T, typename W, int RB, int NW, bool LAST, typename SM>
 __device__ __forceinline__ void shrink_gemv(const DevW &w, int a, int j0, int nr, const int *toks, int cnt,
                             int num_tokens, const T *__restrict__ x, float *__restrict__ v, SM &sm) {
   int g0 = 0;
-  for (; g0 + 4 <= cnt; g0 += 4)
-    shrink_rows_tile<T, W, 4, RB, NW>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
+  for (; g0 + 4 < cnt; g0 += 4)
+    shrink_rows_tile<T, W, 4, RB, NW, false>(w, a, j0, nr, toks, g0, 4, num_tokens, x, v, sm);
   const int rest = cnt - g0;
-  if (rest == 1) shrink_rows_tile<T, W, 1, RB, NW>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
-  else if (rest == 2) shrink_rows_tile<T, W, 2, RB, NW>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
-  else if (rest == 3) shrink_rows_tile<T, W, 4, RB, NW>(w, a, j0, nr, toks, g0, 3, num_tokens, x, v, sm);
+  if (rest == 1) shrink_rows_tile<T, W, 1, RB, NW, LAST>(w, a, j0, nr, toks, g0, 1, num_tokens, x, v, sm);
+  else if (rest == 2) shrink_rows_tile<T, W, 2, RB, NW, LAST>(w, a, j0, nr, toks, g0, 2, num_tokens, x, v, sm);
+  else if (rest >= 3) shrink_rows_tile<T, W, 4, RB, NW, LAST>(w, a, j0, nr, toks, g0, rest, num_tokens, x, v, sm);
 }
 
 // One MFMA shrink tile: 16 tokens (this lane's token row xp, or a safe row)
@@ -807,7 +830,7 @@ struct alignas(16) ExpandSmem {
 // (16-byte loads, all issued before the first FMA); the y chunks of the tile's
 // tokens are fetched at the start; v is read as uniform values.  Every output
 // is y + sum_j v_j b_j summed in ascending j, independent of TG.
-template <typename T, typename W, int TG, int NT>
+template <typename T, typename W, int TG, int NT, bool ST = false>
 __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, int cb, const int *toks, int g0,
                                  int ntok, int num_tokens, const float *__restrict__ v,
                                  T *__restrict__ y) {
@@ -842,7 +865,7 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
     b_rows16<W>(w, a, j0, r, col, safe, rp, lsc);
     Raw8<W> braw[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wload(braw[i], rp[i]);
+    for (int i = 0; i < 16; ++i) wload<ST>(braw[i], rp[i]);
     // v[tok][j0 .. j0+16): the same address in every lane, read with 16-byte
     // vector loads (one request per wave) where r_max keeps them aligned
     float vj[TG][16];
@@ -894,13 +917,18 @@ __device__ __forceinline__ void expand_cols_tile(const DevW &w, int a, int r, in
   }
 }
 
-template <typename T, typename W, int NT>
+// Gather expand of tokens toks[0..cnt) over column block cb: groups of up to
+// 4 tokens, the last of 1 to 4.  LAST: a one-token item reads its B block
+// non-temporally (a one-token segment, or the last item of a segment in the
+// heaviest-first plan order: no later item reads that block; the hint on the
+// last items of longer segments measured no gain).
+template <typename T, typename W, int NT, bool LAST = false>
 __device__ __forceinline__ void expand_gemv(const DevW &w, int a, int r, int cb, const int *toks, int cnt,
                             int num_tokens, const float *__restrict__ v, T *__restrict__ y) {
   int g0 = 0;
   for (; g0 + 4 <= cnt; g0 += 4) expand_cols_tile<T, W, 4, NT>(w, a, r, cb, toks, g0, 4, num_tokens, v, y);
   const int rest = cnt - g0;
-  if (rest == 1) expand_cols_tile<T, W, 1, NT>(w, a, r, cb, toks, g0, 1, num_tokens, v, y);
+  if (rest == 1) expand_cols_tile<T, W, 1, NT, LAST>(w, a, r, cb, toks, g0, 1, num_tokens, v, y);
   else if (rest == 2) expand_cols_tile<T, W, 2, NT>(w, a, r, cb, toks, g0, 2, num_tokens, v, y);
   else if (rest == 3) expand_cols_tile<T, W, 4, NT>(w, a, r, cb, toks, g0, 3, num_tokens, v, y);
 }
@@ -1491,7 +1519,7 @@ __global__ __launch_bounds__(NT) void sgmv_shrink_kernel(DevW w, const int32_t *
   if (path == LORA_PATH_MFMA)
     shrink_mfma<T, W, NW>(w, a, r, sm.toks, cnt, num_tokens, x, v, sm);
   else
-    shrink_gemv<T, W, kRowGroup, NW>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
+    shrink_gemv<T, W, kRowGroup, NW, true>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt, num_tokens, x, v, sm);
 }
 
 // ----------------------------------------------------------------- tiled shrink
@@ -1561,6 +1589,11 @@ struct alignas(16) TileSmem {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+// Cache-policy operand of the tile loads (2 = non-temporal): the x rows of a
+// tile item are read by that item alone; the A rows are read again by the
+// segment's other token tiles.
+constexpr int kTileAPolicy = 0;
+constexpr int kTileXPolicy = 2;
 
 // v rows of the tokens toks[0..cnt) (token_perm entries) of a chunk = the sum of their k_splits
 // partials part[slice][pb + i][j], added in slice order.  A thread takes four
@@ -1687,7 +1720,8 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_global_load_lds(xp[i] + (int64_t)(k + tile_slot(xrow[i], lc) * 8) * 2,
-                                         (lds_void *)(bx + (16 * wave + 8 * i) * kTileK), 16, 0, 0);
+                                         (lds_void *)(bx + (16 * wave + 8 * i) * kTileK), 16, 0,
+                                         kTileXPolicy);
     }
     const int64_t kbytes = (int64_t)k * WT<W>::kChunk / 8;
 #pragma unroll
@@ -1696,7 +1730,7 @@ __device__ __forceinline__ void tile_item(const DevW &w, int a, int r, int cnt, 
         __builtin_amdgcn_global_load_lds(ap[u] + kbytes + TA::slot(arow[u], alc) * 16,
                                          (lds_void *)(reinterpret_cast<char *>(ba) +
                                                       TA::kArpi * (wave + 4 * u) * TA::kArb),
-                                         16, 0, 0);
+                                         16, 0, kTileAPolicy);
   };
 
   f32x4_t acc[RT];
@@ -1819,7 +1853,7 @@ __global__ __launch_bounds__(kThreads) void sgmv_shrink_tiled_kernel(
 #undef LORA_TILE_CASE
   } else {
     const int j0 = blk * kRowGroup;
-    shrink_gemv<uint16_t, W, kRowGroup, kThreads / 64>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt,
+    shrink_gemv<uint16_t, W, kRowGroup, kThreads / 64, true>(w, a, j0, min(kRowGroup, r - j0), sm.toks, cnt,
                                                         num_tokens, x, v, sm);
   }
 }
@@ -1876,7 +1910,7 @@ void sgmv_expand_kernel(DevW w, const int32_t *__restrict__ perm,
     else expand_mfma<T, W>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y, sm);
   }
   else
-    expand_gemv<T, W, kThreads>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
+    expand_gemv<T, W, kThreads, true>(w, a, r, blk, sm.toks, cnt, num_tokens, v, y);
 }
 
 // Workgroup b of a launch runs on XCD b % 8 (the dispatcher deals workgroups to
@@ -1942,7 +1976,7 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
     if (j0 >= r) return;
     if (threadIdx.x == 0) sm.toks[0] = t;
     __syncthreads();
-    shrink_gemv<T, W, RB, NW>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
+    shrink_gemv<T, W, RB, NW, false>(w, a, j0, min(RB, r - j0), sm.toks, 1, num_tokens, x, v, sm);
   } else {
     const int a = u;
     const int r = adapter_rank(w, a);
@@ -1952,7 +1986,7 @@ __global__ __launch_bounds__(kThreads) void bgmv_shrink_kernel(DevW w, const int
       const int n = gather_adapter_tokens<kThreads, CH>(ids, num_tokens, c0, a, sm.toks, wave_cnt,
                                                           w.num_adapters);
       if (n > 0) used_rank(w, a);
-      if (n > 0) shrink_gemv<T, W, RB, NW>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
+      if (n > 0) shrink_gemv<T, W, RB, NW, false>(w, a, j0, min(RB, r - j0), sm.toks, n, num_tokens, x, v, sm);
       __syncthreads();
     }
   }
@@ -2050,7 +2084,10 @@ __device__ __forceinline__ float a_scale_any(const DevW &w, int a, int j, bool u
 // id or the rank before these loads are consumed -- a token without a valid
 // adapter takes rank 0 and safe addresses, and its first pass runs on them
 // with every store suppressed -- so the compiler cannot sink the loads past
-// the id or rank wait.
+// the id or rank wait.  The A and B^T rows are read with the non-temporal
+// hint: the tokens that share an adapter run together on one XCD, so their
+// reads meet in its L2 while the lines are still there (12.6 -> 11.9 us on a
+// 256-token decode batch).
 template <typename T, typename W, bool AL>
 __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restrict__ ids, int t, int cb,
                                            int block_cols, const T *__restrict__ x,
@@ -2086,9 +2123,9 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
     a_rows16_sc<W, AL>(w, a, 0, rs, kc0, safe_a, ap0, asc);
     b_rows16<W, AL>(w, a, 0, rs, colc0, safe_b, bp0, lsc_b0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wload(a0[i], ap0[i]);
+    for (int i = 0; i < 16; ++i) wload<true>(a0[i], ap0[i]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wload(b0[i], bp0[i]);
+    for (int i = 0; i < 16; ++i) wload<true>(b0[i], bp0[i]);
   } else if constexpr (WT<W>::kScaled) {
     asc = a_scale_any<W>(w, a, tid, tid < rs);
   }
@@ -2122,7 +2159,7 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
     const char *ap[16];
     a_rows16<W, AL>(w, a, jc, r, kc, safe_a, ap);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
+    for (int i = 0; i < 16; ++i) wload<true>(araw[i], ap[i]);
     fma_pass(acc, xraw, araw, kin);
   };
   // reduce the 16 row sums over the workgroup: reduce-scatter in each wave,
@@ -2157,7 +2194,7 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
       const char *ap[16];
       a_rows16<W, AL>(w, a, 0, r, kc0, safe_a, ap);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) wload(araw[i], ap[i]);
+      for (int i = 0; i < 16; ++i) wload<true>(araw[i], ap[i]);
     }
     fma_pass(acc, x0, araw, tid * 8 < w.d_in);
     for (int k0 = kFusedPass; k0 < w.d_in; k0 += kFusedPass) load_pass(acc, 0, k0);
@@ -2194,7 +2231,7 @@ __device__ __forceinline__ void fused_unit(const DevW &w, const int32_t *__restr
         const char *bp[16];
         b_rows16<W, AL>(w, a, j0, r, colc, safe_b, bp, lsc);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) wload(braw[i], bp[i]);
+        for (int i = 0; i < 16; ++i) wload<true>(braw[i], bp[i]);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {

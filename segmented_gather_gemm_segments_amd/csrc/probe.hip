@@ -13,9 +13,20 @@ using namespace lora;
 namespace {
 
 // Workgroup g reads the 16-byte chunks [g n16, (g + 1) n16) of src, eight
-// loads in flight per thread, and folds them into one word that is stored
-// only in the (practically impossible) case that it equals a magic value, so
-// the loads stay live while nothing is written.
+// loads in flight per thread (NT: with the non-temporal hint), and folds them
+// into one word that is stored only in the (practically impossible) case that
+// it equals a magic value, so the loads stay live while nothing is written.
+typedef uint32_t probe_u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 probe_load(const uint4 *p) {
+  if constexpr (NT) {
+    const probe_u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const probe_u32x4 *>(p));
+    return make_uint4(q.x, q.y, q.z, q.w);
+  } else {
+    return *p;
+  }
+}
+template <bool NT>
 __global__ __launch_bounds__(1024) void stream_read_kernel(const uint4 *__restrict__ src, int64_t n16,
                                                            uint32_t *__restrict__ sink) {
   const uint4 *p = src + (int64_t)blockIdx.x * n16;
@@ -25,12 +36,12 @@ __global__ __launch_bounds__(1024) void stream_read_kernel(const uint4 *__restri
   for (; i + 7 * (int64_t)nt < n16; i += 8 * (int64_t)nt) {
     uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * nt];
+    for (int u = 0; u < 8; ++u) v[u] = probe_load<NT>(p + i + u * nt);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += nt) {
-    const uint4 v = p[i];
+    const uint4 v = probe_load<NT>(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
@@ -39,7 +50,8 @@ __global__ __launch_bounds__(1024) void stream_read_kernel(const uint4 *__restri
 }  // namespace
 
 extern "C" lora_status lora_probe_stream_read(const void *src, int64_t bytes_per_group, int32_t groups,
-                                              int32_t threads, uint32_t *sink, hipStream_t stream) {
+                                              int32_t threads, int32_t nontemporal, uint32_t *sink,
+                                              hipStream_t stream) {
   if (groups < 0 || bytes_per_group < 0) return fail(LORA_EINVAL, "negative size");
   if (groups == 0 || bytes_per_group == 0) return ok();
   if (!src || !sink) return fail(LORA_EINVAL, "null pointer");
@@ -47,8 +59,13 @@ extern "C" lora_status lora_probe_stream_read(const void *src, int64_t bytes_per
     return fail(LORA_EINVAL, "src and bytes_per_group must be multiples of 16 bytes");
   if (threads < 64 || threads > 1024 || threads % 64)
     return fail(LORA_EINVAL, "threads must be a multiple of 64 in 64..1024");
-  hipLaunchKernelGGL(stream_read_kernel, dim3(groups), dim3(threads), 0, stream, (const uint4 *)src,
-                     bytes_per_group / 16, sink);
+  if (nontemporal != 0 && nontemporal != 1) return fail(LORA_EINVAL, "nontemporal must be 0 or 1");
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(groups), dim3(threads), 0, stream, (const uint4 *)src,
+                       bytes_per_group / 16, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(groups), dim3(threads), 0, stream, (const uint4 *)src,
+                       bytes_per_group / 16, sink);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   return ok();
