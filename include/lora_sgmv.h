@@ -135,8 +135,12 @@ lora_status lora_segments_build(const int32_t *token_adapter, int32_t num_tokens
  *   shrink, MFMA path: up to LORA_SHRINK_MFMA_TOKENS tokens x every row (block 0);
  *   expand, gather path: up to LORA_EXPAND_GATHER_TOKENS tokens x one block of
  *     LORA_EXPAND_GATHER_COLS columns of y;
- *   expand, MFMA path: up to LORA_EXPAND_MFMA_TOKENS tokens x one block of
- *     LORA_EXPAND_MFMA_COLS columns.
+ *   expand, MFMA path: up to 64 tokens x one block of LORA_EXPAND_MFMA_COLS
+ *     columns; up to LORA_EXPAND_MFMA_TOKENS (128) tokens for output widths
+ *     near 8192 columns (a width takes the choice measured on MI355X for the
+ *     nearest of 1024, 4096, 8192, 14336 and 28672 columns; 128 ran faster
+ *     only at 8192), and only while the plan then still holds at least
+ *     LORA_EXPAND_LONG_TILE_MIN_ITEMS MFMA items.
  * A shrink plan depends on the adapters' ranks (host_rank, or r_max for every
  * adapter when host_rank is NULL) but not on d_in; an expand plan depends on
  * d_out but not on the ranks.  A plan stays valid for every projection with
@@ -163,9 +167,10 @@ typedef struct {
 #define LORA_SHRINK_GATHER_ROWS 4
 #define LORA_SHRINK_MFMA_TOKENS 16
 #define LORA_EXPAND_GATHER_TOKENS 4
-#define LORA_EXPAND_MFMA_TOKENS 64
+#define LORA_EXPAND_MFMA_TOKENS 128
 #define LORA_EXPAND_GATHER_COLS 2048
 #define LORA_EXPAND_MFMA_COLS 256
+#define LORA_EXPAND_LONG_TILE_MIN_ITEMS 256   /* one per compute unit of an MI355X */
 
 /* Builds the plan for `phase` from the host copies of segment_build's output.
  *   host_rank      shrink: host [num_adapters] ranks (1..r_max), or NULL (every

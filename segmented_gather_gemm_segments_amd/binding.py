@@ -28,7 +28,8 @@ LORA_PATH_AUTO, LORA_PATH_GATHER, LORA_PATH_MFMA = 0, 1, 2
 LORA_BGMV_AUTO, LORA_BGMV_TOKEN_MAJOR, LORA_BGMV_ADAPTER_MAJOR = 0, 1, 2
 LORA_DEFAULT_MFMA_MIN_TOKENS = 16
 LORA_SHRINK_GATHER_TOKENS, LORA_SHRINK_GATHER_ROWS, LORA_SHRINK_MFMA_TOKENS = 4, 4, 16
-LORA_EXPAND_GATHER_TOKENS, LORA_EXPAND_MFMA_TOKENS = 4, 64
+LORA_EXPAND_GATHER_TOKENS, LORA_EXPAND_MFMA_TOKENS = 4, 128
+LORA_EXPAND_LONG_TILE_MIN_ITEMS = 256
 LORA_EXPAND_GATHER_COLS, LORA_EXPAND_MFMA_COLS = 2048, 256
 LORA_PATH_TILE = 3
 LORA_SHRINK_TILE_TOKENS, LORA_SHRINK_TILE_K, LORA_SHRINK_TILE_ITEM_BYTES = 64, 64, 262144

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -122,6 +123,22 @@ std::vector<lora_item> device_order(std::vector<PlanItem> &plan) {
 
 }  // namespace
 
+// MFMA expand token tile by output width, measured on MI355X with the
+// batches of the benchmark (heterogeneous ranks, prefill, the 70B layer's
+// projections): 128-token items ran 4-8 % faster at 8192 columns and 1.5-2 %
+// slower (or, at 1024 columns with too few items, much slower) at the other
+// widths.  A width takes the choice of the nearest measured one.
+struct ExpandTile {
+  int32_t cols, tokens;
+};
+static const ExpandTile kExpandTileByWidth[] = {{1024, 64}, {4096, 64}, {8192, 128}, {14336, 64}, {28672, 64}};
+static int32_t expand_tile_by_width(int32_t d_out) {
+  const ExpandTile *best = &kExpandTileByWidth[0];
+  for (const ExpandTile &e : kExpandTileByWidth)
+    if (std::abs((int64_t)d_out - e.cols) < std::abs((int64_t)d_out - best->cols)) best = &e;
+  return best->tokens;
+}
+
 extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
                                       const int32_t *seg_adapter, int32_t num_segments,
                                       int32_t num_adapters, const int32_t *host_rank, int32_t dim,
@@ -155,12 +172,28 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
                     dim);
     }
   }
+  auto is_mfma = [&](int32_t len) {
+    return path_policy == LORA_PATH_MFMA || (path_policy == LORA_PATH_AUTO && len >= mfma_min_tokens);
+  };
+  // Token tile of the expand's MFMA items: LORA_EXPAND_MFMA_TOKENS (two
+  // 64-token passes in one workgroup) where the output width's nearest entry
+  // of kExpandTileByWidth says so and such items still number at least
+  // LORA_EXPAND_LONG_TILE_MIN_ITEMS; 64 tokens otherwise.
+  int32_t expand_mfma_step = 64;
+  if (phase == LORA_PHASE_EXPAND && expand_tile_by_width(dim) == LORA_EXPAND_MFMA_TOKENS) {
+    const int64_t nblk = (dim + LORA_EXPAND_MFMA_COLS - 1) / LORA_EXPAND_MFMA_COLS;
+    int64_t long_items = 0;
+    for (int32_t s = 0; s < num_segments; ++s) {
+      const int32_t len = seg_starts[s + 1] - seg_starts[s];
+      if (is_mfma(len)) long_items += (len + LORA_EXPAND_MFMA_TOKENS - 1) / LORA_EXPAND_MFMA_TOKENS * nblk;
+    }
+    if (long_items >= LORA_EXPAND_LONG_TILE_MIN_ITEMS) expand_mfma_step = LORA_EXPAND_MFMA_TOKENS;
+  }
   std::vector<PlanItem> plan;
   for (int32_t s = 0; s < num_segments; ++s) {
     const int32_t begin = seg_starts[s], len = seg_starts[s + 1] - seg_starts[s];
     const int32_t a = seg_adapter[s];
-    const bool mfma = path_policy == LORA_PATH_MFMA ||
-                      (path_policy == LORA_PATH_AUTO && len >= mfma_min_tokens);
+    const bool mfma = is_mfma(len);
     const int32_t path = mfma ? LORA_PATH_MFMA : LORA_PATH_GATHER;
     if (phase == LORA_PHASE_SHRINK) {
       const int32_t r = host_rank ? host_rank[a] : dim;
@@ -177,7 +210,7 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
         }
       }
     } else {
-      const int32_t step = mfma ? LORA_EXPAND_MFMA_TOKENS : LORA_EXPAND_GATHER_TOKENS;
+      const int32_t step = mfma ? expand_mfma_step : LORA_EXPAND_GATHER_TOKENS;
       const int32_t cols = mfma ? LORA_EXPAND_MFMA_COLS : LORA_EXPAND_GATHER_COLS;
       const int32_t nblk = (dim + cols - 1) / cols;
       for (int32_t m0 = 0; m0 < len; m0 += step) {

@@ -112,6 +112,7 @@ def _coverage(items, starts, adapters, ranks, dim, phase):
                 assert j0 < r                                # no empty row group is planned
             cov[pb:pb + cnt, j0:j1] += 1
         else:
+            assert cnt <= (B.LORA_EXPAND_MFMA_TOKENS if path == B.LORA_PATH_MFMA else B.LORA_EXPAND_GATHER_TOKENS)
             cols = B.LORA_EXPAND_MFMA_COLS if path == B.LORA_PATH_MFMA else B.LORA_EXPAND_GATHER_COLS
             c0, c1 = blk * cols, min(dim, (blk + 1) * cols)
             assert c0 < dim
@@ -170,6 +171,35 @@ def test_plan_path_choice_and_order():
     items = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, 3, 16, B.LORA_PATH_GATHER,
                              host_rank=np.array([8, 16, 16], np.int32))
     assert sorted(int(b) for _, a, _, b in items if a == 0) == [0, 1]
+
+
+def test_expand_mfma_token_tile():
+    """MFMA expand items take 128 tokens for output widths nearest 8192 of the
+    measured widths (1024, 4096, 8192, 14336, 28672) while the plan then still
+    holds >= 256 MFMA items, else 64; every (token, column) stays covered once
+    either way."""
+    def plan(lens, d_out):
+        starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        adapters = np.arange(len(lens), dtype=np.int32)
+        items = B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, starts, adapters, len(lens), d_out)
+        cov = _coverage(items, starts, adapters, np.full(len(lens), 16), d_out, B.LORA_PHASE_EXPAND)
+        assert np.all(cov == 1)
+        m = items[(items[:, 2] >> 16) == B.LORA_PATH_MFMA]
+        return int((m[:, 2] & 0xFFFF).max()), len(m)
+    # the 70B layer's batch: 255 one-token requests and one of 1025 tokens
+    lens = [1] * 255 + [1025]
+    assert plan(lens, 8192) == (128, 9 * 32)     # q, o, down
+    assert plan(lens, 1024) == (64, 17 * 4)      # k, v: 9 x 4 = 36 long items would not fill the device
+    assert plan(lens, 28672) == (64, 17 * 112)   # gate, up
+    assert plan(lens, 4096) == (64, 17 * 16)
+    assert plan(lens, 14336) == (64, 17 * 56)
+    assert plan(lens, 10240) == (128, 9 * 40)    # nearest measured width 8192
+    assert plan(lens, 12288) == (64, 17 * 48)    # nearest 14336
+    # the item threshold: 8 x 32 = 256 long items, 7 x 32 = 224
+    assert plan([1024], 8192) == (128, 256)
+    assert plan([1000], 8192) == (128, 256)
+    assert plan([896], 8192) == (64, 14 * 32)
+    assert plan([896, 100], 8192)[0] == 128     # (7 + 1) x 32
 
 
 def test_plan_errors():
