@@ -99,6 +99,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="bound on each workload's one-thread oracle time (0 disables the CPU baseline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the LLC")
+    ap.add_argument("--expand-tile", type=int, default=0, choices=(0, 64, 128),
+                    help="MFMA token tile of the expand plans (0 = the library's width table)")
     ap.add_argument("--churn", type=int, default=0, metavar="POOL_ADAPTERS",
                     help="adapter churn: decode batches over 1024 adapters through an LRU cache "
                          "whose pools hold POOL_ADAPTERS rank-16 adapters (uploads timed in)")
@@ -501,7 +503,7 @@ def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
             _, _, _, perm_d = dp.segments()
             if not hasattr(one, "_bench_plans"):
                 one._bench_plans = (dp.plan(B.LORA_PHASE_SHRINK, args.policy, mfma_min),
-                                    dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min),
+                                    dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min, args.expand_tile),
                                     dp.plan_tiled(args.policy, args.tile_min, args.max_splits) if tiled else None)
             sp, ep, tp = one._bench_plans
             if tiled:
@@ -563,6 +565,7 @@ def run_config(args, torch, cfg: int, shape: str = "q", wq: str = ""):
                    "mode": mode, "path": ("fused" if fused else "shrink+expand"),
                    "placement": (args.placement if fused else None),
                    "mfma_min_tokens": (mfma_min if mode == "sgmv" else None),
+                   "expand_tile": ((args.expand_tile or "width table") if mode == "sgmv" else None),
                    "shrink": ((f"tiled: 64-token tiles, {one._bench_plans[2][1]} d_in slices" if tiled
                                else "one launch") if mode == "sgmv" else None),
                    "replicas": n_rep, "timed": "HIP graph replay of the K steps",
@@ -636,7 +639,7 @@ def run_layer(args, torch):
             base()
         _, _, _, perm_d = dp.segments()
         sp = dp.plan(B.LORA_PHASE_SHRINK, args.policy, mfma_min)
-        ep = dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min)
+        ep = dp.plan(B.LORA_PHASE_EXPAND, args.policy, mfma_min, args.expand_tile)
         use_tiled = args.shrink == "tiled" or (args.shrink == "auto" and dp.tiled_pays(args.tile_min))
         tp = dp.plan_tiled(args.policy, args.tile_min, args.max_splits) if use_tiled else None
         sb = acc.shrink_bytes(p.ids, p.ranks, p.d_in, 2)
@@ -725,6 +728,7 @@ def run_layer(args, torch):
         "config": {"workload": LAYER_WORKLOAD, "tokens": tokens, "adapters": 256, "ranks": [16],
                    "projections": [q["name"] for q in projs], "mode": "sgmv",
                    "mfma_min_tokens": mfma_min,
+                   "expand_tile": args.expand_tile or "width table",
                    "shrink": sorted(set(q["shrink"] for q in projs)),
                    "timed": "HIP graph replay of K layer deltas (7 projections x shrink + expand)",
                    "streams": " then ".join("|".join(g) for g in groups),

@@ -190,6 +190,18 @@ lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
                            int32_t num_adapters, const int32_t *host_rank, int32_t dim,
                            int32_t path_policy, int32_t mfma_min_tokens, lora_item *items,
                            int32_t capacity, int32_t *num_items);
+/* lora_sgmv_plan with the expand's MFMA token tile given: expand_tile_tokens
+ * 0 takes the width table above (what lora_sgmv_plan does), 64 or
+ * LORA_EXPAND_MFMA_TOKENS forces that tile (a shrink plan ignores it); for
+ * other devices or shapes, and to reproduce the table's measurements.  The
+ * kernels give every token the same bits under either tile.  Errors as
+ * lora_sgmv_plan, and LORA_EINVAL for another expand_tile_tokens.          */
+lora_status lora_sgmv_plan_tile(int32_t phase, const int32_t *seg_starts,
+                                const int32_t *seg_adapter, int32_t num_segments,
+                                int32_t num_adapters, const int32_t *host_rank, int32_t dim,
+                                int32_t path_policy, int32_t mfma_min_tokens,
+                                int32_t expand_tile_tokens, lora_item *items, int32_t capacity,
+                                int32_t *num_items);
 
 /* ------------------------------------------------------------------------ */
 /* Adapter weights as the kernels read them (the adapter-row gather through the

@@ -76,6 +76,7 @@ EXPORTS = {
     "lora_status_name": ([_I32], ctypes.c_char_p),
     "lora_segments_build": ([_P, _I32, _I32, _P, _P, _P, _P], _I32),
     "lora_sgmv_plan": ([_I32, _P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I32, _P], _I32),
+    "lora_sgmv_plan_tile": ([_I32, _P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _P], _I32),
     "lora_sgmv_shrink": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_sgmv_expand": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _P], _I32),
     "lora_sgmv_plan_tiled": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
@@ -192,20 +193,24 @@ def lora_segments_build(token_adapter, num_adapters: int):
 def lora_sgmv_plan(phase: int, seg_starts, seg_adapter, num_adapters: int, dim: int,
                    path_policy: int = LORA_PATH_AUTO,
                    mfma_min_tokens: int = LORA_DEFAULT_MFMA_MIN_TOKENS,
-                   host_rank=None) -> np.ndarray:
+                   host_rank=None, expand_tile_tokens: int = 0) -> np.ndarray:
     """Work plan as an int32 array [num_items, 4] (perm_begin, adapter, count|path<<16, block).
-    dim: r_max for a shrink plan, d_out for an expand plan."""
+    dim: r_max for a shrink plan, d_out for an expand plan.  expand_tile_tokens:
+    0 = the library's width table (lora_sgmv_plan), 64 or 128 = that MFMA
+    expand tile (lora_sgmv_plan_tile)."""
     starts, adapters = _i32(seg_starts), _i32(seg_adapter)
     ranks = None if host_rank is None else _i32(host_rank)
     s = adapters.size
     n = ctypes.c_int32(0)
-    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters,
-                                _np_ptr(ranks), dim, path_policy, mfma_min_tokens, None, 0,
-                                ctypes.byref(n)))
+    head = (phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters, _np_ptr(ranks), dim, path_policy,
+            mfma_min_tokens)
+    if expand_tile_tokens:
+        call = lambda *tail: lib().lora_sgmv_plan_tile(*head, int(expand_tile_tokens), *tail)
+    else:
+        call = lambda *tail: lib().lora_sgmv_plan(*head, *tail)
+    _check(call(None, 0, ctypes.byref(n)))
     items = np.zeros((max(n.value, 1), 4), np.int32)
-    _check(lib().lora_sgmv_plan(phase, _np_ptr(starts), _np_ptr(adapters), s, num_adapters,
-                                _np_ptr(ranks), dim, path_policy, mfma_min_tokens, _np_ptr(items),
-                                n.value, ctypes.byref(n)))
+    _check(call(_np_ptr(items), n.value, ctypes.byref(n)))
     return items[: n.value]
 
 

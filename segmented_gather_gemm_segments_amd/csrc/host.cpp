@@ -144,7 +144,20 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
                                       int32_t num_adapters, const int32_t *host_rank, int32_t dim,
                                       int32_t path_policy, int32_t mfma_min_tokens,
                                       lora_item *items, int32_t capacity, int32_t *num_items) {
+  return lora_sgmv_plan_tile(phase, seg_starts, seg_adapter, num_segments, num_adapters, host_rank, dim,
+                             path_policy, mfma_min_tokens, 0, items, capacity, num_items);
+}
+
+extern "C" lora_status lora_sgmv_plan_tile(int32_t phase, const int32_t *seg_starts,
+                                           const int32_t *seg_adapter, int32_t num_segments,
+                                           int32_t num_adapters, const int32_t *host_rank, int32_t dim,
+                                           int32_t path_policy, int32_t mfma_min_tokens,
+                                           int32_t expand_tile_tokens, lora_item *items, int32_t capacity,
+                                           int32_t *num_items) {
   if (!num_items) return fail(LORA_EINVAL, "null num_items");
+  if (expand_tile_tokens != 0 && expand_tile_tokens != 64 && expand_tile_tokens != LORA_EXPAND_MFMA_TOKENS)
+    return fail(LORA_EINVAL, "expand_tile_tokens must be 0, 64 or %d (got %d)", LORA_EXPAND_MFMA_TOKENS,
+                expand_tile_tokens);
   if (phase != LORA_PHASE_SHRINK && phase != LORA_PHASE_EXPAND)
     return fail(LORA_EINVAL, "unknown phase %d", phase);
   if (path_policy < LORA_PATH_AUTO || path_policy > LORA_PATH_MFMA)
@@ -175,12 +188,13 @@ extern "C" lora_status lora_sgmv_plan(int32_t phase, const int32_t *seg_starts,
   auto is_mfma = [&](int32_t len) {
     return path_policy == LORA_PATH_MFMA || (path_policy == LORA_PATH_AUTO && len >= mfma_min_tokens);
   };
-  // Token tile of the expand's MFMA items: LORA_EXPAND_MFMA_TOKENS (two
-  // 64-token passes in one workgroup) where the output width's nearest entry
-  // of kExpandTileByWidth says so and such items still number at least
-  // LORA_EXPAND_LONG_TILE_MIN_ITEMS; 64 tokens otherwise.
-  int32_t expand_mfma_step = 64;
-  if (phase == LORA_PHASE_EXPAND && expand_tile_by_width(dim) == LORA_EXPAND_MFMA_TOKENS) {
+  // Token tile of the expand's MFMA items: the caller's expand_tile_tokens,
+  // or (0) LORA_EXPAND_MFMA_TOKENS (two 64-token passes in one workgroup)
+  // where the output width's nearest entry of kExpandTileByWidth says so and
+  // such items still number at least LORA_EXPAND_LONG_TILE_MIN_ITEMS, else 64.
+  int32_t expand_mfma_step = expand_tile_tokens ? expand_tile_tokens : 64;
+  if (phase == LORA_PHASE_EXPAND && expand_tile_tokens == 0 &&
+      expand_tile_by_width(dim) == LORA_EXPAND_MFMA_TOKENS) {
     const int64_t nblk = (dim + LORA_EXPAND_MFMA_COLS - 1) / LORA_EXPAND_MFMA_COLS;
     int64_t long_items = 0;
     for (int32_t s = 0; s < num_segments; ++s) {

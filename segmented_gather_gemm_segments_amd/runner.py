@@ -198,12 +198,13 @@ class DeviceProblem:
         return self._seg
 
     def plan(self, phase: int, policy: int = B.LORA_PATH_AUTO,
-             mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS):
+             mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS, expand_tile_tokens: int = 0):
         torch = _torch()
         _, starts, adapters, _ = self.segments()
         dim = self.r_max if phase == B.LORA_PHASE_SHRINK else self.p.d_out
         items = B.lora_sgmv_plan(phase, starts, adapters, self.p.num_adapters, dim, policy,
-                                 mfma_min_tokens, host_rank=self.p.ranks.astype(np.int32))
+                                 mfma_min_tokens, host_rank=self.p.ranks.astype(np.int32),
+                                 expand_tile_tokens=expand_tile_tokens)
         return torch.from_numpy(np.ascontiguousarray(items)).to(self.device)
 
     def tiled_pays(self, tile_min_tokens: int = 0) -> bool:
@@ -232,11 +233,13 @@ class DeviceProblem:
 
     def run_sgmv(self, policy: int = B.LORA_PATH_AUTO,
                  mfma_min_tokens: int = B.LORA_DEFAULT_MFMA_MIN_TOKENS, y=None, v=None,
-                 tiled: bool = False, tile_min_tokens: int = 0, max_splits: int = 0):
+                 tiled: bool = False, tile_min_tokens: int = 0, max_splits: int = 0,
+                 expand_tile_tokens: int = 0):
         """shrink then expand over the segmented batch; returns (y, v).
-        tiled: the tiled shrink (its own plan, threshold and workspace)."""
+        tiled: the tiled shrink (its own plan, threshold and workspace);
+        expand_tile_tokens: the expand plan's MFMA token tile (0: the library's)."""
         _, _, _, perm_d = self.segments()
-        ep = self.plan(B.LORA_PHASE_EXPAND, policy, mfma_min_tokens)
+        ep = self.plan(B.LORA_PHASE_EXPAND, policy, mfma_min_tokens, expand_tile_tokens)
         y = self.y0.clone() if y is None else y
         v = self.new_v() if v is None else v
         if tiled:

@@ -74,6 +74,19 @@ static void segments_and_plans(std::mt19937 &rng) {
           const int32_t cnt = items[(size_t)i].count_path & 0xffff;
           CHECK(cnt == 0 || (items[(size_t)i].perm_begin + cnt <= starts[(size_t)ns]));
         }
+      // the same plan with a given expand tile, and a rejected one
+      const int32_t tiles[4] = {0, 64, LORA_EXPAND_MFMA_TOKENS, 96};
+      const int32_t tile = tiles[rng() % 4];
+      int32_t count3 = -1;
+      s = lora_sgmv_plan_tile(phase, starts.data(), seg.data(), ns, n_adapters, ranks.data(), dim, policy,
+                              mfma_min, tile, nullptr, 0, &count3);
+      CHECK(tile == 96 ? s == LORA_EINVAL : (s == LORA_OK && count3 >= 0));
+      if (s == LORA_OK) {
+        std::vector<lora_item> it3((size_t)count3 + 1);
+        s = lora_sgmv_plan_tile(phase, starts.data(), seg.data(), ns, n_adapters, ranks.data(), dim, policy,
+                                mfma_min, tile, it3.data(), count3, &count3);
+        CHECK(s == LORA_OK);
+      }
     }
   // the tiled planner, its workspace query and the tiled-or-plain choice
   const int32_t d_in = 64 * (int32_t)(rng() % 500) + (rng() % 8 == 0 ? 8 : 0);  // sometimes not a multiple

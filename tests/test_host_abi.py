@@ -202,6 +202,38 @@ def test_expand_mfma_token_tile():
     assert plan([896, 100], 8192)[0] == 128     # (7 + 1) x 32
 
 
+@pytest.mark.parametrize("tile", [64, 128])
+def test_expand_tile_forced(tile):
+    """lora_sgmv_plan_tile with a given MFMA expand tile: every MFMA item of a
+    long segment but its last holds exactly `tile` tokens, the coverage holds,
+    a shrink plan is unchanged, and other tiles are rejected."""
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        n = int(rng.integers(1, 12))
+        ids = rng.integers(-1, n, size=int(rng.integers(1, 900))).astype(np.int32)
+        perm, starts, adapters = B.lora_segments_build(ids, n)
+        if adapters.size == 0:
+            continue
+        ranks = rng.integers(1, 65, size=n).astype(np.int32)
+        d_out = int(rng.integers(1, 300)) * 8
+        items = B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, starts, adapters, n, d_out, expand_tile_tokens=tile)
+        assert np.all(_coverage(items, starts, adapters, ranks, d_out, B.LORA_PHASE_EXPAND) == 1)
+        for pb, a, cp, blk in items:
+            cnt, path = cp & 0xFFFF, cp >> 16
+            if path == B.LORA_PATH_MFMA:
+                s = int(np.searchsorted(starts, pb, side="right")) - 1
+                assert cnt == min(tile, int(starts[s + 1]) - pb) and (pb - int(starts[s])) % tile == 0
+        sh = B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, n, int(ranks.max()), host_rank=ranks,
+                              expand_tile_tokens=tile)
+        assert np.array_equal(sh, B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, starts, adapters, n, int(ranks.max()),
+                                                   host_rank=ranks))
+    for bad in (32, 96, 256, -64):
+        with pytest.raises(B.LoraError) as e:
+            B.lora_sgmv_plan(B.LORA_PHASE_EXPAND, np.array([0, 300], np.int32), np.array([0], np.int32), 1, 1024,
+                             expand_tile_tokens=bad)
+        assert e.value.status == B.LORA_EINVAL
+
+
 def test_plan_errors():
     with pytest.raises(B.LoraError) as e:
         B.lora_sgmv_plan(B.LORA_PHASE_SHRINK, np.array([0, 2], np.int32), np.array([7], np.int32), 3, 16)

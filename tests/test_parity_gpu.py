@@ -311,6 +311,35 @@ def test_repeat_runs_bit_identical():
     assert torch.equal(outs[5], outs[6])
 
 
+@pytest.mark.parametrize("layout", ["dense", "paged"])
+@pytest.mark.parametrize("dtype,wq", [("bf16", ""), ("bf16", "fp8"), ("f32", "")])
+def test_expand_tiles_bit_identical(layout, dtype, wq):
+    """MFMA expand items of 64 and of 128 tokens (two passes per workgroup)
+    give every token the same bits, and both match the oracle: segments of
+    1..300 tokens (several 128-token items, ragged last ones), ranks 8..72
+    (one- and two-chunk ranks), d_out ragged against the 256-column blocks."""
+    R = runner()
+    lens = [300, 1, 128, 129, 64, 65, 17, 3, 200, 16]
+    p = wl.make_problem(f"exp_tiles_{dtype}{wq}_{layout}", lens, [i % 5 for i in range(len(lens))],
+                        [8, 16, 40, 64, 72], 512, 1288, dtype, 61, paged=layout == "paged", page_rows=16, wq=wq)
+    dp = R.DeviceProblem(p, layout=layout)
+    say(f"expand tiles 64 / 128 {dtype}{wq} {layout}")
+    _, _, _, perm_d = dp.segments()
+    v = dp.new_v()
+    B.lora_sgmv_shrink(dp.weights, perm_d, dp.plan(B.LORA_PHASE_SHRINK), dp.x, v)
+    ys = {}
+    for tile in (64, 128):
+        ep = dp.plan(B.LORA_PHASE_EXPAND, expand_tile_tokens=tile)
+        cnt = (ep[:, 2] & 0xFFFF)[(ep[:, 2] >> 16) == B.LORA_PATH_MFMA]
+        assert int(cnt.max()) == tile
+        ys[tile] = dp.y0.clone()
+        B.lora_sgmv_expand(dp.weights, perm_d, ep, v, ys[tile])
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(ys[64].view(bits), ys[128].view(bits))
+    check_y(dp, ys[128], oracle_y(p), f"expand tile 128 {dtype}{wq} {layout}")
+
+
 @pytest.mark.parametrize("case", ["one_token", "all_single", "one_segment", "ragged_d", "none_ids",
                                   "unused_adapters", "rank128", "odd_ranks"])
 def test_edge_cases(case):
