@@ -113,6 +113,9 @@ def parse():
     ap.add_argument("--warm", action="store_true",
                     help="also time every kernel warm: K launches on one replica, its operands left in "
                          "cache by the previous launch (the default timings are all cold)")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="the fused decode launch on decode batches of 32 .. 256 tokens (one workgroup per "
+                         "token): how one workgroup's pass times against the number of workgroups")
     ap.add_argument("--floor", action="store_true",
                     help="only time bare streaming reads and a read-modify-write of given sizes "
                          "and workgroup counts (the device's floors for launches of that size)")
@@ -770,6 +773,35 @@ def run_layer(args, torch):
     return out
 
 
+def run_decode_sweep(args, torch):
+    """The fused decode launch (grouped placement, cold replicas) on the decode
+    batch's shape with 32 .. 256 tokens over 128 adapters: with one workgroup
+    per token, the time at few tokens is one workgroup's own pass."""
+    from segmented_gather_gemm_segments_amd import accounting as acc
+    from segmented_gather_gemm_segments_amd import binding as B
+    from segmented_gather_gemm_segments_amd import runner as R
+    from segmented_gather_gemm_segments_amd import workloads as wl
+
+    stream = torch.cuda.Stream()
+    K = args.steps
+    rows = []
+    for n in (32, 64, 128, 192, 256):
+        p = wl.bgmv_decode(num_tokens=n)
+        nb = acc.fused_bytes(p.ids, p.ranks, p.d_in, p.d_out, 2, p.wq)
+        n_rep = n_replicas(args, nb)
+        one = R.DeviceProblem(p)
+        reps = [one] + [one.replica() for _ in range(n_rep - 1)]
+        calls = [B.prepare_bgmv_fused(dp.weights, dp.ids, dp.x, dp.y0.clone(), None, B.LORA_BGMV_AUTO,
+                                      stream=stream, token_order=dp.segments()[3]) for dp in reps]
+        torch.cuda.synchronize()
+        t = graph_span(torch, stream, [calls[i % n_rep] for i in range(K)], 3)
+        rows.append({"tokens": n, "adapters_used": int(np.unique(p.ids).size), "us": round(t * 1e6, 3),
+                     "algorithmic_bytes": int(nb), "replicas": n_rep})
+        del reps, calls, one
+        torch.cuda.empty_cache()
+    print(json.dumps({"decode_sweep": rows, "steps": K, "kernel_sources_sha256_16": kernel_hash()}), flush=True)
+
+
 def run_floor(args, torch):
     """Bare streaming reads (the library's probe kernel) and a torch
     read-modify-write, each rotating over buffers totalling more than twice the
@@ -847,6 +879,8 @@ def main():
     B.lib()
     if args.floor:
         return run_floor(args, torch)
+    if args.decode_sweep:
+        return run_decode_sweep(args, torch)
     if args.churn > 0:
         return bench_churn(args, torch)
     if args.multi:
