@@ -839,6 +839,21 @@ def run_floor(args, torch):
         table.append({"launch": label, "bytes": size, "us": round(t * 1e6, 3),
                       "gbs": round(size / t / 1e9, 1), "frac_of_peak": round(size / t / 1e9 / HBM_PEAK_GBS, 4)})
         del buf, fns
+    # a device-scope release per workgroup (what a reduction across the
+    # workgroups of one launch needs), against the same launch without it
+    for pairs in (128, 256):
+        part = torch.empty(2 * pairs * 64, dtype=torch.float32, device="cuda")
+        out = torch.empty(pairs * 64, dtype=torch.float32, device="cuda")
+        cnt = torch.zeros(pairs, dtype=torch.int32, device="cuda")
+        t = {}
+        for fence in (False, True):
+            fn = B.prepare_probe_release(pairs, fence, part, cnt, out, stream)
+            t[fence] = graph_span(torch, stream, [fn] * K, 3)
+        table.append({"launch": f"{2 * pairs} workgroups, each a device-scope release and an atomic "
+                                f"(the last of each pair adds both)", "bytes": 0, "us": round(t[True] * 1e6, 3),
+                      "us_without_release": round(t[False] * 1e6, 3),
+                      "us_per_release": round((t[True] - t[False]) * 1e6 / (2 * pairs), 4)})
+        del part, out, cnt
     for mib in (64, 224):
         n = mib * 2**20 // 2
         n_rep = int(max(2, np.ceil(2 * LLC_BYTES / (2 * n))))

@@ -105,6 +105,7 @@ EXPORTS = {
     "lora_base_gemm_workspace": ([_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int64)], _I32),
     "lora_base_gemm_noalloc": ([_I32, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "lora_probe_stream_read": ([_P, ctypes.c_int64, _I32, _I32, _I32, _P, _P], _I32),
+    "lora_probe_release": ([_I32, _I32, _P, _P, _P, _P], _I32),
     "lora_debug_flags": ([_P, _I32], _I32),
 }
 LORA_DEBUG_BAD_PAGE, LORA_DEBUG_BAD_ADAPTER, LORA_DEBUG_BAD_RANK = 1, 2, 4
@@ -552,6 +553,16 @@ def prepare_probe_stream_read(src, bytes_per_group: int, groups: int, threads: i
     assert sink.numel() * sink.element_size() >= 4 * groups
     return Prepared("lora_probe_stream_read", (_dptr(src), int(bytes_per_group), int(groups), int(threads),
                                                int(bool(nontemporal)), _dptr(sink), _stream(stream)), (src, sink))
+
+
+def prepare_probe_release(pairs: int, fence: bool, part, counters, out, stream=None):
+    """Prepared release-per-workgroup probe (a measurement, not the delta path);
+    counters must start at zero (every call leaves them zero)."""
+    assert part.numel() * part.element_size() >= 2 * pairs * 64 * 4
+    assert out.numel() * out.element_size() >= pairs * 64 * 4
+    assert counters.numel() * counters.element_size() >= pairs * 4
+    return Prepared("lora_probe_release", (int(pairs), int(bool(fence)), _dptr(part), _dptr(counters), _dptr(out),
+                                           _stream(stream)), (part, counters, out))
 
 
 # ---------------------------------------------------------------- prepared launches

@@ -47,7 +47,51 @@ __global__ __launch_bounds__(1024) void stream_read_kernel(const uint4 *__restri
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
+// The cost of a device-scope release per workgroup (the pattern a reduction
+// across workgroups of one launch needs): workgroup b of 2 * pairs writes 64
+// values; with FENCE it then releases them at device scope, counts itself on
+// its pair's counter, and the pair's second arriver acquires and adds both
+// workgroups' values in a fixed order, then puts the counter back to zero so
+// that the next launch starts from zero.  Nothing waits on another workgroup.
+template <bool FENCE>
+__global__ __launch_bounds__(256) void release_pair_kernel(float *__restrict__ part, unsigned *__restrict__ cnt,
+                                                           float *__restrict__ out) {
+  const int b = blockIdx.x, tid = threadIdx.x, pair = b >> 1;
+  float acc = 0.f;
+  for (int i = 0; i < 64; ++i) acc = fmaf(acc, 1.0001f, (float)(tid + i));
+  if (tid < 64) part[(size_t)b * 64 + tid] = acc;
+  if constexpr (FENCE) {
+    __shared__ unsigned arrived;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) arrived = atomicAdd(&cnt[pair], 1u);
+    __syncthreads();
+    if (arrived == 1u) {
+      __threadfence();
+      if (tid < 64) out[(size_t)pair * 64 + tid] = part[(size_t)(2 * pair) * 64 + tid] +
+                                                    part[(size_t)(2 * pair + 1) * 64 + tid];
+      if (tid == 0) atomicExch(&cnt[pair], 0u);
+    }
+  }
+}
+
 }  // namespace
+
+extern "C" lora_status lora_probe_release(int32_t pairs, int32_t fence, float *part, uint32_t *counters,
+                                          float *out, hipStream_t stream) {
+  if (pairs < 0) return fail(LORA_EINVAL, "negative pairs");
+  if (fence != 0 && fence != 1) return fail(LORA_EINVAL, "fence must be 0 or 1");
+  if (pairs == 0) return ok();
+  if (!part || !counters || !out) return fail(LORA_EINVAL, "null pointer");
+  if (pairs > (1 << 20)) return fail(LORA_EINVAL, "more than 2^20 pairs");
+  if (fence)
+    hipLaunchKernelGGL(release_pair_kernel<true>, dim3(2 * pairs), dim3(256), 0, stream, part, counters, out);
+  else
+    hipLaunchKernelGGL(release_pair_kernel<false>, dim3(2 * pairs), dim3(256), 0, stream, part, counters, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
 
 extern "C" lora_status lora_probe_stream_read(const void *src, int64_t bytes_per_group, int32_t groups,
                                               int32_t threads, int32_t nontemporal, uint32_t *sink,
