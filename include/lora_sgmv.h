@@ -593,17 +593,6 @@ lora_status lora_debug_flags(uint32_t *flags, int32_t clear);
 lora_status lora_probe_stream_read(const void *src, int64_t bytes_per_group, int32_t groups,
                                    int32_t threads, int32_t nontemporal, uint32_t *sink,
                                    hipStream_t stream);
-/* Measurement helper, not part of the delta path: 2 * pairs workgroups each
- * write 64 floats to part [2 * pairs * 64]; with fence = 1 each then makes a
- * device-scope release and counts itself on counters[pair] [pairs], and the
- * second of each pair acquires and writes the sum of both to out
- * [pairs * 64], resetting its counter to 0 (fence = 0: the writes only).
- * counters must hold zeros before the first call; every call leaves them
- * zero.  Calls that overlap race on the counters.  The benchmark times both to
- * price a release per workgroup, what a reduction across the workgroups of
- * one launch costs.  Errors: LORA_EINVAL, LORA_EHIP. */
-lora_status lora_probe_release(int32_t pairs, int32_t fence, float *part, uint32_t *counters, float *out,
-                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ DEBUG_LIB = os.path.join(HERE, "liblora_sgmv_debug.so")
 SOURCES = [os.path.join(HERE, "csrc", "host.cpp"), os.path.join(HERE, "csrc", "kernels.hip"),
            os.path.join(HERE, "csrc", "base_gemm.hip"), os.path.join(HERE, "csrc", "residency.hip"),
            os.path.join(HERE, "csrc", "probe.hip")]
-HEADERS = [os.path.join(ROOT, "include", "lora_sgmv.h"),
+HEADERS = [os.path.join(ROOT, "include", "lora_sgmv.h"), os.path.join(ROOT, "include", "lora_probe.h"),
            os.path.join(HERE, "csrc", "lora_internal.h")]
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

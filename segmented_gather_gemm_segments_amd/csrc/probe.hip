@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "lora_internal.h"
+#include "lora_probe.h"
 
 using namespace lora;
 

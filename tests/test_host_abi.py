@@ -23,9 +23,14 @@ def built_lib():
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "lora_sgmv.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", src)))
+    """Every function declared in include/*.h."""
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
